@@ -1,0 +1,207 @@
+"""Benchmark: cyclic-prefill tokens/s per pass (1.3B-scale WhiteMatter model,
+L=28 D=1792 14/2 heads x 128, FFN 4864, k=14, p=2, V=32768, B=64, T=2048,
+g=16) and decode tokens/s (L=16 D=512 8/4 x 64, k=16, B=64, 2047 cached
+positions) on one GPU, with the dominant kernel's roofline fraction and the
+oracle timed on the host cores.
+
+A step is one cyclic Gauss-Seidel prefill pass over the whole batch; the
+first (warmup) pass starts from the zero cache and later passes refine it,
+as in a 1 + 2 pass prefill. Prints one JSON line.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def profile(kinds_mask):
+    from decode_token_rmsnorm_amd import _lib as C
+    C.check("wm_profile_begin", C.lib().wm_profile_begin(kinds_mask))
+
+
+def profile_read():
+    from decode_token_rmsnorm_amd import _lib as C
+    n = len(C.KINDS)
+    counts = (ctypes.c_int64 * n)()
+    ms = (ctypes.c_double * n)()
+    C.check("wm_profile_read", C.lib().wm_profile_read(counts, ms))
+    C.lib().wm_profile_end()
+    return {k: (counts[i], ms[i]) for i, k in enumerate(C.KINDS) if counts[i]}
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from wm_inputs import WORKLOADS, make_tokens, make_weights
+
+    w = WORKLOADS["prefill_1p3b"]
+    t0 = time.time()
+    W = make_weights(w, seed=0)
+    log(f"[prefill] weights generated in {time.time() - t0:.1f}s")
+    model = wm.Model(w, W, "bf16")
+    del W
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    cache = wm.new_cache(model, w.B)
+    rows = wm.prefill_rows(w.B, w.T, w.g)
+    ws = model.workspace(rows)
+    logits = torch.empty(w.B, w.V, dtype=torch.float32, device="cuda")
+    for i in range(warmup):
+        wm.cyclic_prefill_pass(model, tok, w.g, cache, 1, logits, ws)
+        torch.cuda.synchronize()
+        log(f"[prefill] warmup pass {i + 1} done")
+    from decode_token_rmsnorm_amd import _lib as C
+    profile(1 << C.KINDS.index("gateup") | 1 << C.KINDS.index("attn") | 1 << C.KINDS.index("qproj")
+            | 1 << C.KINDS.index("oproj") | 1 << C.KINDS.index("down"))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        wm.cyclic_prefill_pass(model, tok, w.g, cache, 1, logits, ws)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_pass = [a.elapsed_time(b) for a, b in evs]
+    prof = profile_read()
+    log(f"[prefill] {steps} passes in {wall:.3f}s: {per_pass}")
+    assert torch.isfinite(logits).all(), "non-finite logits"
+    n_ga, ms_ga = prof["gateup"]
+    flops_ga = 2.0 * rows * (2 * w.F) * w.D
+    kern = {k: {"launches": c, "avg_us": 1e3 * m / c} for k, (c, m) in prof.items()}
+    res = {
+        "wall_s": wall, "per_pass_ms": per_pass, "rows_per_group": rows, "kernels": kern,
+        "roofline": {"kernel": "gateup (fused gate/up projection + SwiGLU GEMM)", "bound": "mfma",
+                     "achieved": flops_ga / (ms_ga / n_ga * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "traffic": None,
+                     "algorithmic_per_launch": f"{flops_ga:.4e} FLOP = 2*{rows}*{2 * w.F}*{w.D}"},
+    }
+    res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
+    # whole-pass MFMA fraction: algorithmic FLOP per pass / pass time
+    flop_pass = pass_flops(w)
+    res["pass_tflops"] = flop_pass / (wall / steps) / 1e12
+    res["pass_flop"] = flop_pass
+    del cache, ws, model
+    torch.cuda.empty_cache()
+    return w, res
+
+
+def pass_flops(w):
+    """Algorithmic FLOP of one cyclic pass (strict-causal triangle counted once)."""
+    T, B, L, D, F, k, R = w.T, w.B, w.L, w.D, w.F, w.k, w.R
+    qd, kvd = w.Hq * w.d, w.Hkv * w.d
+    per_tok = L * (2 * D * qd * 2 + 2 * D * 2 * F + 2 * F * D)      # Q, O, gate/up, down
+    per_tok += 2 * (2 * R * D * L * k) + 2 * (2 * k * L * D) + 2 * (2 * k * D * kvd)  # router, mix, K/V proj
+    attn = L * w.Hq * w.d * 4 * (T * (T - 1) / 2) / T                # QK^T + PV over s < i, per token
+    return B * T * (per_tok + attn)
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from wm_inputs import WORKLOADS, make_cache_device, make_tokens, make_weights
+
+    w = WORKLOADS["decode_d512"]
+    t = 2047
+    W = make_weights(w, seed=0)
+    model = wm.Model(w, W, "bf16")
+    K, V = make_cache_device(w, w.B, filled=t, seed=3)
+    cache = wm.Cache(K, V)
+    tok = torch.from_numpy(make_tokens(w, seed=1, B=w.B, T=1)[:, 0].copy()).cuda()
+    ws = model.workspace(w.B)
+    logits = torch.empty(w.B, w.V, dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        wm.decode_step(model, tok, t, cache, logits, ws)
+    from decode_token_rmsnorm_amd import _lib as C
+    profile(1 << C.KINDS.index("attn"))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wm.decode_step(model, tok, t, cache, logits, ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = profile_read()
+    n_at, ms_at = prof["attn"]
+    kv_bytes = 2.0 * w.B * w.Hkv * t * w.d * 2  # K and V of one channel, bf16, per layer launch
+    ach = kv_bytes / (ms_at / n_at * 1e-3) / 1e9
+    return {"workload": "decode_d512: L16 D512 Hq8 Hkv4 d64 F1536 k16 p2 V32768 B64, t=2047 cached, bf16",
+            "value": w.B * steps / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall / steps, "steps": steps,
+            "roofline": {"kernel": "attn (strict-causal channel attention, split keys)", "bound": "hbm",
+                         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                         "traffic": None,
+                         "algorithmic_per_launch": f"{kv_bytes:.4e} B = 2*{w.B}*{w.Hkv}*{t}*{w.d}*2"}}
+
+
+def cpu_baseline():
+    """The float64 oracle on a bounded sample of the prefill workload: the first
+    group step (q=0, 128 positions) of sequence 0 against the zero cache."""
+    import numpy as np
+    import oracle as O
+    from wm_inputs import WORKLOADS, make_tokens, make_weights
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    w = WORKLOADS["prefill_1p3b"]
+    M = O.Model(w, make_weights(w, seed=0))
+    tokens = make_tokens(w, seed=1)[:1]
+    cache = O.new_cache(w.replace(T_max=w.T), 1)
+    bidx, pos = O.tokset_rows(1, len(O.group_positions(w.T, w.g, 0)), 0, w.g)
+    t0 = time.perf_counter()
+    O.step(M, tokens, cache, bidx, pos, want_logits=False)
+    dt = time.perf_counter() - t0
+    return {"value": len(pos) / dt, "unit": "tokens/s/pass", "cores": threads, "kind": "oracle",
+            "sample": f"sequence 0, group q=0 ({len(pos)} positions) of the first pass, float64 numpy, {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the method's batch elements are independent "
+              "and would shard as pure data parallelism, which this build does not run.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    w, pre = bench_prefill(a.steps, a.warmup)
+    dec = None if a.skip_decode else bench_decode(a.decode_steps, 5)
+    cpu = None if a.no_cpu_baseline else cpu_baseline()
+    value = w.B * w.T / (pre["wall_s"] / a.steps)
+    line = {
+        "metric": "cyclic-prefill tokens/s per pass + decode tok/s (1 GPU); % HBM/MFMA peak",
+        "value": value, "unit": "tokens/s/pass", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": 1e3 * pre["wall_s"] / a.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, Zipf(1.1) tokens)",
+        "config": {"workload": "prefill_1p3b: L28 D1792 Hq14 Hkv2 d128 F4864 k14 p2 V32768, B64 T2048, cyclic g16",
+                   "global_batch": w.B, "seq_len": w.T, "groups": w.g, "parallelism": "single GPU"},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+        "per_pass_ms": pre["per_pass_ms"],
+        "pass_tflops": pre["pass_tflops"],
+        "pass_mfma_frac": pre["pass_tflops"] / BF16_PEAK_TFLOPS,
+        "kernels_avg_us": pre["kernels"],
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+"""Thin torch-facing wrappers over the C ABI (include/wm.h).
+
+torch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's kernels. Names follow the C entry points:
+``mix_kv``, ``channel_attn``, ``cyclic_prefill_pass``, ``decode_step``.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as C
+
+GAINS = {"final_norm", "attn_norm", "q_norm", "ffn_norm", "src_norm", "chan_norm", "k_norm"}
+
+
+def torch_dtype(dtype: str):
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+
+
+def make_config(shape, dtype: str) -> C.WmConfig:
+    """shape: any object with L, D, Hq, Hkv, d, F, k, p, V, T_max, eps, rope_base."""
+    return C.WmConfig(shape.L, shape.D, shape.Hq, shape.Hkv, shape.d, shape.F, shape.k, shape.p, shape.V,
+                      shape.T_max, shape.eps, shape.rope_base, C.WM_BF16 if dtype == "bf16" else C.WM_F32)
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+class Model:
+    """Device copies of the weights plus the config and RoPE tables.
+
+    ``weights`` maps the names of include/wm.h to host arrays (float32 holding
+    values representable in the workload's dtype); matrices are uploaded in
+    that dtype, gains as float32. Missing names stay NULL (a mix-only model).
+    """
+
+    def __init__(self, shape, weights: dict, dtype: str, device="cuda"):
+        self.shape, self.dtype, self.device = shape, dtype, torch.device(device)
+        self.cfg = make_config(shape, dtype)
+        C.check("wm_check_config", C.lib().wm_check_config(ctypes.byref(self.cfg)))
+        td = torch_dtype(dtype)
+        self.t = {}
+        for n, a in weights.items():
+            x = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+            self.t[n] = x.to(self.device, torch.float32 if n in GAINS else td).contiguous()
+        half = shape.d // 2
+        self.t["rope_cos"] = torch.empty(shape.T_max, half, dtype=torch.float32, device=self.device)
+        self.t["rope_sin"] = torch.empty(shape.T_max, half, dtype=torch.float32, device=self.device)
+        C.check("wm_rope_table", C.lib().wm_rope_table(ctypes.byref(self.cfg), self.t["rope_cos"].data_ptr(),
+                                                       self.t["rope_sin"].data_ptr(), _stream()))
+        self.w = C.WmWeights(*[_ptr(self.t.get(n)) for n in C.WEIGHT_FIELDS])
+
+    def workspace(self, rows: int) -> torch.Tensor:
+        n = C.lib().wm_workspace_bytes(ctypes.byref(self.cfg), rows)
+        if n == 0:
+            raise C.WmError("wm_workspace_bytes", -2)
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+
+@dataclass
+class Cache:
+    k: torch.Tensor
+    v: torch.Tensor
+
+    @property
+    def B(self) -> int:
+        return self.k.shape[1]
+
+    def c(self) -> C.WmCache:
+        return C.WmCache(self.k.data_ptr(), self.v.data_ptr(), self.B)
+
+
+def new_cache(model: Model, B: int, fill: float = 0.0) -> Cache:
+    s = model.shape
+    shape = (s.k, B, s.Hkv, s.T_max, s.d)
+    td = torch_dtype(model.dtype)
+    return Cache(torch.full(shape, fill, dtype=td, device=model.device),
+                 torch.full(shape, fill, dtype=td, device=model.device))
+
+
+def cache_from_host(model: Model, K: np.ndarray, V: np.ndarray) -> Cache:
+    td = torch_dtype(model.dtype)
+    return Cache(torch.from_numpy(np.ascontiguousarray(K, np.float32)).to(model.device, td),
+                 torch.from_numpy(np.ascontiguousarray(V, np.float32)).to(model.device, td))
+
+
+def _ws(model, ws, rows):
+    return model.workspace(rows) if ws is None else ws
+
+
+def mix_kv(model: Model, states: torch.Tensor, B: int, M: int, s0: int, s_step: int, cache: Cache, ws=None,
+           stream=None) -> None:
+    """Pool + append of the state stack ``states`` [L, B*M, D] (rows b*M + m at
+    position s0 + m*s_step) into ``cache``."""
+    ws = _ws(model, ws, B * M)
+    cc = cache.c()
+    C.check("wm_mix_kv", C.lib().wm_mix_kv(ctypes.byref(model.cfg), ctypes.byref(model.w), states.data_ptr(),
+                                           C.WmTokset(B, M, s0, s_step), ctypes.byref(cc), ws.data_ptr(),
+                                           ws.numel(), _stream(stream)))
+
+
+def channel_attn(model: Model, layer: int, q: torch.Tensor, B: int, M: int, s0: int, s_step: int, cache: Cache,
+                 out=None, ws=None, stream=None) -> torch.Tensor:
+    """Strict-causal attention of consumer layer ``layer`` for q [B*M, Hq, d]."""
+    s = model.shape
+    if out is None:
+        out = torch.empty(B * M, s.Hq * s.d, dtype=q.dtype, device=q.device)
+    ws = _ws(model, ws, B * M)
+    cc = cache.c()
+    C.check("wm_channel_attn", C.lib().wm_channel_attn(ctypes.byref(model.cfg), layer, q.data_ptr(),
+                                                       C.WmTokset(B, M, s0, s_step), ctypes.byref(cc),
+                                                       out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out
+
+
+def prefill_rows(B: int, T: int, g: int) -> int:
+    return B * (-(-T // g))
+
+
+def cyclic_prefill_pass(model: Model, tokens: torch.Tensor, g: int, cache: Cache, logits_mode: int = 0,
+                        logits=None, ws=None, stream=None):
+    """One cyclic Gauss-Seidel pass over tokens [B, T] (int32, device)."""
+    B, T = tokens.shape
+    if logits_mode and logits is None:
+        shape = (B, model.shape.V) if logits_mode == 1 else (B, T, model.shape.V)
+        logits = torch.empty(shape, dtype=torch.float32, device=tokens.device)
+    ws = _ws(model, ws, prefill_rows(B, T, g))
+    cc = cache.c()
+    C.check("wm_cyclic_prefill_pass",
+            C.lib().wm_cyclic_prefill_pass(ctypes.byref(model.cfg), ctypes.byref(model.w), tokens.data_ptr(), T, g,
+                                           ctypes.byref(cc), _ptr(logits), logits_mode, ws.data_ptr(), ws.numel(),
+                                           _stream(stream)))
+    return logits
+
+
+def decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits=None, ws=None, stream=None):
+    """One decode step: tokens [B] (int32, device) at position t."""
+    B = tokens.shape[0]
+    if logits is None:
+        logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)
+    ws = _ws(model, ws, B)
+    cc = cache.c()
+    C.check("wm_decode_step", C.lib().wm_decode_step(ctypes.byref(model.cfg), ctypes.byref(model.w),
+                                                     tokens.data_ptr(), t, ctypes.byref(cc), logits.data_ptr(),
+                                                     ws.data_ptr(), ws.numel(), _stream(stream)))
+    return logits

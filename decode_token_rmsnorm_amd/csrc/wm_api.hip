@@ -1,0 +1,442 @@
+// wm_api.hip — device entry points of the C ABI (include/wm.h): argument
+// checks, then the kernel sequence of each call on the caller's stream.
+#include "../../include/wm.h"
+#include "wm_attn.hpp"
+#include "wm_gemm.hpp"
+#include "wm_host.hpp"
+#include "wm_pool.hpp"
+
+#include <vector>
+
+namespace wm {
+
+// ------------------------------------------------------------ launch timing
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+struct ProfState {
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<ProfRec> recs;
+};
+static ProfState g_prof;
+
+static hipEvent_t prof_event() {
+  if (g_prof.used == g_prof.pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_prof.pool.push_back(e);
+  }
+  return g_prof.pool[g_prof.used++];
+}
+
+// Brackets the launches of one kernel kind with events while profiling.
+struct ProfScope {
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(int k, hipStream_t st) : kind(k), s(st) {
+    if (g_prof.mask & (1u << k)) {
+      a = prof_event();
+      b = prof_event();
+      if (a && b) hipEventRecord(a, s);
+    }
+  }
+  ~ProfScope() {
+    if (a && b) {
+      hipEventRecord(b, s);
+      g_prof.recs.push_back({kind, a, b});
+    }
+  }
+};
+
+#define WM_TRY(expr)                                                               \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess) {                                                        \
+      set_error("%s failed: %s", #expr, hipGetErrorString(e_));                    \
+      return WM_ERR_HIP;                                                           \
+    }                                                                              \
+  } while (0)
+
+#define WM_CHECK(cond, code, ...) \
+  do {                            \
+    if (!(cond)) {                \
+      set_error(__VA_ARGS__);     \
+      return code;                \
+    }                             \
+  } while (0)
+
+// Everything one call needs, resolved from the C structs.
+template <typename T> struct Run {
+  const wm_config &c;
+  const wm_weights *w;
+  const wm_cache *cache;
+  unsigned char *ws;
+  WsLayout lay;
+  hipStream_t s;
+  int R;
+  int rows_cap;  // rows the workspace was laid out for
+
+  Run(const wm_config &c_, const wm_weights *w_, const wm_cache *ca, void *ws_, int rows, hipStream_t st)
+      : c(c_), w(w_), cache(ca), ws((unsigned char *)ws_), lay(ws_layout(c_, rows)), s(st), R((c_.L + c_.p - 1) / c_.p),
+        rows_cap(rows) {}
+
+  template <typename P> P *at(size_t off) const { return (P *)(ws + off); }
+  T *Kch(int ch) const { return (T *)cache->k + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
+  T *Vch(int ch) const { return (T *)cache->v + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
+
+  // -------------------------------------------------------- channel attention
+  template <int DH> wm_status attn_dh(int layer, const T *q, wm_tokset ts, T *out) {
+    const int ch = layer % c.k, G = c.Hq / c.Hkv, rows = ts.B * ts.M;
+    const int rows_pair = ts.M * G;
+    const bool large = rows_pair >= 128;
+    const int rb = large ? 128 : 16, nw = large ? 4 : 1;
+    const int nrb = (rows_pair + rb - 1) / rb;
+    const int blocks = nrb * ts.B * c.Hkv;
+    int64_t kmax = (int64_t)ts.s0 + (int64_t)(ts.M - 1) * ts.s_step;
+    if (kmax > c.T_max) kmax = c.T_max;
+    const int ntile = (int)((kmax + AKT - 1) / AKT);
+    const int64_t target = large ? 2048 : 4096;  // waves in flight
+    int ns = 1;
+    while ((int64_t)blocks * nw * ns < target && ns * 2 <= 16 && ntile / (ns * 2) >= 2 &&
+           (int64_t)(ns * 2) * rows <= part_rows_cap(rows_cap))
+      ns *= 2;
+    AttnArgs a;
+    a.q = q;
+    a.out = out;
+    a.Kc = Kch(ch);
+    a.Vc = Vch(ch);
+    a.part_o = at<float>(lay.part_o);
+    a.part_ml = at<float>(lay.part_ml);
+    a.B = ts.B;
+    a.M = ts.M;
+    a.s0 = ts.s0;
+    a.step = ts.s_step;
+    a.Hq = c.Hq;
+    a.Hkv = c.Hkv;
+    a.G = G;
+    a.T_max = c.T_max;
+    a.nsplit = ns;
+    a.scale_log2 = 1.4426950408889634f / sqrtf((float)c.d);
+    dim3 grid(nrb, ts.B * c.Hkv, ns);
+    ProfScope prof(WM_K_ATTN, s);
+    if (large)
+      hipLaunchKernelGGL((attn_kernel<T, DH, 4, 2>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<T, DH, 1, 1>), grid, dim3(64), 0, s, a);
+    WM_TRY(hipGetLastError());
+    if (ns > 1) {
+      hipLaunchKernelGGL((attn_combine<T>), dim3(rows), dim3(256), 0, s, a.part_o, a.part_ml, (void *)out, rows, c.Hq,
+                         c.d, ns);
+      WM_TRY(hipGetLastError());
+    }
+    return WM_OK;
+  }
+
+  wm_status attn(int layer, const T *q, wm_tokset ts, T *out) {
+    switch (c.d) {
+      case 32: return attn_dh<32>(layer, q, ts, out);
+      case 64: return attn_dh<64>(layer, q, ts, out);
+      default: return attn_dh<128>(layer, q, ts, out);
+    }
+  }
+
+  // -------------------------------------------------------- KV pool
+  template <int KMAX> wm_status mix(const T *S, int rows) {
+    hipLaunchKernelGGL((pool_mix<T, KMAX>), dim3(rows), dim3(256), 0, s, S, at<float>(lay.rinvS), at<float>(lay.Aw),
+                       w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
+    WM_TRY(hipGetLastError());
+    return WM_OK;
+  }
+
+  wm_status pool(const T *S, wm_tokset ts) {
+    const int rows = ts.B * ts.M;
+    const int64_t nl = (int64_t)c.L * rows;
+    {
+    ProfScope prof(WM_K_MIX, s);
+    hipLaunchKernelGGL((state_rinv<T>), dim3((unsigned)((nl + 3) / 4)), dim3(256), 0, s, S, at<float>(lay.rinvS), nl,
+                       c.D, c.eps);
+    WM_TRY(hipGetLastError());
+    }
+    // router: [rows, R*D] x [L*k, R*D]^T per branch
+    LoadRouterA<T> ra{S, at<float>(lay.rinvS), w->src_norm, rows, c.D, c.L, c.p};
+    BRows<T> rb{LoadRows<T>{(const T *)w->router, (int64_t)R * c.D, (int64_t)c.L * c.k * R * c.D, nullptr}};
+    EpiStoreF32 re{at<float>(lay.Aw), (int64_t)c.L * c.k, (int64_t)rows * c.L * c.k, nullptr, nullptr, nullptr, 0, 0.f,
+                   0.f};
+    {
+      ProfScope prof(WM_K_ROUTER, s);
+      WM_TRY((launch_gemm<T>(ra, rb, re, rows, c.L * c.k, R * c.D, 2, s)));
+    }
+    wm_status st;
+    {
+      ProfScope prof(WM_K_MIX, s);
+      st = c.k <= 4 ? mix<4>(S, rows) : c.k <= 8 ? mix<8>(S, rows) : c.k <= 16 ? mix<16>(S, rows) : mix<32>(S, rows);
+    }
+    if (st != WM_OK) return st;
+    // per-channel projection, z = beta*k + j
+    LoadRows<T> pa{at<T>(lay.mb), c.D, (int64_t)rows * c.D, nullptr};
+    BKV<T> pb{(const T *)w->wk, (const T *)w->wv, c.D, (int64_t)c.Hkv * c.d * c.D, c.k};
+    EpiKV<T> pe{(T *)cache->k, (T *)cache->v, at<float>(lay.rinvM), w->k_norm, w->rope_cos, w->rope_sin, c.k,
+                cache->B, c.Hkv, c.T_max, c.d, rows, c.eps, RowPos{ts.M, ts.s0, ts.s_step}};
+    ProfScope prof(WM_K_KVPROJ, s);
+    WM_TRY((launch_gemm<T>(pa, pb, pe, rows, c.Hkv * c.d, c.D, 2 * c.k, s)));
+    return WM_OK;
+  }
+
+  // -------------------------------------------------------- one group step
+  // Rows of ts; row r = b*M + m takes token tokens[b*tstride + toff + m*tstep].
+  // logit_mode 0: none; 1: row m_sel of every sequence -> logits[b]; 2: all
+  // rows -> logits[b*T + pos].
+  wm_status group_step(const int32_t *tokens, int tstride, int toff, int tstep, wm_tokset ts, int logit_mode,
+                       int m_sel, int Tseq, float *logits) {
+    const int rows = ts.B * ts.M, D = c.D, L = c.L, QD = c.Hq * c.d;
+    const float invD = 1.0f / D;
+    float *h = at<float>(lay.h), *ss = at<float>(lay.ss);
+    T *hb = at<T>(lay.hb), *q = at<T>(lay.q), *o = at<T>(lay.o), *act = at<T>(lay.act), *S = at<T>(lay.S);
+    const T *wq = (const T *)w->wq, *wo = (const T *)w->wo, *wg = (const T *)w->w_gate, *wu = (const T *)w->w_up,
+            *wd = (const T *)w->w_down;
+    const RowPos rp{ts.M, ts.s0, ts.s_step};
+    {
+    ProfScope prof(WM_K_EMBED, s);
+    hipLaunchKernelGGL((embed_rows<T>), dim3(rows), dim3(256), 0, s, tokens, (const T *)w->embed, w->attn_norm, h, hb,
+                       S, ss, ts.M, tstride, toff, tstep, c.V, D);
+    WM_TRY(hipGetLastError());
+    }
+    int nparts = 1;
+    for (int l = 0; l < L; ++l) {
+      // q = RoPE(qnorm(W_Q RMSNorm(h)))
+      {
+        LoadRows<T> a{hb, D, 0, nullptr};
+        BRows<T> b{LoadRows<T>{wq + (int64_t)l * QD * D, D, 0, nullptr}};
+        EpiQ<T> e{q, ss, nparts, invD, c.eps, w->q_norm + (int64_t)l * c.d, w->rope_cos, w->rope_sin, c.d, rp};
+        ProfScope prof(WM_K_QPROJ, s);
+        WM_TRY((launch_gemm<T>(a, b, e, rows, QD, D, 1, s)));
+      }
+      wm_status st = attn(l, q, ts, o);
+      if (st != WM_OK) return st;
+      // h += W_O o; hb = h * ffn_norm
+      {
+        LoadRows<T> a{o, QD, 0, nullptr};
+        BRows<T> b{LoadRows<T>{wo + (int64_t)l * D * QD, QD, 0, nullptr}};
+        EpiResid<T> e{h, hb, w->ffn_norm + (int64_t)l * D, nullptr, ss, lay.ssp};
+        ProfScope prof(WM_K_OPROJ, s);
+        WM_TRY((launch_gemm<T>(a, b, e, rows, D, QD, 1, s)));
+        nparts = lay.ssp;
+      }
+      // act = silu(W_gate b) * (W_up b), b = RMSNorm(h)
+      {
+        LoadRows<T> a{hb, D, 0, nullptr};
+        BGateUp<T> b{LoadGateUp<T>{wg + (int64_t)l * c.F * D, wu + (int64_t)l * c.F * D, D, c.F}};
+        EpiSwiGLU<T> e{act, ss, nparts, invD, c.eps, c.F};
+        ProfScope prof(WM_K_GATEUP, s);
+        WM_TRY((launch_gemm<T>(a, b, e, rows, 2 * c.F, D, 1, s)));
+      }
+      // h += W_down act; next state, next norm operand
+      {
+        LoadRows<T> a{act, c.F, 0, nullptr};
+        BRows<T> b{LoadRows<T>{wd + (int64_t)l * D * c.F, c.F, 0, nullptr}};
+        const float *gnext = l + 1 < L ? w->attn_norm + (int64_t)(l + 1) * D : w->final_norm;
+        T *Snext = l + 1 < L ? S + (int64_t)(l + 1) * rows * D : nullptr;
+        EpiResid<T> e{h, hb, gnext, Snext, ss, lay.ssp};
+        ProfScope prof(WM_K_DOWN, s);
+        WM_TRY((launch_gemm<T>(a, b, e, rows, D, c.F, 1, s)));
+      }
+    }
+    wm_status st = pool(S, ts);
+    if (st != WM_OK) return st;
+    if (logit_mode) {
+      int n = logit_mode == 1 ? ts.B : rows;
+      int *rin = at<int>(lay.rowmap), *rout = rin + rows;
+      hipLaunchKernelGGL(fill_rowmap, dim3((n + 255) / 256), dim3(256), 0, s, rin, rout, n, logit_mode, ts.M, m_sel, Tseq,
+                         ts.s0, ts.s_step);
+      WM_TRY(hipGetLastError());
+      LoadRows<T> a{hb, D, 0, rin};
+      BRows<T> b{LoadRows<T>{(const T *)w->lm_head, D, 0, nullptr}};
+      EpiStoreF32 e{logits, c.V, 0, rout, ss, rin, nparts, invD, c.eps};
+      ProfScope prof(WM_K_LMHEAD, s);
+      WM_TRY((launch_gemm<T>(a, b, e, n, c.V, D, 1, s)));
+    }
+    return WM_OK;
+  }
+};
+
+static bool weights_ok(const wm_weights *w, bool stack) {
+  if (!w) return false;
+  bool pool = w->src_norm && w->router && w->chan_norm && w->wk && w->wv && w->k_norm && w->rope_cos && w->rope_sin;
+  if (!stack) return pool;
+  return pool && w->embed && w->lm_head && w->final_norm && w->attn_norm && w->wq && w->q_norm && w->wo &&
+         w->ffn_norm && w->w_gate && w->w_up && w->w_down;
+}
+
+static wm_status check_common(const wm_config *cfg, const wm_cache *cache, void *ws, size_t ws_bytes, int rows) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cache && cache->k && cache->v, WM_ERR_ARG, "cache or its k/v pointer is NULL");
+  WM_CHECK(cache->B >= 1, WM_ERR_SHAPE, "cache->B = %d must be >= 1", cache->B);
+  WM_CHECK(rows >= 1, WM_ERR_SHAPE, "no rows to process");
+  size_t need = ws_layout(*cfg, rows).total;
+  WM_CHECK(ws && ws_bytes >= need, WM_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for %d rows", ws_bytes, need,
+           rows);
+  return WM_OK;
+}
+
+static wm_status check_tokset(const wm_config *cfg, const wm_cache *cache, wm_tokset ts, int64_t pos_limit) {
+  WM_CHECK(ts.B >= 1 && ts.B <= cache->B, WM_ERR_SHAPE, "token set B = %d outside [1, cache->B = %d]", ts.B,
+           cache->B);
+  WM_CHECK(ts.M >= 1, WM_ERR_SHAPE, "token set M = %d must be >= 1", ts.M);
+  WM_CHECK(ts.s0 >= 0 && (ts.M == 1 || ts.s_step >= 1), WM_ERR_RANGE, "token set s0 = %d / step = %d invalid", ts.s0,
+           ts.s_step);
+  int64_t last = (int64_t)ts.s0 + (int64_t)(ts.M - 1) * (ts.M == 1 ? 0 : ts.s_step);
+  WM_CHECK(last <= pos_limit, WM_ERR_RANGE, "last position %lld beyond %lld", (long long)last, (long long)pos_limit);
+  return WM_OK;
+}
+
+template <typename T>
+static wm_status prefill_impl(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int Tseq, int g,
+                              const wm_cache *cache, float *logits, int mode, void *ws, int rows, hipStream_t s) {
+  Run<T> r(*cfg, w, cache, ws, rows, s);
+  const int B = cache->B, ng = g < Tseq ? g : Tseq;
+  for (int q = 0; q < ng; ++q) {
+    int Mq = (Tseq - q + g - 1) / g;
+    wm_tokset ts{B, Mq, q, g};
+    int lm = 0, msel = 0;
+    if (mode == 2) lm = 2;
+    if (mode == 1 && (Tseq - 1) % g == q) {
+      lm = 1;
+      msel = (Tseq - 1 - q) / g;
+    }
+    wm_status st = r.group_step(tokens, Tseq, q, g, ts, lm, msel, Tseq, logits);
+    if (st != WM_OK) return st;
+  }
+  return WM_OK;
+}
+
+}  // namespace wm
+
+using namespace wm;
+
+extern "C" {
+
+wm_status wm_rope_table(const wm_config *cfg, float *cosT, float *sinT, wm_stream stream) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cosT && sinT, WM_ERR_ARG, "rope table pointer is NULL");
+  int half = cfg->d / 2;
+  int64_t n = (int64_t)cfg->T_max * half;
+  hipLaunchKernelGGL(rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, cosT, sinT,
+                     cfg->T_max, half, (double)cfg->rope_base, cfg->d);
+  WM_TRY(hipGetLastError());
+  return WM_OK;
+}
+
+wm_status wm_mix_kv(const wm_config *cfg, const wm_weights *w, const void *states, wm_tokset ts, const wm_cache *cache,
+                    void *ws, size_t ws_bytes, wm_stream stream) {
+  WM_CHECK(cfg, WM_ERR_ARG, "config is NULL");
+  wm_status st = check_common(cfg, cache, ws, ws_bytes, ts.B * ts.M);
+  if (st != WM_OK) return st;
+  WM_CHECK(weights_ok(w, false) && states, WM_ERR_ARG, "a pool weight, the rope table or states is NULL");
+  st = check_tokset(cfg, cache, ts, (int64_t)cfg->T_max - 1);
+  if (st != WM_OK) return st;
+  if (ts.M == 1) ts.s_step = 1;
+  int rows = ts.B * ts.M;
+  if (cfg->dtype == WM_BF16) {
+    Run<bf16> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+    return r.pool((const bf16 *)states, ts);
+  }
+  Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+  return r.pool((const float *)states, ts);
+}
+
+wm_status wm_channel_attn(const wm_config *cfg, int32_t layer, const void *q, wm_tokset ts, const wm_cache *cache,
+                          void *out, void *ws, size_t ws_bytes, wm_stream stream) {
+  WM_CHECK(cfg, WM_ERR_ARG, "config is NULL");
+  wm_status st = check_common(cfg, cache, ws, ws_bytes, ts.B * ts.M);
+  if (st != WM_OK) return st;
+  WM_CHECK(q && out, WM_ERR_ARG, "q or out is NULL");
+  WM_CHECK(layer >= 0 && layer < cfg->L, WM_ERR_RANGE, "layer %d outside [0, L = %d)", layer, cfg->L);
+  st = check_tokset(cfg, cache, ts, cfg->T_max);
+  if (st != WM_OK) return st;
+  if (ts.M == 1) ts.s_step = 1;
+  int rows = ts.B * ts.M;
+  if (cfg->dtype == WM_BF16) {
+    Run<bf16> r(*cfg, nullptr, cache, ws, rows, (hipStream_t)stream);
+    return r.attn(layer, (const bf16 *)q, ts, (bf16 *)out);
+  }
+  Run<float> r(*cfg, nullptr, cache, ws, rows, (hipStream_t)stream);
+  return r.attn(layer, (const float *)q, ts, (float *)out);
+}
+
+wm_status wm_cyclic_prefill_pass(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t T,
+                                 int32_t g, const wm_cache *cache, float *logits, int32_t logits_mode, void *ws,
+                                 size_t ws_bytes, wm_stream stream) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cache && cache->k && cache->v && cache->B >= 1, WM_ERR_ARG, "cache, its pointers or B invalid");
+  WM_CHECK(g >= 1, WM_ERR_SHAPE, "g = %d must be >= 1", g);
+  WM_CHECK(T >= 1 && T <= cfg->T_max, WM_ERR_RANGE, "T = %d outside [1, T_max = %d]", T, cfg->T_max);
+  WM_CHECK(logits_mode >= 0 && logits_mode <= 2, WM_ERR_ARG, "logits_mode %d not in {0, 1, 2}", logits_mode);
+  WM_CHECK(logits_mode == 0 || logits, WM_ERR_ARG, "logits is NULL but logits_mode = %d", logits_mode);
+  WM_CHECK(tokens && weights_ok(w, true), WM_ERR_ARG, "tokens or a weight pointer is NULL");
+  int rows = cache->B * ((T + g - 1) / g);
+  st = check_common(cfg, cache, ws, ws_bytes, rows);
+  if (st != WM_OK) return st;
+  if (cfg->dtype == WM_BF16)
+    return prefill_impl<bf16>(cfg, w, tokens, T, g, cache, logits, logits_mode, ws, rows, (hipStream_t)stream);
+  return prefill_impl<float>(cfg, w, tokens, T, g, cache, logits, logits_mode, ws, rows, (hipStream_t)stream);
+}
+
+wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
+                         const wm_cache *cache, float *logits, void *ws, size_t ws_bytes, wm_stream stream) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cache && cache->k && cache->v && cache->B >= 1, WM_ERR_ARG, "cache, its pointers or B invalid");
+  WM_CHECK(t >= 0 && t < cfg->T_max, WM_ERR_RANGE, "t = %d outside [0, T_max = %d)", t, cfg->T_max);
+  WM_CHECK(tokens && logits && weights_ok(w, true), WM_ERR_ARG, "tokens, logits or a weight pointer is NULL");
+  int rows = cache->B;
+  st = check_common(cfg, cache, ws, ws_bytes, rows);
+  if (st != WM_OK) return st;
+  wm_tokset ts{cache->B, 1, t, 1};
+  if (cfg->dtype == WM_BF16) {
+    Run<bf16> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+    return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+  }
+  Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+  return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+}
+
+wm_status wm_profile_begin(uint32_t kind_mask) {
+  g_prof.mask = kind_mask;
+  g_prof.used = 0;
+  g_prof.recs.clear();
+  return WM_OK;
+}
+
+wm_status wm_profile_read(int64_t *counts, double *total_ms) {
+  WM_CHECK(counts && total_ms, WM_ERR_ARG, "counts or total_ms is NULL");
+  for (int i = 0; i < WM_K_COUNT; ++i) {
+    counts[i] = 0;
+    total_ms[i] = 0.0;
+  }
+  for (const ProfRec &r : g_prof.recs) {
+    WM_TRY(hipEventSynchronize(r.b));
+    float ms = 0.f;
+    WM_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+    counts[r.kind] += 1;
+    total_ms[r.kind] += ms;
+  }
+  return WM_OK;
+}
+
+wm_status wm_profile_end(void) {
+  g_prof.mask = 0;
+  for (hipEvent_t e : g_prof.pool) hipEventDestroy(e);
+  g_prof.pool.clear();
+  g_prof.used = 0;
+  g_prof.recs.clear();
+  return WM_OK;
+}
+
+}  // extern "C"

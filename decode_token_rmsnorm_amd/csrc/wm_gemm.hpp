@@ -1,0 +1,406 @@
+// wm_gemm.hpp — tiled MFMA GEMM  C[M, N] = A[M, K] * B[N, K]^T  with pluggable
+// operand loaders and fused epilogues.
+//
+// Block tile 128 x 128, k-tile of 128 bytes (64 bf16 / 32 float), 256 threads
+// = 4 wave64s in a 2 x 2 grid, each wave a 64 x 64 sub-tile of 4 x 4 MFMA
+// 16x16 tiles.  Operands go global -> registers -> LDS (rows padded by 16 B so
+// the 16-lane fragment reads hit distinct banks), two LDS stages, the next
+// k-tile's global loads in flight while the current one is multiplied.  After
+// the k loop the fp32 C tile is staged in LDS and an epilogue functor walks
+// it row by row (one wave per row, lane owns columns lane and lane + 64),
+// which keeps stores coalesced and lets row / head reductions (RMSNorm, key
+// and query norms, RoPE partners, residual sums of squares) be done in place.
+#pragma once
+
+#include "wm_common.hpp"
+
+namespace wm {
+
+constexpr int GM = 128;            // block rows
+constexpr int GN = 128;            // block columns
+constexpr int GKB = 128;           // k-tile, bytes
+constexpr int GROW = GKB + 16;     // LDS row pitch, bytes
+constexpr int GTHREADS = 256;
+constexpr int GSTAGE = 2 * GM * GROW;  // A + B tile bytes of one stage
+constexpr int GCP = GN + 4;        // C tile pitch in floats
+static_assert(2 * GSTAGE >= GM * GCP * 4, "C tile must fit in the operand LDS");
+
+// Position of row r of a token set (row r = b*M + m sits at s0 + m*step).
+struct RowPos {
+  int M, s0, step;
+  __device__ __forceinline__ int pos(int r) const { return s0 + (r % M) * step; }
+  __device__ __forceinline__ int seq(int r) const { return r / M; }
+};
+
+// 1 / sqrt(mean(x^2) + eps) of a row from `nparts` partial sums of squares.
+__device__ __forceinline__ float rinv_from_parts(const float *ss, int row, int nparts, float invD, float eps) {
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += ss[(int64_t)row * nparts + p];
+  return rsqrtf(s * invD + eps);
+}
+
+// ---------------------------------------------------------------- loaders
+
+// Plain row-major operand [rows, K] with leading dimension ld (elements), an
+// optional row gather and a per-blockIdx.z offset.
+template <typename T> struct LoadRows {
+  const T *p;
+  int64_t ld, zstride;
+  const int *gather;  // nullable: logical row r reads row gather[r]
+  __device__ __forceinline__ u32x4 load(int z, int row, int nrows, int kbyte) const {
+    if (row >= nrows) return u32x4{0, 0, 0, 0};
+    int64_t r = gather ? gather[row] : row;
+    const char *base = (const char *)(p + z * zstride + r * ld);
+    return *(const u32x4 *)(base + kbyte);
+  }
+};
+
+// B operand of the fused gate/up projection: tile-local rows [0, GN/2) are
+// gate rows, [GN/2, GN) the matching up rows, so that gate and up of one
+// output column sit GN/2 apart in the C tile.
+template <typename T> struct LoadGateUp {
+  const T *gate, *up;
+  int64_t ld;
+  int F;
+  __device__ __forceinline__ u32x4 load(int n0, int jl, int kbyte) const {
+    int f = n0 / 2 + (jl & (GN / 2 - 1));
+    if (f >= F) return u32x4{0, 0, 0, 0};
+    const T *m = jl < GN / 2 ? gate : up;
+    return *(const u32x4 *)((const char *)(m + (int64_t)f * ld) + kbyte);
+  }
+};
+
+// A operand of the router: row r is the concatenation over blocks b < R of
+// RMSNorm(S[b*p][r]; src_gain[beta][b*p]) — normalised on the fly from the
+// state stack S [L, rows, D] and per-layer row scales rinvS [L, rows];
+// blockIdx.z is the branch beta.
+template <typename T> struct LoadRouterA {
+  const T *S;
+  const float *rinvS;
+  const float *gain;  // [2, L, D]
+  int rows, D, L, p;
+  __device__ __forceinline__ u32x4 load(int z, int row, int nrows, int kbyte) const {
+    if (row >= nrows) return u32x4{0, 0, 0, 0};
+    constexpr int E = Elt<T>::E16;
+    int kel = kbyte / (int)sizeof(T);
+    int blk = kel / D, col = kel - blk * D;
+    int layer = blk * p;
+    u32x4 v = *(const u32x4 *)(S + ((int64_t)layer * rows + row) * D + col);
+    float f[E];
+    unpack16<T>(v, f);
+    float s = rinvS[(int64_t)layer * rows + row];
+    const float *g = gain + ((int64_t)z * L + layer) * D + col;
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] *= s * g[e];
+    return pack16<T>(f);
+  }
+};
+
+// ---------------------------------------------------------------- epilogues
+// All epilogues get the fp32 C tile in LDS (pitch GCP floats) and run on all
+// 256 threads: wave w handles tile rows w, w+4, ...; lane owns columns lane
+// and lane+64.
+
+// q = RoPE(RMSNorm_head(rinv_row * C; q_norm)) -> q [rows, Hq*d].
+template <typename T> struct EpiQ {
+  T *q;
+  const float *ss;
+  int nparts;
+  float invD, eps;
+  const float *qnorm;  // [d]
+  const float *cosT, *sinT;
+  int d;
+  RowPos rp;
+};
+
+// RMSNorm over head groups of d columns + RoPE for the two values a lane owns
+// (columns c0 = lane, c1 = lane + 64 of a 128-wide head-aligned tile).
+__device__ __forceinline__ void head_norm_rope(float x[2], int lane, int d, float eps, const float *gain,
+                                               const float *cosT, const float *sinT, int pos) {
+  float s0 = x[0] * x[0], s1 = x[1] * x[1];
+  float h0, h1;
+  if (d == 128) {
+    h0 = h1 = wave_sum(s0 + s1);
+  } else {
+    h0 = group_sum(s0, d);
+    h1 = group_sum(s1, d);
+  }
+  float invd = 1.0f / d;
+  float y[2];
+  int cc[2] = {lane, lane + 64};
+  y[0] = x[0] * rsqrtf(h0 * invd + eps) * gain[cc[0] & (d - 1)];
+  y[1] = x[1] * rsqrtf(h1 * invd + eps) * gain[cc[1] & (d - 1)];
+  float pr[2];
+  if (d == 128) {
+    pr[0] = y[1];
+    pr[1] = y[0];
+  } else {
+    pr[0] = __shfl_xor(y[0], d / 2);
+    pr[1] = __shfl_xor(y[1], d / 2);
+  }
+  const int half = d / 2;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int cd = cc[i] & (d - 1);
+    int m = cd & (half - 1);
+    float cs = cosT[(int64_t)pos * half + m], sn = sinT[(int64_t)pos * half + m];
+    x[i] = cd < half ? y[i] * cs - pr[i] * sn : pr[i] * sn + y[i] * cs;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void run_epi(const EpiQ<T> &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+    int r = m0 + rl;
+    if (r >= M) break;
+    float rs = rinv_from_parts(e.ss, r, e.nparts, e.invD, e.eps);
+    float x[2] = {Cs[rl * GCP + lane] * rs, Cs[rl * GCP + lane + 64] * rs};
+    head_norm_rope(x, lane, e.d, e.eps, e.qnorm, e.cosT, e.sinT, e.rp.pos(r));
+    T *dst = e.q + (int64_t)r * N + n0;
+    if (n0 + lane < N) dst[lane] = from_f<T>(x[0]);
+    if (n0 + lane + 64 < N) dst[lane + 64] = from_f<T>(x[1]);
+  }
+}
+
+// Residual: h += C; hb = h * gain_next; optionally S_next = h; and the row's
+// sum of squares over this tile's columns -> ss_out[r, tileN].
+template <typename T> struct EpiResid {
+  float *h;
+  T *hb;
+  const float *gain_next;  // [N]
+  T *S_next;               // nullable, [rows, N]
+  float *ss_out;
+  int nparts_out;
+};
+
+template <typename T>
+__device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+    int r = m0 + rl;
+    if (r >= M) break;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int c = n0 + lane + 64 * i;
+      if (c < N) {
+        int64_t o = (int64_t)r * N + c;
+        float v = e.h[o] + Cs[rl * GCP + lane + 64 * i];
+        e.h[o] = v;
+        e.hb[o] = from_f<T>(v * e.gain_next[c]);
+        if (e.S_next) e.S_next[o] = from_f<T>(v);
+        sq += v * v;
+      }
+    }
+    sq = wave_sum(sq);
+    if (lane == 0) e.ss_out[(int64_t)r * e.nparts_out + n0 / GN] = sq;
+  }
+}
+
+// SwiGLU: act[r, n0/2 + c] = silu(rs*C[r, c]) * (rs*C[r, c + GN/2]), c < GN/2.
+template <typename T> struct EpiSwiGLU {
+  T *act;
+  const float *ss;
+  int nparts;
+  float invD, eps;
+  int F;
+};
+
+template <typename T>
+__device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+    int r = m0 + rl;
+    if (r >= M) break;
+    float rs = rinv_from_parts(e.ss, r, e.nparts, e.invD, e.eps);
+    int f = n0 / 2 + lane;
+    if (f < e.F) {
+      float gt = Cs[rl * GCP + lane] * rs, up = Cs[rl * GCP + lane + GN / 2] * rs;
+      e.act[(int64_t)r * e.F + f] = from_f<T>(silu(gt) * up);
+    }
+  }
+}
+
+// Plain fp32 store with an optional row scale from partial sums and an
+// optional output row map: out[(map ? map[r] : r) * ldo + c] (per z offset).
+struct EpiStoreF32 {
+  float *out;
+  int64_t ldo, zstride;
+  const int *out_rows;  // nullable
+  const float *ss;      // nullable: no row scale
+  const int *ss_rows;   // nullable: ss row = ss_rows[r]
+  int nparts;
+  float invD, eps;
+};
+
+template <typename T>
+__device__ __forceinline__ void run_epi_f32(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int M,
+                                            int N) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+    int r = m0 + rl;
+    if (r >= M) break;
+    float rs = 1.f;
+    if (e.ss) rs = rinv_from_parts(e.ss, e.ss_rows ? e.ss_rows[r] : r, e.nparts, e.invD, e.eps);
+    int64_t orow = e.out_rows ? e.out_rows[r] : r;
+    float *dst = e.out + z * e.zstride + orow * e.ldo;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int c = n0 + lane + 64 * i;
+      if (c < N) dst[c] = Cs[rl * GCP + lane + 64 * i] * rs;
+    }
+  }
+}
+
+// Pool projection, blockIdx.z = beta*k + j: rows scaled by the channel's
+// 1/rms (rinvM [2k, rows]); keys then get the per-head key norm (k_norm[j])
+// and RoPE, values stay raw; both go to cache[j, b, h, pos, :].
+template <typename T> struct EpiKV {
+  T *Kc, *Vc;  // [k, B, Hkv, T_max, d]
+  const float *rinvM;
+  const float *knorm;  // [k, d]
+  const float *cosT, *sinT;
+  int k, B, Hkv, T_max, d, rows;
+  float eps;
+  RowPos rp;
+};
+
+template <typename T>
+__device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int beta = z / e.k, j = z - beta * e.k;
+  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+    int r = m0 + rl;
+    if (r >= M) break;
+    float rs = e.rinvM[(int64_t)z * e.rows + r];
+    float x[2] = {Cs[rl * GCP + lane] * rs, Cs[rl * GCP + lane + 64] * rs};
+    int pos = e.rp.pos(r), b = e.rp.seq(r);
+    if (beta == 0) head_norm_rope(x, lane, e.d, e.eps, e.knorm + (int64_t)j * e.d, e.cosT, e.sinT, pos);
+    T *dst = beta == 0 ? e.Kc : e.Vc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int c = n0 + lane + 64 * i;
+      if (c < N) {
+        int h = c / e.d, dd = c - h * e.d;
+        int64_t o = ((((int64_t)j * e.B + b) * e.Hkv + h) * e.T_max + pos) * e.d + dd;
+        dst[o] = from_f<T>(x[i]);
+      }
+    }
+  }
+}
+
+template <typename T, class E>
+__device__ __forceinline__ void epilogue(const E &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+  run_epi<T>(e, z, m0, n0, Cs, M, N);
+}
+template <typename T>
+__device__ __forceinline__ void epilogue(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+  run_epi_f32<T>(e, z, m0, n0, Cs, M, N);
+}
+
+// ---------------------------------------------------------------- B loaders
+template <typename T> struct BRows {
+  LoadRows<T> L;
+  __device__ __forceinline__ u32x4 load(int z, int n0, int jl, int N, int kbyte) const {
+    return L.load(z, n0 + jl, N, kbyte);
+  }
+};
+template <typename T> struct BGateUp {
+  LoadGateUp<T> L;
+  __device__ __forceinline__ u32x4 load(int z, int n0, int jl, int N, int kbyte) const { return L.load(n0, jl, kbyte); }
+};
+// Pool projection weights: z = beta*k + j -> wk[j] or wv[j].
+template <typename T> struct BKV {
+  const T *wk, *wv;
+  int64_t ld, mstride;
+  int k;
+  __device__ __forceinline__ u32x4 load(int z, int n0, int jl, int N, int kbyte) const {
+    int n = n0 + jl;
+    if (n >= N) return u32x4{0, 0, 0, 0};
+    int beta = z / k, j = z - beta * k;
+    const T *m = (beta == 0 ? wk : wv) + j * mstride + (int64_t)n * ld;
+    return *(const u32x4 *)((const char *)m + kbyte);
+  }
+};
+
+// ---------------------------------------------------------------- kernel
+template <typename T, class AL, class BL, class EP>
+__global__ __launch_bounds__(GTHREADS) void gemm_kernel(AL al, BL bl, EP ep, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * GSTAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int z = blockIdx.z;
+  const int m0 = blockIdx.y * GM, n0 = blockIdx.x * GN;
+  const int nk = (int)((int64_t)K * (int64_t)sizeof(T) / GKB);
+
+  u32x4 ra[4], rb[4];
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + GTHREADS * i, r = c >> 3, cb = c & 7;
+      ra[i] = al.load(z, m0 + r, M, kt * GKB + cb * 16);
+      rb[i] = bl.load(z, n0, r, N, kt * GKB + cb * 16);
+    }
+  };
+  auto sstore = [&](int buf) {
+    unsigned char *As = smem + buf * GSTAGE, *Bs = As + GM * GROW;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + GTHREADS * i, r = c >> 3, cb = c & 7;
+      *(u32x4 *)(As + r * GROW + cb * 16) = ra[i];
+      *(u32x4 *)(Bs + r * GROW + cb * 16) = rb[i];
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload(kt + 1);
+    const unsigned char *As = smem + (kt & 1) * GSTAGE, *Bs = As + GM * GROW;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *(const u32x4 *)(As + (wm * 64 + i * 16 + (lane & 15)) * GROW + ks * 64 + (lane >> 4) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *(const u32x4 *)(Bs + (wn * 64 + j * 16 + (lane & 15)) * GROW + ks * 64 + (lane >> 4) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma16<T>(acc[i][j], af[i], bfr[j]);
+    }
+    if (kt + 1 < nk) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  float *Cs = (float *)smem;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Cs[(wm * 64 + i * 16 + (lane >> 4) * 4 + e) * GCP + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][e];
+  __syncthreads();
+  epilogue<T>(ep, z, m0, n0, Cs, M, N);
+}
+
+template <typename T, class AL, class BL, class EP>
+hipError_t launch_gemm(const AL &al, const BL &bl, const EP &ep, int M, int N, int K, int Z, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  dim3 grid((N + GN - 1) / GN, (M + GM - 1) / GM, Z);
+  hipLaunchKernelGGL((gemm_kernel<T, AL, BL, EP>), grid, dim3(GTHREADS), 0, s, al, bl, ep, M, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace wm

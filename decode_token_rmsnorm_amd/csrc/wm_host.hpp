@@ -1,0 +1,55 @@
+// wm_host.hpp — host-side shape checks, workspace layout and the error
+// string; plain C++ (no HIP), shared by the C ABI entry points.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/wm.h"
+
+namespace wm {
+
+void set_error(const char *fmt, ...);
+
+// Attention partials are kept for at most max(rows, 16384) split-rows.
+inline int64_t part_rows_cap(int rows) {
+  int64_t c = rows > 16384 ? rows : 16384;
+  int64_t m = 16 * (int64_t)rows;
+  return c < m ? c : m;
+}
+
+struct WsLayout {
+  size_t h, hb, ss, q, o, act, S, rinvS, Aw, mb, rinvM, part_o, part_ml, rowmap, total;
+  int ssp;  // partial sums of squares per row
+};
+
+inline WsLayout ws_layout(const wm_config &c, int rows) {
+  WsLayout w{};
+  size_t es = c.dtype == WM_BF16 ? 2 : 4, off = 0, R = (size_t)rows;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  w.ssp = (c.D + 127) / 128;
+  size_t qd = (size_t)c.Hq * c.d;
+  w.h = take(R * c.D * 4);
+  w.hb = take(R * c.D * es);
+  w.ss = take(R * w.ssp * 4);
+  w.q = take(R * qd * es);
+  w.o = take(R * qd * es);
+  w.act = take(R * c.F * es);
+  w.S = take((size_t)c.L * R * c.D * es);
+  w.rinvS = take((size_t)c.L * R * 4);
+  w.Aw = take(2 * R * c.L * c.k * 4);
+  w.mb = take(2 * (size_t)c.k * R * c.D * es);
+  w.rinvM = take(2 * (size_t)c.k * R * 4);
+  size_t cap = (size_t)part_rows_cap(rows);
+  w.part_o = take(cap * qd * 4);
+  w.part_ml = take(cap * c.Hq * 2 * 4);
+  w.rowmap = take(2 * R * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace wm

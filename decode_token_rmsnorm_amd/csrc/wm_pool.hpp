@@ -1,0 +1,150 @@
+// wm_pool.hpp — the streaming parts of the cross-layer KV pool and small
+// helper kernels.
+//
+//  state_rinv   1/rms of every (layer, row) of the state stack S [L, rows, D]
+//  pool_mix     for both branches and every channel j of one token:
+//                 m_j = sum_l A[l, j] * rinv_l * (gamma_l (.) S[l])   (signed A)
+//               stores rho_j (.) m_j (channel gain folded in; the channel's
+//               1/rms is applied after the projection, which is linear) and
+//               1/rms(m_j) for the projection epilogue.
+//  embed_rows   h_0 = E[token] (+ the first state, the next GEMM's operand and
+//               its sum of squares)
+//  rope_table   cos/sin of s * base^(-2m/d), double precision, rounded
+//  fill_rowmap  gather/scatter row lists of the LM head
+#pragma once
+
+#include "wm_common.hpp"
+
+namespace wm {
+
+// One wave per (layer, row): rinv[l*rows + r] = 1/sqrt(mean(S^2) + eps).
+template <typename T>
+__global__ __launch_bounds__(256) void state_rinv(const T *S, float *rinv, int64_t nrowsL, int D, float eps) {
+  int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (w >= nrowsL) return;
+  constexpr int E = Elt<T>::E16;
+  const T *x = S + w * D;
+  float s = 0.f;
+  for (int c = lane * E; c < D; c += 64 * E) {
+    float f[E];
+    unpack16<T>(*(const u32x4 *)(x + c), f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) s += f[e] * f[e];
+  }
+  s = wave_sum(s);
+  if (lane == 0) rinv[w] = rsqrtf(s / D + eps);
+}
+
+// One block per token row; thread owns columns tid, tid + 256, ...
+// A [2, rows, L*k] router output; S [L, rows, D]; mb [2, k, rows, D];
+// rinvM [2, k, rows].
+template <typename T, int KMAX>
+__global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, const float *A, const float *src_gain,
+                                                const float *chan_gain, T *mb, float *rinvM, int rows, int L, int k,
+                                                int D, float eps) {
+  __shared__ float Aw[2][32][KMAX];  // L <= 32
+  __shared__ float red[4][2 * KMAX];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 2 * L * k; i += 256) {
+    int beta = i / (L * k), rem = i - beta * L * k, l = rem / k, j = rem - l * k;
+    Aw[beta][l][j] = A[((int64_t)beta * rows + r) * L * k + rem] * rinvS[(int64_t)l * rows + r];
+  }
+  __syncthreads();
+  float ss[2][KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) ss[0][j] = ss[1][j] = 0.f;
+  for (int c = tid; c < D; c += 256) {
+    float acc[2][KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) acc[0][j] = acc[1][j] = 0.f;
+    for (int l = 0; l < L; ++l) {
+      float x = to_f(S[((int64_t)l * rows + r) * D + c]);
+      float xk = x * src_gain[(int64_t)l * D + c];
+      float xv = x * src_gain[((int64_t)L + l) * D + c];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          acc[0][j] += Aw[0][l][j] * xk;
+          acc[1][j] += Aw[1][l][j] * xv;
+        }
+      }
+    }
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          float m = acc[beta][j];
+          ss[beta][j] += m * m;
+          mb[(((int64_t)beta * k + j) * rows + r) * D + c] = from_f<T>(m * chan_gain[((int64_t)beta * k + j) * D + c]);
+        }
+      }
+  }
+#pragma unroll
+  for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      float v = wave_sum(ss[beta][j]);
+      if (lane == 0) red[wave][beta * KMAX + j] = v;
+    }
+  __syncthreads();
+  if (tid < 2 * k) {
+    int beta = tid / k, j = tid - beta * k;
+    float v = red[0][beta * KMAX + j] + red[1][beta * KMAX + j] + red[2][beta * KMAX + j] + red[3][beta * KMAX + j];
+    rinvM[((int64_t)beta * k + j) * rows + r] = rsqrtf(v / D + eps);
+  }
+}
+
+// Row r = b*M + m reads token tokens[b*tstride + toff + m*tstep] (clamped to
+// [0, V)).  Writes h = E[tok] (fp32), S0 = E[tok], hb = E[tok] * gain, and the
+// row's sum of squares (one part).
+template <typename T>
+__global__ __launch_bounds__(256) void embed_rows(const int32_t *tokens, const T *E, const float *gain, float *h, T *hb,
+                                                  T *S0, float *ss, int M, int tstride, int toff, int tstep, int V,
+                                                  int D) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int b = r / M, m = r - b * M;
+  int tok = tokens[(int64_t)b * tstride + toff + (int64_t)m * tstep];
+  tok = min(max(tok, 0), V - 1);
+  float s = 0.f;
+  for (int c = tid; c < D; c += 256) {
+    T e = E[(int64_t)tok * D + c];
+    float v = to_f(e);
+    h[(int64_t)r * D + c] = v;
+    S0[(int64_t)r * D + c] = e;
+    hb[(int64_t)r * D + c] = from_f<T>(v * gain[c]);
+    s += v * v;
+  }
+  __shared__ float red[4];
+  s = wave_sum(s);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) ss[r] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ void rope_table(float *cosT, float *sinT, int T_max, int half, double base, int d) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T_max * half) return;
+  int s = (int)(i / half), m = (int)(i - (int64_t)s * half);
+  double ang = (double)s * pow(base, -2.0 * m / d);
+  cosT[i] = (float)cos(ang);
+  sinT[i] = (float)sin(ang);
+}
+
+// mode 1: rows_in[b] = b*M + m_sel, rows_out[b] = b
+// mode 2: rows_in[r] = r, rows_out[r] = b*T + s0 + m*step
+__global__ void fill_rowmap(int *rows_in, int *rows_out, int n, int mode, int M, int m_sel, int T, int s0, int step) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (mode == 1) {
+    rows_in[i] = i * M + m_sel;
+    rows_out[i] = i;
+  } else {
+    int b = i / M, m = i - b * M;
+    rows_in[i] = i;
+    rows_out[i] = b * T + s0 + m * step;
+  }
+}
+
+}  // namespace wm

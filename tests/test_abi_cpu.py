@@ -1,0 +1,129 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/wm.h
+declares, its host-only helpers match the oracle bit for bit, and every
+validated error path returns its code before anything is launched."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle as O
+from decode_token_rmsnorm_amd import _lib as C
+from wm_inputs import WORKLOADS
+
+pytestmark = pytest.mark.skipif(not os.path.exists(C.LIB_PATH), reason="libwm.so not built")
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def cfg_of(w, dtype=C.WM_BF16, **kw):
+    c = C.WmConfig(w.L, w.D, w.Hq, w.Hkv, w.d, w.F, w.k, w.p, w.V, w.T_max, w.eps, w.rope_base, dtype)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_library_exports_every_declared_function():
+    names = C.header_functions()
+    assert len(names) == 14
+    out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= exported, set(names) - exported
+    L = C.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+@pytest.mark.parametrize("T,g", [(128, 16), (2048, 16), (7, 3), (5, 9), (1, 1), (100, 1), (10, 10)])
+def test_group_positions_bit_exact(T, g):
+    L = C.lib()
+    for q in range(g):
+        buf = (ctypes.c_int32 * (T + 1))()
+        n = L.wm_group_positions(T, g, q, buf)
+        assert n == len(O.group_positions(T, g, q))
+        assert list(buf[:n]) == O.group_positions(T, g, q)
+    assert L.wm_group_positions(T, g, g, None) == -1
+    assert L.wm_group_positions(T, 0, 0, None) == -1
+
+
+def test_channel_of_layer_and_cache_elems_bit_exact():
+    L = C.lib()
+    for k in range(1, 17):
+        for layer in range(40):
+            assert L.wm_channel_of_layer(layer, k) == O.channel_of_layer(layer, k)
+    assert L.wm_channel_of_layer(3, 0) == -1
+    for name, w in WORKLOADS.items():
+        c = cfg_of(w)
+        assert L.wm_cache_elems(ctypes.byref(c), w.B) == O.cache_elems(w.k, w.B, w.T_max, w.Hkv, w.d)
+
+
+def test_workspace_bytes_positive_and_monotone():
+    L = C.lib()
+    c = cfg_of(WORKLOADS["prefill_1p3b"])
+    sizes = [L.wm_workspace_bytes(ctypes.byref(c), r) for r in (1, 64, 1024, 8192)]
+    assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
+    assert L.wm_workspace_bytes(ctypes.byref(c), 0) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("k", 0, -2), ("k", 17, -2), ("p", 0, -2), ("d", 48, -2), ("Hq", 6, -2), ("D", 96, -2), ("F", 100, -2),
+    ("L", 33, -2), ("dtype", 7, -3), ("eps", 0.0, -1), ("T_max", 0, -2),
+])
+def test_check_config_rejects(field, value, code):
+    c = cfg_of(WORKLOADS["decode_d512"], **{field: value})
+    assert C.lib().wm_check_config(ctypes.byref(c)) == code
+    assert C.last_error() != ""
+
+
+def _weights(fake=FAKE):
+    return C.WmWeights(*[fake] * len(C.WEIGHT_FIELDS))
+
+
+def test_entry_points_validate_before_launch():
+    L = C.lib()
+    w = WORKLOADS["small_prefill"]
+    c = cfg_of(w)
+    W = _weights()
+    cache = C.WmCache(FAKE, FAKE, w.B)
+    rows = w.B * w.T
+    need = L.wm_workspace_bytes(ctypes.byref(c), rows)
+    ts = C.WmTokset(w.B, w.T, 0, 1)
+    st = lambda: C.lib().wm_last_error()
+    # null config / cache / weights
+    assert L.wm_mix_kv(None, ctypes.byref(W), FAKE, ts, ctypes.byref(cache), FAKE, need, None) == -1
+    assert L.wm_mix_kv(ctypes.byref(c), ctypes.byref(W), FAKE, ts, None, FAKE, need, None) == -1
+    assert L.wm_mix_kv(ctypes.byref(c), None, FAKE, ts, ctypes.byref(cache), FAKE, need, None) == -1
+    # workspace too small
+    assert L.wm_mix_kv(ctypes.byref(c), ctypes.byref(W), FAKE, ts, ctypes.byref(cache), FAKE, need - 1, None) == -4
+    # positions beyond the cache
+    bad = C.WmTokset(w.B, w.T, 1, 1)
+    assert L.wm_mix_kv(ctypes.byref(c), ctypes.byref(W), FAKE, bad, ctypes.byref(cache), FAKE, need, None) == -5
+    assert b"beyond" in st()
+    # more sequences than the cache holds
+    assert L.wm_mix_kv(ctypes.byref(c), ctypes.byref(W), FAKE, C.WmTokset(w.B + 1, 4, 0, 1), ctypes.byref(cache),
+                       FAKE, need, None) == -2
+    # channel_attn: layer out of range
+    assert L.wm_channel_attn(ctypes.byref(c), w.L, FAKE, ts, ctypes.byref(cache), FAKE, FAKE, need, None) == -5
+    # prefill: g < 1, T > T_max, bad logits mode, missing logits
+    ws_p = L.wm_workspace_bytes(ctypes.byref(c), w.B * 128)
+    assert L.wm_cyclic_prefill_pass(ctypes.byref(c), ctypes.byref(W), FAKE, w.T, 0, ctypes.byref(cache), None, 0,
+                                    FAKE, ws_p, None) == -2
+    assert L.wm_cyclic_prefill_pass(ctypes.byref(c), ctypes.byref(W), FAKE, w.T_max + 1, 16, ctypes.byref(cache),
+                                    None, 0, FAKE, ws_p, None) == -5
+    assert L.wm_cyclic_prefill_pass(ctypes.byref(c), ctypes.byref(W), FAKE, w.T, 16, ctypes.byref(cache), FAKE, 3,
+                                    FAKE, ws_p, None) == -1
+    assert L.wm_cyclic_prefill_pass(ctypes.byref(c), ctypes.byref(W), FAKE, w.T, 16, ctypes.byref(cache), None, 1,
+                                    FAKE, ws_p, None) == -1
+    assert L.wm_cyclic_prefill_pass(ctypes.byref(c), ctypes.byref(W), FAKE, w.T, 16, ctypes.byref(cache), None, 0,
+                                    FAKE, ws_p - 256, None) == -4
+    W0 = _weights()
+    W0.router = None
+    assert L.wm_cyclic_prefill_pass(ctypes.byref(c), ctypes.byref(W0), FAKE, w.T, 16, ctypes.byref(cache), None, 0,
+                                    FAKE, ws_p, None) == -1
+    # decode: t outside [0, T_max)
+    ws_d = L.wm_workspace_bytes(ctypes.byref(c), w.B)
+    for t in (-1, w.T_max):
+        assert L.wm_decode_step(ctypes.byref(c), ctypes.byref(W), FAKE, t, ctypes.byref(cache), FAKE, FAKE, ws_d,
+                                None) == -5
+    # rope table: null output
+    assert L.wm_rope_table(ctypes.byref(c), None, FAKE, None) == -1

@@ -1,0 +1,264 @@
+"""HIP path vs the float64 oracle, through the C ABI (needs an MI355X).
+
+Tolerances (max-abs-relative over a tensor, max|a-b| / max|b|): 1e-4 for
+fp32 workloads, 2e-2 for bf16 workloads. Integer structure (which slots are
+written, which channel a layer reads, the group schedule) is checked exactly:
+unwritten slots must keep their NaN poison, and the pass count at which a
+schedule reaches the autoregressive fixed point must agree.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_token_rmsnorm_amd as wm
+import oracle as O
+from tests.helpers import max_abs_rel
+from wm_inputs import (WORKLOADS, make_cache, make_queries, make_state_stack, make_tokens, make_weights)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda"
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from decode_token_rmsnorm_amd import _lib
+
+    _lib.lib()  # fail loudly if the HIP library is missing
+
+
+def gpu_model(w, W):
+    return wm.Model(w, W, w.dtype, device=DEV)
+
+
+def np_of(t):
+    return t.float().cpu().numpy()
+
+
+def written_mask(w, B, bidx, pos):
+    m = np.zeros((B, w.T_max), bool)
+    m[bidx, pos] = True
+    return m
+
+
+def assert_cache(w, gk, gv, ref, mask, tol, poison=True):
+    """Compare written slots; unwritten slots must still hold the NaN poison."""
+    K, V = np_of(gk), np_of(gv)
+    for got, exp, name in ((K, ref[0], "K"), (V, ref[1], "V")):
+        sel = got.transpose(1, 3, 0, 2, 4)[mask]  # [n, k, Hkv, d]
+        ref_sel = np.asarray(exp).transpose(1, 3, 0, 2, 4)[mask]
+        err = max_abs_rel(sel, ref_sel)
+        print(f"{name}: max-abs-rel {err:.3e} over {sel.shape[0]} slots", flush=True)
+        assert err <= tol, (name, err)
+        if poison:
+            assert np.isnan(got.transpose(1, 3, 0, 2, 4)[~mask]).all(), f"{name}: an unwritten slot was written"
+
+
+# ---------------------------------------------------------------- wm_mix_kv
+
+@pytest.mark.parametrize("name,B,M,s0,step", [
+    ("tiny_fp32", 1, 128, 0, 1),        # every position of cfg tiny
+    ("mix_bf16", 3, 37, 5, 7),          # ragged rows (111), strided positions
+    ("tiny_fp32", 2, 9, 3, 13),         # ragged fp32
+])
+def test_mix_kv_matches_oracle(name, B, M, s0, step):
+    w = WORKLOADS[name].replace(B=B)
+    print(f"mix_kv {name} B={B} M={M} s0={s0} step={step}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    S = make_state_stack(w, B * M, seed=2)
+    model = gpu_model(w, {n: W[n] for n in ("src_norm", "router", "chan_norm", "wk", "wv", "k_norm")})
+    cache = wm.new_cache(model, B, fill=float("nan"))
+    St = torch.from_numpy(S).to(DEV, wm.api.torch_dtype(w.dtype))
+    wm.mix_kv(model, St, B, M, s0, step, cache)
+    torch.cuda.synchronize()
+    ref = O.new_cache(w, B)
+    O.mix_kv(O.Model(w, W), S, B, M, s0, step, ref)
+    bidx, pos = O.tokset_rows(B, M, s0, step)
+    assert_cache(w, cache.k, cache.v, ref, written_mask(w, B, bidx, pos), TOL[w.dtype])
+
+
+def test_mix_kv_full_size_sampled_rows_and_deterministic():
+    """Mix-only workload at full size [16, 8*2048, 512]; the oracle recomputes a
+    seeded sample of 96 rows (rows are independent), and a second launch must
+    reproduce the first bit for bit."""
+    w = WORKLOADS["mix_bf16"]
+    B, M = w.B, w.T
+    print("mix_kv full size", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    S = make_state_stack(w, B * M, seed=2)
+    model = gpu_model(w, {n: W[n] for n in ("src_norm", "router", "chan_norm", "wk", "wv", "k_norm")})
+    cache = wm.new_cache(model, B, fill=float("nan"))
+    St = torch.from_numpy(S).to(DEV, torch.bfloat16)
+    ws = model.workspace(B * M)
+    wm.mix_kv(model, St, B, M, 0, 1, cache, ws=ws)
+    torch.cuda.synchronize()
+    k1, v1 = cache.k.clone(), cache.v.clone()
+    wm.mix_kv(model, St, B, M, 0, 1, cache, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.int16), cache.k.view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), cache.v.view(torch.int16))
+    rows = np.sort(np.random.default_rng(11).choice(B * M, 96, replace=False))
+    bidx, pos = rows // M, rows % M
+    Kn, Vn = O.pool(O.Model(w, W), S[:, rows], pos)
+    K, V = np_of(cache.k), np_of(cache.v)
+    gotK = np.stack([K[:, b, :, p] for b, p in zip(bidx, pos)], 1)
+    gotV = np.stack([V[:, b, :, p] for b, p in zip(bidx, pos)], 1)
+    eK, eV = max_abs_rel(gotK, Kn), max_abs_rel(gotV, Vn)
+    print(f"full-size mix sampled: K {eK:.3e} V {eV:.3e}", flush=True)
+    assert eK <= TOL["bf16"] and eV <= TOL["bf16"]
+    assert not np.isnan(K[:, :, :, :M]).any()
+
+
+# ---------------------------------------------------------------- wm_channel_attn
+
+@pytest.mark.parametrize("name,B,M,s0,step,layer", [
+    ("tiny_fp32", 1, 8, 3, 16, 1),             # fp32, d=32, MHA
+    ("small_prefill", 8, 128, 5, 16, 9),       # one cyclic group step of the small model
+    ("small_prefill", 2, 300, 0, 1, 3),        # Jacobi-like rows incl. position 0, ragged blocks
+    ("prefill_1p3b", 2, 128, 15, 16, 13),      # d=128, G=7 (rows per pair not a tile multiple)
+    ("decode_d512", 64, 1, 2047, 1, 5),        # decode shape: one query per sequence, split keys
+])
+def test_channel_attn_matches_oracle(name, B, M, s0, step, layer):
+    w = WORKLOADS[name]
+    print(f"channel_attn {name} B={B} M={M} s0={s0} step={step} layer={layer}", flush=True)
+    maxpos = s0 + (M - 1) * step
+    K, V = make_cache(w, B, filled=maxpos, seed=3, poison=True)
+    q = make_queries(w, B * M, seed=4)
+    model = wm.Model(w, {}, w.dtype, device=DEV)
+    cache = wm.cache_from_host(model, K, V)
+    qt = torch.from_numpy(q).to(DEV, wm.api.torch_dtype(w.dtype))
+    out = wm.channel_attn(model, layer, qt, B, M, s0, step, cache)
+    torch.cuda.synchronize()
+    Kz, Vz = np.nan_to_num(K, nan=0.0), np.nan_to_num(V, nan=0.0)  # the oracle only reads s < i anyway
+    ref = O.channel_attn(w, layer, q, B, M, s0, step, (Kz, Vz))
+    got = np_of(out)
+    assert np.isfinite(got).all()
+    err = max_abs_rel(got, ref)
+    print(f"attn err {err:.3e}", flush=True)
+    assert err <= TOL[w.dtype]
+    bidx, pos = O.tokset_rows(B, M, s0, step)
+    assert np.all(got[pos == 0] == 0.0)
+
+
+# ---------------------------------------------------------------- prefill passes (tiny fp32)
+
+def _run_passes(w, W, tokens, g, npass):
+    """GPU and oracle caches/logits after each of npass passes of schedule g."""
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, w.B)
+    tok = torch.from_numpy(tokens).to(DEV)
+    M = O.Model(w, W)
+    ref = O.new_cache(w, w.B)
+    out = []
+    for n in range(npass):
+        lg = wm.cyclic_prefill_pass(model, tok, g, cache, logits_mode=2)
+        rl = O.cyclic_pass(M, tokens, ref, g, want_logits=True)
+        torch.cuda.synchronize()
+        out.append(((np_of(cache.k), np_of(cache.v)), np_of(lg), (ref[0].copy(), ref[1].copy()), rl))
+    return out
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = WORKLOADS["tiny_fp32"]
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    return w, W, tokens
+
+
+@pytest.mark.parametrize("g,npass", [(16, 4), (1, 4), (128, 1), (5, 2)])
+def test_prefill_passes_tiny_fp32(tiny, g, npass):
+    w, W, tokens = tiny
+    print(f"prefill tiny g={g} passes={npass}", flush=True)
+    for n, (gc, gl, rc, rl) in enumerate(_run_passes(w, W, tokens, g, npass)):
+        ek = max_abs_rel(gc[0][:, :, :, :w.T], rc[0][:, :, :, :w.T])
+        ev = max_abs_rel(gc[1][:, :, :, :w.T], rc[1][:, :, :, :w.T])
+        el = max_abs_rel(gl, rl)
+        print(f"  pass {n + 1}: K {ek:.2e} V {ev:.2e} logits {el:.2e}", flush=True)
+        assert max(ek, ev, el) <= TOL["f32"]
+
+
+def _pass_count(caches, ar, tau):
+    """First pass (1-based) whose cache is within tau of the AR cache, or None."""
+    for n, c in enumerate(caches):
+        if max(max_abs_rel(c[0], ar[0]), max_abs_rel(c[1], ar[1])) <= tau:
+            return n + 1
+    return None
+
+
+def test_pass_counts_agree_tiny_fp32(tiny):
+    """Cyclic g=16 reaches the AR fixed point after ceil(T/g) = 8 passes at the
+    latest (prefix exactness); the first pass within 1e-5 of AR must be the same
+    pass on the GPU and in the oracle, for cyclic g=16 and for Jacobi."""
+    w, W, tokens = tiny
+    T = w.T
+    ar = _run_passes(w, W, tokens, T, 1)[0]
+    gpu_ar = tuple(x[:, :, :, :T] for x in ar[0])
+    ref_ar = tuple(x[:, :, :, :T] for x in ar[2])
+    for g, npass in ((16, 9), (1, 24)):
+        runs = _run_passes(w, W, tokens, g, npass)
+        n_gpu = _pass_count([tuple(x[:, :, :, :T] for x in r[0]) for r in runs], gpu_ar, 1e-5)
+        n_ref = _pass_count([tuple(x[:, :, :, :T] for x in r[2]) for r in runs], ref_ar, 1e-5)
+        print(f"g={g}: pass count GPU {n_gpu} oracle {n_ref}", flush=True)
+        assert n_gpu == n_ref
+        if g == 16:
+            assert n_ref is not None and n_ref <= -(-T // g)
+
+
+# ---------------------------------------------------------------- prefill (bf16)
+
+@pytest.mark.parametrize("B,T,g,npass", [(2, 256, 16, 3), (1, 130, 7, 2)])
+def test_prefill_small_bf16(B, T, g, npass):
+    w = WORKLOADS["small_prefill"].replace(B=B)
+    print(f"prefill small bf16 B={B} T={T} g={g} passes={npass}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1, B=B, T=T)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, B, fill=float("nan"))
+    cache.k[:, :, :, :T] = 0
+    cache.v[:, :, :, :T] = 0
+    tok = torch.from_numpy(tokens).to(DEV)
+    M = O.Model(w, W)
+    ref = O.new_cache(w, B)
+    mask = np.zeros((B, w.T_max), bool)
+    mask[:, :T] = True
+    for n in range(npass):
+        lg = wm.cyclic_prefill_pass(model, tok, g, cache, logits_mode=1)
+        rl = O.cyclic_pass(M, tokens, ref, g, want_logits=True)
+        torch.cuda.synchronize()
+        assert_cache(w, cache.k, cache.v, ref, mask, TOL["bf16"])
+        el = max_abs_rel(np_of(lg), rl[:, T - 1])
+        print(f"  pass {n + 1}: last-position logits {el:.3e}", flush=True)
+        assert el <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- decode (full size)
+
+def test_decode_step_full_size():
+    """Decode workload at full size: B=64, 2047 cached positions (seeded N(0,1)
+    keys/values in all 16 channels), one new token per sequence at t=2047;
+    slots beyond t are NaN-poisoned and must stay so."""
+    w = WORKLOADS["decode_d512"]
+    t = 2047
+    print("decode full size", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    K, V = make_cache(w, w.B, filled=t, seed=3, poison=True)
+    tokens = make_tokens(w, seed=1, B=w.B, T=1)[:, 0]
+    model = gpu_model(w, W)
+    cache = wm.cache_from_host(model, K, V)
+    lg = wm.decode_step(model, torch.from_numpy(tokens).to(DEV), t, cache)
+    torch.cuda.synchronize()
+    ref = (np.nan_to_num(K, nan=0.0).astype(np.float64), np.nan_to_num(V, nan=0.0).astype(np.float64))
+    rl = O.decode_step(O.Model(w, W), tokens, t, ref)
+    el = max_abs_rel(np_of(lg), rl)
+    print(f"decode logits {el:.3e}", flush=True)
+    assert el <= TOL["bf16"]
+    mask = np.zeros((w.B, w.T_max), bool)
+    mask[:, t] = True
+    gk, gv = np_of(cache.k), np_of(cache.v)
+    for got, exp in ((gk, ref[0]), (gv, ref[1])):
+        e = max_abs_rel(got[:, :, :, t], exp[:, :, :, t])
+        print(f"decode appended slot {e:.3e}", flush=True)
+        assert e <= TOL["bf16"]
+        assert np.array_equal(got[:, :, :, :t], np.asarray(exp[:, :, :, :t], np.float32))  # history untouched

@@ -210,3 +210,20 @@ def make_queries(w: Workload, rows: int, seed: int = 4) -> np.ndarray:
     """[rows, Hq, d] N(0,1) queries (already normed and rotated, for the attention alone)."""
     r = _rng(seed, "queries")
     return _finish(r.standard_normal(size=(rows, w.Hq, w.d), dtype=np.float32), w.dtype)
+
+
+def make_cache_device(w: Workload, B: int, filled: int, seed: int = 3, device="cuda"):
+    """Like ``make_cache`` but drawn on the device with torch's seeded generator
+    (for full-size timing inputs that are never compared with the oracle)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shape = (w.k, B, w.Hkv, w.T_max, w.d)
+    out = []
+    for _ in range(2):
+        x = torch.zeros(shape, dtype=td, device=device)
+        x[:, :, :, :filled] = torch.randn((w.k, B, w.Hkv, filled, w.d), generator=g, device=device).to(td)
+        out.append(x)
+    return out[0], out[1]
