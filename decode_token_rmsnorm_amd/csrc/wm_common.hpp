@@ -37,31 +37,38 @@ template <> __device__ __forceinline__ void mma16<bf16>(f32x4 &acc, const u32x4 
                                                 0, 0, 0);
 }
 
+// (Vector elements are passed by value: a bit cast applied directly to an
+// ext-vector element lvalue was seen to read element 0 for every e.)
 template <> __device__ __forceinline__ void mma16<float>(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[e]), __builtin_bit_cast(float, b[e]), acc,
-                                               0, 0, 0);
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ae = a[e], be = b[e];
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ae), __uint_as_float(be), acc, 0, 0, 0);
+  }
 }
 
 // Unpack / pack a 16-byte fragment to / from floats.
 template <typename T> __device__ __forceinline__ void unpack16(const u32x4 &v, float *f);
 template <> __device__ __forceinline__ void unpack16<float>(const u32x4 &v, float *f) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) f[e] = __builtin_bit_cast(float, v[e]);
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t x = v[e];
+    f[e] = __uint_as_float(x);
+  }
 }
 template <> __device__ __forceinline__ void unpack16<bf16>(const u32x4 &v, float *f) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    f[2 * e] = __builtin_bit_cast(float, v[e] << 16);
-    f[2 * e + 1] = __builtin_bit_cast(float, v[e] & 0xffff0000u);
+    const uint32_t x = v[e];
+    f[2 * e] = __uint_as_float(x << 16);
+    f[2 * e + 1] = __uint_as_float(x & 0xffff0000u);
   }
 }
 template <typename T> __device__ __forceinline__ u32x4 pack16(const float *f);
 template <> __device__ __forceinline__ u32x4 pack16<float>(const float *f) {
   u32x4 v;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = __builtin_bit_cast(uint32_t, f[e]);
+  for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(f[e]);
   return v;
 }
 template <> __device__ __forceinline__ u32x4 pack16<bf16>(const float *f) {
