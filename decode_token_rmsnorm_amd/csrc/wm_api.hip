@@ -3,9 +3,11 @@
 #include "../../include/wm.h"
 #include "wm_attn.hpp"
 #include "wm_gemm.hpp"
+#include "wm_gemm2.hpp"
 #include "wm_host.hpp"
 #include "wm_pool.hpp"
 
+#include <type_traits>
 #include <vector>
 
 namespace wm {
@@ -41,12 +43,12 @@ struct ProfScope {
     if (g_prof.mask & (1u << k)) {
       a = prof_event();
       b = prof_event();
-      if (a && b) hipEventRecord(a, s);
+      if (a && b) (void)hipEventRecord(a, s);
     }
   }
   ~ProfScope() {
     if (a && b) {
-      hipEventRecord(b, s);
+      (void)hipEventRecord(b, s);
       g_prof.recs.push_back({kind, a, b});
     }
   }
@@ -85,8 +87,22 @@ template <typename T> struct Run {
         rows_cap(rows) {}
 
   template <typename P> P *at(size_t off) const { return (P *)(ws + off); }
+  // The 256 x 256 kernel (bf16 only) for steps with enough rows to fill the chip.
+  static constexpr bool kBig = std::is_same<T, bf16>::value;
+  bool big(int M) const { return kBig && M >= 2048; }
+  int parts(int M, int N) const { return (N + (big(M) ? G2N : GN) - 1) / (big(M) ? G2N : GN); }
   T *Kch(int ch) const { return (T *)cache->k + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
   T *Vch(int ch) const { return (T *)cache->v + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
+
+  // A [M, K] (row-major, lda) times B [N, K]^T on the large-tile kernel.
+  template <class EP>
+  hipError_t gemm2_rows(const T *A, int64_t lda, const T *B, int64_t ldb, const EP &ep, int M, int N, int K) {
+    if constexpr (kBig) {
+      return launch_gemm2(PRows<T>{A, lda, 0, M}, PBRows<T>{PRows<T>{B, ldb, 0, N}}, ep, M, N, K, 1, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
 
   // -------------------------------------------------------- channel attention
   template <int DH> wm_status attn_dh(int layer, const T *q, wm_tokset ts, T *out) {
@@ -182,6 +198,14 @@ template <typename T> struct Run {
     EpiKV<T> pe{(T *)cache->k, (T *)cache->v, at<float>(lay.rinvM), w->k_norm, w->rope_cos, w->rope_sin, c.k,
                 cache->B, c.Hkv, c.T_max, c.d, rows, c.eps, RowPos{ts.M, ts.s0, ts.s_step}};
     ProfScope prof(WM_K_KVPROJ, s);
+    if constexpr (kBig) {
+      if (big(rows)) {
+        PRows<T> a2{at<T>(lay.mb), c.D, (int64_t)rows * c.D, rows};
+        PKV<T> b2{(const T *)w->wk, (const T *)w->wv, c.D, (int64_t)c.Hkv * c.d * c.D, c.k, c.Hkv * c.d};
+        WM_TRY((launch_gemm2(a2, b2, pe, rows, c.Hkv * c.d, c.D, 2 * c.k, s)));
+        return WM_OK;
+      }
+    }
     WM_TRY((launch_gemm<T>(pa, pb, pe, rows, c.Hkv * c.d, c.D, 2 * c.k, s)));
     return WM_OK;
   }
@@ -213,7 +237,10 @@ template <typename T> struct Run {
         BRows<T> b{LoadRows<T>{wq + (int64_t)l * QD * D, D, 0, nullptr}};
         EpiQ<T> e{q, ss, nparts, invD, c.eps, w->q_norm + (int64_t)l * c.d, w->rope_cos, w->rope_sin, c.d, rp};
         ProfScope prof(WM_K_QPROJ, s);
-        WM_TRY((launch_gemm<T>(a, b, e, rows, QD, D, 1, s)));
+        if (big(rows))
+          WM_TRY(gemm2_rows(hb, D, wq + (int64_t)l * QD * D, D, e, rows, QD, D));
+        else
+          WM_TRY((launch_gemm<T>(a, b, e, rows, QD, D, 1, s)));
       }
       wm_status st = attn(l, q, ts, o);
       if (st != WM_OK) return st;
@@ -221,10 +248,13 @@ template <typename T> struct Run {
       {
         LoadRows<T> a{o, QD, 0, nullptr};
         BRows<T> b{LoadRows<T>{wo + (int64_t)l * D * QD, QD, 0, nullptr}};
-        EpiResid<T> e{h, hb, w->ffn_norm + (int64_t)l * D, nullptr, ss, lay.ssp};
+        EpiResid<T> e{h, hb, w->ffn_norm + (int64_t)l * D, nullptr, ss, parts(rows, D)};
         ProfScope prof(WM_K_OPROJ, s);
-        WM_TRY((launch_gemm<T>(a, b, e, rows, D, QD, 1, s)));
-        nparts = lay.ssp;
+        if (big(rows))
+          WM_TRY(gemm2_rows(o, QD, wo + (int64_t)l * D * QD, QD, e, rows, D, QD));
+        else
+          WM_TRY((launch_gemm<T>(a, b, e, rows, D, QD, 1, s)));
+        nparts = parts(rows, D);
       }
       // act = silu(W_gate b) * (W_up b), b = RMSNorm(h)
       {
@@ -232,7 +262,16 @@ template <typename T> struct Run {
         BGateUp<T> b{LoadGateUp<T>{wg + (int64_t)l * c.F * D, wu + (int64_t)l * c.F * D, D, c.F}};
         EpiSwiGLU<T> e{act, ss, nparts, invD, c.eps, c.F};
         ProfScope prof(WM_K_GATEUP, s);
-        WM_TRY((launch_gemm<T>(a, b, e, rows, 2 * c.F, D, 1, s)));
+        bool done = false;
+        if constexpr (kBig) {
+          if (big(rows)) {
+            PRows<T> a2{hb, D, 0, rows};
+            PGateUp<T> b2{wg + (int64_t)l * c.F * D, wu + (int64_t)l * c.F * D, D, c.F};
+            WM_TRY((launch_gemm2(a2, b2, e, rows, 2 * c.F, D, 1, s)));
+            done = true;
+          }
+        }
+        if (!done) WM_TRY((launch_gemm<T>(a, b, e, rows, 2 * c.F, D, 1, s)));
       }
       // h += W_down act; next state, next norm operand
       {
@@ -240,9 +279,12 @@ template <typename T> struct Run {
         BRows<T> b{LoadRows<T>{wd + (int64_t)l * D * c.F, c.F, 0, nullptr}};
         const float *gnext = l + 1 < L ? w->attn_norm + (int64_t)(l + 1) * D : w->final_norm;
         T *Snext = l + 1 < L ? S + (int64_t)(l + 1) * rows * D : nullptr;
-        EpiResid<T> e{h, hb, gnext, Snext, ss, lay.ssp};
+        EpiResid<T> e{h, hb, gnext, Snext, ss, parts(rows, D)};
         ProfScope prof(WM_K_DOWN, s);
-        WM_TRY((launch_gemm<T>(a, b, e, rows, D, c.F, 1, s)));
+        if (big(rows))
+          WM_TRY(gemm2_rows(act, c.F, wd + (int64_t)l * D * c.F, c.F, e, rows, D, c.F));
+        else
+          WM_TRY((launch_gemm<T>(a, b, e, rows, D, c.F, 1, s)));
       }
     }
     wm_status st = pool(S, ts);
@@ -432,7 +474,7 @@ wm_status wm_profile_read(int64_t *counts, double *total_ms) {
 
 wm_status wm_profile_end(void) {
   g_prof.mask = 0;
-  for (hipEvent_t e : g_prof.pool) hipEventDestroy(e);
+  for (hipEvent_t e : g_prof.pool) (void)hipEventDestroy(e);
   g_prof.pool.clear();
   g_prof.used = 0;
   g_prof.recs.clear();

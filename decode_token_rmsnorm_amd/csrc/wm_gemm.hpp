@@ -97,9 +97,10 @@ template <typename T> struct LoadRouterA {
 };
 
 // ---------------------------------------------------------------- epilogues
-// All epilogues get the fp32 C tile in LDS (pitch GCP floats) and run on all
-// 256 threads: wave w handles tile rows w, w+4, ...; lane owns columns lane
-// and lane+64.
+// Every epilogue walks a staged fp32 C tile in LDS: `nrows` rows of pitch
+// `pitch` floats, tile row rl being output row m0 + rl.  Wave w handles rows
+// w, w+4, ...; lane owns columns lane + 64*i (i < NI) of the tile, whose first
+// column is output column n0.
 
 // q = RoPE(RMSNorm_head(rinv_row * C; q_norm)) -> q [rows, Hq*d].
 template <typename T> struct EpiQ {
@@ -113,58 +114,66 @@ template <typename T> struct EpiQ {
   RowPos rp;
 };
 
-// RMSNorm over head groups of d columns + RoPE for the two values a lane owns
-// (columns c0 = lane, c1 = lane + 64 of a 128-wide head-aligned tile).
-__device__ __forceinline__ void head_norm_rope(float x[2], int lane, int d, float eps, const float *gain,
+// RMSNorm over the head groups of d columns, then RoPE, for the NI values a
+// lane owns (tile columns lane + 64*i; tiles start on a head boundary).
+template <int NI>
+__device__ __forceinline__ void head_norm_rope(float *x, int lane, int d, float eps, const float *gain,
                                                const float *cosT, const float *sinT, int pos) {
-  float s0 = x[0] * x[0], s1 = x[1] * x[1];
-  float h0, h1;
+  float y[NI], pr[NI];
+  const float invd = 1.0f / d;
   if (d == 128) {
-    h0 = h1 = wave_sum(s0 + s1);
+#pragma unroll
+    for (int p = 0; p < NI / 2; ++p) {
+      float h = wave_sum(x[2 * p] * x[2 * p] + x[2 * p + 1] * x[2 * p + 1]);
+      float sc = rsqrtf(h * invd + eps);
+      y[2 * p] = x[2 * p] * sc * gain[lane];
+      y[2 * p + 1] = x[2 * p + 1] * sc * gain[lane + 64];
+    }
+#pragma unroll
+    for (int p = 0; p < NI / 2; ++p) {
+      pr[2 * p] = y[2 * p + 1];
+      pr[2 * p + 1] = y[2 * p];
+    }
   } else {
-    h0 = group_sum(s0, d);
-    h1 = group_sum(s1, d);
-  }
-  float invd = 1.0f / d;
-  float y[2];
-  int cc[2] = {lane, lane + 64};
-  y[0] = x[0] * rsqrtf(h0 * invd + eps) * gain[cc[0] & (d - 1)];
-  y[1] = x[1] * rsqrtf(h1 * invd + eps) * gain[cc[1] & (d - 1)];
-  float pr[2];
-  if (d == 128) {
-    pr[0] = y[1];
-    pr[1] = y[0];
-  } else {
-    pr[0] = __shfl_xor(y[0], d / 2);
-    pr[1] = __shfl_xor(y[1], d / 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float h = group_sum(x[i] * x[i], d);
+      y[i] = x[i] * rsqrtf(h * invd + eps) * gain[(lane + 64 * i) & (d - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) pr[i] = __shfl_xor(y[i], d / 2);
   }
   const int half = d / 2;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int cd = cc[i] & (d - 1);
+  for (int i = 0; i < NI; ++i) {
+    int cd = (lane + 64 * i) & (d - 1);
     int m = cd & (half - 1);
     float cs = cosT[(int64_t)pos * half + m], sn = sinT[(int64_t)pos * half + m];
     x[i] = cd < half ? y[i] * cs - pr[i] * sn : pr[i] * sn + y[i] * cs;
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void run_epi(const EpiQ<T> &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+template <typename T, int NI>
+__device__ __forceinline__ void run_epi(const EpiQ<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
+                                        int nrows, int M, int N) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+  for (int rl = wave; rl < nrows; rl += 4) {
     int r = m0 + rl;
     if (r >= M) break;
     float rs = rinv_from_parts(e.ss, r, e.nparts, e.invD, e.eps);
-    float x[2] = {Cs[rl * GCP + lane] * rs, Cs[rl * GCP + lane + 64] * rs};
-    head_norm_rope(x, lane, e.d, e.eps, e.qnorm, e.cosT, e.sinT, e.rp.pos(r));
+    float x[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) x[i] = Cs[rl * pitch + lane + 64 * i] * rs;
+    head_norm_rope<NI>(x, lane, e.d, e.eps, e.qnorm, e.cosT, e.sinT, e.rp.pos(r));
     T *dst = e.q + (int64_t)r * N + n0;
-    if (n0 + lane < N) dst[lane] = from_f<T>(x[0]);
-    if (n0 + lane + 64 < N) dst[lane + 64] = from_f<T>(x[1]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (n0 + lane + 64 * i < N) dst[lane + 64 * i] = from_f<T>(x[i]);
   }
 }
 
 // Residual: h += C; hb = h * gain_next; optionally S_next = h; and the row's
-// sum of squares over this tile's columns -> ss_out[r, tileN].
+// sum of squares over this tile's columns -> ss_out[r, n0 / tile width].
 template <typename T> struct EpiResid {
   float *h;
   T *hb;
@@ -174,19 +183,20 @@ template <typename T> struct EpiResid {
   int nparts_out;
 };
 
-template <typename T>
-__device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+template <typename T, int NI>
+__device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
+                                        int nrows, int M, int N) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+  for (int rl = wave; rl < nrows; rl += 4) {
     int r = m0 + rl;
     if (r >= M) break;
     float sq = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
       int c = n0 + lane + 64 * i;
       if (c < N) {
         int64_t o = (int64_t)r * N + c;
-        float v = e.h[o] + Cs[rl * GCP + lane + 64 * i];
+        float v = e.h[o] + Cs[rl * pitch + lane + 64 * i];
         e.h[o] = v;
         e.hb[o] = from_f<T>(v * e.gain_next[c]);
         if (e.S_next) e.S_next[o] = from_f<T>(v);
@@ -194,11 +204,12 @@ __device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int
       }
     }
     sq = wave_sum(sq);
-    if (lane == 0) e.ss_out[(int64_t)r * e.nparts_out + n0 / GN] = sq;
+    if (lane == 0) e.ss_out[(int64_t)r * e.nparts_out + n0 / (64 * NI)] = sq;
   }
 }
 
-// SwiGLU: act[r, n0/2 + c] = silu(rs*C[r, c]) * (rs*C[r, c + GN/2]), c < GN/2.
+// SwiGLU: tile columns [0, 32*NI) are gate, [32*NI, 64*NI) the matching up
+// columns; act[r, n0/2 + c] = silu(rs*gate) * (rs*up).
 template <typename T> struct EpiSwiGLU {
   T *act;
   const float *ss;
@@ -207,17 +218,21 @@ template <typename T> struct EpiSwiGLU {
   int F;
 };
 
-template <typename T>
-__device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+template <typename T, int NI>
+__device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
+                                        int nrows, int M, int N) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+  for (int rl = wave; rl < nrows; rl += 4) {
     int r = m0 + rl;
     if (r >= M) break;
     float rs = rinv_from_parts(e.ss, r, e.nparts, e.invD, e.eps);
-    int f = n0 / 2 + lane;
-    if (f < e.F) {
-      float gt = Cs[rl * GCP + lane] * rs, up = Cs[rl * GCP + lane + GN / 2] * rs;
-      e.act[(int64_t)r * e.F + f] = from_f<T>(silu(gt) * up);
+#pragma unroll
+    for (int i = 0; i < NI / 2; ++i) {
+      int f = n0 / 2 + lane + 64 * i;
+      if (f < e.F) {
+        float gt = Cs[rl * pitch + lane + 64 * i] * rs, up = Cs[rl * pitch + lane + 64 * i + 32 * NI] * rs;
+        e.act[(int64_t)r * e.F + f] = from_f<T>(silu(gt) * up);
+      }
     }
   }
 }
@@ -234,11 +249,11 @@ struct EpiStoreF32 {
   float invD, eps;
 };
 
-template <typename T>
-__device__ __forceinline__ void run_epi_f32(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int M,
-                                            int N) {
+template <typename T, int NI>
+__device__ __forceinline__ void run_epi(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int pitch,
+                                        int nrows, int M, int N) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+  for (int rl = wave; rl < nrows; rl += 4) {
     int r = m0 + rl;
     if (r >= M) break;
     float rs = 1.f;
@@ -246,9 +261,9 @@ __device__ __forceinline__ void run_epi_f32(const EpiStoreF32 &e, int z, int m0,
     int64_t orow = e.out_rows ? e.out_rows[r] : r;
     float *dst = e.out + z * e.zstride + orow * e.ldo;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
       int c = n0 + lane + 64 * i;
-      if (c < N) dst[c] = Cs[rl * GCP + lane + 64 * i] * rs;
+      if (c < N) dst[c] = Cs[rl * pitch + lane + 64 * i] * rs;
     }
   }
 }
@@ -266,20 +281,23 @@ template <typename T> struct EpiKV {
   RowPos rp;
 };
 
-template <typename T>
-__device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0, const float *Cs, int M, int N) {
+template <typename T, int NI>
+__device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
+                                        int nrows, int M, int N) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int beta = z / e.k, j = z - beta * e.k;
-  for (int rl = wave; rl < GM; rl += GTHREADS / 64) {
+  for (int rl = wave; rl < nrows; rl += 4) {
     int r = m0 + rl;
     if (r >= M) break;
     float rs = e.rinvM[(int64_t)z * e.rows + r];
-    float x[2] = {Cs[rl * GCP + lane] * rs, Cs[rl * GCP + lane + 64] * rs};
+    float x[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) x[i] = Cs[rl * pitch + lane + 64 * i] * rs;
     int pos = e.rp.pos(r), b = e.rp.seq(r);
-    if (beta == 0) head_norm_rope(x, lane, e.d, e.eps, e.knorm + (int64_t)j * e.d, e.cosT, e.sinT, pos);
+    if (beta == 0) head_norm_rope<NI>(x, lane, e.d, e.eps, e.knorm + (int64_t)j * e.d, e.cosT, e.sinT, pos);
     T *dst = beta == 0 ? e.Kc : e.Vc;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
       int c = n0 + lane + 64 * i;
       if (c < N) {
         int h = c / e.d, dd = c - h * e.d;
@@ -288,15 +306,6 @@ __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0
       }
     }
   }
-}
-
-template <typename T, class E>
-__device__ __forceinline__ void epilogue(const E &e, int z, int m0, int n0, const float *Cs, int M, int N) {
-  run_epi<T>(e, z, m0, n0, Cs, M, N);
-}
-template <typename T>
-__device__ __forceinline__ void epilogue(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int M, int N) {
-  run_epi_f32<T>(e, z, m0, n0, Cs, M, N);
 }
 
 // ---------------------------------------------------------------- B loaders
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(AL al, BL bl, EP ep, int
       for (int e = 0; e < 4; ++e)
         Cs[(wm * 64 + i * 16 + (lane >> 4) * 4 + e) * GCP + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][e];
   __syncthreads();
-  epilogue<T>(ep, z, m0, n0, Cs, M, N);
+  run_epi<T, GN / 64>(ep, z, m0, n0, Cs, GCP, GM, M, N);
 }
 
 template <typename T, class AL, class BL, class EP>
