@@ -23,7 +23,7 @@ constexpr int GROW = GKB + 16;     // LDS row pitch, bytes
 constexpr int GTHREADS = 256;
 constexpr int GSTAGE = 2 * GM * GROW;  // A + B tile bytes of one stage
 constexpr int GCP = GN + 4;        // C tile pitch in floats
-static_assert(2 * GSTAGE >= GM * GCP * 4, "C tile must fit in the operand LDS");
+static_assert(2 * GSTAGE >= GM * GCP * 4 + GM * 4, "C tile and row scales must fit in the operand LDS");
 
 // Position of row r of a token set (row r = b*M + m sits at s0 + m*step).
 struct RowPos {
@@ -98,9 +98,79 @@ template <typename T> struct LoadRouterA {
 
 // ---------------------------------------------------------------- epilogues
 // Every epilogue walks a staged fp32 C tile in LDS: `nrows` rows of pitch
-// `pitch` floats, tile row rl being output row m0 + rl.  Wave w handles rows
-// w, w+4, ...; lane owns columns lane + 64*i (i < NI) of the tile, whose first
-// column is output column n0.
+// `pitch` floats, tile row rl being output row m0 + rl; lane owns columns
+// lane + 64*i (i < NI) of the tile, whose first column is output column n0.
+// First every thread computes per-row scales (RMSNorm 1/rms from partial sums
+// of squares) into `rowbuf` in LDS; then each wave takes blocks of ER rows
+// and issues all of their global loads (residual values, RoPE table entries)
+// before using any, so the loads of a block are in flight together.
+constexpr int ER = 4;  // rows per wave per step
+
+// Row scale helpers.
+__device__ __forceinline__ void fill_rowbuf_parts(float *rowbuf, const float *ss, const int *ss_rows, int nparts,
+                                                  float invD, float eps, int m0, int nrows, int M) {
+  for (int rl = threadIdx.x; rl < nrows; rl += 256) {
+    int r = m0 + rl;
+    rowbuf[rl] = r < M ? rinv_from_parts(ss, ss_rows ? ss_rows[r] : r, nparts, invD, eps) : 0.f;
+  }
+  __syncthreads();
+}
+
+// RMSNorm over the head groups of d columns, then RoPE, for the NI values a
+// lane owns (tile columns lane + 64*i; tiles start on a head boundary).
+// g[i] = gain of column i's head position, cs/sn = RoPE table entries.
+template <int NI>
+__device__ __forceinline__ void head_norm_rope(float *x, int lane, int d, float eps, const float *g, const float *cs,
+                                               const float *sn) {
+  float y[NI], pr[NI];
+  const float invd = 1.0f / d;
+  if (d == 128) {
+#pragma unroll
+    for (int p = 0; p < NI / 2; ++p) {
+      float h = wave_sum(x[2 * p] * x[2 * p] + x[2 * p + 1] * x[2 * p + 1]);
+      float sc = rsqrtf(h * invd + eps);
+      y[2 * p] = x[2 * p] * sc * g[2 * p];
+      y[2 * p + 1] = x[2 * p + 1] * sc * g[2 * p + 1];
+    }
+#pragma unroll
+    for (int p = 0; p < NI / 2; ++p) {
+      pr[2 * p] = y[2 * p + 1];
+      pr[2 * p + 1] = y[2 * p];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float h = group_sum(x[i] * x[i], d);
+      y[i] = x[i] * rsqrtf(h * invd + eps) * g[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) pr[i] = __shfl_xor(y[i], d / 2);
+  }
+  const int half = d / 2;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    int cd = (lane + 64 * i) & (d - 1);
+    x[i] = cd < half ? y[i] * cs[i] - pr[i] * sn[i] : pr[i] * sn[i] + y[i] * cs[i];
+  }
+}
+
+// Gains and RoPE table entries of a lane's columns.
+template <int NI>
+__device__ __forceinline__ void head_gains(float *g, const float *gain, int lane, int d) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) g[i] = gain[(lane + 64 * i) & (d - 1)];
+}
+template <int NI>
+__device__ __forceinline__ void rope_entries(float *cs, float *sn, const float *cosT, const float *sinT, int pos,
+                                             int lane, int d) {
+  const int half = d / 2;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    int m = (lane + 64 * i) & (half - 1);
+    cs[i] = cosT[(int64_t)pos * half + m];
+    sn[i] = sinT[(int64_t)pos * half + m];
+  }
+}
 
 // q = RoPE(RMSNorm_head(rinv_row * C; q_norm)) -> q [rows, Hq*d].
 template <typename T> struct EpiQ {
@@ -114,61 +184,33 @@ template <typename T> struct EpiQ {
   RowPos rp;
 };
 
-// RMSNorm over the head groups of d columns, then RoPE, for the NI values a
-// lane owns (tile columns lane + 64*i; tiles start on a head boundary).
-template <int NI>
-__device__ __forceinline__ void head_norm_rope(float *x, int lane, int d, float eps, const float *gain,
-                                               const float *cosT, const float *sinT, int pos) {
-  float y[NI], pr[NI];
-  const float invd = 1.0f / d;
-  if (d == 128) {
-#pragma unroll
-    for (int p = 0; p < NI / 2; ++p) {
-      float h = wave_sum(x[2 * p] * x[2 * p] + x[2 * p + 1] * x[2 * p + 1]);
-      float sc = rsqrtf(h * invd + eps);
-      y[2 * p] = x[2 * p] * sc * gain[lane];
-      y[2 * p + 1] = x[2 * p + 1] * sc * gain[lane + 64];
-    }
-#pragma unroll
-    for (int p = 0; p < NI / 2; ++p) {
-      pr[2 * p] = y[2 * p + 1];
-      pr[2 * p + 1] = y[2 * p];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float h = group_sum(x[i] * x[i], d);
-      y[i] = x[i] * rsqrtf(h * invd + eps) * gain[(lane + 64 * i) & (d - 1)];
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) pr[i] = __shfl_xor(y[i], d / 2);
-  }
-  const int half = d / 2;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    int cd = (lane + 64 * i) & (d - 1);
-    int m = cd & (half - 1);
-    float cs = cosT[(int64_t)pos * half + m], sn = sinT[(int64_t)pos * half + m];
-    x[i] = cd < half ? y[i] * cs - pr[i] * sn : pr[i] * sn + y[i] * cs;
-  }
-}
-
 template <typename T, int NI>
 __device__ __forceinline__ void run_epi(const EpiQ<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
-                                        int nrows, int M, int N) {
+                                        int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int rl = wave; rl < nrows; rl += 4) {
-    int r = m0 + rl;
-    if (r >= M) break;
-    float rs = rinv_from_parts(e.ss, r, e.nparts, e.invD, e.eps);
-    float x[NI];
+  fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
+  float g[NI];
+  head_gains<NI>(g, e.qnorm, lane, e.d);
+  for (int rb = wave * ER; rb < nrows; rb += 4 * ER) {
+    float cs[ER][NI], sn[ER][NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) x[i] = Cs[rl * pitch + lane + 64 * i] * rs;
-    head_norm_rope<NI>(x, lane, e.d, e.eps, e.qnorm, e.cosT, e.sinT, e.rp.pos(r));
-    T *dst = e.q + (int64_t)r * N + n0;
+    for (int u = 0; u < ER; ++u) {
+      int r = m0 + rb + u;
+      rope_entries<NI>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
+    }
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if (n0 + lane + 64 * i < N) dst[lane + 64 * i] = from_f<T>(x[i]);
+    for (int u = 0; u < ER; ++u) {
+      int rl = rb + u, r = m0 + rl;
+      if (r >= M) break;
+      float x[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) x[i] = Cs[rl * pitch + lane + 64 * i] * rowbuf[rl];
+      head_norm_rope<NI>(x, lane, e.d, e.eps, g, cs[u], sn[u]);
+      T *dst = e.q + (int64_t)r * N + n0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (n0 + lane + 64 * i < N) dst[lane + 64 * i] = from_f<T>(x[i]);
+    }
   }
 }
 
@@ -185,26 +227,42 @@ template <typename T> struct EpiResid {
 
 template <typename T, int NI>
 __device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
-                                        int nrows, int M, int N) {
+                                        int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int rl = wave; rl < nrows; rl += 4) {
-    int r = m0 + rl;
-    if (r >= M) break;
-    float sq = 0.f;
+  float g[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      int c = n0 + lane + 64 * i;
-      if (c < N) {
-        int64_t o = (int64_t)r * N + c;
-        float v = e.h[o] + Cs[rl * pitch + lane + 64 * i];
-        e.h[o] = v;
-        e.hb[o] = from_f<T>(v * e.gain_next[c]);
-        if (e.S_next) e.S_next[o] = from_f<T>(v);
-        sq += v * v;
+  for (int i = 0; i < NI; ++i) g[i] = n0 + lane + 64 * i < N ? e.gain_next[n0 + lane + 64 * i] : 0.f;
+  for (int rb = wave * ER; rb < nrows; rb += 4 * ER) {
+    float hv[ER][NI];
+#pragma unroll
+    for (int u = 0; u < ER; ++u) {
+      int r = m0 + rb + u;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        int c = n0 + lane + 64 * i;
+        hv[u][i] = (r < M && c < N) ? e.h[(int64_t)r * N + c] : 0.f;
       }
     }
-    sq = wave_sum(sq);
-    if (lane == 0) e.ss_out[(int64_t)r * e.nparts_out + n0 / (64 * NI)] = sq;
+#pragma unroll
+    for (int u = 0; u < ER; ++u) {
+      int rl = rb + u, r = m0 + rl;
+      if (r >= M) break;
+      float sq = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        int c = n0 + lane + 64 * i;
+        if (c < N) {
+          int64_t o = (int64_t)r * N + c;
+          float v = hv[u][i] + Cs[rl * pitch + lane + 64 * i];
+          e.h[o] = v;
+          e.hb[o] = from_f<T>(v * g[i]);
+          if (e.S_next) e.S_next[o] = from_f<T>(v);
+          sq += v * v;
+        }
+      }
+      sq = wave_sum(sq);
+      if (lane == 0) e.ss_out[(int64_t)r * e.nparts_out + n0 / (64 * NI)] = sq;
+    }
   }
 }
 
@@ -220,12 +278,13 @@ template <typename T> struct EpiSwiGLU {
 
 template <typename T, int NI>
 __device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
-                                        int nrows, int M, int N) {
+                                        int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
   for (int rl = wave; rl < nrows; rl += 4) {
     int r = m0 + rl;
     if (r >= M) break;
-    float rs = rinv_from_parts(e.ss, r, e.nparts, e.invD, e.eps);
+    float rs = rowbuf[rl];
 #pragma unroll
     for (int i = 0; i < NI / 2; ++i) {
       int f = n0 / 2 + lane + 64 * i;
@@ -251,13 +310,13 @@ struct EpiStoreF32 {
 
 template <typename T, int NI>
 __device__ __forceinline__ void run_epi(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int pitch,
-                                        int nrows, int M, int N) {
+                                        int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (e.ss) fill_rowbuf_parts(rowbuf, e.ss, e.ss_rows, e.nparts, e.invD, e.eps, m0, nrows, M);
   for (int rl = wave; rl < nrows; rl += 4) {
     int r = m0 + rl;
     if (r >= M) break;
-    float rs = 1.f;
-    if (e.ss) rs = rinv_from_parts(e.ss, e.ss_rows ? e.ss_rows[r] : r, e.nparts, e.invD, e.eps);
+    float rs = e.ss ? rowbuf[rl] : 1.f;
     int64_t orow = e.out_rows ? e.out_rows[r] : r;
     float *dst = e.out + z * e.zstride + orow * e.ldo;
 #pragma unroll
@@ -283,26 +342,43 @@ template <typename T> struct EpiKV {
 
 template <typename T, int NI>
 __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
-                                        int nrows, int M, int N) {
+                                        int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int beta = z / e.k, j = z - beta * e.k;
-  for (int rl = wave; rl < nrows; rl += 4) {
+  for (int rl = threadIdx.x; rl < nrows; rl += 256) {
     int r = m0 + rl;
-    if (r >= M) break;
-    float rs = e.rinvM[(int64_t)z * e.rows + r];
-    float x[NI];
+    rowbuf[rl] = r < M ? e.rinvM[(int64_t)z * e.rows + r] : 0.f;
+  }
+  __syncthreads();
+  float g[NI];
+  head_gains<NI>(g, e.knorm + (int64_t)j * e.d, lane, e.d);
+  for (int rb = wave * ER; rb < nrows; rb += 4 * ER) {
+    float cs[ER][NI], sn[ER][NI];
+    if (beta == 0) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) x[i] = Cs[rl * pitch + lane + 64 * i] * rs;
-    int pos = e.rp.pos(r), b = e.rp.seq(r);
-    if (beta == 0) head_norm_rope<NI>(x, lane, e.d, e.eps, e.knorm + (int64_t)j * e.d, e.cosT, e.sinT, pos);
-    T *dst = beta == 0 ? e.Kc : e.Vc;
+      for (int u = 0; u < ER; ++u) {
+        int r = m0 + rb + u;
+        rope_entries<NI>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      int c = n0 + lane + 64 * i;
-      if (c < N) {
-        int h = c / e.d, dd = c - h * e.d;
-        int64_t o = ((((int64_t)j * e.B + b) * e.Hkv + h) * e.T_max + pos) * e.d + dd;
-        dst[o] = from_f<T>(x[i]);
+    for (int u = 0; u < ER; ++u) {
+      int rl = rb + u, r = m0 + rl;
+      if (r >= M) break;
+      float x[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) x[i] = Cs[rl * pitch + lane + 64 * i] * rowbuf[rl];
+      int pos = e.rp.pos(r), b = e.rp.seq(r);
+      if (beta == 0) head_norm_rope<NI>(x, lane, e.d, e.eps, g, cs[u], sn[u]);
+      T *dst = beta == 0 ? e.Kc : e.Vc;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        int c = n0 + lane + 64 * i;
+        if (c < N) {
+          int h = c / e.d, dd = c - h * e.d;
+          int64_t o = ((((int64_t)j * e.B + b) * e.Hkv + h) * e.T_max + pos) * e.d + dd;
+          dst[o] = from_f<T>(x[i]);
+        }
       }
     }
   }
@@ -401,7 +477,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(AL al, BL bl, EP ep, int
       for (int e = 0; e < 4; ++e)
         Cs[(wm * 64 + i * 16 + (lane >> 4) * 4 + e) * GCP + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][e];
   __syncthreads();
-  run_epi<T, GN / 64>(ep, z, m0, n0, Cs, GCP, GM, M, N);
+  run_epi<T, GN / 64>(ep, z, m0, n0, Cs, GCP, GM, M, N, (float *)(smem + GM * GCP * 4));
 }
 
 template <typename T, class AL, class BL, class EP>

@@ -24,7 +24,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int G2M = 256, G2N = 256, G2KB = 128;
 constexpr int G2STAGE = (G2M + G2N) * G2KB;  // 64 KB
 constexpr int G2CP = G2N + 4;                // C tile pitch (floats)
-constexpr int G2SMEM = (2 * G2STAGE > 128 * G2CP * 4) ? 2 * G2STAGE : 128 * G2CP * 4;
+constexpr int G2CT = 128 * G2CP * 4;         // staged half C tile, bytes
+constexpr int G2SMEM = (2 * G2STAGE > G2CT + 512) ? 2 * G2STAGE : G2CT + 512;
 
 // 16-byte chunk position of logical chunk c in tile row r.
 __device__ __forceinline__ int g2_swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
@@ -128,32 +129,38 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+  // Fragments of k-step ks+1 are read from LDS while the MFMAs of step ks run.
+  auto frags = [&](const unsigned char *As, const unsigned char *Bs, int ks, u32x4 *af, u32x4 *bfr) {
+    const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int r = wm * 128 + i * 32 + (lane & 31);
+      af[i] = *(const u32x4 *)(As + r * G2KB + g2_swz(r, c) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int r = wn * 128 + j * 32 + (lane & 31);
+      bfr[j] = *(const u32x4 *)(Bs + r * G2KB + g2_swz(r, c) * 16);
+    }
+  };
   issue(0, 0);
+  u32x4 fa[2][4], fb[2][4];
   for (int kt = 0; kt < nk; ++kt) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
     const unsigned char *As = smem + (kt & 1) * G2STAGE, *Bs = As + G2M * G2KB;
+    frags(As, Bs, 0, fa[0], fb[0]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int c = 2 * ks + (lane >> 5);
-      u32x4 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int r = wm * 128 + i * 32 + (lane & 31);
-        af[i] = *(const u32x4 *)(As + r * G2KB + g2_swz(r, c) * 16);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int r = wn * 128 + j * 32 + (lane & 31);
-        bfr[j] = *(const u32x4 *)(Bs + r * G2KB + g2_swz(r, c) * 16);
-      }
+      if (ks + 1 < 4) frags(As, Bs, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
-                                                              __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[ks & 1][i]),
+                                                              __builtin_bit_cast(bf16x8, fb[ks & 1][j]), acc[i][j],
+                                                              0, 0, 0);
     }
   }
   __syncthreads();
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
                 acc[i][j][e];
     }
     __syncthreads();
-    run_epi<bf16, G2N / 64>(ep, z, m0 + h * 128, n0, Cs, G2CP, 128, M, N);
+    run_epi<bf16, G2N / 64>(ep, z, m0 + h * 128, n0, Cs, G2CP, 128, M, N, (float *)(smem + G2CT));
     __syncthreads();
   }
 }
