@@ -109,7 +109,7 @@ template <typename T> struct Run {
     const int ch = layer % c.k, G = c.Hq / c.Hkv, rows = ts.B * ts.M;
     const int rows_pair = ts.M * G;
     const bool large = rows_pair >= 128;
-    const int rb = large ? 128 : 16, nw = large ? 4 : 1;
+    const int rb = large ? 128 : 16, nw = large ? 8 : 1;
     const int nrb = (rows_pair + rb - 1) / rb;
     const int blocks = nrb * ts.B * c.Hkv;
     int64_t kmax = (int64_t)ts.s0 + (int64_t)(ts.M - 1) * ts.s_step;
@@ -140,7 +140,7 @@ template <typename T> struct Run {
     dim3 grid(nrb, ts.B * c.Hkv, ns);
     ProfScope prof(WM_K_ATTN, s);
     if (large)
-      hipLaunchKernelGGL((attn_kernel<T, DH, 4, 2>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_kernel<T, DH, 8, 1>), grid, dim3(512), 0, s, a);
     else
       hipLaunchKernelGGL((attn_kernel<T, DH, 1, 1>), grid, dim3(64), 0, s, a);
     WM_TRY(hipGetLastError());

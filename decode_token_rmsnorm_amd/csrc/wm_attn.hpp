@@ -33,17 +33,44 @@ struct AttnArgs {
   float scale_log2;    // log2(e) / sqrt(d)
 };
 
+// Transposed value tile: row dd (head dim), 64 keys in 16 quads of 4. Quad q
+// of row dd is stored at quad position q ^ (dd / E % 16) (E = elements per 16
+// bytes), which makes both the transposing stores (16 lanes writing 16 rows of
+// one quad) and the MFMA fragment reads (16 lanes reading 16 consecutive rows)
+// hit distinct banks.
+__device__ __forceinline__ int vswz(int q, int chunk) { return q ^ (chunk & 15); }
+
+// Raw element e of a 16-byte fragment, as bits (no conversion).
+template <typename T> __device__ __forceinline__ uint32_t elt_bits(const u32x4 &v, int e);
+template <> __device__ __forceinline__ uint32_t elt_bits<float>(const u32x4 &v, int e) { return v[e]; }
+template <> __device__ __forceinline__ uint32_t elt_bits<bf16>(const u32x4 &v, int e) {
+  return (v[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+}
+// Store element e of four keys' fragments as 4 consecutive elements.
+template <typename T> __device__ __forceinline__ void store4(T *dst, const u32x4 *v, int e);
+template <> __device__ __forceinline__ void store4<float>(float *dst, const u32x4 *v, int e) {
+  *(u32x4 *)dst = u32x4{v[0][e], v[1][e], v[2][e], v[3][e]};
+}
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *dst, const u32x4 *v, int e) {
+  *(u32x2 *)dst = u32x2{elt_bits<bf16>(v[0], e) | (elt_bits<bf16>(v[1], e) << 16),
+                        elt_bits<bf16>(v[2], e) | (elt_bits<bf16>(v[3], e) << 16)};
+}
+
 template <typename T, int DH, int NW, int NQ>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int E = Elt<T>::E16;       // elements per 16-byte fragment
   constexpr int KCH = 4 * E;           // k (head dim) per MFMA step
   constexpr int NCH = DH / KCH;        // MFMA steps over the head dim
-  constexpr int KP = DH + 16 / (int)sizeof(T) * 1;  // key-row pitch (elements), +16 B
-  constexpr int VP = AKT + 16 / (int)sizeof(T);     // transposed value pitch (elements)
+  constexpr int KP = DH + 16 / (int)sizeof(T);  // key-row pitch (elements), +16 B
+  constexpr int VP = AKT + 16 / (int)sizeof(T); // transposed value pitch (elements)
   constexpr int PVK = 4 * E;           // keys per PV MFMA step
   constexpr int RB = NW * NQ * 16;     // rows per block
-  __shared__ __attribute__((aligned(16))) T Ks[AKT * KP];
-  __shared__ __attribute__((aligned(16))) T Vt[DH * VP];
+  constexpr int NT = NW * 64;
+  constexpr int CPR = DH / E;          // 16-byte chunks per key row
+  constexpr int KPT = (AKT * CPR + NT - 1) / NT;        // key chunks per thread
+  constexpr int VPT = ((AKT / 4) * CPR + NT - 1) / NT;  // 4-key value items per thread
+  __shared__ __attribute__((aligned(16))) T Ks[2][AKT * KP];
+  __shared__ __attribute__((aligned(16))) T Vt[2][DH * VP];
 
   const T *qp = (const T *)a.q;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -75,6 +102,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int c = 0; c < NCH; ++c)
       qf[nq][c] = rvalid[nq] ? *(const u32x4 *)(src + c * KCH + (lane >> 4) * E) : u32x4{0, 0, 0, 0};
   }
+  // Wait for the query fragments here, so the compiler knows they are
+  // resident and does not drain the in-flight K/V prefetch to read them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  int wave_minpos = 0x7fffffff;
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) wave_minpos = min(wave_minpos, rvalid[nq] ? rpos[nq] : 0x7fffffff);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wave_minpos = min(wave_minpos, __shfl_xor(wave_minpos, off));
 
   f32x4 o[DH / 16][NQ];
   float mrun[NQ], lrun[NQ];
@@ -89,33 +124,60 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const T *Kb = (const T *)a.Kc + ((int64_t)b * a.Hkv + hk) * a.T_max * DH;
   const T *Vb = (const T *)a.Vc + ((int64_t)b * a.Hkv + hk) * a.T_max * DH;
 
-  for (int t = t0; t < t1; ++t) {
+  // Tile t: global -> registers. Loads are unconditional (addresses clamped
+  // to the last valid key, so no branch stalls the prefetch); keys past kmax
+  // are zeroed when the registers are written to LDS.
+  u32x4 kreg[KPT], vreg[VPT][4];
+  int kmaxk = kmax - 1;
+  auto gload = [&](int t) {
     const int key0 = t * AKT;
-    // keys: 16-byte chunks, row-major with padding
-    for (int c = tid; c < AKT * DH / E; c += NW * 64) {
-      int kr = c / (DH / E), cc = c - kr * (DH / E);
-      int key = key0 + kr;
-      u32x4 v = key < kmax ? *(const u32x4 *)(Kb + (int64_t)key * DH + cc * E) : u32x4{0, 0, 0, 0};
-      *(u32x4 *)(Ks + kr * KP + cc * E) = v;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      int c = min(tid + NT * i, AKT * CPR - 1), kr = c / CPR, cc = c - kr * CPR;
+      int key = min(key0 + kr, kmaxk);
+      kreg[i] = *(const u32x4 *)(Kb + (int64_t)key * DH + cc * E);
     }
-    // values: 4 keys x E columns per item, written transposed
-    for (int c = tid; c < (AKT / 4) * (DH / E); c += NW * 64) {
-      int kq = c / (DH / E), cc = c - kq * (DH / E);
-      float f[4][E];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int key = key0 + 4 * kq + i;
-        u32x4 v = key < kmax ? *(const u32x4 *)(Vb + (int64_t)key * DH + cc * E) : u32x4{0, 0, 0, 0};
-        unpack16<T>(v, f[i]);
-      }
+    for (int i = 0; i < VPT; ++i) {
+      int c = min(tid + NT * i, (AKT / 4) * CPR - 1), kq = c / CPR, cc = c - kq * CPR;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        T *dst = Vt + (cc * E + e) * VP + 4 * kq;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f<T>(f[i][e]);
+      for (int q = 0; q < 4; ++q) {
+        int key = min(key0 + 4 * kq + q, kmaxk);
+        vreg[i][q] = *(const u32x4 *)(Vb + (int64_t)key * DH + cc * E);
       }
     }
-    __syncthreads();
+  };
+  // ... registers -> LDS stage st (keys row-major, values transposed).
+  auto sstore = [&](int st, int t) {
+    const int key0 = t * AKT;
+    const u32x4 zero{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      int c = tid + NT * i, kr = c / CPR, cc = c - kr * CPR;
+      if (c < AKT * CPR) *(u32x4 *)(&Ks[st][kr * KP + cc * E]) = key0 + kr <= kmaxk ? kreg[i] : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      int c = tid + NT * i, kq = c / CPR, cc = c - kq * CPR;
+      if (c < (AKT / 4) * CPR) {
+        u32x4 v4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v4[q] = key0 + 4 * kq + q <= kmaxk ? vreg[i][q] : zero;
+#pragma unroll
+        for (int e = 0; e < E; ++e) store4<T>(&Vt[st][(cc * E + e) * VP + 4 * vswz(kq, cc)], v4, e);
+      }
+    }
+  };
+
+  if (t0 < t1) {
+    gload(t0);
+    sstore(0, t0);
+  }
+  __syncthreads();
+  for (int t = t0; t < t1; ++t) {
+    const int st = (t - t0) & 1;
+    const int key0 = t * AKT;
+    if (t + 1 < t1) gload(t + 1);
 
     // S^T = K Q^T for 4 key sub-tiles
     f32x4 s[4][NQ];
@@ -127,35 +189,44 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        u32x4 kf = *(const u32x4 *)(Ks + (kt * 16 + (lane & 15)) * KP + c * KCH + (lane >> 4) * E);
+        u32x4 kf = *(const u32x4 *)(&Ks[st][(kt * 16 + (lane & 15)) * KP + c * KCH + (lane >> 4) * E]);
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq) mma16<T>(s[kt][nq], kf, qf[nq][c]);
       }
     }
 
-    // mask, online softmax
+    // online softmax. Tiles whose keys all precede every row of this wave need
+    // no mask; the max is taken on raw scores (the scale is positive) and the
+    // scale folded into one fma before the exponential.
+    const bool full = key0 + AKT <= wave_minpos;
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
+      if (!full) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            int key = key0 + kt * 16 + (lane >> 4) * 4 + e;
+            if (key >= rpos[nq]) s[kt][nq][e] = -INFINITY;
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          int key = key0 + kt * 16 + (lane >> 4) * 4 + e;
-          float v = (key < rpos[nq]) ? s[kt][nq][e] * a.scale_log2 : -INFINITY;
-          s[kt][nq][e] = v;
-          tmax = fmaxf(tmax, v);
-        }
+        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, s[kt][nq][e]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      float mnew = fmaxf(mrun[nq], tmax);
-      float alpha = mnew == -INFINITY ? 1.f : exp2f(mrun[nq] - mnew);
+      const float mnew = fmaxf(mrun[nq], tmax * a.scale_log2);
+      const bool none = mnew == -INFINITY;
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(mrun[nq] - mnew);
+      const float nm = none ? 0.f : -mnew;
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = mnew == -INFINITY ? 0.f : exp2f(s[kt][nq][e] - mnew);
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[kt][nq][e], a.scale_log2, nm));
           s[kt][nq][e] = pv;
           psum += pv;
         }
@@ -163,8 +234,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       psum += __shfl_xor(psum, 32);
       lrun[nq] = lrun[nq] * alpha + psum;
       mrun[nq] = mnew;
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int u = 0; u < DH / 16; ++u) o[u][nq] *= alpha;
+        for (int u = 0; u < DH / 16; ++u) o[u][nq] *= alpha;
+      }
     }
 
     // O^T += V^T P^T
@@ -182,18 +255,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < DH / 16; ++u) {
-        const T *vrow = Vt + (u * 16 + (lane & 15)) * VP + kc * PVK + (lane >> 4) * 4;
+        const int dd = u * 16 + (lane & 15), q0 = kc * (PVK / 4) + (lane >> 4);
+        const T *vrow = &Vt[st][dd * VP];
         u32x4 vf;
         if constexpr (E == 8) {
-          u32x2 lo = *(const u32x2 *)vrow, hi = *(const u32x2 *)(vrow + 16);
+          u32x2 lo = *(const u32x2 *)(vrow + 4 * vswz(q0, dd / E)),
+                hi = *(const u32x2 *)(vrow + 4 * vswz(q0 + 4, dd / E));
           vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
-          vf = *(const u32x4 *)vrow;
+          vf = *(const u32x4 *)(vrow + 4 * vswz(q0, dd / E));
         }
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq) mma16<T>(o[u][nq], vf, pf[nq]);
       }
     }
+    if (t + 1 < t1) sstore(st ^ 1, t + 1);
     __syncthreads();
   }
 

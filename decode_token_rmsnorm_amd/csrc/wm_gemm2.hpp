@@ -1,18 +1,21 @@
 // wm_gemm2.hpp — large-tile bf16 GEMM  C[M, N] = A[M, K] * B[N, K]^T  for the
 // big projections (rows >= a few thousand).
 //
-// Block tile 256 x 256, k-tile 64 (128 bytes per row), 256 threads = 4 wave64s
-// in a 2 x 2 grid; each wave owns a 128 x 128 sub-tile of 4 x 4 MFMA
-// 32x32x16 bf16 tiles (256 fp32 accumulators per lane).  Both operands are
-// copied global -> LDS by the 16-byte LDS DMA (global_load_lds_dwordx4): lane
-// i of a wave writes LDS bytes [16i, 16i + 16) of its 1 KB slot, so each
-// instruction fills 8 rows of 128 bytes; which global 16-byte chunk a lane
-// fetches is XOR-swizzled by the row, and the MFMA fragment reads undo the
-// swizzle, which spreads the 32 rows a fragment read touches over all banks
-// without padding.  Two LDS stages: the DMA of k-tile t+1 runs while the MFMAs
-// of k-tile t execute, one barrier per k-tile.  The C tile is staged through
-// LDS in two 128-row halves for the same row-wise epilogues as the 128 x 128
-// kernel (wm_gemm.hpp).
+// Block tile 256 x 256, 256 threads = 4 wave64s in a 2 x 2 grid; each wave
+// owns a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 tiles (256 fp32
+// accumulators per lane).  Both operands are copied global -> LDS by the
+// 16-byte LDS DMA (global_load_lds_dwordx4): lane i of a wave writes LDS bytes
+// [16i, 16i + 16) of its 1 KB slot, so one instruction fills 1 KB of rows;
+// which global 16-byte chunk a lane fetches is XOR-swizzled by the row, and
+// the MFMA fragment reads undo the swizzle, which spreads the 32 rows a
+// fragment read touches over all banks without padding.  The k-tile is KB
+// bytes per row (128 or 64) in ST LDS stages: the DMAs of the next ST-1
+// k-tiles are in flight while the MFMAs of the current one run; each k-tile
+// starts with a wait for its own DMAs and a bare barrier (every LDS read of a
+// stage is consumed by an MFMA before the barrier that lets it be refilled, so
+// no memory fence, which would also drain the prefetch, is needed).  The C
+// tile is staged through LDS in two 128-row halves for the same row-wise
+// epilogues as the 128 x 128 kernel (wm_gemm.hpp).
 #pragma once
 
 #include "wm_gemm.hpp"
@@ -21,14 +24,25 @@ namespace wm {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int G2M = 256, G2N = 256, G2KB = 128;
-constexpr int G2STAGE = (G2M + G2N) * G2KB;  // 64 KB
-constexpr int G2CP = G2N + 4;                // C tile pitch (floats)
-constexpr int G2CT = 128 * G2CP * 4;         // staged half C tile, bytes
-constexpr int G2SMEM = (2 * G2STAGE > G2CT + 512) ? 2 * G2STAGE : G2CT + 512;
+constexpr int G2M = 256, G2N = 256;
+constexpr int G2CP = G2N + 4;         // C tile pitch (floats)
+constexpr int G2CT = 128 * G2CP * 4;  // staged half C tile, bytes
+constexpr int G2KB = 64, G2ST = 4;    // k-tile bytes per row, LDS stages
+constexpr int g2_smem(int kb, int st) {
+  return (st * (G2M + G2N) * kb > G2CT + 512) ? st * (G2M + G2N) * kb : G2CT + 512;
+}
 
-// 16-byte chunk position of logical chunk c in tile row r.
-__device__ __forceinline__ int g2_swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// 16-byte chunk position of logical chunk c in tile row r (rows of KB bytes).
+template <int KB> __device__ __forceinline__ int g2_swz(int r, int c) {
+  if constexpr (KB == 128) return c ^ ((r ^ (r >> 3)) & 7);
+  else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
+
+// s_waitcnt vmcnt(n) (expcnt / lgkmcnt unconstrained), n < 64.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 15));
+}
 
 // Row-pointer providers (rows past the end are clamped to the last row: their
 // products are computed and discarded by the epilogue).
@@ -93,33 +107,39 @@ __device__ __forceinline__ void g2_tile(int b, int nM, int nN, int &tm, int &tn,
   tn = tt / bm;
 }
 
-template <class AP, class BP, class EP>
+template <int KB, int ST, class AP, class BP, class EP>
 __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, int N, int K, int nM, int nN) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[G2SMEM];
+  constexpr int STAGE = (G2M + G2N) * KB;
+  constexpr int RPI = 1024 / KB;          // rows per DMA instruction
+  constexpr int NI = G2M / RPI / 4;       // DMA instructions per wave per operand
+  constexpr int PI = 2 * NI;              // DMA instructions per wave per k-tile
+  constexpr int KS = KB / 32;             // 16-deep MFMA steps per k-tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[g2_smem(KB, ST)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn, z;
   g2_tile(blockIdx.x, nM, nN, tm, tn, z);
   const int m0 = tm * G2M, n0 = tn * G2N;
-  const int nk = K / 64;
+  const int nk = K * 2 / KB;
 
-  // This thread's DMA sources: rows (wave*8 + j)*8 + lane/8 of each operand,
-  // chunk chosen so that LDS slot (row, lane%8) holds the swizzled chunk.
-  const char *pa[8], *pb[8];
+  // This thread's DMA sources: rows (wave*NI + j)*RPI + lane/(KB/16) of each
+  // operand, chunk chosen so that LDS slot (row, lane % (KB/16)) holds the
+  // swizzled chunk (the swizzle is an XOR, its own inverse).
+  const char *pa[NI], *pb[NI];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int row = (wave * 8 + j) * 8 + (lane >> 3);
-    int c = g2_swz(row, lane & 7);  // the swizzle is an involution on the chunk index
+  for (int j = 0; j < NI; ++j) {
+    int row = (wave * NI + j) * RPI + lane / (KB / 16);
+    int c = g2_swz<KB>(row, lane % (KB / 16));
     pa[j] = ap.row(z, m0 + row) + c * 16;
     pb[j] = bp.row(z, n0, row) + c * 16;
   }
   auto issue = [&](int kt, int stage) {
-    unsigned char *As = smem + stage * G2STAGE, *Bs = As + G2M * G2KB;
+    unsigned char *As = smem + stage * STAGE, *Bs = As + G2M * KB;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      dma16(pa[j] + kt * G2KB, As + (wave * 8 + j) * 1024);
-      dma16(pb[j] + kt * G2KB, Bs + (wave * 8 + j) * 1024);
+    for (int j = 0; j < NI; ++j) {
+      dma16(pa[j] + kt * KB, As + (wave * NI + j) * 1024);
+      dma16(pb[j] + kt * KB, Bs + (wave * NI + j) * 1024);
     }
   };
 
@@ -135,33 +155,77 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int r = wm * 128 + i * 32 + (lane & 31);
-      af[i] = *(const u32x4 *)(As + r * G2KB + g2_swz(r, c) * 16);
+      af[i] = *(const u32x4 *)(As + r * KB + g2_swz<KB>(r, c) * 16);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int r = wn * 128 + j * 32 + (lane & 31);
-      bfr[j] = *(const u32x4 *)(Bs + r * G2KB + g2_swz(r, c) * 16);
+      bfr[j] = *(const u32x4 *)(Bs + r * KB + g2_swz<KB>(r, c) * 16);
     }
   };
-  issue(0, 0);
-  u32x4 fa[2][4], fb[2][4];
-  for (int kt = 0; kt < nk; ++kt) {
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    const unsigned char *As = smem + (kt & 1) * G2STAGE, *Bs = As + G2M * G2KB;
-    frags(As, Bs, 0, fa[0], fb[0]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) frags(As, Bs, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[ks & 1][i]),
-                                                              __builtin_bit_cast(bf16x8, fb[ks & 1][j]), acc[i][j],
-                                                              0, 0, 0);
+  // Wait until at most `later` k-tiles after the awaited one are in flight.
+  auto wait_tiles = [&](int later) {
+    if constexpr (ST >= 4) {
+      if (later >= 2) wait_vmcnt<2 * PI>();
+      else if (later == 1) wait_vmcnt<PI>();
+      else wait_vmcnt<0>();
+    } else if constexpr (ST == 3) {
+      if (later >= 1) wait_vmcnt<PI>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
     }
+  };
+  auto mfmas = [&](const u32x4 *af, const u32x4 *bfr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                            __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+  };
+  // 2 MFMAs : 1 fragment read, so LDS latency hides under the MFMAs.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+  };
+
+  // Prologue: k-tiles 0..ST-2 in flight; wait for tile 0, then refill and read
+  // its first fragments.
+#pragma unroll
+  for (int t = 0; t < ST - 1; ++t)
+    if (t < nk) issue(t, t);
+  wait_tiles(min(ST - 2, nk - 1));
+  __builtin_amdgcn_s_barrier();
+  if (ST - 1 < nk) issue(ST - 1, (ST - 1) % ST);
+  u32x4 fa[2][4], fb[2][4];
+  frags(smem, smem + G2M * KB, 0, fa[0], fb[0]);
+
+  // Steady state. The barrier that makes k-tile kt+1 visible (and frees the
+  // stage of tile kt for tile kt+ST) sits before the last MFMA step of tile
+  // kt, so tile kt+1's first fragments load while that step's MFMAs run.
+  for (int kt = 0; kt < nk; ++kt) {
+    const unsigned char *As = smem + (kt % ST) * STAGE, *Bs = As + G2M * KB;
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      frags(As, Bs, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      mfmas(fa[ks & 1], fb[ks & 1]);
+      interleave();
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of tile kt are done
+    if (kt + 1 < nk) wait_tiles(min(ST - 2, nk - kt - 2));
+    __builtin_amdgcn_s_barrier();
+    if (kt + ST < nk) issue(kt + ST, (kt + ST) % ST);
+    {  // (on the last k-tile this reads a stale stage; the values are unused)
+      const unsigned char *An = smem + ((kt + 1) % ST) * STAGE;
+      frags(An, An + G2M * KB, 0, fa[KS & 1], fb[KS & 1]);
+    }
+    mfmas(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * NI, 0);  // DMA issue first
+    interleave();
   }
   __syncthreads();
 
@@ -186,11 +250,12 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
   }
 }
 
-template <class AP, class BP, class EP>
+template <int KB = G2KB, int ST = G2ST, class AP, class BP, class EP>
 hipError_t launch_gemm2(const AP &ap, const BP &bp, const EP &ep, int M, int N, int K, int Z, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const int nM = (M + G2M - 1) / G2M, nN = (N + G2N - 1) / G2N;
-  hipLaunchKernelGGL((gemm2_kernel<AP, BP, EP>), dim3(nM * nN * Z), dim3(256), 0, s, ap, bp, ep, M, N, K, nM, nN);
+  hipLaunchKernelGGL((gemm2_kernel<KB, ST, AP, BP, EP>), dim3(nM * nN * Z), dim3(256), 0, s, ap, bp, ep, M, N, K, nM,
+                     nN);
   return hipGetLastError();
 }
 
