@@ -22,6 +22,29 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_1p3b_gateup_traffic.md")
+KERNEL_SOURCES = ["decode_token_rmsnorm_amd/csrc/wm_common.hpp", "decode_token_rmsnorm_amd/csrc/wm_gemm.hpp",
+                  "decode_token_rmsnorm_amd/csrc/wm_gemm2.hpp"]
+
+
+def profiled_traffic():
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (calibrated against a plain copy), or None
+    when the kernel sources changed since those counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in text.splitlines() if ": " in l and not l.startswith(("-", "|", "#")))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("source_sha256_16", "").strip() != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -84,7 +107,7 @@ def bench_prefill(steps, warmup):
         "wall_s": wall, "per_pass_ms": per_pass, "rows_per_group": rows, "kernels": kern,
         "roofline": {"kernel": "gateup (fused gate/up projection + SwiGLU GEMM)", "bound": "mfma",
                      "achieved": flops_ga / (ms_ga / n_ga * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "traffic": None,
+                     "unit": "TFLOP/s", "traffic": profiled_traffic(),
                      "algorithmic_per_launch": f"{flops_ga:.4e} FLOP = 2*{rows}*{2 * w.F}*{w.D}"},
     }
     res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
@@ -174,7 +197,18 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
     a = ap.parse_args()
+    if a.copy_calibration:
+        import torch
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": 1 << 30, "copies": 3}))
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the method's batch elements are independent "
               "and would shard as pure data parallelism, which this build does not run.", file=sys.stderr)
