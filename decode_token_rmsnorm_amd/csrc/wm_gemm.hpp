@@ -14,6 +14,8 @@
 
 #include "wm_common.hpp"
 
+#include <type_traits>
+
 namespace wm {
 
 constexpr int GM = 128;            // block rows
@@ -98,13 +100,47 @@ template <typename T> struct LoadRouterA {
 
 // ---------------------------------------------------------------- epilogues
 // Every epilogue walks a staged fp32 C tile in LDS: `nrows` rows of pitch
-// `pitch` floats, tile row rl being output row m0 + rl; lane owns columns
-// lane + 64*i (i < NI) of the tile, whose first column is output column n0.
-// First every thread computes per-row scales (RMSNorm 1/rms from partial sums
-// of squares) into `rowbuf` in LDS; then each wave takes blocks of ER rows
-// and issues all of their global loads (residual values, RoPE table entries)
-// before using any, so the loads of a block are in flight together.
-constexpr int ER = 4;  // rows per wave per step
+// `pitch` floats, tile row rl being output row m0 + rl, 64*CPL columns wide,
+// first column = output column n0.  Lane l owns the CPL contiguous columns
+// CPL*l .. CPL*l + CPL-1, so global loads and stores are 8- or 16-byte
+// vectors.  First every thread computes per-row scales (RMSNorm 1/rms from
+// partial sums of squares) into `rowbuf` in LDS; then each wave takes blocks
+// of ER rows and issues all of their global loads (residual values, RoPE
+// table entries) before using any, so the loads of a block are in flight
+// together.  Output widths are multiples of 64, so a lane's CPL columns are
+// either all inside the output or all outside.
+constexpr int ER = 8;    // rows per wave per step (epilogues with RoPE tables)
+constexpr int ERR = 16;  // rows per wave per step (residual epilogue)
+
+template <int CPL> struct VecF;
+template <> struct VecF<2> { typedef float __attribute__((ext_vector_type(2))) t; };
+template <> struct VecF<4> { typedef float __attribute__((ext_vector_type(4))) t; };
+
+template <int CPL> __device__ __forceinline__ void ldf(float *x, const float *p) {
+  typename VecF<CPL>::t v = *(const typename VecF<CPL>::t *)p;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) x[i] = v[i];
+}
+template <int CPL> __device__ __forceinline__ void stf(float *p, const float *x) {
+  typename VecF<CPL>::t v;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) v[i] = x[i];
+  *(typename VecF<CPL>::t *)p = v;
+}
+// Store CPL values converted to T (float: 8/16 B, bf16: 4/8 B).
+template <typename T, int CPL> __device__ __forceinline__ void stT(T *p, const float *x) {
+  if constexpr (std::is_same<T, float>::value) {
+    stf<CPL>((float *)p, x);
+  } else {
+    uint32_t w[CPL / 2];
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i)
+      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[2 * i]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[2 * i + 1]) << 16);
+    if constexpr (CPL == 4) *(u32x2 *)p = u32x2{w[0], w[1]};
+    else *(uint32_t *)p = w[0];
+  }
+}
 
 // Row scale helpers.
 __device__ __forceinline__ void fill_rowbuf_parts(float *rowbuf, const float *ss, const int *ss_rows, int nparts,
@@ -116,60 +152,32 @@ __device__ __forceinline__ void fill_rowbuf_parts(float *rowbuf, const float *ss
   __syncthreads();
 }
 
-// RMSNorm over the head groups of d columns, then RoPE, for the NI values a
-// lane owns (tile columns lane + 64*i; tiles start on a head boundary).
-// g[i] = gain of column i's head position, cs/sn = RoPE table entries.
-template <int NI>
+// RMSNorm over heads of d columns (d/CPL lanes each), then RoPE: element m of
+// a head pairs with m + d/2, which sits d/(2*CPL) lanes away at the same
+// position in the lane.  g = gains, cs/sn = RoPE table entries of the lane's
+// columns.
+template <int CPL>
 __device__ __forceinline__ void head_norm_rope(float *x, int lane, int d, float eps, const float *g, const float *cs,
                                                const float *sn) {
-  float y[NI], pr[NI];
-  const float invd = 1.0f / d;
-  if (d == 128) {
+  float sq = 0.f;
 #pragma unroll
-    for (int p = 0; p < NI / 2; ++p) {
-      float h = wave_sum(x[2 * p] * x[2 * p] + x[2 * p + 1] * x[2 * p + 1]);
-      float sc = rsqrtf(h * invd + eps);
-      y[2 * p] = x[2 * p] * sc * g[2 * p];
-      y[2 * p + 1] = x[2 * p + 1] * sc * g[2 * p + 1];
-    }
+  for (int i = 0; i < CPL; ++i) sq += x[i] * x[i];
+  const float sc = rsqrtf(group_sum(sq, d / CPL) / d + eps);
+  const bool first = ((CPL * lane) & (d - 1)) < d / 2;
 #pragma unroll
-    for (int p = 0; p < NI / 2; ++p) {
-      pr[2 * p] = y[2 * p + 1];
-      pr[2 * p + 1] = y[2 * p];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float h = group_sum(x[i] * x[i], d);
-      y[i] = x[i] * rsqrtf(h * invd + eps) * g[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) pr[i] = __shfl_xor(y[i], d / 2);
-  }
-  const int half = d / 2;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    int cd = (lane + 64 * i) & (d - 1);
-    x[i] = cd < half ? y[i] * cs[i] - pr[i] * sn[i] : pr[i] * sn[i] + y[i] * cs[i];
+  for (int i = 0; i < CPL; ++i) {
+    float y = x[i] * sc * g[i];
+    float pr = __shfl_xor(y, d / (2 * CPL));
+    x[i] = first ? y * cs[i] - pr * sn[i] : pr * sn[i] + y * cs[i];
   }
 }
 
-// Gains and RoPE table entries of a lane's columns.
-template <int NI>
-__device__ __forceinline__ void head_gains(float *g, const float *gain, int lane, int d) {
-#pragma unroll
-  for (int i = 0; i < NI; ++i) g[i] = gain[(lane + 64 * i) & (d - 1)];
-}
-template <int NI>
+template <int CPL>
 __device__ __forceinline__ void rope_entries(float *cs, float *sn, const float *cosT, const float *sinT, int pos,
                                              int lane, int d) {
-  const int half = d / 2;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    int m = (lane + 64 * i) & (half - 1);
-    cs[i] = cosT[(int64_t)pos * half + m];
-    sn[i] = sinT[(int64_t)pos * half + m];
-  }
+  const int half = d / 2, m = (CPL * lane) & (half - 1);
+  ldf<CPL>(cs, cosT + (int64_t)pos * half + m);
+  ldf<CPL>(sn, sinT + (int64_t)pos * half + m);
 }
 
 // q = RoPE(RMSNorm_head(rinv_row * C; q_norm)) -> q [rows, Hq*d].
@@ -184,32 +192,32 @@ template <typename T> struct EpiQ {
   RowPos rp;
 };
 
-template <typename T, int NI>
+template <typename T, int CPL>
 __device__ __forceinline__ void run_epi(const EpiQ<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
                                         int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
-  float g[NI];
-  head_gains<NI>(g, e.qnorm, lane, e.d);
+  const int c0 = n0 + CPL * lane;
+  if (c0 >= N) return;  // no __syncthreads below
+  float g[CPL];
+  ldf<CPL>(g, e.qnorm + ((CPL * lane) & (e.d - 1)));
   for (int rb = wave * ER; rb < nrows; rb += 4 * ER) {
-    float cs[ER][NI], sn[ER][NI];
+    float cs[ER][CPL], sn[ER][CPL];
 #pragma unroll
     for (int u = 0; u < ER; ++u) {
       int r = m0 + rb + u;
-      rope_entries<NI>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
+      rope_entries<CPL>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
     }
 #pragma unroll
     for (int u = 0; u < ER; ++u) {
       int rl = rb + u, r = m0 + rl;
       if (r >= M) break;
-      float x[NI];
+      float x[CPL];
+      ldf<CPL>(x, Cs + rl * pitch + CPL * lane);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) x[i] = Cs[rl * pitch + lane + 64 * i] * rowbuf[rl];
-      head_norm_rope<NI>(x, lane, e.d, e.eps, g, cs[u], sn[u]);
-      T *dst = e.q + (int64_t)r * N + n0;
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if (n0 + lane + 64 * i < N) dst[lane + 64 * i] = from_f<T>(x[i]);
+      for (int i = 0; i < CPL; ++i) x[i] *= rowbuf[rl];
+      head_norm_rope<CPL>(x, lane, e.d, e.eps, g, cs[u], sn[u]);
+      stT<T, CPL>(e.q + (int64_t)r * N + c0, x);
     }
   }
 }
@@ -225,49 +233,49 @@ template <typename T> struct EpiResid {
   int nparts_out;
 };
 
-template <typename T, int NI>
+template <typename T, int CPL>
 __device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
                                         int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float g[NI];
+  const int c0 = n0 + CPL * lane;
+  const bool on = c0 < N;
+  float g[CPL];
+  if (on) ldf<CPL>(g, e.gain_next + c0);
+  for (int rb = wave * ERR; rb < nrows; rb += 4 * ERR) {
+    float hv[ERR][CPL];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) g[i] = n0 + lane + 64 * i < N ? e.gain_next[n0 + lane + 64 * i] : 0.f;
-  for (int rb = wave * ER; rb < nrows; rb += 4 * ER) {
-    float hv[ER][NI];
-#pragma unroll
-    for (int u = 0; u < ER; ++u) {
+    for (int u = 0; u < ERR; ++u) {
       int r = m0 + rb + u;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        int c = n0 + lane + 64 * i;
-        hv[u][i] = (r < M && c < N) ? e.h[(int64_t)r * N + c] : 0.f;
-      }
+      if (on && r < M) ldf<CPL>(hv[u], e.h + (int64_t)r * N + c0);
     }
 #pragma unroll
-    for (int u = 0; u < ER; ++u) {
+    for (int u = 0; u < ERR; ++u) {
       int rl = rb + u, r = m0 + rl;
       if (r >= M) break;
       float sq = 0.f;
+      if (on) {
+        float x[CPL], xb[CPL];
+        ldf<CPL>(x, Cs + rl * pitch + CPL * lane);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        int c = n0 + lane + 64 * i;
-        if (c < N) {
-          int64_t o = (int64_t)r * N + c;
-          float v = hv[u][i] + Cs[rl * pitch + lane + 64 * i];
-          e.h[o] = v;
-          e.hb[o] = from_f<T>(v * g[i]);
-          if (e.S_next) e.S_next[o] = from_f<T>(v);
-          sq += v * v;
+        for (int i = 0; i < CPL; ++i) {
+          x[i] += hv[u][i];
+          xb[i] = x[i] * g[i];
+          sq += x[i] * x[i];
         }
+        int64_t o = (int64_t)r * N + c0;
+        stf<CPL>(e.h + o, x);
+        stT<T, CPL>(e.hb + o, xb);
+        if (e.S_next) stT<T, CPL>(e.S_next + o, x);
       }
       sq = wave_sum(sq);
-      if (lane == 0) e.ss_out[(int64_t)r * e.nparts_out + n0 / (64 * NI)] = sq;
+      if (lane == 0) e.ss_out[(int64_t)r * e.nparts_out + n0 / (64 * CPL)] = sq;
     }
   }
 }
 
-// SwiGLU: tile columns [0, 32*NI) are gate, [32*NI, 64*NI) the matching up
-// columns; act[r, n0/2 + c] = silu(rs*gate) * (rs*up).
+// SwiGLU: tile columns [0, 32*CPL) are gate, [32*CPL, 64*CPL) the matching up
+// columns; each lane takes CPL/2 consecutive gate columns and reads their up
+// partners from the staged tile: act[r, n0/2 + c] = silu(rs*gate) * (rs*up).
 template <typename T> struct EpiSwiGLU {
   T *act;
   const float *ss;
@@ -276,28 +284,34 @@ template <typename T> struct EpiSwiGLU {
   int F;
 };
 
-template <typename T, int NI>
+template <typename T, int CPL>
 __device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
                                         int nrows, int M, int N, float *rowbuf) {
+  constexpr int OPL = CPL / 2;  // outputs per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
+  const int f0 = n0 / 2 + OPL * lane;
+  if (f0 >= e.F) return;  // no __syncthreads below
   for (int rl = wave; rl < nrows; rl += 4) {
     int r = m0 + rl;
     if (r >= M) break;
-    float rs = rowbuf[rl];
+    const float rs = rowbuf[rl];
+    const float *row = Cs + rl * pitch + OPL * lane;
+    float y[OPL];
 #pragma unroll
-    for (int i = 0; i < NI / 2; ++i) {
-      int f = n0 / 2 + lane + 64 * i;
-      if (f < e.F) {
-        float gt = Cs[rl * pitch + lane + 64 * i] * rs, up = Cs[rl * pitch + lane + 64 * i + 32 * NI] * rs;
-        e.act[(int64_t)r * e.F + f] = from_f<T>(silu(gt) * up);
-      }
+    for (int i = 0; i < OPL; ++i) y[i] = silu(row[i] * rs) * (row[i + 32 * CPL] * rs);
+    T *dst = e.act + (int64_t)r * e.F + f0;
+    if constexpr (OPL == 2) {
+      stT<T, 2>(dst, y);
+    } else {
+      dst[0] = from_f<T>(y[0]);
     }
   }
 }
 
 // Plain fp32 store with an optional row scale from partial sums and an
 // optional output row map: out[(map ? map[r] : r) * ldo + c] (per z offset).
+// (Element-wise: the router's output width L*k need not be a multiple of 4.)
 struct EpiStoreF32 {
   float *out;
   int64_t ldo, zstride;
@@ -308,7 +322,7 @@ struct EpiStoreF32 {
   float invD, eps;
 };
 
-template <typename T, int NI>
+template <typename T, int CPL>
 __device__ __forceinline__ void run_epi(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int pitch,
                                         int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -320,7 +334,7 @@ __device__ __forceinline__ void run_epi(const EpiStoreF32 &e, int z, int m0, int
     int64_t orow = e.out_rows ? e.out_rows[r] : r;
     float *dst = e.out + z * e.zstride + orow * e.ldo;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < CPL; ++i) {
       int c = n0 + lane + 64 * i;
       if (c < N) dst[c] = Cs[rl * pitch + lane + 64 * i] * rs;
     }
@@ -340,7 +354,7 @@ template <typename T> struct EpiKV {
   RowPos rp;
 };
 
-template <typename T, int NI>
+template <typename T, int CPL>
 __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
                                         int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -350,36 +364,32 @@ __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0
     rowbuf[rl] = r < M ? e.rinvM[(int64_t)z * e.rows + r] : 0.f;
   }
   __syncthreads();
-  float g[NI];
-  head_gains<NI>(g, e.knorm + (int64_t)j * e.d, lane, e.d);
+  const int c0 = n0 + CPL * lane;
+  if (c0 >= N) return;  // no __syncthreads below
+  const int h = c0 / e.d, dd = c0 - h * e.d;
+  float g[CPL];
+  ldf<CPL>(g, e.knorm + (int64_t)j * e.d + ((CPL * lane) & (e.d - 1)));
+  T *base = beta == 0 ? e.Kc : e.Vc;
   for (int rb = wave * ER; rb < nrows; rb += 4 * ER) {
-    float cs[ER][NI], sn[ER][NI];
+    float cs[ER][CPL], sn[ER][CPL];
     if (beta == 0) {
 #pragma unroll
       for (int u = 0; u < ER; ++u) {
         int r = m0 + rb + u;
-        rope_entries<NI>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
+        rope_entries<CPL>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
       }
     }
 #pragma unroll
     for (int u = 0; u < ER; ++u) {
       int rl = rb + u, r = m0 + rl;
       if (r >= M) break;
-      float x[NI];
+      float x[CPL];
+      ldf<CPL>(x, Cs + rl * pitch + CPL * lane);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) x[i] = Cs[rl * pitch + lane + 64 * i] * rowbuf[rl];
+      for (int i = 0; i < CPL; ++i) x[i] *= rowbuf[rl];
       int pos = e.rp.pos(r), b = e.rp.seq(r);
-      if (beta == 0) head_norm_rope<NI>(x, lane, e.d, e.eps, g, cs[u], sn[u]);
-      T *dst = beta == 0 ? e.Kc : e.Vc;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        int c = n0 + lane + 64 * i;
-        if (c < N) {
-          int h = c / e.d, dd = c - h * e.d;
-          int64_t o = ((((int64_t)j * e.B + b) * e.Hkv + h) * e.T_max + pos) * e.d + dd;
-          dst[o] = from_f<T>(x[i]);
-        }
-      }
+      if (beta == 0) head_norm_rope<CPL>(x, lane, e.d, e.eps, g, cs[u], sn[u]);
+      stT<T, CPL>(base + ((((int64_t)j * e.B + b) * e.Hkv + h) * e.T_max + pos) * e.d + dd, x);
     }
   }
 }

@@ -87,18 +87,24 @@ __device__ __forceinline__ void dma16(const void *g, unsigned char *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
-// Block order: tiles are split into 8 contiguous ranges, one per XCD (blocks
-// are dispatched to XCDs round-robin), and inside a range walk M-bands of 4
-// tiles so that neighbouring tiles on one XCD share operand panels in its L2.
+// Block order. MAP bit 0: split the tiles into 8 contiguous ranges, one per
+// XCD (assuming round-robin dispatch); MAP >> 1 selects M-bands of 1, 4, 8 or
+// 2 tiles walked before moving along N. Measured on the gate/up shape with
+// weights that do not stay cached: plain order with 4-tile bands is fastest
+// (the per-XCD ranges were slowest), so MAP = 2 is the default.
+template <int MAP>
 __device__ __forceinline__ void g2_tile(int b, int nM, int nN, int &tm, int &tn, int &z) {
   const int total = gridDim.x;
-  const int q = total / 8, r = total % 8;
-  const int x = b % 8, i = b / 8;
-  int t = x * q + (x < r ? x : r) + i;
+  int t = b;
+  if constexpr (MAP & 1) {  // contiguous tile range per XCD
+    const int q = total / 8, r = total % 8;
+    const int x = b % 8, i = b / 8;
+    t = x * q + (x < r ? x : r) + i;
+  }
   const int per_z = nM * nN;
   z = t / per_z;
   t -= z * per_z;
-  const int band = 4;
+  constexpr int band = (MAP >> 1) == 0 ? 1 : (MAP >> 1) == 1 ? 4 : (MAP >> 1) == 2 ? 8 : 2;
   const int g = t / (band * nN);
   const int m_first = g * band;
   const int bm = (nM - m_first) < band ? (nM - m_first) : band;
@@ -107,7 +113,7 @@ __device__ __forceinline__ void g2_tile(int b, int nM, int nN, int &tm, int &tn,
   tn = tt / bm;
 }
 
-template <int KB, int ST, class AP, class BP, class EP>
+template <int KB, int ST, int MAP, class AP, class BP, class EP>
 __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, int N, int K, int nM, int nN) {
   constexpr int STAGE = (G2M + G2N) * KB;
   constexpr int RPI = 1024 / KB;          // rows per DMA instruction
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn, z;
-  g2_tile(blockIdx.x, nM, nN, tm, tn, z);
+  g2_tile<MAP>(blockIdx.x, nM, nN, tm, tn, z);
   const int m0 = tm * G2M, n0 = tn * G2N;
   const int nk = K * 2 / KB;
 
@@ -250,12 +256,12 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
   }
 }
 
-template <int KB = G2KB, int ST = G2ST, class AP, class BP, class EP>
+template <int KB = G2KB, int ST = G2ST, int MAP = 2, class AP, class BP, class EP>
 hipError_t launch_gemm2(const AP &ap, const BP &bp, const EP &ep, int M, int N, int K, int Z, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const int nM = (M + G2M - 1) / G2M, nN = (N + G2N - 1) / G2N;
-  hipLaunchKernelGGL((gemm2_kernel<KB, ST, AP, BP, EP>), dim3(nM * nN * Z), dim3(256), 0, s, ap, bp, ep, M, N, K, nM,
-                     nN);
+  hipLaunchKernelGGL((gemm2_kernel<KB, ST, MAP, AP, BP, EP>), dim3(nM * nN * Z), dim3(256), 0, s, ap, bp, ep, M, N,
+                     K, nM, nN);
   return hipGetLastError();
 }
 
