@@ -156,10 +156,17 @@ def bench_decode(steps, warmup):
     wall = time.perf_counter() - t0
     prof = profile_read()
     n_at, ms_at = prof["attn"]
+    # per-kind breakdown from a few further (untimed) steps
+    profile((1 << len(C.KINDS)) - 1)
+    for _ in range(5):
+        wm.decode_step(model, tok, t, cache, logits, ws)
+    torch.cuda.synchronize()
+    kern = {k: {"launches": c, "avg_us": 1e3 * m / c} for k, (c, m) in profile_read().items()}
     kv_bytes = 2.0 * w.B * w.Hkv * t * w.d * 2  # K and V of one channel, bf16, per layer launch
     ach = kv_bytes / (ms_at / n_at * 1e-3) / 1e9
     return {"workload": "decode_d512: L16 D512 Hq8 Hkv4 d64 F1536 k16 p2 V32768 B64, t=2047 cached, bf16",
             "value": w.B * steps / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall / steps, "steps": steps,
+            "kernels_avg_us": kern,
             "roofline": {"kernel": "attn (strict-causal channel attention, split keys)", "bound": "hbm",
                          "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                          "traffic": None,

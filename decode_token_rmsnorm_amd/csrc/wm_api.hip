@@ -6,6 +6,7 @@
 #include "wm_gemm2.hpp"
 #include "wm_host.hpp"
 #include "wm_pool.hpp"
+#include "wm_skinny.hpp"
 
 #include <type_traits>
 #include <vector>
@@ -104,6 +105,13 @@ template <typename T> struct Run {
     }
   }
 
+  // Few rows: the k-split skinny kernel; otherwise the 128 x 128 tiled one.
+  template <class AL, class BL, class EP>
+  hipError_t gemm1(const AL &al, const BL &bl, const EP &ep, int M, int N, int K, int Z) {
+    if (M <= SK_MAX_ROWS) return launch_skinny<T>(al, bl, ep, M, N, K, Z, at<float>(lay.skp), s);
+    return launch_gemm<T>(al, bl, ep, M, N, K, Z, s);
+  }
+
   // -------------------------------------------------------- channel attention
   template <int DH> wm_status attn_dh(int layer, const T *q, wm_tokset ts, T *out) {
     const int ch = layer % c.k, G = c.Hq / c.Hkv, rows = ts.B * ts.M;
@@ -117,7 +125,7 @@ template <typename T> struct Run {
     const int ntile = (int)((kmax + AKT - 1) / AKT);
     const int64_t target = large ? 2048 : 4096;  // waves in flight
     int ns = 1;
-    while ((int64_t)blocks * nw * ns < target && ns * 2 <= 16 && ntile / (ns * 2) >= 2 &&
+    while ((int64_t)blocks * nw * ns < target && ns * 2 <= ACS && ntile / (ns * 2) >= 2 &&
            (int64_t)(ns * 2) * rows <= part_rows_cap(rows_cap))
       ns *= 2;
     AttnArgs a;
@@ -145,8 +153,9 @@ template <typename T> struct Run {
       hipLaunchKernelGGL((attn_kernel<T, DH, 1, 1>), grid, dim3(64), 0, s, a);
     WM_TRY(hipGetLastError());
     if (ns > 1) {
-      hipLaunchKernelGGL((attn_combine<T>), dim3(rows), dim3(256), 0, s, a.part_o, a.part_ml, (void *)out, rows, c.Hq,
-                         c.d, ns);
+      const int64_t nout = (int64_t)rows * c.Hq * c.d;
+      hipLaunchKernelGGL((attn_combine<T>), dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, s, a.part_o, a.part_ml,
+                         (void *)out, rows, c.Hq, c.d, ns);
       WM_TRY(hipGetLastError());
     }
     return WM_OK;
@@ -178,13 +187,21 @@ template <typename T> struct Run {
     WM_TRY(hipGetLastError());
     }
     // router: [rows, R*D] x [L*k, R*D]^T per branch
-    LoadRouterA<T> ra{S, at<float>(lay.rinvS), w->src_norm, rows, c.D, c.L, c.p};
     BRows<T> rb{LoadRows<T>{(const T *)w->router, (int64_t)R * c.D, (int64_t)c.L * c.k * R * c.D, nullptr}};
     EpiStoreF32 re{at<float>(lay.Aw), (int64_t)c.L * c.k, (int64_t)rows * c.L * c.k, nullptr, nullptr, nullptr, 0, 0.f,
                    0.f};
     {
       ProfScope prof(WM_K_ROUTER, s);
-      WM_TRY((launch_gemm<T>(ra, rb, re, rows, c.L * c.k, R * c.D, 2, s)));
+      if (rows <= kSkinnyRows) {
+        hipLaunchKernelGGL((router_input<T>), dim3(rows, 2), dim3(256), 0, s, S, at<float>(lay.rinvS), w->src_norm,
+                           at<T>(lay.u), rows, c.L, c.p, R, c.D);
+        WM_TRY(hipGetLastError());
+        LoadRows<T> ua{at<T>(lay.u), (int64_t)R * c.D, (int64_t)rows * R * c.D, nullptr};
+        WM_TRY((gemm1(ua, rb, re, rows, c.L * c.k, R * c.D, 2)));
+      } else {
+        LoadRouterA<T> ra{S, at<float>(lay.rinvS), w->src_norm, rows, c.D, c.L, c.p};
+        WM_TRY((gemm1(ra, rb, re, rows, c.L * c.k, R * c.D, 2)));
+      }
     }
     wm_status st;
     {
@@ -206,7 +223,7 @@ template <typename T> struct Run {
         return WM_OK;
       }
     }
-    WM_TRY((launch_gemm<T>(pa, pb, pe, rows, c.Hkv * c.d, c.D, 2 * c.k, s)));
+    WM_TRY((gemm1(pa, pb, pe, rows, c.Hkv * c.d, c.D, 2 * c.k)));
     return WM_OK;
   }
 
@@ -240,7 +257,7 @@ template <typename T> struct Run {
         if (big(rows))
           WM_TRY(gemm2_rows(hb, D, wq + (int64_t)l * QD * D, D, e, rows, QD, D));
         else
-          WM_TRY((launch_gemm<T>(a, b, e, rows, QD, D, 1, s)));
+          WM_TRY((gemm1(a, b, e, rows, QD, D, 1)));
       }
       wm_status st = attn(l, q, ts, o);
       if (st != WM_OK) return st;
@@ -253,7 +270,7 @@ template <typename T> struct Run {
         if (big(rows))
           WM_TRY(gemm2_rows(o, QD, wo + (int64_t)l * D * QD, QD, e, rows, D, QD));
         else
-          WM_TRY((launch_gemm<T>(a, b, e, rows, D, QD, 1, s)));
+          WM_TRY((gemm1(a, b, e, rows, D, QD, 1)));
         nparts = parts(rows, D);
       }
       // act = silu(W_gate b) * (W_up b), b = RMSNorm(h)
@@ -271,7 +288,7 @@ template <typename T> struct Run {
             done = true;
           }
         }
-        if (!done) WM_TRY((launch_gemm<T>(a, b, e, rows, 2 * c.F, D, 1, s)));
+        if (!done) WM_TRY((gemm1(a, b, e, rows, 2 * c.F, D, 1)));
       }
       // h += W_down act; next state, next norm operand
       {
@@ -284,7 +301,7 @@ template <typename T> struct Run {
         if (big(rows))
           WM_TRY(gemm2_rows(act, c.F, wd + (int64_t)l * D * c.F, c.F, e, rows, D, c.F));
         else
-          WM_TRY((launch_gemm<T>(a, b, e, rows, D, c.F, 1, s)));
+          WM_TRY((gemm1(a, b, e, rows, D, c.F, 1)));
       }
     }
     wm_status st = pool(S, ts);
@@ -299,7 +316,7 @@ template <typename T> struct Run {
       BRows<T> b{LoadRows<T>{(const T *)w->lm_head, D, 0, nullptr}};
       EpiStoreF32 e{logits, c.V, 0, rout, ss, rin, nparts, invD, c.eps};
       ProfScope prof(WM_K_LMHEAD, s);
-      WM_TRY((launch_gemm<T>(a, b, e, n, c.V, D, 1, s)));
+      WM_TRY((gemm1(a, b, e, n, c.V, D, 1)));
     }
     return WM_OK;
   }

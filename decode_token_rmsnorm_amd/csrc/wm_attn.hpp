@@ -299,27 +299,43 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 }
 
 // Merge split partials: o = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m).
+// One thread per output element; every split's values are loaded before any
+// is used (nsplit <= ACS), so a thread waits for memory once.
+constexpr int ACS = 16;  // most splits the attention dispatch makes
 template <typename T>
-__global__ void attn_combine(const float *part_o, const float *part_ml, void *out, int rows, int Hq, int d,
-                             int nsplit) {
-  int r = blockIdx.x;
-  for (int i = threadIdx.x; i < Hq * d; i += blockDim.x) {
-    int h = i / d;
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_ml[(((int64_t)s * rows + r) * Hq + h) * 2]);
-    float l = 0.f, acc = 0.f;
-    if (mx != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        int64_t base = ((int64_t)s * rows + r) * Hq + h;
-        float ms = part_ml[base * 2];
-        if (ms == -INFINITY) continue;
-        float w = exp2f(ms - mx);
-        l += part_ml[base * 2 + 1] * w;
-        acc += part_o[base * d + (i - h * d)] * w;
+__global__ __launch_bounds__(256) void attn_combine(const float *part_o, const float *part_ml, void *out, int rows,
+                                                    int Hq, int d, int nsplit) {
+  const int64_t n = (int64_t)rows * Hq * d;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t rh = i / d, plane = (int64_t)rows * Hq;
+  const int dd = (int)(i - rh * d);
+  float ms[ACS], ls[ACS], os[ACS];
+#pragma unroll
+  for (int s = 0; s < ACS; ++s) {
+    if (s < nsplit) {
+      const int64_t base = s * plane + rh;
+      ms[s] = part_ml[base * 2];
+      ls[s] = part_ml[base * 2 + 1];
+      os[s] = part_o[base * d + dd];
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < ACS; ++s)
+    if (s < nsplit) mx = fmaxf(mx, ms[s]);
+  float l = 0.f, acc = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < ACS; ++s) {
+      if (s < nsplit && ms[s] != -INFINITY) {
+        const float w = exp2f(ms[s] - mx);
+        l += ls[s] * w;
+        acc += os[s] * w;
       }
     }
-    ((T *)out)[(int64_t)r * Hq * d + i] = from_f<T>(l > 0.f ? acc / l : 0.f);
   }
+  ((T *)out)[i] = from_f<T>(l > 0.f ? acc / l : 0.f);
 }
 
 }  // namespace wm

@@ -42,6 +42,11 @@ __device__ __forceinline__ float rinv_from_parts(const float *ss, int row, int n
 }
 
 // ---------------------------------------------------------------- loaders
+// A loader resolves a tile row once, before the k loop (row(...) -> handle),
+// and then fetches 16-byte chunks of it (load(handle, kbyte)).  Rows past the
+// end are clamped to the last row: their products land in tile rows or
+// columns that every epilogue skips, and no load depends on a branch (a
+// conditional load makes the compiler wait for every load in flight).
 
 // Plain row-major operand [rows, K] with leading dimension ld (elements), an
 // optional row gather and a per-blockIdx.z offset.
@@ -49,12 +54,13 @@ template <typename T> struct LoadRows {
   const T *p;
   int64_t ld, zstride;
   const int *gather;  // nullable: logical row r reads row gather[r]
-  __device__ __forceinline__ u32x4 load(int z, int row, int nrows, int kbyte) const {
-    if (row >= nrows) return u32x4{0, 0, 0, 0};
-    int64_t r = gather ? gather[row] : row;
-    const char *base = (const char *)(p + z * zstride + r * ld);
-    return *(const u32x4 *)(base + kbyte);
+  typedef const char *H;
+  __device__ __forceinline__ H row(int z, int r, int nrows) const {
+    r = r < nrows ? r : nrows - 1;
+    const int64_t rr = gather ? gather[r] : r;
+    return (const char *)(p + z * zstride + rr * ld);
   }
+  __device__ __forceinline__ u32x4 load(H h, int kbyte) const { return *(const u32x4 *)(h + kbyte); }
 };
 
 // B operand of the fused gate/up projection: tile-local rows [0, GN/2) are
@@ -64,12 +70,13 @@ template <typename T> struct LoadGateUp {
   const T *gate, *up;
   int64_t ld;
   int F;
-  __device__ __forceinline__ u32x4 load(int n0, int jl, int kbyte) const {
+  typedef const char *H;
+  __device__ __forceinline__ H row(int n0, int jl) const {
     int f = n0 / 2 + (jl & (GN / 2 - 1));
-    if (f >= F) return u32x4{0, 0, 0, 0};
-    const T *m = jl < GN / 2 ? gate : up;
-    return *(const u32x4 *)((const char *)(m + (int64_t)f * ld) + kbyte);
+    f = f < F ? f : F - 1;
+    return (const char *)((jl < GN / 2 ? gate : up) + (int64_t)f * ld);
   }
+  __device__ __forceinline__ u32x4 load(H h, int kbyte) const { return *(const u32x4 *)(h + kbyte); }
 };
 
 // A operand of the router: row r is the concatenation over blocks b < R of
@@ -81,17 +88,20 @@ template <typename T> struct LoadRouterA {
   const float *rinvS;
   const float *gain;  // [2, L, D]
   int rows, D, L, p;
-  __device__ __forceinline__ u32x4 load(int z, int row, int nrows, int kbyte) const {
-    if (row >= nrows) return u32x4{0, 0, 0, 0};
+  struct H {
+    int row, z;
+  };
+  __device__ __forceinline__ H row(int z, int r, int nrows) const { return H{r < nrows ? r : nrows - 1, z}; }
+  __device__ __forceinline__ u32x4 load(H h, int kbyte) const {
     constexpr int E = Elt<T>::E16;
-    int kel = kbyte / (int)sizeof(T);
-    int blk = kel / D, col = kel - blk * D;
-    int layer = blk * p;
-    u32x4 v = *(const u32x4 *)(S + ((int64_t)layer * rows + row) * D + col);
+    const int kel = kbyte / (int)sizeof(T);
+    const int blk = kel / D, col = kel - blk * D;
+    const int layer = blk * p;
+    u32x4 v = *(const u32x4 *)(S + ((int64_t)layer * rows + h.row) * D + col);
     float f[E];
     unpack16<T>(v, f);
-    float s = rinvS[(int64_t)layer * rows + row];
-    const float *g = gain + ((int64_t)z * L + layer) * D + col;
+    const float s = rinvS[(int64_t)layer * rows + h.row];
+    const float *g = gain + ((int64_t)h.z * L + layer) * D + col;
 #pragma unroll
     for (int e = 0; e < E; ++e) f[e] *= s * g[e];
     return pack16<T>(f);
@@ -142,34 +152,58 @@ template <typename T, int CPL> __device__ __forceinline__ void stT(T *p, const f
   }
 }
 
+// Waves in the block (the epilogues run on 256- and 512-thread blocks).
+__device__ __forceinline__ int nwaves() { return (int)(blockDim.x >> 6); }
+
 // Row scale helpers.
 __device__ __forceinline__ void fill_rowbuf_parts(float *rowbuf, const float *ss, const int *ss_rows, int nparts,
                                                   float invD, float eps, int m0, int nrows, int M) {
-  for (int rl = threadIdx.x; rl < nrows; rl += 256) {
+  for (int rl = threadIdx.x; rl < nrows; rl += blockDim.x) {
     int r = m0 + rl;
     rowbuf[rl] = r < M ? rinv_from_parts(ss, ss_rows ? ss_rows[r] : r, nparts, invD, eps) : 0.f;
   }
   __syncthreads();
 }
 
-// RMSNorm over heads of d columns (d/CPL lanes each), then RoPE: element m of
-// a head pairs with m + d/2, which sits d/(2*CPL) lanes away at the same
-// position in the lane.  g = gains, cs/sn = RoPE table entries of the lane's
-// columns.
-template <int CPL>
-__device__ __forceinline__ void head_norm_rope(float *x, int lane, int d, float eps, const float *g, const float *cs,
-                                               const float *sn) {
-  float sq = 0.f;
+// RMSNorm over heads of d columns (d/CPL lanes each), then RoPE, for NR rows
+// at once (their lane reductions and exchanges overlap instead of forming one
+// long chain per row): element m of a head pairs with m + d/2, which sits
+// d/(2*CPL) lanes away at the same position in the lane.  g = gains, cs/sn =
+// RoPE table entries of the lane's columns per row.
+template <int CPL, int NR>
+__device__ __forceinline__ void head_norm_rope(float (&x)[NR][CPL], int lane, int d, float eps, const float *g,
+                                               const float (&cs)[NR][CPL], const float (&sn)[NR][CPL]) {
+  const int width = d / CPL;
+  float sq[NR];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) sq += x[i] * x[i];
-  const float sc = rsqrtf(group_sum(sq, d / CPL) / d + eps);
+  for (int u = 0; u < NR; ++u) {
+    sq[u] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) sq[u] += x[u][i] * x[u][i];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+    if (o < width) {
+#pragma unroll
+      for (int u = 0; u < NR; ++u) sq[u] += __shfl_xor(sq[u], o);
+    }
+  float y[NR][CPL], pr[NR][CPL];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const float sc = rsqrtf(sq[u] / d + eps);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) y[u][i] = x[u][i] * sc * g[i];
+  }
+#pragma unroll
+  for (int u = 0; u < NR; ++u)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) pr[u][i] = __shfl_xor(y[u][i], d / (2 * CPL));
   const bool first = ((CPL * lane) & (d - 1)) < d / 2;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    float y = x[i] * sc * g[i];
-    float pr = __shfl_xor(y, d / (2 * CPL));
-    x[i] = first ? y * cs[i] - pr * sn[i] : pr * sn[i] + y * cs[i];
-  }
+  for (int u = 0; u < NR; ++u)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      x[u][i] = first ? y[u][i] * cs[u][i] - pr[u][i] * sn[u][i] : pr[u][i] * sn[u][i] + y[u][i] * cs[u][i];
 }
 
 template <int CPL>
@@ -201,23 +235,26 @@ __device__ __forceinline__ void run_epi(const EpiQ<T> &e, int z, int m0, int n0,
   if (c0 >= N) return;  // no __syncthreads below
   float g[CPL];
   ldf<CPL>(g, e.qnorm + ((CPL * lane) & (e.d - 1)));
-  for (int rb = wave * ER; rb < nrows; rb += 4 * ER) {
+  for (int rb = wave * ER; rb < nrows; rb += nwaves() * ER) {
     float cs[ER][CPL], sn[ER][CPL];
 #pragma unroll
     for (int u = 0; u < ER; ++u) {
       int r = m0 + rb + u;
       rope_entries<CPL>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
     }
+    float x[ER][CPL];
 #pragma unroll
     for (int u = 0; u < ER; ++u) {
-      int rl = rb + u, r = m0 + rl;
-      if (r >= M) break;
-      float x[CPL];
-      ldf<CPL>(x, Cs + rl * pitch + CPL * lane);
+      const int rl = rb + u < nrows ? rb + u : nrows - 1;
+      ldf<CPL>(x[u], Cs + rl * pitch + CPL * lane);
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) x[i] *= rowbuf[rl];
-      head_norm_rope<CPL>(x, lane, e.d, e.eps, g, cs[u], sn[u]);
-      stT<T, CPL>(e.q + (int64_t)r * N + c0, x);
+      for (int i = 0; i < CPL; ++i) x[u][i] *= rowbuf[rl];
+    }
+    head_norm_rope<CPL, ER>(x, lane, e.d, e.eps, g, cs, sn);
+#pragma unroll
+    for (int u = 0; u < ER; ++u) {
+      const int r = m0 + rb + u;
+      if (rb + u < nrows && r < M) stT<T, CPL>(e.q + (int64_t)r * N + c0, x[u]);
     }
   }
 }
@@ -239,36 +276,47 @@ __device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = n0 + CPL * lane;
   const bool on = c0 < N;
+  const int cl = on ? c0 : N - CPL;  // (off lanes read a valid column and store nothing)
   float g[CPL];
-  if (on) ldf<CPL>(g, e.gain_next + c0);
-  for (int rb = wave * ERR; rb < nrows; rb += 4 * ERR) {
-    float hv[ERR][CPL];
+  ldf<CPL>(g, e.gain_next + cl);
+  for (int rb = wave * ERR; rb < nrows; rb += nwaves() * ERR) {
+    float hv[ERR][CPL], sq[ERR];
 #pragma unroll
     for (int u = 0; u < ERR; ++u) {
-      int r = m0 + rb + u;
-      if (on && r < M) ldf<CPL>(hv[u], e.h + (int64_t)r * N + c0);
+      const int r = m0 + rb + u;
+      ldf<CPL>(hv[u], e.h + (int64_t)(r < M ? r : M - 1) * N + cl);
     }
 #pragma unroll
     for (int u = 0; u < ERR; ++u) {
-      int rl = rb + u, r = m0 + rl;
-      if (r >= M) break;
-      float sq = 0.f;
-      if (on) {
-        float x[CPL], xb[CPL];
-        ldf<CPL>(x, Cs + rl * pitch + CPL * lane);
+      const int rl = rb + u, r = m0 + rl;
+      const bool ok = on && rl < nrows && r < M;
+      float x[CPL], xb[CPL];
+      ldf<CPL>(x, Cs + (rl < nrows ? rl : nrows - 1) * pitch + CPL * lane);
+      sq[u] = 0.f;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          x[i] += hv[u][i];
-          xb[i] = x[i] * g[i];
-          sq += x[i] * x[i];
-        }
-        int64_t o = (int64_t)r * N + c0;
+      for (int i = 0; i < CPL; ++i) {
+        x[i] += hv[u][i];
+        xb[i] = x[i] * g[i];
+        sq[u] += ok ? x[i] * x[i] : 0.f;
+      }
+      if (ok) {
+        const int64_t o = (int64_t)r * N + c0;
         stf<CPL>(e.h + o, x);
         stT<T, CPL>(e.hb + o, xb);
         if (e.S_next) stT<T, CPL>(e.S_next + o, x);
       }
-      sq = wave_sum(sq);
-      if (lane == 0) e.ss_out[(int64_t)r * e.nparts_out + n0 / (64 * CPL)] = sq;
+    }
+    // the rows' sums over the wave, reduced together
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+      for (int u = 0; u < ERR; ++u) sq[u] += __shfl_xor(sq[u], o);
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < ERR; ++u) {
+        const int r = m0 + rb + u;
+        if (rb + u < nrows && r < M) e.ss_out[(int64_t)r * e.nparts_out + n0 / (64 * CPL)] = sq[u];
+      }
     }
   }
 }
@@ -292,7 +340,7 @@ __device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, in
   fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
   const int f0 = n0 / 2 + OPL * lane;
   if (f0 >= e.F) return;  // no __syncthreads below
-  for (int rl = wave; rl < nrows; rl += 4) {
+  for (int rl = wave; rl < nrows; rl += nwaves()) {
     int r = m0 + rl;
     if (r >= M) break;
     const float rs = rowbuf[rl];
@@ -327,7 +375,7 @@ __device__ __forceinline__ void run_epi(const EpiStoreF32 &e, int z, int m0, int
                                         int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (e.ss) fill_rowbuf_parts(rowbuf, e.ss, e.ss_rows, e.nparts, e.invD, e.eps, m0, nrows, M);
-  for (int rl = wave; rl < nrows; rl += 4) {
+  for (int rl = wave; rl < nrows; rl += nwaves()) {
     int r = m0 + rl;
     if (r >= M) break;
     float rs = e.ss ? rowbuf[rl] : 1.f;
@@ -359,7 +407,7 @@ __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0
                                         int nrows, int M, int N, float *rowbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int beta = z / e.k, j = z - beta * e.k;
-  for (int rl = threadIdx.x; rl < nrows; rl += 256) {
+  for (int rl = threadIdx.x; rl < nrows; rl += blockDim.x) {
     int r = m0 + rl;
     rowbuf[rl] = r < M ? e.rinvM[(int64_t)z * e.rows + r] : 0.f;
   }
@@ -370,7 +418,7 @@ __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0
   float g[CPL];
   ldf<CPL>(g, e.knorm + (int64_t)j * e.d + ((CPL * lane) & (e.d - 1)));
   T *base = beta == 0 ? e.Kc : e.Vc;
-  for (int rb = wave * ER; rb < nrows; rb += 4 * ER) {
+  for (int rb = wave * ER; rb < nrows; rb += nwaves() * ER) {
     float cs[ER][CPL], sn[ER][CPL];
     if (beta == 0) {
 #pragma unroll
@@ -379,44 +427,53 @@ __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0
         rope_entries<CPL>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
       }
     }
+    float x[ER][CPL];
 #pragma unroll
     for (int u = 0; u < ER; ++u) {
-      int rl = rb + u, r = m0 + rl;
-      if (r >= M) break;
-      float x[CPL];
-      ldf<CPL>(x, Cs + rl * pitch + CPL * lane);
+      const int rl = rb + u < nrows ? rb + u : nrows - 1;
+      ldf<CPL>(x[u], Cs + rl * pitch + CPL * lane);
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) x[i] *= rowbuf[rl];
-      int pos = e.rp.pos(r), b = e.rp.seq(r);
-      if (beta == 0) head_norm_rope<CPL>(x, lane, e.d, e.eps, g, cs[u], sn[u]);
-      stT<T, CPL>(base + ((((int64_t)j * e.B + b) * e.Hkv + h) * e.T_max + pos) * e.d + dd, x);
+      for (int i = 0; i < CPL; ++i) x[u][i] *= rowbuf[rl];
+    }
+    if (beta == 0) head_norm_rope<CPL, ER>(x, lane, e.d, e.eps, g, cs, sn);
+#pragma unroll
+    for (int u = 0; u < ER; ++u) {
+      const int r = m0 + rb + u;
+      if (rb + u < nrows && r < M) {
+        const int pos = e.rp.pos(r), b = e.rp.seq(r);
+        stT<T, CPL>(base + ((((int64_t)j * e.B + b) * e.Hkv + h) * e.T_max + pos) * e.d + dd, x[u]);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- B loaders
+// row(z, n0, jl, N): tile row jl of the block whose first output column is n0.
 template <typename T> struct BRows {
   LoadRows<T> L;
-  __device__ __forceinline__ u32x4 load(int z, int n0, int jl, int N, int kbyte) const {
-    return L.load(z, n0 + jl, N, kbyte);
-  }
+  typedef const char *H;
+  __device__ __forceinline__ H row(int z, int n0, int jl, int N) const { return L.row(z, n0 + jl, N); }
+  __device__ __forceinline__ u32x4 load(H h, int kbyte) const { return L.load(h, kbyte); }
 };
 template <typename T> struct BGateUp {
   LoadGateUp<T> L;
-  __device__ __forceinline__ u32x4 load(int z, int n0, int jl, int N, int kbyte) const { return L.load(n0, jl, kbyte); }
+  typedef const char *H;
+  __device__ __forceinline__ H row(int z, int n0, int jl, int N) const { return L.row(n0, jl); }
+  __device__ __forceinline__ u32x4 load(H h, int kbyte) const { return L.load(h, kbyte); }
 };
 // Pool projection weights: z = beta*k + j -> wk[j] or wv[j].
 template <typename T> struct BKV {
   const T *wk, *wv;
   int64_t ld, mstride;
   int k;
-  __device__ __forceinline__ u32x4 load(int z, int n0, int jl, int N, int kbyte) const {
+  typedef const char *H;
+  __device__ __forceinline__ H row(int z, int n0, int jl, int N) const {
     int n = n0 + jl;
-    if (n >= N) return u32x4{0, 0, 0, 0};
-    int beta = z / k, j = z - beta * k;
-    const T *m = (beta == 0 ? wk : wv) + j * mstride + (int64_t)n * ld;
-    return *(const u32x4 *)((const char *)m + kbyte);
+    n = n < N ? n : N - 1;
+    const int beta = z / k, j = z - beta * k;
+    return (const char *)((beta == 0 ? wk : wv) + j * mstride + (int64_t)n * ld);
   }
+  __device__ __forceinline__ u32x4 load(H h, int kbyte) const { return *(const u32x4 *)(h + kbyte); }
 };
 
 // ---------------------------------------------------------------- kernel
@@ -436,12 +493,20 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(AL al, BL bl, EP ep, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  typename AL::H ha[4];
+  typename BL::H hb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid + GTHREADS * i) >> 3;
+    ha[i] = al.row(z, m0 + r, M);
+    hb[i] = bl.row(z, n0, r, N);
+  }
   auto gload = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int c = tid + GTHREADS * i, r = c >> 3, cb = c & 7;
-      ra[i] = al.load(z, m0 + r, M, kt * GKB + cb * 16);
-      rb[i] = bl.load(z, n0, r, N, kt * GKB + cb * 16);
+      const int cb = (tid + GTHREADS * i) & 7;
+      ra[i] = al.load(ha[i], kt * GKB + cb * 16);
+      rb[i] = bl.load(hb[i], kt * GKB + cb * 16);
     }
   };
   auto sstore = [&](int buf) {

@@ -18,8 +18,24 @@ inline int64_t part_rows_cap(int rows) {
   return c < m ? c : m;
 }
 
+// Steps with at most this many rows run their GEMMs on the k-split skinny
+// kernel and build the router input explicitly (workspace region u).  That
+// kernel gives each block one k slice of this many bytes per row; with more
+// than one slice the 64 x 128 fp32 tile of every (tile, slice) goes through
+// the workspace region skp.
+constexpr int kSkinnyRows = 128;
+constexpr int kSkinnySliceBytes = 1024;
+inline int skinny_slices(int64_t k_bytes) { return (int)((k_bytes + kSkinnySliceBytes - 1) / kSkinnySliceBytes); }
+// Partial tiles (floats) one skinny GEMM [rows, N, K] x Z needs (0 with one slice).
+inline size_t skinny_partial_floats(int rows, int N, int64_t k_bytes, int Z) {
+  const int S = skinny_slices(k_bytes);
+  if (S <= 1) return 0;
+  const size_t nM = (size_t)(rows + 63) / 64, nN = (size_t)(N + 127) / 128;
+  return (size_t)Z * nM * nN * S * 64 * 128;
+}
+
 struct WsLayout {
-  size_t h, hb, ss, q, o, act, S, rinvS, Aw, mb, rinvM, part_o, part_ml, rowmap, total;
+  size_t h, hb, ss, q, o, act, S, rinvS, Aw, mb, rinvM, u, skp, part_o, part_ml, rowmap, total;
   int ssp;  // partial sums of squares per row
 };
 
@@ -44,6 +60,21 @@ inline WsLayout ws_layout(const wm_config &c, int rows) {
   w.Aw = take(2 * R * c.L * c.k * 4);
   w.mb = take(2 * (size_t)c.k * R * c.D * es);
   w.rinvM = take(2 * (size_t)c.k * R * 4);
+  const size_t nR = (size_t)(c.L + c.p - 1) / c.p;
+  const int sr = rows < kSkinnyRows ? rows : kSkinnyRows;
+  w.u = take(2 * (size_t)sr * nR * c.D * es);
+  {  // the largest split GEMM of a few-row step
+    const int64_t D = c.D, F = c.F, QD = (int64_t)c.Hq * c.d, KVD = (int64_t)c.Hkv * c.d, LK = (int64_t)c.L * c.k;
+    size_t m = skinny_partial_floats(sr, (int)QD, D * es, 1);
+    auto mx = [&](size_t v) { m = v > m ? v : m; };
+    mx(skinny_partial_floats(sr, (int)D, QD * es, 1));
+    mx(skinny_partial_floats(sr, (int)(2 * F), D * es, 1));
+    mx(skinny_partial_floats(sr, (int)D, F * es, 1));
+    mx(skinny_partial_floats(sr, (int)LK, (int64_t)nR * D * es, 2));
+    mx(skinny_partial_floats(sr, (int)KVD, D * es, 2 * c.k));
+    mx(skinny_partial_floats(sr, c.V, D * es, 1));
+    w.skp = take(m * 4);
+  }
   size_t cap = (size_t)part_rows_cap(rows);
   w.part_o = take(cap * qd * 4);
   w.part_ml = take(cap * c.Hq * 2 * 4);

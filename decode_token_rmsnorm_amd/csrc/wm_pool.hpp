@@ -7,6 +7,7 @@
 //               stores rho_j (.) m_j (channel gain folded in; the channel's
 //               1/rms is applied after the projection, which is linear) and
 //               1/rms(m_j) for the projection epilogue.
+//  router_input the router's normalised input rows, written out (few rows)
 //  embed_rows   h_0 = E[token] (+ the first state, the next GEMM's operand and
 //               its sum of squares)
 //  rope_table   cos/sin of s * base^(-2m/d), double precision, rounded
@@ -93,6 +94,29 @@ __global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, 
     int beta = tid / k, j = tid - beta * k;
     float v = red[0][beta * KMAX + j] + red[1][beta * KMAX + j] + red[2][beta * KMAX + j] + red[3][beta * KMAX + j];
     rinvM[((int64_t)beta * k + j) * rows + r] = rsqrtf(v / D + eps);
+  }
+}
+
+// Router input of few-row steps, both branches:
+// u[beta, r, b*D + c] = S[b*p, r, c] * rinvS[b*p, r] * gain[beta, b*p, c].
+template <typename T>
+__global__ __launch_bounds__(256) void router_input(const T *S, const float *rinvS, const float *gain, T *u, int rows,
+                                                    int L, int p, int R, int D) {
+  constexpr int E = Elt<T>::E16;
+  const int r = blockIdx.x, beta = blockIdx.y;
+  for (int b = 0; b < R; ++b) {
+    const int l = b * p;
+    const float s = rinvS[(int64_t)l * rows + r];
+    const T *src = S + ((int64_t)l * rows + r) * D;
+    const float *g = gain + ((int64_t)beta * L + l) * D;
+    T *dst = u + ((int64_t)beta * rows + r) * R * D + (int64_t)b * D;
+    for (int c = threadIdx.x * E; c < D; c += 256 * E) {
+      float f[E];
+      unpack16<T>(*(const u32x4 *)(src + c), f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] *= s * g[c + e];
+      *(u32x4 *)(dst + c) = pack16<T>(f);
+    }
   }
 }
 
