@@ -1,8 +1,8 @@
 """Benchmark: cyclic-prefill tokens/s per pass (1.3B-scale WhiteMatter model,
 L=28 D=1792 14/2 heads x 128, FFN 4864, k=14, p=2, V=32768, B=64, T=2048,
-g=16) and decode tokens/s (L=16 D=512 8/4 x 64, k=16, B=64, 2047 cached
-positions) on one GPU, with the dominant kernel's roofline fraction and the
-oracle timed on the host cores.
+g=16), decode tokens/s (L=16 D=512 8/4 x 64, k=16, B=64, 2047 cached
+positions) and the KV-pool mix/append call on a [16, 16384, 512] state stack,
+on one GPU, with roofline fractions and the oracle timed on the host cores.
 
 A step is one cyclic Gauss-Seidel prefill pass over the whole batch; the
 first (warmup) pass starts from the zero cache and later passes refine it,
@@ -173,6 +173,48 @@ def bench_decode(steps, warmup):
                          "algorithmic_per_launch": f"{kv_bytes:.4e} B = 2*{w.B}*{w.Hkv}*{t}*{w.d}*2"}}
 
 
+def bench_mix(calls, warmup):
+    """One wm_mix_kv over the whole state stack [16, 8*2048, 512] (bf16, k=8,
+    4 KV heads x 64): pool + append of 16,384 tokens."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from decode_token_rmsnorm_amd import _lib as C
+    from wm_inputs import WORKLOADS, make_state_stack_device, make_weights
+
+    w = WORKLOADS["mix_bf16"]
+    rows = w.B * w.T
+    model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    states = make_state_stack_device(w, rows, seed=2)
+    cache = wm.new_cache(model, w.B)
+    ws = model.workspace(rows)
+    for _ in range(warmup):
+        wm.mix_kv(model, states, w.B, w.T, 0, 1, cache, ws)
+    profile(1 << C.KINDS.index("router") | 1 << C.KINDS.index("mix") | 1 << C.KINDS.index("kvproj"))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(calls):
+        wm.mix_kv(model, states, w.B, w.T, 0, 1, cache, ws)
+    b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / calls
+    kern = {k: {"launches": c, "avg_us": 1e3 * m / c} for k, (c, m) in profile_read().items()}
+    R = w.R
+    per_tok = w.L * w.D * 2 + 2 * w.k * w.Hkv * w.d * 2
+    wbytes = 2 * (w.L * w.k) * (R * w.D) * 2 + 2 * w.k * (w.Hkv * w.d) * w.D * 2
+    nbytes = rows * per_tok + wbytes
+    ach = nbytes / (us * 1e-6) / 1e9
+    del states, cache, ws, model
+    torch.cuda.empty_cache()
+    return {"workload": "mix_bf16: state stack [L16, B8*T2048, D512] bf16, router over layers 0,2..14, k8, "
+                        "K/V 512 -> 4 x 64, RoPE base 1e6, whole cache written",
+            "us_per_call": us, "calls": calls, "kernels_avg_us": kern,
+            "roofline": {"kernel": "wm_mix_kv (router + mix + K/V projection and append)", "bound": "hbm",
+                         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                         "traffic": None,
+                         "algorithmic_per_launch": f"{nbytes:.4e} B = {rows}*{per_tok} + {wbytes} weights"}}
+
+
 def cpu_baseline():
     """The float64 oracle on a bounded sample of the prefill workload: the first
     group step (q=0, 128 positions) of sequence 0 against the zero cache."""
@@ -204,6 +246,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-mix", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
     a = ap.parse_args()
@@ -224,6 +267,7 @@ def main():
     torch.cuda.set_device(0)
     w, pre = bench_prefill(a.steps, a.warmup)
     dec = None if a.skip_decode else bench_decode(a.decode_steps, 5)
+    mix = None if a.skip_mix else bench_mix(20, 3)
     cpu = None if a.no_cpu_baseline else cpu_baseline()
     value = w.B * w.T / (pre["wall_s"] / a.steps)
     line = {
@@ -240,6 +284,7 @@ def main():
         "pass_mfma_frac": pre["pass_tflops"] / BF16_PEAK_TFLOPS,
         "kernels_avg_us": pre["kernels"],
         "decode": dec,
+        "mix_kv": mix,
     }
     print(json.dumps(line), flush=True)
 

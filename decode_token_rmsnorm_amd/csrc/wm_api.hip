@@ -7,6 +7,8 @@
 #include "wm_host.hpp"
 #include "wm_pool.hpp"
 #include "wm_skinny.hpp"
+#include "wm_attn2.hpp"
+#include "wm_pool2.hpp"
 
 #include <type_traits>
 #include <vector>
@@ -117,13 +119,15 @@ template <typename T> struct Run {
     const int ch = layer % c.k, G = c.Hq / c.Hkv, rows = ts.B * ts.M;
     const int rows_pair = ts.M * G;
     const bool large = rows_pair >= 128;
-    const int rb = large ? 128 : 16, nw = large ? 8 : 1;
+    // bf16 with many rows: 4 waves of 32 rows on 32x32 MFMAs (attn2_kernel)
+    const bool v2 = large && std::is_same<T, bf16>::value && DH >= 64;
+    const int rb = large ? 128 : 16, nw = v2 ? 4 : large ? 8 : 1;
     const int nrb = (rows_pair + rb - 1) / rb;
     const int blocks = nrb * ts.B * c.Hkv;
     int64_t kmax = (int64_t)ts.s0 + (int64_t)(ts.M - 1) * ts.s_step;
     if (kmax > c.T_max) kmax = c.T_max;
     const int ntile = (int)((kmax + AKT - 1) / AKT);
-    const int64_t target = large ? 2048 : 4096;  // waves in flight
+    const int64_t target = v2 ? 4096 : large ? 2048 : 4096;  // waves in flight
     int ns = 1;
     while ((int64_t)blocks * nw * ns < target && ns * 2 <= ACS && ntile / (ns * 2) >= 2 &&
            (int64_t)(ns * 2) * rows <= part_rows_cap(rows_cap))
@@ -147,7 +151,12 @@ template <typename T> struct Run {
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)c.d);
     dim3 grid(nrb, ts.B * c.Hkv, ns);
     ProfScope prof(WM_K_ATTN, s);
-    if (large)
+    if constexpr (std::is_same<T, bf16>::value && DH >= 64) {
+      if (v2) hipLaunchKernelGGL((attn2_kernel<DH, 1>), grid, dim3(256), 0, s, a);
+    }
+    if (v2)
+      ;
+    else if (large)
       hipLaunchKernelGGL((attn_kernel<T, DH, 8, 1>), grid, dim3(512), 0, s, a);
     else
       hipLaunchKernelGGL((attn_kernel<T, DH, 1, 1>), grid, dim3(64), 0, s, a);
@@ -171,8 +180,20 @@ template <typename T> struct Run {
 
   // -------------------------------------------------------- KV pool
   template <int KMAX> wm_status mix(const T *S, int rows) {
-    hipLaunchKernelGGL((pool_mix<T, KMAX>), dim3(rows), dim3(256), 0, s, S, at<float>(lay.rinvS), at<float>(lay.Aw),
-                       w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
+    if constexpr (std::is_same<T, bf16>::value) {  // MFMA mix (wm_pool2.hpp)
+      const int64_t zs = 2 * (int64_t)rows * c.L * c.k;
+      if (c.k <= 16)
+        hipLaunchKernelGGL((pool_mix2<1>), dim3((rows + PM_RT4 - 1) / PM_RT4), dim3(256), 0, s, S, at<float>(lay.rinvS),
+                           at<float>(lay.Aw), 1, zs, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM),
+                           rows, c.L, c.k, c.D, c.eps);
+      else
+        hipLaunchKernelGGL((pool_mix2<2>), dim3((rows + PM_RT4 / 2 - 1) / (PM_RT4 / 2)), dim3(256), 0, s, S, at<float>(lay.rinvS),
+                           at<float>(lay.Aw), 1, zs, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM),
+                           rows, c.L, c.k, c.D, c.eps);
+    } else {
+      hipLaunchKernelGGL((pool_mix<T, KMAX>), dim3(rows), dim3(256), 0, s, S, at<float>(lay.rinvS), at<float>(lay.Aw),
+                         w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
+    }
     WM_TRY(hipGetLastError());
     return WM_OK;
   }

@@ -1,0 +1,280 @@
+// wm_attn2.hpp — strict-causal channel attention, bf16, for token sets with
+// many query rows per (sequence, KV head) pair (prefill group steps).
+//
+// Same contract as attn_kernel (wm_attn.hpp): grid (row blocks, B*Hkv,
+// splits), rows rho = m*G + g of one (b, hk) pair at position s0 + m*step,
+// keys s < position, partials for the split combine.  A block is 4 waves of
+// 32*QB query rows; 64-key tiles of K and V are staged row-major in LDS,
+// double buffered, and shared by the waves.
+//
+// Both products use 32x32x16 MFMAs, so every K and V element read from LDS
+// serves 32 queries.  Scores are computed transposed, S^T = K Q^T, in two
+// independent 32-key accumulators: a lane holds 32 keys of one query (column
+// lane%32), the other 32 keys of the tile sit in lane ^ 32, so the
+// online-softmax statistics need one exchange and the output rescale is
+// lane-local.  The probabilities feed O^T += V^T P^T straight from the
+// accumulators: the MFMA k slot j of lane half h stands for key 4h + j
+// (j < 4) or 8 + 4h + (j - 4) of each 16-key slice.  V stays row-major in
+// LDS and its transposed fragments come from the LDS transpose read
+// (ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of
+// the 8-byte rows addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12), with
+// lane i addressing key 4h + i/4 (+ slice offset) at head dims 4(i%4) of its
+// 16-dim half; two reads give the 8 slots.
+//
+// LDS layouts (rows padded, not swizzled, so every fragment address is a
+// per-lane base plus an immediate offset):
+//  K tile: row = key, DH bf16 + 16 bytes; the 32-row fragment reads and the
+//          row-wise stores are conflict-free in a 64-bank model.
+//  V tile: row = key, DH bf16 + 64 bytes, so the 4 keys x 32 bytes read by a
+//          16-lane group and the other half of the head dims fall on disjoint
+//          banks.
+#pragma once
+
+#include "wm_attn.hpp"
+#include "wm_gemm.hpp"
+
+namespace wm {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+
+// QB 32-row query blocks per wave (block = 4 waves = 128*QB rows): with QB = 2
+// every K and V fragment read from LDS feeds two MFMAs.
+template <int DH, int QB>
+__global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
+  static_assert(DH == 64 || DH == 128, "head dim");
+  static_assert(QB == 1 || QB == 2, "query blocks per wave");
+  constexpr int KT = 64;                          // keys per tile
+  constexpr int NCH = DH / 16;                    // 16-deep MFMA steps over the head dim
+  constexpr int CPR = DH / 8;                     // 16-byte chunks per key row
+  constexpr int ND = DH / 32;                     // 32-row blocks of O^T
+  constexpr int KP = DH + 8;                      // K row pitch (elements)
+  constexpr int VP = DH + 32;                     // V row pitch (elements)
+  constexpr int RB = 128 * QB;                    // rows per block
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][KT * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][KT * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
+  const int pair = blockIdx.y, b = pair / a.Hkv, hk = pair - b * a.Hkv;
+  const int nrows = a.M * a.G;
+  const int rb0 = blockIdx.x * RB;
+  if (rb0 >= nrows) return;
+  const int last = min(nrows, rb0 + RB) - 1;
+  const int kmax = min(a.s0 + (last / a.G) * a.step, a.T_max);  // keys s < kmax for the block
+  const int ntile = (kmax + KT - 1) / KT;
+  const int tps = (ntile + a.nsplit - 1) / a.nsplit;
+  const int t0 = blockIdx.z * tps, t1 = min(ntile, t0 + tps);
+
+  // this lane's query in each block qb (rows past the end read the last row
+  // and store nothing)
+  bool rvalid[QB];
+  int rpos[QB], rrow[QB], rhead[QB];
+  u32x4 qf[QB][NCH];
+  int minpos = 0x7fffffff;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int rho_raw = rb0 + wave * 32 * QB + qb * 32 + ql;
+    rvalid[qb] = rho_raw < nrows;
+    const int rho = rvalid[qb] ? rho_raw : nrows - 1;
+    const int m = rho / a.G, g = rho - m * a.G;
+    rpos[qb] = a.s0 + m * a.step;
+    rrow[qb] = b * a.M + m;
+    rhead[qb] = hk * a.G + g;
+    const bf16 *src = (const bf16 *)a.q + ((int64_t)rrow[qb] * a.Hq + rhead[qb]) * DH + 8 * h;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qf[qb][c] = *(const u32x4 *)(src + 16 * c);
+    if (rvalid[qb]) minpos = min(minpos, rpos[qb]);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries resident before the K/V prefetch starts
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) minpos = min(minpos, __shfl_xor(minpos, off));
+
+  f32x16 o[QB][ND];
+  float mrun[QB], lrun[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mrun[qb] = -INFINITY;
+    lrun[qb] = 0.f;
+#pragma unroll
+    for (int u = 0; u < ND; ++u) o[qb][u] = f32x16{};
+  }
+
+  const bf16 *Kb = (const bf16 *)a.Kc + ((int64_t)b * a.Hkv + hk) * a.T_max * DH;
+  const bf16 *Vb = (const bf16 *)a.Vc + ((int64_t)b * a.Hkv + hk) * a.T_max * DH;
+  const int klast = kmax - 1;
+
+  // global -> registers (addresses clamped to the last key, no branches)
+  constexpr int RPT = KT * CPR / 256;  // 16-byte chunks per thread of each of K and V
+  u32x4 kreg[RPT], vreg[RPT];
+  auto gload = [&](int t) {
+    const int key0 = t * KT;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c = tid + 256 * i, kr = c / CPR, cc = c - kr * CPR;
+      const int64_t off = (int64_t)min(key0 + kr, klast) * DH + 8 * cc;
+      kreg[i] = *(const u32x4 *)(Kb + off);
+      vreg[i] = *(const u32x4 *)(Vb + off);
+    }
+  };
+  // registers -> LDS stage st
+  auto sstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c = tid + 256 * i, kr = c / CPR, cc = c - kr * CPR;
+      *(u32x4 *)(&Ks[st][kr * KP + 8 * cc]) = kreg[i];
+      *(u32x4 *)(&Vs[st][kr * VP + 8 * cc]) = vreg[i];
+    }
+  };
+  // transpose-read base of this lane: key 4h + (lane%16)/4, head dim 16*((lane/16)%2) + 4*(lane%4)
+  const int vbase = (4 * h + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+  if (t0 < t1) {
+    gload(t0);
+    sstore(0);
+  }
+  __syncthreads();
+  const float sc = a.scale_log2;
+  for (int t = t0; t < t1; ++t) {
+    const int st = (t - t0) & 1;
+    const int key0 = t * KT;
+    if (t + 1 < t1) gload(t + 1);
+
+    const bf16 *vst = &Vs[st][vbase];
+    // The tile in two 32-key halves kb: S^T = K Q^T (each K fragment feeds QB
+    // MFMAs), online softmax, then O^T += V^T P^T over the half's two 16-key
+    // slices (each V fragment feeds QB MFMAs).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // All K fragments of the half are read before the first MFMA (the
+      // scheduler would otherwise place each read just before its MFMA and
+      // wait out the LDS latency every time); even and odd head-dim steps
+      // accumulate separately (two independent MFMA chains).
+      u32x4 kf[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) kf[c] = *(const u32x4 *)(&Ks[st][(32 * kb + ql) * KP + 16 * c + 8 * h]);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s[QB], s2[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] = s2[qb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NCH; c += 2) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c]),
+                                                          __builtin_bit_cast(bf16x8, qf[qb][c]), s[qb], 0, 0, 0);
+          s2[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c + 1]),
+                                                           __builtin_bit_cast(bf16x8, qf[qb][c + 1]), s2[qb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] += s2[qb];
+      // element i of s[qb] is key key0 + 32*kb + 8*(i/4) + 4h + i%4
+      const int kb0 = key0 + 32 * kb;
+      const bool edge = kb0 + 32 > minpos;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (edge) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kb0 + 8 * (i >> 2) + 4 * h + (i & 3) >= rpos[qb]) s[qb][i] = -INFINITY;
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[qb][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        // Lazy rescaling: the reference max moves only when the tile's max
+        // exceeds it by more than 2^8, so probabilities stay <= 256 and the
+        // output is rescaled rarely; numerator and denominator share the
+        // reference, so the result is unchanged.
+        const float tm = tmax * sc;
+        const bool upd = tm > mrun[qb] + 8.f;
+        const float mnew = upd ? tm : mrun[qb];
+        const float alpha =
+            upd && mrun[qb] != -INFINITY ? __builtin_amdgcn_exp2f(mrun[qb] - mnew) : (upd ? 0.f : 1.f);
+        const float nm = mnew == -INFINITY ? 0.f : -mnew;
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], sc, nm));
+          s[qb][i] = p;
+          psum += p;
+        }
+        psum += __shfl_xor(psum, 32);
+        lrun[qb] = lrun[qb] * alpha + psum;
+        mrun[qb] = mnew;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int u = 0; u < ND; ++u) o[qb][u] *= alpha;
+        }
+      }
+      // V^T fragments of the half's two slices, all read before the MFMAs
+      u32x4 vf[2][ND];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int u = 0; u < ND; ++u) {
+          const int sl = 2 * kb + half;  // 16-key slice of the tile
+          const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vst + 16 * sl * VP + 32 * u));
+          const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vst + (16 * sl + 8) * VP + 32 * u));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          vf[half][u] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 pf[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float pv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv[j] = s[qb][8 * half + j];
+          pf[qb] = pack16<bf16>(pv);
+        }
+#pragma unroll
+        for (int u = 0; u < ND; ++u)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[half][u]),
+                                                               __builtin_bit_cast(bf16x8, pf[qb]), o[qb][u], 0, 0, 0);
+      }
+    }
+    if (t + 1 < t1) sstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // write out: lane holds query ql of block qb, head dims u*32 + 8*(i/4) + 4h + i%4
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (!rvalid[qb]) continue;
+    if (a.nsplit == 1) {
+      const float inv = lrun[qb] > 0.f ? 1.f / lrun[qb] : 0.f;
+      bf16 *dst = (bf16 *)a.out + (int64_t)rrow[qb] * a.Hq * DH + rhead[qb] * DH;
+#pragma unroll
+      for (int u = 0; u < ND; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[qb][u][4 * j + e] * inv;
+          stT<bf16, 4>(dst + u * 32 + 8 * j + 4 * h, v);
+        }
+    } else {
+      const int64_t base = ((int64_t)blockIdx.z * a.B * a.M + rrow[qb]) * a.Hq + rhead[qb];
+      float *dst = a.part_o + base * DH;
+#pragma unroll
+      for (int u = 0; u < ND; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(f32x4 *)(dst + u * 32 + 8 * j + 4 * h) =
+              f32x4{o[qb][u][4 * j], o[qb][u][4 * j + 1], o[qb][u][4 * j + 2], o[qb][u][4 * j + 3]};
+      if (h == 0) {
+        a.part_ml[base * 2] = mrun[qb];
+        a.part_ml[base * 2 + 1] = lrun[qb];
+      }
+    }
+  }
+}
+
+}  // namespace wm

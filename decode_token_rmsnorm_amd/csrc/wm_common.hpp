@@ -9,6 +9,7 @@ namespace wm {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -71,13 +72,13 @@ template <> __device__ __forceinline__ u32x4 pack16<float>(const float *f) {
   for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(f[e]);
   return v;
 }
+// (a pair converted as one 2-vector becomes a single v_cvt_pk_bf16_f32, RNE)
 template <> __device__ __forceinline__ u32x4 pack16<bf16>(const float *f) {
   u32x4 v;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    uint32_t lo = __builtin_bit_cast(uint16_t, (bf16)f[2 * e]);
-    uint32_t hi = __builtin_bit_cast(uint16_t, (bf16)f[2 * e + 1]);
-    v[e] = lo | (hi << 16);
+    const bf16x2 p = {(bf16)f[2 * e], (bf16)f[2 * e + 1]};
+    v[e] = __builtin_bit_cast(uint32_t, p);
   }
   return v;
 }

@@ -1,0 +1,192 @@
+// wm_pool2.hpp — the pool mix of bf16 state stacks on MFMA.
+//
+// For one token row and one branch the mix is a small product,
+//   m[j, c] = sum_l W[j, l] * (gamma_l[c] * S_l[c]),   W[j, l] = A[l, j] * rinv_l,
+// channels j (k <= 16*KB) by layers l (L <= 32) times layers by columns c.
+// A block takes RT token rows and walks the columns in 64-wide chunks; each
+// of its 4 waves owns one 16-column slice of the chunk and, for every row,
+// runs one 16x16x32 MFMA per branch and channel block: A = W (16 channels x
+// 32 layers, bf16, built once per block into LDS), B = the gained states (32
+// layers x 16 columns).  The states of the chunk are staged row-major in LDS
+// ([row][layer][64 columns], 192-byte pitch) and the B fragments (8
+// consecutive layers of one column per lane) come from the LDS transpose read
+// ds_read_b64_tr_b16: in each 16-lane group lane i receives element i%4 of
+// the 8-byte rows addressed by lanes i/4 + 4e, so lane i addresses layer
+// i/4 (+4) at column 4*(i%4) and receives 4 layers of column i per read.  The
+// source gains multiply the fragment in fp32 before it is rounded to bf16, so
+// one staged chunk serves both branches, and each wave loads its slice's gains
+// once per chunk for all RT rows.  The output m * rho (channel gain folded, its
+// 1/rms applied after the projection) is stored as bf16; the per-channel sums
+// of squares are reduced in a fixed order into rinvM.
+#pragma once
+
+#include "wm_common.hpp"
+
+namespace wm {
+
+constexpr int PM_RT4 = 4;   // token rows per block with one channel block (k <= 16)
+constexpr int PM_CW = 64;   // columns per chunk
+constexpr int PM_SP = 96;   // staged row pitch (elements): 64 columns + 64 bytes
+
+// A [Z, 2, rows, L*k] router output (summed over z); S [L, rows, D];
+// mb [2, k, rows, D]; rinvM [2, k, rows].
+template <int KB>
+__global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *rinvS, const float *A, int Z,
+                                                 int64_t zstride, const float *src_gain, const float *chan_gain,
+                                                 bf16 *mb, float *rinvM, int rows, int L, int k, int D, float eps) {
+  constexpr int PM_RT = PM_RT4 / KB;                 // token rows per block
+  constexpr int NPT = (PM_RT * 32 * 8 + 255) / 256;  // 16-byte pieces per thread (L <= 32)
+  __shared__ __attribute__((aligned(16))) bf16 Sl[PM_RT * 32 * PM_SP];
+  __shared__ __attribute__((aligned(16))) u32x4 Wl[PM_RT][2][KB][64];
+  __shared__ float red[4][PM_RT][2][KB][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int r0 = blockIdx.x * PM_RT;
+  const int Lk = L * k;
+
+  // W fragments: lane holds channel 16*kb + li, layers 8*g .. 8*g + 7
+  for (int item = wave; item < PM_RT * 2 * KB; item += 4) {
+    const int rr = item / (2 * KB), beta = (item / KB) & 1, kb = item % KB;
+    const int row = min(r0 + rr, rows - 1), j = 16 * kb + li;
+    float wv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int l = 8 * g + e;
+      float a = 0.f;
+      if (j < k && l < L) {
+        for (int z = 0; z < Z; ++z) a += A[z * zstride + ((int64_t)beta * rows + row) * Lk + l * k + j];
+        a *= rinvS[(int64_t)l * rows + row];
+      }
+      wv[e] = a;
+    }
+    Wl[rr][beta][kb][lane] = pack16<bf16>(wv);
+  }
+
+  // staging of one chunk: piece q = (rr, layer, p), 16 bytes, layer < L
+  const int npieces = PM_RT * L * 8;
+  u32x4 pre[NPT];
+  auto gload = [&](int chunk) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int q = min(tid + 256 * i, npieces - 1);
+      const int rr = q / (L * 8), rem = q - rr * L * 8, l = rem >> 3, p = rem & 7;
+      const int row = min(r0 + rr, rows - 1);
+      pre[i] = *(const u32x4 *)(S + ((int64_t)l * rows + row) * D + chunk * PM_CW + 8 * p);
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int q = tid + 256 * i;
+      if (q < npieces) {
+        const int rr = q / (L * 8), rem = q - rr * L * 8, l = rem >> 3, p = rem & 7;
+        *(u32x4 *)(&Sl[(rr * 32 + l) * PM_SP + 8 * p]) = pre[i];
+      }
+    }
+  };
+
+  float ss[PM_RT][2][KB][4];
+#pragma unroll
+  for (int rr = 0; rr < PM_RT; ++rr)
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss[rr][beta][kb][i] = 0.f;
+
+  // transpose-read sources of this lane: layers 8g + li/4 and 8g + 4 + li/4
+  // (clamped to L-1: rows past L are never staged; their weights are zero),
+  // column 4*(li%4) of the wave's slice
+  typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const int tr_lo = min(8 * g + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
+  const int tr_hi = min(8 * g + 4 + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
+  const int nchunk = D / PM_CW;
+
+  gload(0);
+  for (int chunk = 0; chunk < nchunk; ++chunk) {
+    __syncthreads();  // the previous chunk's reads of Sl are done
+    sstore();
+    if (chunk + 1 < nchunk) gload(chunk + 1);
+    __syncthreads();
+    const int col = chunk * PM_CW + 16 * wave + li;
+    // gains of this lane's column: source gains for layers 8g..8g+7, channel
+    // gains for channels 16kb + 4g + i
+    float gs[2][8], gr[2][KB][4];
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gs[beta][e] = src_gain[((int64_t)beta * L + min(8 * g + e, L - 1)) * D + col];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          gr[beta][kb][i] = chan_gain[((int64_t)beta * k + min(16 * kb + 4 * g + i, k - 1)) * D + col];
+    }
+#pragma unroll
+    for (int rr = 0; rr < PM_RT; ++rr) {
+      const int row = r0 + rr;
+      const bf16 *base = &Sl[rr * 32 * PM_SP];
+      const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + tr_lo));
+      const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + tr_hi));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      float x[8];
+      unpack16<bf16>(u32x4{l2[0], l2[1], h2[0], h2[1]}, x);
+#pragma unroll
+      for (int beta = 0; beta < 2; ++beta) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * gs[beta][e];
+        const u32x4 bfr = pack16<bf16>(y);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
+          mma16<bf16>(m, Wl[rr][beta][kb][lane], bfr);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ss[rr][beta][kb][i] += m[i] * m[i];
+            const int j = 16 * kb + 4 * g + i;
+            if (j < k && row < rows) mb[(((int64_t)beta * k + j) * rows + row) * D + col] = (bf16)(m[i] * gr[beta][kb][i]);
+          }
+        }
+      }
+    }
+  }
+
+  // sums of squares: over the 16 columns of the slice (lanes of a group),
+  // then over the 4 slices in wave order
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1)
+#pragma unroll
+    for (int rr = 0; rr < PM_RT; ++rr)
+#pragma unroll
+      for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ss[rr][beta][kb][i] += __shfl_xor(ss[rr][beta][kb][i], o);
+  if (li == 0) {
+#pragma unroll
+    for (int rr = 0; rr < PM_RT; ++rr)
+#pragma unroll
+      for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[wave][rr][beta][kb][4 * g + i] = ss[rr][beta][kb][i];
+  }
+  __syncthreads();
+  for (int item = tid; item < PM_RT * 2 * KB * 16; item += 256) {
+    const int rr = item / (2 * KB * 16), rem = item % (2 * KB * 16), beta = rem / (KB * 16), kb = (rem / 16) % KB,
+              jj = rem % 16;
+    const int j = 16 * kb + jj, row = r0 + rr;
+    if (j < k && row < rows) {
+      const float v = ((red[0][rr][beta][kb][jj] + red[1][rr][beta][kb][jj]) + red[2][rr][beta][kb][jj]) +
+                      red[3][rr][beta][kb][jj];
+      rinvM[((int64_t)beta * k + j) * rows + row] = rsqrtf(v / D + eps);
+    }
+  }
+}
+
+}  // namespace wm

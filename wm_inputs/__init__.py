@@ -227,3 +227,18 @@ def make_cache_device(w: Workload, B: int, filled: int, seed: int = 3, device="c
         x[:, :, :, :filled] = torch.randn((w.k, B, w.Hkv, filled, w.d), generator=g, device=device).to(td)
         out.append(x)
     return out[0], out[1]
+
+
+def make_state_stack_device(w: Workload, rows: int, seed: int = 2, device="cuda"):
+    """Like ``make_state_stack`` but drawn on the device with torch's seeded
+    generator (full-size timing inputs, never compared with the oracle)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    scale = torch.rand((w.L, 1, 1), generator=g, device=device) * 3.5 + 0.5
+    out = torch.empty((w.L, rows, w.D), dtype=td, device=device)
+    for l in range(w.L):  # one layer at a time keeps the fp32 temporary small
+        out[l] = (torch.randn((rows, w.D), generator=g, device=device) * scale[l]).to(td)
+    return out
