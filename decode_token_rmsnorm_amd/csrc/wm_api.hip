@@ -127,7 +127,7 @@ template <typename T> struct Run {
     int64_t kmax = (int64_t)ts.s0 + (int64_t)(ts.M - 1) * ts.s_step;
     if (kmax > c.T_max) kmax = c.T_max;
     const int ntile = (int)((kmax + AKT - 1) / AKT);
-    const int64_t target = v2 ? 4096 : large ? 2048 : 4096;  // waves in flight
+    const int64_t target = large ? 2048 : 4096;  // waves in flight
     int ns = 1;
     while ((int64_t)blocks * nw * ns < target && ns * 2 <= ACS && ntile / (ns * 2) >= 2 &&
            (int64_t)(ns * 2) * rows <= part_rows_cap(rows_cap))
@@ -179,21 +179,39 @@ template <typename T> struct Run {
   }
 
   // -------------------------------------------------------- KV pool
-  template <int KMAX> wm_status mix(const T *S, int rows) {
+  // Router output layout (see pool): element (z, beta, row, l*k + j) at
+  // z*az + beta*ab + row*ar + l*k + j, Z split partials.
+  struct RouterOut {
+    int Z;
+    int64_t az, ab, ar;
+  };
+
+  template <int KMAX> wm_status mix(const T *S, int rows, RouterOut ro) {
     if constexpr (std::is_same<T, bf16>::value) {  // MFMA mix (wm_pool2.hpp)
-      const int64_t zs = 2 * (int64_t)rows * c.L * c.k;
       if (c.k <= 16)
         hipLaunchKernelGGL((pool_mix2<1>), dim3((rows + PM_RT4 - 1) / PM_RT4), dim3(256), 0, s, S, at<float>(lay.rinvS),
-                           at<float>(lay.Aw), 1, zs, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM),
-                           rows, c.L, c.k, c.D, c.eps);
+                           at<float>(lay.Aw), ro.Z, ro.az, ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb),
+                           at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
       else
-        hipLaunchKernelGGL((pool_mix2<2>), dim3((rows + PM_RT4 / 2 - 1) / (PM_RT4 / 2)), dim3(256), 0, s, S, at<float>(lay.rinvS),
-                           at<float>(lay.Aw), 1, zs, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM),
-                           rows, c.L, c.k, c.D, c.eps);
+        hipLaunchKernelGGL((pool_mix2<2>), dim3((rows + PM_RT4 / 2 - 1) / (PM_RT4 / 2)), dim3(256), 0, s, S,
+                           at<float>(lay.rinvS), at<float>(lay.Aw), ro.Z, ro.az, ro.ab, ro.ar, w->src_norm,
+                           w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
     } else {
       hipLaunchKernelGGL((pool_mix<T, KMAX>), dim3(rows), dim3(256), 0, s, S, at<float>(lay.rinvS), at<float>(lay.Aw),
-                         w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
+                         ro.Z, ro.az, ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM),
+                         rows, c.L, c.k, c.D, c.eps);
     }
+    WM_TRY(hipGetLastError());
+    return WM_OK;
+  }
+
+  // Router weights with the source gains folded in, for steps with more than
+  // kSkinnyRows rows (once per call; the workspace keeps them).
+  wm_status prep_router() {
+    if (rows_cap <= kSkinnyRows) return WM_OK;
+    const int64_t n = 2 * (int64_t)c.L * c.k * R * c.D / Elt<T>::E16;
+    hipLaunchKernelGGL((fold_router<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const T *)w->router,
+                       w->src_norm, at<T>(lay.wf), c.L * c.k, c.L, c.p, R, c.D);
     WM_TRY(hipGetLastError());
     return WM_OK;
   }
@@ -201,33 +219,66 @@ template <typename T> struct Run {
   wm_status pool(const T *S, wm_tokset ts) {
     const int rows = ts.B * ts.M;
     const int64_t nl = (int64_t)c.L * rows;
-    {
-    ProfScope prof(WM_K_MIX, s);
-    hipLaunchKernelGGL((state_rinv<T>), dim3((unsigned)((nl + 3) / 4)), dim3(256), 0, s, S, at<float>(lay.rinvS), nl,
-                       c.D, c.eps);
-    WM_TRY(hipGetLastError());
-    }
-    // router: [rows, R*D] x [L*k, R*D]^T per branch
-    BRows<T> rb{LoadRows<T>{(const T *)w->router, (int64_t)R * c.D, (int64_t)c.L * c.k * R * c.D, nullptr}};
-    EpiStoreF32 re{at<float>(lay.Aw), (int64_t)c.L * c.k, (int64_t)rows * c.L * c.k, nullptr, nullptr, nullptr, 0, 0.f,
-                   0.f};
-    {
-      ProfScope prof(WM_K_ROUTER, s);
-      if (rows <= kSkinnyRows) {
-        hipLaunchKernelGGL((router_input<T>), dim3(rows, 2), dim3(256), 0, s, S, at<float>(lay.rinvS), w->src_norm,
-                           at<T>(lay.u), rows, c.L, c.p, R, c.D);
+    const int Lk = c.L * c.k;
+    const int64_t RD = (int64_t)R * c.D;
+    RouterOut ro;
+    if (rows <= kSkinnyRows) {
+      // few rows: per-branch gained router input and the skinny GEMM, Z = branch
+      {
+        ProfScope prof(WM_K_MIX, s);
+        hipLaunchKernelGGL((state_rinv<T>), dim3((unsigned)((nl + 3) / 4)), dim3(256), 0, s, S, at<float>(lay.rinvS),
+                           nl, c.D, c.eps);
         WM_TRY(hipGetLastError());
-        LoadRows<T> ua{at<T>(lay.u), (int64_t)R * c.D, (int64_t)rows * R * c.D, nullptr};
-        WM_TRY((gemm1(ua, rb, re, rows, c.L * c.k, R * c.D, 2)));
-      } else {
-        LoadRouterA<T> ra{S, at<float>(lay.rinvS), w->src_norm, rows, c.D, c.L, c.p};
-        WM_TRY((gemm1(ra, rb, re, rows, c.L * c.k, R * c.D, 2)));
       }
+      ProfScope prof(WM_K_ROUTER, s);
+      hipLaunchKernelGGL((router_input<T>), dim3(rows, 2), dim3(256), 0, s, S, at<float>(lay.rinvS), w->src_norm,
+                         at<T>(lay.u), rows, c.L, c.p, R, c.D);
+      WM_TRY(hipGetLastError());
+      LoadRows<T> ua{at<T>(lay.u), RD, (int64_t)rows * RD, nullptr};
+      BRows<T> rb{LoadRows<T>{(const T *)w->router, RD, (int64_t)Lk * RD, nullptr}};
+      EpiStoreF32 re{at<float>(lay.Aw), Lk, (int64_t)rows * Lk, nullptr, nullptr, nullptr, 0, 0.f, 0.f};
+      WM_TRY((gemm1(ua, rb, re, rows, Lk, (int)RD, 2)));
+      ro = RouterOut{1, 0, (int64_t)rows * Lk, Lk};
+    } else {
+      // many rows: one normalised router input (gains folded into the
+      // weights), both branches in one GEMM, k split in Zs ranges whose
+      // partials the mix adds
+      {
+        ProfScope prof(WM_K_MIX, s);
+        hipLaunchKernelGGL((state_rinv_u<T>), dim3((unsigned)((nl + 3) / 4)), dim3(256), 0, s, S, at<float>(lay.rinvS),
+                           at<T>(lay.u), rows, c.L, c.p, R, c.D, c.eps);
+        WM_TRY(hipGetLastError());
+      }
+      const int N = 2 * Lk;
+      const bool g2 = big(rows);
+      const int64_t tiles = g2 ? (int64_t)((rows + G2M - 1) / G2M) * ((N + G2N - 1) / G2N)
+                               : (int64_t)((rows + GM - 1) / GM) * ((N + GN - 1) / GN);
+      int Zs = 1;
+      while (Zs < kRouterMaxSplits && tiles * Zs < 256 && RD % (2 * Zs * 64) == 0) Zs *= 2;
+      const int64_t Kz = RD / Zs;
+      EpiStoreF32 re{at<float>(lay.Aw), N, (int64_t)rows * N, nullptr, nullptr, nullptr, 0, 0.f, 0.f};
+      ProfScope prof(WM_K_ROUTER, s);
+      bool done = false;
+      if constexpr (kBig) {
+        if (g2) {
+          PRows<T> a2{at<T>(lay.u), RD, Kz, rows};
+          PBRows<T> b2{PRows<T>{at<T>(lay.wf), RD, Kz, N}};
+          WM_TRY((launch_gemm2(a2, b2, re, rows, N, (int)Kz, Zs, s)));
+          done = true;
+        }
+      }
+      if (!done) {
+        LoadRows<T> ua{at<T>(lay.u), RD, Kz, nullptr};
+        BRows<T> rb{LoadRows<T>{at<T>(lay.wf), RD, Kz, nullptr}};
+        WM_TRY((gemm1(ua, rb, re, rows, N, (int)Kz, Zs)));
+      }
+      ro = RouterOut{Zs, (int64_t)rows * N, Lk, N};
     }
     wm_status st;
     {
       ProfScope prof(WM_K_MIX, s);
-      st = c.k <= 4 ? mix<4>(S, rows) : c.k <= 8 ? mix<8>(S, rows) : c.k <= 16 ? mix<16>(S, rows) : mix<32>(S, rows);
+      st = c.k <= 4 ? mix<4>(S, rows, ro) : c.k <= 8 ? mix<8>(S, rows, ro) : c.k <= 16 ? mix<16>(S, rows, ro)
+                                                                                       : mix<32>(S, rows, ro);
     }
     if (st != WM_OK) return st;
     // per-channel projection, z = beta*k + j
@@ -378,6 +429,8 @@ template <typename T>
 static wm_status prefill_impl(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int Tseq, int g,
                               const wm_cache *cache, float *logits, int mode, void *ws, int rows, hipStream_t s) {
   Run<T> r(*cfg, w, cache, ws, rows, s);
+  wm_status pst = r.prep_router();
+  if (pst != WM_OK) return pst;
   const int B = cache->B, ng = g < Tseq ? g : Tseq;
   for (int q = 0; q < ng; ++q) {
     int Mq = (Tseq - q + g - 1) / g;
@@ -424,10 +477,12 @@ wm_status wm_mix_kv(const wm_config *cfg, const wm_weights *w, const void *state
   int rows = ts.B * ts.M;
   if (cfg->dtype == WM_BF16) {
     Run<bf16> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
-    return r.pool((const bf16 *)states, ts);
+    st = r.prep_router();
+    return st != WM_OK ? st : r.pool((const bf16 *)states, ts);
   }
   Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
-  return r.pool((const float *)states, ts);
+  st = r.prep_router();
+  return st != WM_OK ? st : r.pool((const float *)states, ts);
 }
 
 wm_status wm_channel_attn(const wm_config *cfg, int32_t layer, const void *q, wm_tokset ts, const wm_cache *cache,

@@ -79,35 +79,6 @@ template <typename T> struct LoadGateUp {
   __device__ __forceinline__ u32x4 load(H h, int kbyte) const { return *(const u32x4 *)(h + kbyte); }
 };
 
-// A operand of the router: row r is the concatenation over blocks b < R of
-// RMSNorm(S[b*p][r]; src_gain[beta][b*p]) — normalised on the fly from the
-// state stack S [L, rows, D] and per-layer row scales rinvS [L, rows];
-// blockIdx.z is the branch beta.
-template <typename T> struct LoadRouterA {
-  const T *S;
-  const float *rinvS;
-  const float *gain;  // [2, L, D]
-  int rows, D, L, p;
-  struct H {
-    int row, z;
-  };
-  __device__ __forceinline__ H row(int z, int r, int nrows) const { return H{r < nrows ? r : nrows - 1, z}; }
-  __device__ __forceinline__ u32x4 load(H h, int kbyte) const {
-    constexpr int E = Elt<T>::E16;
-    const int kel = kbyte / (int)sizeof(T);
-    const int blk = kel / D, col = kel - blk * D;
-    const int layer = blk * p;
-    u32x4 v = *(const u32x4 *)(S + ((int64_t)layer * rows + h.row) * D + col);
-    float f[E];
-    unpack16<T>(v, f);
-    const float s = rinvS[(int64_t)layer * rows + h.row];
-    const float *g = gain + ((int64_t)h.z * L + layer) * D + col;
-#pragma unroll
-    for (int e = 0; e < E; ++e) f[e] *= s * g[e];
-    return pack16<T>(f);
-  }
-};
-
 // ---------------------------------------------------------------- epilogues
 // Every epilogue walks a staged fp32 C tile in LDS: `nrows` rows of pitch
 // `pitch` floats, tile row rl being output row m0 + rl, 64*CPL columns wide,

@@ -34,8 +34,11 @@ inline size_t skinny_partial_floats(int rows, int N, int64_t k_bytes, int Z) {
   return (size_t)Z * nM * nN * S * 64 * 128;
 }
 
+// Router split-K partials kept for steps with more rows than kSkinnyRows.
+constexpr int kRouterMaxSplits = 4;
+
 struct WsLayout {
-  size_t h, hb, ss, q, o, act, S, rinvS, Aw, mb, rinvM, u, skp, part_o, part_ml, rowmap, total;
+  size_t h, hb, ss, q, o, act, S, rinvS, Aw, mb, rinvM, u, wf, skp, part_o, part_ml, rowmap, total;
   int ssp;  // partial sums of squares per row
 };
 
@@ -57,12 +60,15 @@ inline WsLayout ws_layout(const wm_config &c, int rows) {
   w.act = take(R * c.F * es);
   w.S = take((size_t)c.L * R * c.D * es);
   w.rinvS = take((size_t)c.L * R * 4);
-  w.Aw = take(2 * R * c.L * c.k * 4);
+  w.Aw = take((rows > kSkinnyRows ? (size_t)kRouterMaxSplits : 1) * 2 * R * c.L * c.k * 4);
   w.mb = take(2 * (size_t)c.k * R * c.D * es);
   w.rinvM = take(2 * (size_t)c.k * R * 4);
   const size_t nR = (size_t)(c.L + c.p - 1) / c.p;
   const int sr = rows < kSkinnyRows ? rows : kSkinnyRows;
-  w.u = take(2 * (size_t)sr * nR * c.D * es);
+  // router input: two gained copies of few rows, or one normalised copy
+  const size_t urows = 2 * (size_t)sr > R ? 2 * (size_t)sr : R;
+  w.u = take(urows * nR * c.D * es);
+  w.wf = take(rows > kSkinnyRows ? 2 * (size_t)c.L * c.k * nR * c.D * es : 0);
   {  // the largest split GEMM of a few-row step
     const int64_t D = c.D, F = c.F, QD = (int64_t)c.Hq * c.d, KVD = (int64_t)c.Hkv * c.d, LK = (int64_t)c.L * c.k;
     size_t m = skinny_partial_floats(sr, (int)QD, D * es, 1);

@@ -8,6 +8,8 @@
 //               1/rms is applied after the projection, which is linear) and
 //               1/rms(m_j) for the projection epilogue.
 //  router_input the router's normalised input rows, written out (few rows)
+//  state_rinv_u state_rinv plus the normalised router-layer rows (many rows)
+//  fold_router  router weights times the source gains
 //  embed_rows   h_0 = E[token] (+ the first state, the next GEMM's operand and
 //               its sum of squares)
 //  rope_table   cos/sin of s * base^(-2m/d), double precision, rounded
@@ -37,11 +39,65 @@ __global__ __launch_bounds__(256) void state_rinv(const T *S, float *rinv, int64
   if (lane == 0) rinv[w] = rsqrtf(s / D + eps);
 }
 
+// state_rinv plus, for the router's layers (layer % p == 0), the normalised
+// router input u[r, (layer/p)*D + c] = S[layer, r, c] * rinv (source gains are
+// folded into the router weights instead).  One wave per (layer, row).
+template <typename T>
+__global__ __launch_bounds__(256) void state_rinv_u(const T *S, float *rinv, T *u, int rows, int L, int p, int R,
+                                                    int D, float eps) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= (int64_t)L * rows) return;
+  const int layer = (int)(w / rows), r = (int)(w - (int64_t)layer * rows);
+  constexpr int E = Elt<T>::E16;
+  const T *x = S + w * D;
+  float s = 0.f;
+  for (int c = lane * E; c < D; c += 64 * E) {
+    float f[E];
+    unpack16<T>(*(const u32x4 *)(x + c), f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) s += f[e] * f[e];
+  }
+  s = wave_sum(s);
+  const float ri = rsqrtf(s / D + eps);
+  if (lane == 0) rinv[w] = ri;
+  if (layer % p) return;
+  T *dst = u + (int64_t)r * R * D + (int64_t)(layer / p) * D;
+  for (int c = lane * E; c < D; c += 64 * E) {
+    float f[E];
+    unpack16<T>(*(const u32x4 *)(x + c), f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] *= ri;
+    *(u32x4 *)(dst + c) = pack16<T>(f);
+  }
+}
+
+// Router weights with the source gains folded in, both branches stacked:
+// Wf[o, s*D + c] = W[o, s*D + c] * gain[o / Lk, s*p, c]  (W is [2*Lk, R*D]).
+template <typename T>
+__global__ __launch_bounds__(256) void fold_router(const T *W, const float *gain, T *Wf, int Lk, int L, int p, int R,
+                                                   int D) {
+  constexpr int E = Elt<T>::E16;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * E;
+  const int64_t RD = (int64_t)R * D;
+  if (i >= 2 * (int64_t)Lk * RD) return;
+  const int o = (int)(i / RD);
+  const int kk = (int)(i - (int64_t)o * RD), sg = kk / D, c = kk - sg * D;
+  const float *g = gain + ((int64_t)(o / Lk) * L + (int64_t)sg * p) * D + c;
+  float f[E];
+  unpack16<T>(*(const u32x4 *)(W + i), f);
+#pragma unroll
+  for (int e = 0; e < E; ++e) f[e] *= g[e];
+  *(u32x4 *)(Wf + i) = pack16<T>(f);
+}
+
 // One block per token row; thread owns columns tid, tid + 256, ...
-// A [2, rows, L*k] router output; S [L, rows, D]; mb [2, k, rows, D];
-// rinvM [2, k, rows].
+// Router output A: element (z, beta, row, l*k + j) at z*az + beta*ab +
+// row*ar + l*k + j, summed over Z partials; S [L, rows, D]; mb [2, k, rows,
+// D]; rinvM [2, k, rows].
 template <typename T, int KMAX>
-__global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, const float *A, const float *src_gain,
+__global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, const float *A, int Z, int64_t az,
+                                                int64_t ab, int64_t ar, const float *src_gain,
                                                 const float *chan_gain, T *mb, float *rinvM, int rows, int L, int k,
                                                 int D, float eps) {
   __shared__ float Aw[2][32][KMAX];  // L <= 32
@@ -49,7 +105,9 @@ __global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < 2 * L * k; i += 256) {
     int beta = i / (L * k), rem = i - beta * L * k, l = rem / k, j = rem - l * k;
-    Aw[beta][l][j] = A[((int64_t)beta * rows + r) * L * k + rem] * rinvS[(int64_t)l * rows + r];
+    float v = 0.f;
+    for (int z = 0; z < Z; ++z) v += A[z * az + beta * ab + r * ar + rem];
+    Aw[beta][l][j] = v * rinvS[(int64_t)l * rows + r];
   }
   __syncthreads();
   float ss[2][KMAX];

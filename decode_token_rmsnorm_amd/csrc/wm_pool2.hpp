@@ -28,36 +28,51 @@ constexpr int PM_RT4 = 4;   // token rows per block with one channel block (k <=
 constexpr int PM_CW = 64;   // columns per chunk
 constexpr int PM_SP = 96;   // staged row pitch (elements): 64 columns + 64 bytes
 
-// A [Z, 2, rows, L*k] router output (summed over z); S [L, rows, D];
-// mb [2, k, rows, D]; rinvM [2, k, rows].
+// Router output A: element (z, beta, row, l*k + j) at z*zstride +
+// beta*bstride + row*rstride + l*k + j, summed over the Z split partials;
+// S [L, rows, D]; mb [2, k, rows, D]; rinvM [2, k, rows].
 template <int KB>
 __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *rinvS, const float *A, int Z,
-                                                 int64_t zstride, const float *src_gain, const float *chan_gain,
-                                                 bf16 *mb, float *rinvM, int rows, int L, int k, int D, float eps) {
+                                                 int64_t zstride, int64_t bstride, int64_t rstride,
+                                                 const float *src_gain, const float *chan_gain, bf16 *mb,
+                                                 float *rinvM, int rows, int L, int k, int D, float eps) {
   constexpr int PM_RT = PM_RT4 / KB;                 // token rows per block
   constexpr int NPT = (PM_RT * 32 * 8 + 255) / 256;  // 16-byte pieces per thread (L <= 32)
   __shared__ __attribute__((aligned(16))) bf16 Sl[PM_RT * 32 * PM_SP];
   __shared__ __attribute__((aligned(16))) u32x4 Wl[PM_RT][2][KB][64];
   __shared__ float red[4][PM_RT][2][KB][16];
+  // output chunk [beta][row][channel][64 columns], 144-byte rows: the four
+  // lane groups of a wave write channels 16 banks apart
+  constexpr int OP = 72;
+  __shared__ __attribute__((aligned(16))) bf16 Ol[2 * PM_RT * 16 * KB * OP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int r0 = blockIdx.x * PM_RT;
-  const int Lk = L * k;
 
   // W fragments: lane holds channel 16*kb + li, layers 8*g .. 8*g + 7
   for (int item = wave; item < PM_RT * 2 * KB; item += 4) {
     const int rr = item / (2 * KB), beta = (item / KB) & 1, kb = item % KB;
     const int row = min(r0 + rr, rows - 1), j = 16 * kb + li;
+    // (every load of the item is issued before any is used: Z <= 4 partials
+    // of 8 layers plus their row scales, addresses clamped into range)
+    const int jc = min(j, k - 1);
+    float part[4][8], rs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int lc = min(8 * g + e, L - 1);
+#pragma unroll
+      for (int z = 0; z < 4; ++z)
+        part[z][e] = A[min(z, Z - 1) * zstride + beta * bstride + row * rstride + lc * k + jc];
+      rs[e] = rinvS[(int64_t)lc * rows + row];
+    }
     float wv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int l = 8 * g + e;
-      float a = 0.f;
-      if (j < k && l < L) {
-        for (int z = 0; z < Z; ++z) a += A[z * zstride + ((int64_t)beta * rows + row) * Lk + l * k + j];
-        a *= rinvS[(int64_t)l * rows + row];
-      }
-      wv[e] = a;
+      float a = part[0][e];
+#pragma unroll
+      for (int z = 1; z < 4; ++z)
+        if (z < Z) a += part[z][e];
+      wv[e] = (j < k && 8 * g + e < L) ? a * rs[e] : 0.f;
     }
     Wl[rr][beta][kb][lane] = pack16<bf16>(wv);
   }
@@ -136,6 +151,7 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
 #pragma unroll
       for (int beta = 0; beta < 2; ++beta) {
         float y[8];
+        (void)row;
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = x[e] * gs[beta][e];
         const u32x4 bfr = pack16<bf16>(y);
@@ -146,11 +162,20 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             ss[rr][beta][kb][i] += m[i] * m[i];
-            const int j = 16 * kb + 4 * g + i;
-            if (j < k && row < rows) mb[(((int64_t)beta * k + j) * rows + row) * D + col] = (bf16)(m[i] * gr[beta][kb][i]);
+            Ol[((beta * PM_RT + rr) * 16 * KB + 16 * kb + 4 * g + i) * OP + 16 * wave + li] =
+                (bf16)(m[i] * gr[beta][kb][i]);
           }
         }
       }
+    }
+    // the chunk's outputs: 16-byte pieces of 128-byte rows
+    __syncthreads();
+    for (int q = tid; q < 2 * PM_RT * k * 8; q += 256) {
+      const int pc = q & 7, t = q >> 3, j = t % k, br = t / k, rr = br % PM_RT, beta = br / PM_RT;
+      const int row = r0 + rr;
+      if (row < rows)
+        *(u32x4 *)(mb + (((int64_t)beta * k + j) * rows + row) * D + chunk * PM_CW + 8 * pc) =
+            *(const u32x4 *)(&Ol[((beta * PM_RT + rr) * 16 * KB + j) * OP + 8 * pc]);
     }
   }
 

@@ -77,6 +77,8 @@ def assert_cache(w, gk, gv, ref, mask, tol, poison=True):
     ("tiny_fp32", 1, 128, 0, 1),        # every position of cfg tiny
     ("mix_bf16", 3, 37, 5, 7),          # ragged rows (111), strided positions
     ("tiny_fp32", 2, 9, 3, 13),         # ragged fp32
+    ("tiny_fp32", 2, 100, 0, 1),        # fp32 past the few-row path (200 rows, split router)
+    ("mix_bf16", 3, 300, 2, 5),         # bf16, 900 rows: 128x128 router tiles with k splits
 ])
 def test_mix_kv_matches_oracle(name, B, M, s0, step):
     w = WORKLOADS[name].replace(B=B)
