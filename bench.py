@@ -22,25 +22,35 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_1p3b_gateup_traffic.md")
-KERNEL_SOURCES = ["decode_token_rmsnorm_amd/csrc/wm_common.hpp", "decode_token_rmsnorm_amd/csrc/wm_gemm.hpp",
-                  "decode_token_rmsnorm_amd/csrc/wm_gemm2.hpp"]
+CSRC = "decode_token_rmsnorm_amd/csrc/"
+# committed rocprofv3 HBM-byte summaries and the kernel sources they were taken from
+TRAFFIC = {
+    "gateup": ("prefill_1p3b_gateup_traffic.md", ["wm_common.hpp", "wm_gemm.hpp", "wm_gemm2.hpp"]),
+    "decode_attn": ("decode_d512_attn_traffic.md", ["wm_common.hpp", "wm_attn.hpp"]),
+    "mix_kv": ("mix_bf16_mix_kv_traffic.md", ["wm_common.hpp", "wm_gemm.hpp", "wm_gemm2.hpp", "wm_pool.hpp",
+                                              "wm_pool2.hpp", "wm_api.hip"]),
+}
 
 
-def profiled_traffic():
-    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+def source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, CSRC + f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(key):
+    """HBM bytes per launch (per call for mix_kv) from a committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (calibrated against a plain copy), or None
     when the kernel sources changed since those counters were taken."""
-    import hashlib
+    name, files = TRAFFIC[key]
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(os.path.join(ROOT, "profiles", name)).read()
     except OSError:
         return None
     fields = dict(l.split(": ", 1) for l in text.splitlines() if ": " in l and not l.startswith(("-", "|", "#")))
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if fields.get("source_sha256_16", "").strip() != h.hexdigest()[:16]:
+    if fields.get("source_sha256_16", "").strip() != source_hash(files):
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -107,7 +117,7 @@ def bench_prefill(steps, warmup):
         "wall_s": wall, "per_pass_ms": per_pass, "rows_per_group": rows, "kernels": kern,
         "roofline": {"kernel": "gateup (fused gate/up projection + SwiGLU GEMM)", "bound": "mfma",
                      "achieved": flops_ga / (ms_ga / n_ga * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "traffic": profiled_traffic(),
+                     "unit": "TFLOP/s", "traffic": profiled_traffic("gateup"),
                      "algorithmic_per_launch": f"{flops_ga:.4e} FLOP = 2*{rows}*{2 * w.F}*{w.D}"},
     }
     res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
@@ -169,7 +179,7 @@ def bench_decode(steps, warmup):
             "kernels_avg_us": kern,
             "roofline": {"kernel": "attn (strict-causal channel attention, split keys)", "bound": "hbm",
                          "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                         "traffic": None,
+                         "traffic": profiled_traffic("decode_attn"),
                          "algorithmic_per_launch": f"{kv_bytes:.4e} B = 2*{w.B}*{w.Hkv}*{t}*{w.d}*2"}}
 
 
@@ -211,7 +221,7 @@ def bench_mix(calls, warmup):
             "us_per_call": us, "calls": calls, "kernels_avg_us": kern,
             "roofline": {"kernel": "wm_mix_kv (router + mix + K/V projection and append)", "bound": "hbm",
                          "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                         "traffic": None,
+                         "traffic": profiled_traffic("mix_kv"),
                          "algorithmic_per_launch": f"{nbytes:.4e} B = {rows}*{per_tok} + {wbytes} weights"}}
 
 
@@ -247,6 +257,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-mix", action="store_true")
+    ap.add_argument("--only", choices=["decode", "mix"], default=None,
+                    help="profiling aid: run only this part and print its object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
     a = ap.parse_args()
@@ -265,6 +277,10 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if a.only:
+        part = bench_decode(a.decode_steps, 5) if a.only == "decode" else bench_mix(20, 3)
+        print(json.dumps({a.only: part}), flush=True)
+        return
     w, pre = bench_prefill(a.steps, a.warmup)
     dec = None if a.skip_decode else bench_decode(a.decode_steps, 5)
     mix = None if a.skip_mix else bench_mix(20, 3)
