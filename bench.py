@@ -26,7 +26,7 @@ CSRC = "decode_token_rmsnorm_amd/csrc/"
 # committed rocprofv3 HBM-byte summaries and the kernel sources they were taken from
 TRAFFIC = {
     "gateup": ("prefill_1p3b_gateup_traffic.md", ["wm_common.hpp", "wm_gemm.hpp", "wm_gemm2.hpp"]),
-    "decode_attn": ("decode_d512_attn_traffic.md", ["wm_common.hpp", "wm_attn.hpp"]),
+    "decode_attn": ("decode_d512_attn_traffic.md", ["wm_common.hpp", "wm_attn.hpp", "wm_attn2.hpp"]),
     "mix_kv": ("mix_bf16_mix_kv_traffic.md", ["wm_common.hpp", "wm_gemm.hpp", "wm_gemm2.hpp", "wm_pool.hpp",
                                               "wm_pool2.hpp", "wm_api.hip"]),
 }
@@ -177,7 +177,7 @@ def bench_decode(steps, warmup):
     return {"workload": "decode_d512: L16 D512 Hq8 Hkv4 d64 F1536 k16 p2 V32768 B64, t=2047 cached, bf16",
             "value": w.B * steps / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall / steps, "steps": steps,
             "kernels_avg_us": kern,
-            "roofline": {"kernel": "attn (strict-causal channel attention, split keys)", "bound": "hbm",
+            "roofline": {"kernel": "attn (strict-causal channel attention, attn_few)", "bound": "hbm",
                          "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                          "traffic": profiled_traffic("decode_attn"),
                          "algorithmic_per_launch": f"{kv_bytes:.4e} B = 2*{w.B}*{w.Hkv}*{t}*{w.d}*2"}}

@@ -119,17 +119,23 @@ template <typename T> struct Run {
     const int ch = layer % c.k, G = c.Hq / c.Hkv, rows = ts.B * ts.M;
     const int rows_pair = ts.M * G;
     const bool large = rows_pair >= 128;
-    // bf16 with many rows: 4 waves of 32 rows on 32x32 MFMAs (attn2_kernel)
-    const bool v2 = large && std::is_same<T, bf16>::value && DH >= 64;
-    const int rb = large ? 128 : 16, nw = v2 ? 4 : large ? 8 : 1;
+    constexpr bool bfd = std::is_same<T, bf16>::value && DH >= 64;
+    // bf16 with many rows: 4 waves of 32 rows on 32x32 MFMAs (attn2_kernel);
+    // bf16 with at most 32 rows: a block of waves per (pair, split) (attn_few)
+    const bool v2 = large && bfd;
+    const bool few = bfd && rows_pair <= 32;
+    constexpr int few_nw = DH == 64 ? 8 : 4;
+    const int rb = large ? 128 : few ? 32 : 16, nw = v2 ? 4 : large ? 8 : few ? few_nw : 1;
     const int nrb = (rows_pair + rb - 1) / rb;
     const int blocks = nrb * ts.B * c.Hkv;
     int64_t kmax = (int64_t)ts.s0 + (int64_t)(ts.M - 1) * ts.s_step;
     if (kmax > c.T_max) kmax = c.T_max;
-    const int ntile = (int)((kmax + AKT - 1) / AKT);
-    const int64_t target = large ? 2048 : 4096;  // waves in flight
+    const int kt = few ? 32 : AKT;
+    const int ntile = (int)((kmax + kt - 1) / kt);
+    // waves in flight; attn_few keeps at least 4 tiles per wave
+    const int64_t target = large ? 2048 : few ? 1024 : 4096;
     int ns = 1;
-    while ((int64_t)blocks * nw * ns < target && ns * 2 <= ACS && ntile / (ns * 2) >= 2 &&
+    while ((int64_t)blocks * nw * ns < target && ns * 2 <= ACS && ntile / (ns * 2 * (few ? few_nw : 1)) >= (few ? 4 : 2) &&
            (int64_t)(ns * 2) * rows <= part_rows_cap(rows_cap))
       ns *= 2;
     AttnArgs a;
@@ -151,10 +157,11 @@ template <typename T> struct Run {
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)c.d);
     dim3 grid(nrb, ts.B * c.Hkv, ns);
     ProfScope prof(WM_K_ATTN, s);
-    if constexpr (std::is_same<T, bf16>::value && DH >= 64) {
+    if constexpr (bfd) {
       if (v2) hipLaunchKernelGGL((attn2_kernel<DH, 1>), grid, dim3(256), 0, s, a);
+      if (few) hipLaunchKernelGGL((attn_few<DH, few_nw>), dim3(ns, ts.B * c.Hkv), dim3(64 * few_nw), 0, s, a);
     }
-    if (v2)
+    if (v2 || few)
       ;
     else if (large)
       hipLaunchKernelGGL((attn_kernel<T, DH, 8, 1>), grid, dim3(512), 0, s, a);

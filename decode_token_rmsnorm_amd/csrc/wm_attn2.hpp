@@ -277,4 +277,203 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
   }
 }
 
+// Few query rows per (sequence, KV head) pair (decode steps): attn_few.
+// A block of NW waves takes one (pair, key split); wave w walks the split's
+// 32-key tiles w, w+NW, ... with up to 32 query rows as the columns of
+// S^T = K Q^T (32x32x16 MFMA; columns past the pair's rows are padding that is
+// computed and never stored).  The K fragments of a tile are loaded straight
+// from global memory in the MFMA operand layout (lane: key lane%32, head dims
+// 8*(lane/32) of each 16-dim step); the V tile goes through a wave-private LDS
+// buffer for the transpose reads of O^T += V^T P^T, as in attn2_kernel.  The
+// next tile's loads are issued before the current tile is multiplied.  At the
+// end the waves' (o, m, l) are merged through LDS in wave order, so one launch
+// covers a pair without a combine kernel unless the keys are split further.
+template <int DH, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_few(AttnArgs a) {
+  static_assert(DH == 64 || DH == 128, "head dim");
+  constexpr int KT = 32;                // keys per tile
+  constexpr int NCH = DH / 16;          // 16-deep MFMA steps over the head dim
+  constexpr int ND = DH / 32;           // 32-row blocks of O^T
+  constexpr int VP = DH + 32;           // V row pitch (elements), as in attn2_kernel
+  constexpr int VC = KT * DH / 8 / 64;  // 16-byte V chunks per lane per tile
+  constexpr int OP = DH + 4;            // merge buffer pitch (floats)
+  constexpr int VBYTES = NW * KT * VP * 2, OBYTES = NW * 32 * OP * 4;
+  __shared__ __attribute__((aligned(16))) char smem[VBYTES > OBYTES ? VBYTES : OBYTES];
+  __shared__ float mls[NW][2][32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
+  bf16 *Vs = (bf16 *)smem + wave * KT * VP;
+  const int split = blockIdx.x, pair = blockIdx.y, b = pair / a.Hkv, hk = pair - b * a.Hkv;
+  const int nrows = a.M * a.G;  // <= 32
+  const int kmax = min(a.s0 + ((nrows - 1) / a.G) * a.step, a.T_max);
+  const int ntile = (kmax + KT - 1) / KT;
+  const int tps = (ntile + a.nsplit - 1) / a.nsplit;
+  const int t0 = split * tps, t1 = min(ntile, t0 + tps);
+
+  const bool rvalid = ql < nrows;
+  const int rho = rvalid ? ql : nrows - 1;
+  const int m = rho / a.G, g = rho - m * a.G;
+  const int rpos = a.s0 + m * a.step;
+  const int rrow = b * a.M + m, rhead = hk * a.G + g;
+  u32x4 qf[NCH];
+  {
+    const bf16 *src = (const bf16 *)a.q + ((int64_t)rrow * a.Hq + rhead) * DH + 8 * h;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qf[c] = *(const u32x4 *)(src + 16 * c);
+  }
+  int minpos = rvalid ? rpos : 0x7fffffff;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) minpos = min(minpos, __shfl_xor(minpos, off));
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int u = 0; u < ND; ++u) o[u] = f32x16{};
+  float mrun = -INFINITY, lrun = 0.f;
+  const bf16 *Kb = (const bf16 *)a.Kc + ((int64_t)b * a.Hkv + hk) * a.T_max * DH;
+  const bf16 *Vb = (const bf16 *)a.Vc + ((int64_t)b * a.Hkv + hk) * a.T_max * DH;
+  const int klast = max(kmax - 1, 0);
+
+  u32x4 kf[NCH], vr[VC];
+  auto gload = [&](int t) {  // addresses clamped to the last key: no branches
+    const int key0 = t * KT;
+    const bf16 *kr = Kb + (int64_t)min(key0 + ql, klast) * DH + 8 * h;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kf[c] = *(const u32x4 *)(kr + 16 * c);
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+      const int ch = lane + 64 * i, key = ch / (DH / 8), cc = ch - key * (DH / 8);
+      vr[i] = *(const u32x4 *)(Vb + (int64_t)min(key0 + key, klast) * DH + 8 * cc);
+    }
+  };
+  const int vbase = (4 * h + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const float sc = a.scale_log2;
+
+  int t = t0 + wave;
+  if (t < t1) gload(t);
+  for (; t < t1; t += NW) {
+    const int key0 = t * KT;
+    u32x4 kc[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kc[c] = kf[c];
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+      const int ch = lane + 64 * i, key = ch / (DH / 8), cc = ch - key * (DH / 8);
+      *(u32x4 *)(&Vs[key * VP + 8 * cc]) = vr[i];
+    }
+    if (t + NW < t1) gload(t + NW);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's V stores landed
+    __builtin_amdgcn_wave_barrier();
+
+    f32x16 sa = f32x16{}, sb = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NCH; c += 2) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[c]), __builtin_bit_cast(bf16x8, qf[c]),
+                                                   sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[c + 1]),
+                                                   __builtin_bit_cast(bf16x8, qf[c + 1]), sb, 0, 0, 0);
+    }
+    f32x16 s = sa + sb;
+    // element i is key key0 + 8*(i/4) + 4h + i%4 of query column ql
+    if (key0 + KT > minpos) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + 8 * (i >> 2) + 4 * h + (i & 3) >= rpos) s[i] = -INFINITY;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // lazy rescaling, as in attn2_kernel
+    const float tm = tmax * sc;
+    const bool upd = tm > mrun + 8.f;
+    const float mnew = upd ? tm : mrun;
+    const float alpha = upd && mrun != -INFINITY ? __builtin_amdgcn_exp2f(mrun - mnew) : (upd ? 0.f : 1.f);
+    const float nm = mnew == -INFINITY ? 0.f : -mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sc, nm));
+      s[i] = p;
+      psum += p;
+    }
+    psum += __shfl_xor(psum, 32);
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int u = 0; u < ND; ++u) o[u] *= alpha;
+    }
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = s[8 * sl + j];
+      const u32x4 pf = pack16<bf16>(pv);
+#pragma unroll
+      for (int u = 0; u < ND; ++u) {
+        const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(&Vs[vbase + 16 * sl * VP + 32 * u]));
+        const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(&Vs[vbase + (16 * sl + 8) * VP + 32 * u]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 vf{l2[0], l2[1], h2[0], h2[1]};
+        o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf),
+                                                       o[u], 0, 0, 0);
+      }
+    }
+    // the next tile's V stores must not overtake this tile's transpose reads
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // merge of the waves, in wave order: M = max m_w, o = sum o_w 2^(m_w - M),
+  // l = sum l_w 2^(m_w - M)
+  if (h == 0) {
+    mls[wave][0][ql] = mrun;
+    mls[wave][1][ql] = lrun;
+  }
+  __syncthreads();  // also: every wave is done with its V buffer
+  float mmax = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mmax = fmaxf(mmax, mls[w][0][ql]);
+  const float f = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mmax);
+  float *Os = (float *)smem;
+  if (rvalid) {
+#pragma unroll
+    for (int u = 0; u < ND; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(f32x4 *)(&Os[(wave * 32 + ql) * OP + u * 32 + 8 * j + 4 * h]) =
+            f32x4{o[u][4 * j] * f, o[u][4 * j + 1] * f, o[u][4 * j + 2] * f, o[u][4 * j + 3] * f};
+  }
+  __syncthreads();
+  // thread -> (query row, 4 head dims)
+  for (int item = tid; item < nrows * (DH / 4); item += 64 * NW) {
+    const int q = item / (DH / 4), d4 = 4 * (item - q * (DH / 4));
+    float lsum = 0.f, mq = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mq = fmaxf(mq, mls[w][0][q]);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = mls[w][0][q];
+      lsum += mw == -INFINITY ? 0.f : mls[w][1][q] * __builtin_amdgcn_exp2f(mw - mq);
+      acc += *(const f32x4 *)(&Os[(w * 32 + q) * OP + d4]);
+    }
+    const int mm = q / a.G, gg = q - mm * a.G;
+    const int orow = b * a.M + mm, ohead = hk * a.G + gg;
+    if (a.nsplit == 1) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      float v[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+      stT<bf16, 4>((bf16 *)a.out + (int64_t)orow * a.Hq * DH + ohead * DH + d4, v);
+    } else {
+      const int64_t base = ((int64_t)split * a.B * a.M + orow) * a.Hq + ohead;
+      *(f32x4 *)(a.part_o + base * DH + d4) = acc;
+      if (d4 == 0) {
+        a.part_ml[base * 2] = mq;
+        a.part_ml[base * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
 }  // namespace wm

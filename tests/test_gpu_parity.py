@@ -135,7 +135,11 @@ def test_mix_kv_full_size_sampled_rows_and_deterministic():
     ("small_prefill", 8, 128, 5, 16, 9),       # one cyclic group step of the small model
     ("small_prefill", 2, 300, 0, 1, 3),        # Jacobi-like rows incl. position 0, ragged blocks
     ("prefill_1p3b", 2, 128, 15, 16, 13),      # d=128, G=7 (rows per pair not a tile multiple)
-    ("decode_d512", 64, 1, 2047, 1, 5),        # decode shape: one query per sequence, split keys
+    ("decode_d512", 64, 1, 2047, 1, 5),        # decode shape: one query per sequence, waves split the keys
+    ("prefill_1p3b", 4, 1, 2047, 1, 13),       # decode at d=128, G=7: key splits and the combine kernel
+    ("small_prefill", 2, 4, 100, 16, 3),       # few rows at 4 positions: per-row masks, idle waves
+    ("small_prefill", 1, 16, 0, 1, 2),         # 32 rows exactly, incl. position 0, one partial tile
+    ("decode_d512", 2, 1, 0, 1, 0),            # position 0 only: no keys at all
 ])
 def test_channel_attn_matches_oracle(name, B, M, s0, step, layer):
     w = WORKLOADS[name]
