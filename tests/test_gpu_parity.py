@@ -1,8 +1,11 @@
 """HIP path vs the float64 oracle, through the C ABI (needs an MI355X).
 
 Tolerances (max-abs-relative over a tensor, max|a-b| / max|b|):
-  * fp32 runs: 1e-4 (the tiny fp32 model at every schedule and pass, the
-    kernels alone, decode). The same kernels (templated on the element type)
+  * fp32 runs: 1e-4 (the tiny fp32 model up to 32 dependent group steps, the
+    kernels alone, decode); TOL_F32_CHAIN = 4e-4 for tiny-model caches that
+    depend on more group steps (g * passes > 32), where plain fp32 evaluation
+    of the oracle's own formulas already drifts past 1e-4
+    (tests/test_fp32_error_model.py). The same kernels (templated on the element type)
     also run the deep 16- and 28-layer shapes in fp32; where a prefill pass
     feeds the cache back over several positions there the bound is
     TOL_F32_DEEP = 1e-3: fp32 rounding (~6e-8) times the exact oracle's own
@@ -34,6 +37,7 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 TOL_BF16_DEEP = 1e-1
 TOL_F32_DEEP = 1e-3
+TOL_F32_CHAIN = 4e-4
 DEV = "cuda"
 
 
@@ -197,8 +201,9 @@ def test_prefill_passes_tiny_fp32(tiny, g, npass):
         ek = max_abs_rel(gc[0][:, :, :, :w.T], rc[0][:, :, :, :w.T])
         ev = max_abs_rel(gc[1][:, :, :, :w.T], rc[1][:, :, :, :w.T])
         el = max_abs_rel(gl, rl)
-        print(f"  pass {n + 1}: K {ek:.2e} V {ev:.2e} logits {el:.2e}", flush=True)
-        assert max(ek, ev, el) <= TOL["f32"]
+        tol = TOL["f32"] if g * (n + 1) <= 32 else TOL_F32_CHAIN
+        print(f"  pass {n + 1}: K {ek:.2e} V {ev:.2e} logits {el:.2e} (tol {tol:.0e})", flush=True)
+        assert max(ek, ev, el) <= tol
 
 
 def _pass_count(caches, ar, tau):
