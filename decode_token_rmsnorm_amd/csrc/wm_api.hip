@@ -6,7 +6,7 @@
 #include "wm_gemm2.hpp"
 #include "wm_host.hpp"
 #include "wm_pool.hpp"
-#include "wm_skinny.hpp"
+#include "wm_few.hpp"
 #include "wm_attn2.hpp"
 #include "wm_pool2.hpp"
 
@@ -93,7 +93,11 @@ template <typename T> struct Run {
   // The 256 x 256 kernel (bf16 only) for steps with enough rows to fill the chip.
   static constexpr bool kBig = std::is_same<T, bf16>::value;
   bool big(int M) const { return kBig && M >= 2048; }
-  int parts(int M, int N) const { return (N + (big(M) ? G2N : GN) - 1) / (big(M) ? G2N : GN); }
+  // partial sums of squares per row written by a residual epilogue on M rows
+  int parts(int M, int N) const {
+    if (M <= kFewRows) return few_parts(M, N);
+    return (N + (big(M) ? G2N : GN) - 1) / (big(M) ? G2N : GN);
+  }
   T *Kch(int ch) const { return (T *)cache->k + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
   T *Vch(int ch) const { return (T *)cache->v + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
 
@@ -107,10 +111,12 @@ template <typename T> struct Run {
     }
   }
 
-  // Few rows: the k-split skinny kernel; otherwise the 128 x 128 tiled one.
+  // Few rows: the few-row kernel; otherwise the 128 x 128 tiled one.
   template <class AL, class BL, class EP>
   hipError_t gemm1(const AL &al, const BL &bl, const EP &ep, int M, int N, int K, int Z) {
-    if (M <= SK_MAX_ROWS) return launch_skinny<T>(al, bl, ep, M, N, K, Z, at<float>(lay.skp), s);
+    if constexpr (!std::is_same<BL, BGateUp<T>>::value) {  // (few-row gate/up: FGateUp)
+      if (M <= kFewRows) return launch_few<T>(al, bl, ep, M, N, K, Z, s);
+    }
     return launch_gemm<T>(al, bl, ep, M, N, K, Z, s);
   }
 
@@ -213,9 +219,9 @@ template <typename T> struct Run {
   }
 
   // Router weights with the source gains folded in, for steps with more than
-  // kSkinnyRows rows (once per call; the workspace keeps them).
+  // kFewRows rows (once per call; the workspace keeps them).
   wm_status prep_router() {
-    if (rows_cap <= kSkinnyRows) return WM_OK;
+    if (rows_cap <= kFewRows) return WM_OK;
     const int64_t n = 2 * (int64_t)c.L * c.k * R * c.D / Elt<T>::E16;
     hipLaunchKernelGGL((fold_router<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const T *)w->router,
                        w->src_norm, at<T>(lay.wf), c.L * c.k, c.L, c.p, R, c.D);
@@ -229,8 +235,8 @@ template <typename T> struct Run {
     const int Lk = c.L * c.k;
     const int64_t RD = (int64_t)R * c.D;
     RouterOut ro;
-    if (rows <= kSkinnyRows) {
-      // few rows: per-branch gained router input and the skinny GEMM, Z = branch
+    if (rows <= kFewRows) {
+      // few rows: per-branch gained router input and the few-row GEMM, Z = branch
       {
         ProfScope prof(WM_K_MIX, s);
         hipLaunchKernelGGL((state_rinv<T>), dim3((unsigned)((nl + 3) / 4)), dim3(256), 0, s, S, at<float>(lay.rinvS),
@@ -367,7 +373,12 @@ template <typename T> struct Run {
             done = true;
           }
         }
-        if (!done) WM_TRY((gemm1(a, b, e, rows, 2 * c.F, D, 1)));
+        if (!done && rows <= kFewRows) {
+          FGateUp<T> bf{wg + (int64_t)l * c.F * D, wu + (int64_t)l * c.F * D, D, c.F, 0};
+          WM_TRY((launch_few<T>(a, bf, e, rows, 2 * c.F, D, 1, s)));
+        } else if (!done) {
+          WM_TRY((gemm1(a, b, e, rows, 2 * c.F, D, 1)));
+        }
       }
       // h += W_down act; next state, next norm operand
       {
