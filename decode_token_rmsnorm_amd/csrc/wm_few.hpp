@@ -16,8 +16,13 @@
 //
 // Narrow-tile epilogues: thread t of the block takes tile row t / (TN/4) and
 // the 4 contiguous columns 4*(t % (TN/4)), so the TN/4 lanes of a row are
-// adjacent in one wave and row reductions are shuffles among them.  Epilogues
-// that normalise per attention head (q, cached keys) use TN = head dim.
+// adjacent in one wave and row reductions are shuffles among them.  Each
+// epilogue issues the global loads it needs (residual rows, gains, RoPE table
+// entries, the row's partial sums of squares) before the main loop, so they
+// travel with the operand loads and the epilogue itself makes no round trip.
+// A row's RMSNorm scale comes from its partial sums spread over the row's
+// lanes and added with shuffles.  Epilogues that normalise per attention head
+// (q, cached keys) use TN = head dim.
 #pragma once
 
 #include "wm_gemm.hpp"
@@ -25,12 +30,42 @@
 
 namespace wm {
 
-constexpr int FM = 16;  // rows per block
+constexpr int FM = 16;  // rows per MFMA block
 
-template <int TN> struct FewCfg {
-  static constexpr int NWK = TN == 128 ? 8 : 16;  // most waves per block
-  static constexpr int R = TN == 128 ? 2 : 4;     // k-steps per wave and round
-  static constexpr int P = TN + 4;                // LDS tile pitch (floats)
+// TR row blocks of 16 per block (4 only for wide plain stores, where the
+// weight matrix is then read once instead of once per 16 rows).
+template <int TN, int TR> struct FewCfg {
+  static constexpr int NWK = (TN >= 64 || TR > 1) ? 8 : 16;  // most waves per block
+  static constexpr int R = 4;                                // k-steps per wave and round
+  static constexpr int P = TN + 4;                           // LDS tile pitch (floats)
+  static constexpr int ROWS = FM * TR;
+};
+
+// Sum over the partial sums of squares p < nparts of one row, spread over the
+// LPR lanes of the row (lane cq loads p = cq, cq + LPR, ...; the first 8*LPR
+// parts are loaded ahead, more are added when summed), then added across the
+// lanes with shuffles; every lane of the row gets the sum.
+template <int LPR> struct PartSum {
+  static constexpr int NL = 8;
+  float v[NL];
+  const float *row;
+  int np, cq;
+  __device__ __forceinline__ void load(const float *ss, int64_t ssrow, int nparts, int lane_cq) {
+    row = ss + ssrow * nparts;
+    np = nparts;
+    cq = lane_cq;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) v[i] = row[min(cq + LPR * i, np - 1)];
+  }
+  __device__ __forceinline__ float sum() const {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) s += cq + LPR * i < np ? v[i] : 0.f;
+    for (int p = cq + LPR * NL; p < np; p += LPR) s += row[p];
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    return s;
+  }
 };
 
 // B operand of the fused gate/up projection on a TN-wide tile: tile rows
@@ -50,24 +85,30 @@ template <typename T> struct FGateUp {
 };
 
 // ---------------------------------------------------------------- epilogues
-// run_epi_few(ep, z, m0, n0, Cs, P, M, N, rowbuf): Cs = the 16 x TN fp32 tile
-// (pitch P), tile row rl = output row m0 + rl, first column n0.  Every thread
-// of the block calls it (row-scale set-up synchronises the block).
+// FewEpi<EP, T, TN, ROWS>: load(...) before the main loop, run(...) on the
+// reduced ROWS x TN tile Cs (pitch P) in LDS; tile row rl is output row
+// m0 + rl, first column n0.  Thread t < NT = ROWS * LPR owns one (row, 4
+// columns) item, and blocks have at least NT threads.
+template <class EP, typename T, int TN, int ROWS> struct FewEpi;
 
 // h += C; hb = h * gain_next; optionally S_next = h; the row's sum of squares
 // over the tile's columns -> ss_out[r, n0 / TN].
-template <typename T, int TN>
-__device__ __forceinline__ void run_epi_few(const EpiResid<T> &e, int z, int m0, int n0, const float *Cs, int P,
-                                            int M, int N, float *rowbuf) {
-  constexpr int LPR = TN / 4;
-  for (int t = threadIdx.x; t < FM * LPR; t += blockDim.x) {
-    const int rl = t / LPR, cq = t - rl * LPR, c = n0 + 4 * cq, r = m0 + rl;
-    const bool on = c < N, ok = on && r < M;
-    const int cl = on ? c : N - 4;
-    const int rc = r < M ? r : M - 1;
-    float g[4], hv[4], x[4], xb[4];
+template <typename T, int TN, int ROWS> struct FewEpi<EpiResid<T>, T, TN, ROWS> {
+  static constexpr int LPR = TN / 4, NT = ROWS * LPR;
+  float g[4], hv[4];
+  __device__ __forceinline__ void load(const EpiResid<T> &e, int z, int m0, int n0, int M, int N) {
+    const int t = min((int)threadIdx.x, NT - 1), rl = t / LPR, cq = t - rl * LPR, c = n0 + 4 * cq;
+    const int cl = c < N ? c : N - 4, rc = min(m0 + rl, M - 1);
     ldf<4>(g, e.gain_next + cl);
     ldf<4>(hv, e.h + (int64_t)rc * N + cl);
+  }
+  __device__ __forceinline__ void run(const EpiResid<T> &e, int z, int m0, int n0, const float *Cs, int P, int M,
+                                      int N) {
+    const int t = threadIdx.x;
+    if (t >= NT) return;  // (whole waves: NT is a multiple of 64 or the block's only wave)
+    const int rl = t / LPR, cq = t - rl * LPR, c = n0 + 4 * cq, r = m0 + rl;
+    const bool ok = c < N && r < M;
+    float x[4], xb[4];
     ldf<4>(x, Cs + rl * P + 4 * cq);
     float sq = 0.f;
 #pragma unroll
@@ -88,19 +129,24 @@ __device__ __forceinline__ void run_epi_few(const EpiResid<T> &e, int z, int m0,
     for (int o = LPR / 2; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
     if (cq == 0 && r < M) e.ss_out[(int64_t)r * e.nparts_out + n0 / TN] = sq;
   }
-}
+};
 
 // act[r, n0/2 + f] = silu(rs * gate) * (rs * up); gate columns [0, TN/2) of
-// the tile, up columns [TN/2, TN).
-template <typename T, int TN>
-__device__ __forceinline__ void run_epi_few(const EpiSwiGLU<T> &e, int z, int m0, int n0, const float *Cs, int P,
-                                            int M, int N, float *rowbuf) {
-  constexpr int LPR = TN / 8;  // 4 outputs per thread
-  fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, FM, M);
-  for (int t = threadIdx.x; t < FM * LPR; t += blockDim.x) {
+// the tile, up columns [TN/2, TN); 4 outputs per thread.
+template <typename T, int TN, int ROWS> struct FewEpi<EpiSwiGLU<T>, T, TN, ROWS> {
+  static constexpr int LPR = TN / 8, NT = ROWS * LPR;
+  PartSum<LPR> ps;
+  __device__ __forceinline__ void load(const EpiSwiGLU<T> &e, int z, int m0, int n0, int M, int N) {
+    const int t = min((int)threadIdx.x, NT - 1), rl = t / LPR, cq = t - rl * LPR;
+    ps.load(e.ss, min(m0 + rl, M - 1), e.nparts, cq);
+  }
+  __device__ __forceinline__ void run(const EpiSwiGLU<T> &e, int z, int m0, int n0, const float *Cs, int P, int M,
+                                      int N) {
+    const int t = threadIdx.x;
+    if (t >= NT) return;
     const int rl = t / LPR, cq = t - rl * LPR, f = n0 / 2 + 4 * cq, r = m0 + rl;
-    if (r >= M || f >= e.F) continue;
-    const float rs = rowbuf[rl];
+    const float rs = rsqrtf(ps.sum() * e.invD + e.eps);  // (shuffles: all lanes of the row)
+    if (r >= M || f >= e.F) return;
     float gt[4], up[4], y[4];
     ldf<4>(gt, Cs + rl * P + 4 * cq);
     ldf<4>(up, Cs + rl * P + TN / 2 + 4 * cq);
@@ -108,83 +154,91 @@ __device__ __forceinline__ void run_epi_few(const EpiSwiGLU<T> &e, int z, int m0
     for (int i = 0; i < 4; ++i) y[i] = silu(gt[i] * rs) * (up[i] * rs);
     stT<T, 4>(e.act + (int64_t)r * e.F + f, y);
   }
-}
+};
 
 // q = RoPE(RMSNorm_head(rinv_row * C; q_norm)); TN = head dim.
-template <typename T, int TN>
-__device__ __forceinline__ void run_epi_few(const EpiQ<T> &e, int z, int m0, int n0, const float *Cs, int P, int M,
-                                            int N, float *rowbuf) {
-  constexpr int LPR = TN / 4;
-  fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, FM, M);
-  const int lane = threadIdx.x & 63;
-  for (int t = threadIdx.x; t < FM * LPR; t += blockDim.x) {  // whole waves: FM * LPR is a multiple of 64
-    const int rl = t / LPR, cq = t - rl * LPR, r = m0 + rl;
-    const int rc = r < M ? r : M - 1;
-    float g[4], cs[1][4], sn[1][4], x[1][4];
+template <typename T, int TN, int ROWS> struct FewEpi<EpiQ<T>, T, TN, ROWS> {
+  static constexpr int LPR = TN / 4, NT = ROWS * LPR;
+  PartSum<LPR> ps;
+  float g[4], cs[1][4], sn[1][4];
+  __device__ __forceinline__ void load(const EpiQ<T> &e, int z, int m0, int n0, int M, int N) {
+    const int t = min((int)threadIdx.x, NT - 1), rl = t / LPR, cq = t - rl * LPR, rc = min(m0 + rl, M - 1);
+    ps.load(e.ss, rc, e.nparts, cq);
     ldf<4>(g, e.qnorm + 4 * cq);
-    rope_entries<4>(cs[0], sn[0], e.cosT, e.sinT, e.rp.pos(rc), lane, TN);
+    rope_entries<4>(cs[0], sn[0], e.cosT, e.sinT, e.rp.pos(rc), threadIdx.x & 63, TN);
+  }
+  __device__ __forceinline__ void run(const EpiQ<T> &e, int z, int m0, int n0, const float *Cs, int P, int M,
+                                      int N) {
+    const int t = threadIdx.x;
+    if (t >= NT) return;
+    const int rl = t / LPR, cq = t - rl * LPR, r = m0 + rl;
+    const float rs = rsqrtf(ps.sum() * e.invD + e.eps);
+    float x[1][4];
     ldf<4>(x[0], Cs + rl * P + 4 * cq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[0][i] *= rowbuf[rl];
-    head_norm_rope<4, 1>(x, lane, TN, e.eps, g, cs, sn);
+    for (int i = 0; i < 4; ++i) x[0][i] *= rs;
+    head_norm_rope<4, 1>(x, t & 63, TN, e.eps, g, cs, sn);
     if (r < M) stT<T, 4>(e.q + (int64_t)r * N + n0 + 4 * cq, x[0]);
   }
-}
+};
 
 // Pool projection, z = beta*k + j: rows scaled by the channel's 1/rms; keys
 // get the per-head key norm and RoPE; both go to cache[j, b, h, pos, :].
 // TN = head dim, so the block's columns are head n0 / TN.
-template <typename T, int TN>
-__device__ __forceinline__ void run_epi_few(const EpiKV<T> &e, int z, int m0, int n0, const float *Cs, int P, int M,
-                                            int N, float *rowbuf) {
-  constexpr int LPR = TN / 4;
-  const int beta = z / e.k, j = z - beta * e.k, hh = n0 / TN;
-  for (int rl = threadIdx.x; rl < FM; rl += blockDim.x) {
-    const int r = m0 + rl;
-    rowbuf[rl] = r < M ? e.rinvM[(int64_t)z * e.rows + r] : 0.f;
+template <typename T, int TN, int ROWS> struct FewEpi<EpiKV<T>, T, TN, ROWS> {
+  static constexpr int LPR = TN / 4, NT = ROWS * LPR;
+  float rs, g[4], cs[1][4], sn[1][4];
+  __device__ __forceinline__ void load(const EpiKV<T> &e, int z, int m0, int n0, int M, int N) {
+    const int t = min((int)threadIdx.x, NT - 1), rl = t / LPR, cq = t - rl * LPR, rc = min(m0 + rl, M - 1);
+    const int beta = z / e.k, j = z - beta * e.k;
+    rs = e.rinvM[(int64_t)z * e.rows + rc];
+    ldf<4>(g, e.knorm + (int64_t)j * TN + 4 * cq);
+    rope_entries<4>(cs[0], sn[0], e.cosT, e.sinT, e.rp.pos(rc), threadIdx.x & 63, TN);
   }
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  T *base = beta == 0 ? e.Kc : e.Vc;
-  for (int t = threadIdx.x; t < FM * LPR; t += blockDim.x) {  // whole waves
+  __device__ __forceinline__ void run(const EpiKV<T> &e, int z, int m0, int n0, const float *Cs, int P, int M,
+                                      int N) {
+    const int t = threadIdx.x;
+    if (t >= NT) return;
     const int rl = t / LPR, cq = t - rl * LPR, r = m0 + rl;
-    const int rc = r < M ? r : M - 1;
+    const int beta = z / e.k, j = z - beta * e.k, hh = n0 / TN;
     float x[1][4];
     ldf<4>(x[0], Cs + rl * P + 4 * cq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[0][i] *= rowbuf[rl];
-    if (beta == 0) {
-      float g[4], cs[1][4], sn[1][4];
-      ldf<4>(g, e.knorm + (int64_t)j * TN + 4 * cq);
-      rope_entries<4>(cs[0], sn[0], e.cosT, e.sinT, e.rp.pos(rc), lane, TN);
-      head_norm_rope<4, 1>(x, lane, TN, e.eps, g, cs, sn);
-    }
+    for (int i = 0; i < 4; ++i) x[0][i] *= rs;
+    if (beta == 0) head_norm_rope<4, 1>(x, t & 63, TN, e.eps, g, cs, sn);
     if (r < M) {
       const int pos = e.rp.pos(r), b = e.rp.seq(r);
+      T *base = beta == 0 ? e.Kc : e.Vc;
       stT<T, 4>(base + ((((int64_t)j * e.B + b) * e.Hkv + hh) * e.T_max + pos) * TN + 4 * cq, x[0]);
     }
   }
-}
+};
 
-// out[(map ? map[r] : r) * ldo + c] (+ z * zstride) = rs * C, rs from
-// partial sums of squares when ss is given.
-template <typename T, int TN>
-__device__ __forceinline__ void run_epi_few(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int P,
-                                            int M, int N, float *rowbuf) {
-  constexpr int LPR = TN / 4;
-  if (e.ss) fill_rowbuf_parts(rowbuf, e.ss, e.ss_rows, e.nparts, e.invD, e.eps, m0, FM, M);
-  const bool vec = ((e.ldo | e.zstride) & 3) == 0;
-  for (int t = threadIdx.x; t < FM * LPR; t += blockDim.x) {
+// out[(map ? map[r] : r) * ldo + c] (+ z * zstride) = rs * C, rs from the
+// row's partial sums of squares when ss is given (ss row = ss_rows[r] when
+// that map is given).
+template <typename T, int TN, int ROWS> struct FewEpi<EpiStoreF32, T, TN, ROWS> {
+  static constexpr int LPR = TN / 4, NT = ROWS * LPR;
+  PartSum<LPR> ps;
+  int64_t orow;
+  __device__ __forceinline__ void load(const EpiStoreF32 &e, int z, int m0, int n0, int M, int N) {
+    const int t = min((int)threadIdx.x, NT - 1), rl = t / LPR, cq = t - rl * LPR, rc = min(m0 + rl, M - 1);
+    orow = e.out_rows ? e.out_rows[rc] : rc;
+    if (e.ss) ps.load(e.ss, e.ss_rows ? e.ss_rows[rc] : rc, e.nparts, cq);
+  }
+  __device__ __forceinline__ void run(const EpiStoreF32 &e, int z, int m0, int n0, const float *Cs, int P, int M,
+                                      int N) {
+    const int t = threadIdx.x;
+    if (t >= NT) return;
     const int rl = t / LPR, cq = t - rl * LPR, c = n0 + 4 * cq, r = m0 + rl;
-    if (r >= M || c >= N) continue;
-    const float rs = e.ss ? rowbuf[rl] : 1.f;
-    const int64_t orow = e.out_rows ? e.out_rows[r] : r;
+    const float rs = e.ss ? rsqrtf(ps.sum() * e.invD + e.eps) : 1.f;
+    if (r >= M || c >= N) return;
     float *dst = e.out + z * e.zstride + orow * e.ldo + c;
     float x[4];
     ldf<4>(x, Cs + rl * P + 4 * cq);
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] *= rs;
-    if (vec && c + 4 <= N) {
+    if (((e.ldo | e.zstride) & 3) == 0 && c + 4 <= N) {
       stf<4>(dst, x);
     } else {
 #pragma unroll
@@ -192,68 +246,89 @@ __device__ __forceinline__ void run_epi_few(const EpiStoreF32 &e, int z, int m0,
         if (c + i < N) dst[i] = x[i];
     }
   }
-}
+};
 
 // ---------------------------------------------------------------- kernel
-// Grid (ceil(N / TN), ceil(M / FM), Z); block 64 * nwk threads, nwk <= NWK.
-template <typename T, int TN, class AL, class BL, class EP>
-__global__ __launch_bounds__(64 * FewCfg<TN>::NWK) void gemm_few(AL al, BL bl, EP ep, int M, int N, int K) {
-  constexpr int NJ = TN / 16, R = FewCfg<TN>::R, P = FewCfg<TN>::P;
-  __shared__ __attribute__((aligned(16))) float part[FewCfg<TN>::NWK * FM * P + FM];
+// Grid (ceil(N / TN), ceil(M / ROWS), Z); block 64 * nwk threads with
+// NT / 64 <= nwk <= NWK.
+template <typename T, int TN, int TR, class AL, class BL, class EP>
+__global__ __launch_bounds__((64 * FewCfg<TN, TR>::NWK)) void gemm_few(AL al, BL bl, EP ep, int M, int N, int K) {
+  using C = FewCfg<TN, TR>;
+  constexpr int NJ = TN / 16, R = C::R, P = C::P, ROWS = C::ROWS;
+  __shared__ __attribute__((aligned(16))) float part[C::NWK * ROWS * P];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwk = blockDim.x >> 6;
-  const int z = blockIdx.z, m0 = blockIdx.y * FM, n0 = blockIdx.x * TN;
+  const int z = blockIdx.z, m0 = blockIdx.y * ROWS, n0 = blockIdx.x * TN;
   const int rl = lane & 15, kl = (lane >> 4) * 16;
   const int nks = (int)((int64_t)K * (int64_t)sizeof(T) / 64);
   const int per = (nks + nwk - 1) / nwk, s0 = min(wave * per, nks), s1 = min(s0 + per, nks);
 
-  const typename AL::H ha = al.row(z, m0 + rl, M);
+  FewEpi<EP, T, TN, ROWS> epi;
+  epi.load(ep, z, m0, n0, M, N);  // in flight during the main loop
+
+  typename AL::H ha[TR];
+#pragma unroll
+  for (int i = 0; i < TR; ++i) ha[i] = al.row(z, m0 + i * FM + rl, M);
   typename BL::H hb[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) hb[j] = bl.row(z, n0, j * 16 + rl, N);
-  f32x4 acc[NJ];
+  f32x4 acc[TR][NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s = s0; s < s1; s += R) {
     // a round: R k-steps, all loads first; a step past the range re-reads the
-    // last one and is multiplied with its A fragment masked to zero
-    u32x4 a[R], b[R][NJ];
+    // last one and is multiplied with its A fragments masked to zero
+    u32x4 a[R][TR], b[R][NJ];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int kb = min(s + u, s1 - 1) * 64 + kl;
-      a[u] = al.load(ha, kb);
+#pragma unroll
+      for (int i = 0; i < TR; ++i) a[u][i] = al.load(ha[i], kb);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) b[u][j] = bl.load(hb[j], kb);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const u32x4 am = a[u] & (s + u < s1 ? ~0u : 0u);
+      const uint32_t msk = s + u < s1 ? ~0u : 0u;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) mma16<T>(acc[j], am, b[u][j]);
+      for (int i = 0; i < TR; ++i) {
+        const u32x4 am = a[u][i] & msk;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) mma16<T>(acc[i][j], am, b[u][j]);
+      }
     }
   }
 
   // wave partials -> LDS, summed in wave order into tile 0
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
+  for (int i = 0; i < TR; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) part[(wave * FM + 4 * (lane >> 4) + e) * P + j * 16 + rl] = acc[j][e];
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        part[(wave * ROWS + i * FM + 4 * (lane >> 4) + e) * P + j * 16 + rl] = acc[i][j][e];
   __syncthreads();
-  for (int idx = tid * 4; idx < FM * TN; idx += blockDim.x * 4) {
+  for (int idx = tid * 4; idx < ROWS * TN; idx += blockDim.x * 4) {
     const int r = idx / TN, c = idx - r * TN;
     f32x4 v = *(const f32x4 *)(&part[r * P + c]);
-    for (int w = 1; w < nwk; ++w) v += *(const f32x4 *)(&part[(w * FM + r) * P + c]);
+    for (int w = 1; w < nwk; ++w) v += *(const f32x4 *)(&part[(w * ROWS + r) * P + c]);
     *(f32x4 *)(&part[r * P + c]) = v;
   }
   __syncthreads();
-  run_epi_few<T, TN>(ep, z, m0, n0, part, P, M, N, part + FewCfg<TN>::NWK * FM * P);
+  epi.run(ep, z, m0, n0, part, P, M, N);
 }
 
-// Waves per block: enough for one round of R k-steps each, 4 at least.
-template <int TN> inline int few_waves(int nks) {
-  int w = (nks + FewCfg<TN>::R - 1) / FewCfg<TN>::R;
-  w = w < 4 ? 4 : w;
-  return w > FewCfg<TN>::NWK ? FewCfg<TN>::NWK : w;
+// Waves per block: enough for one round of R k-steps each, and at least 4
+// and enough for one epilogue item per thread.
+template <int TN, int TR, int NT> inline int few_waves(int nks) {
+  using C = FewCfg<TN, TR>;
+  static_assert(NT <= 64 * C::NWK, "epilogue items exceed the block");
+  int w = (nks + C::R - 1) / C::R;
+  const int lo = NT / 64 > 4 ? NT / 64 : 4;
+  w = w < lo ? lo : w;
+  return w > C::NWK ? C::NWK : w;
 }
 
 // A loader's view of the tile width (the gate/up split sits at TN/2).
@@ -264,12 +339,13 @@ template <typename T> inline FGateUp<T> few_bind(const FGateUp<T> &b, int tn) {
   return r;
 }
 
-template <typename T, int TN, class AL, class BL, class EP>
+template <typename T, int TN, int TR, class AL, class BL, class EP>
 hipError_t launch_few_tn(const AL &al, const BL &bl, const EP &ep, int M, int N, int K, int Z, hipStream_t s) {
+  constexpr int ROWS = FewCfg<TN, TR>::ROWS;
   const int nks = (int)((int64_t)K * (int64_t)sizeof(T) / 64);
-  dim3 grid((N + TN - 1) / TN, (M + FM - 1) / FM, Z);
-  hipLaunchKernelGGL((gemm_few<T, TN, AL, BL, EP>), grid, dim3(64 * few_waves<TN>(nks)), 0, s, al, few_bind(bl, TN), ep,
-                     M, N, K);
+  dim3 grid((N + TN - 1) / TN, (M + ROWS - 1) / ROWS, Z);
+  const int nw = few_waves<TN, TR, FewEpi<EP, T, TN, ROWS>::NT>(nks);
+  hipLaunchKernelGGL((gemm_few<T, TN, TR, AL, BL, EP>), grid, dim3(64 * nw), 0, s, al, few_bind(bl, TN), ep, M, N, K);
   return hipGetLastError();
 }
 
@@ -295,6 +371,11 @@ inline int few_width(int M, int N, int Z) {
   return tn;
 }
 
+// Outputs wide enough that 16-row blocks of 64 columns would pass 1024 blocks.
+inline bool few_wide(int M, int N, int Z) {
+  return (int64_t)((N + 63) / 64) * ((M + FM - 1) / FM) * Z > 1024;
+}
+
 // Number of partial sums of squares a residual epilogue writes per row.
 inline int few_parts(int M, int N) {
   const int tn = few_width(M, N, 1);
@@ -309,16 +390,20 @@ hipError_t launch_few(const AL &al, const BL &bl, const EP &ep, int M, int N, in
   if (((int64_t)K * (int64_t)sizeof(T)) % 64 != 0) return hipErrorInvalidValue;
   if constexpr (FewHead<EP>::value) {
     switch (FewHead<EP>::width(ep)) {
-      case 32: return launch_few_tn<T, 32>(al, bl, ep, M, N, K, Z, s);
-      case 64: return launch_few_tn<T, 64>(al, bl, ep, M, N, K, Z, s);
-      case 128: return launch_few_tn<T, 128>(al, bl, ep, M, N, K, Z, s);
+      case 32: return launch_few_tn<T, 32, 1>(al, bl, ep, M, N, K, Z, s);
+      case 64: return launch_few_tn<T, 64, 1>(al, bl, ep, M, N, K, Z, s);
+      case 128: return launch_few_tn<T, 128, 1>(al, bl, ep, M, N, K, Z, s);
       default: return hipErrorInvalidValue;
     }
   } else {
+    if constexpr (std::is_same<EP, EpiStoreF32>::value) {
+      // wide outputs over more than 16 rows: 64-row blocks, the weights read once
+      if (M > FM && few_wide(M, N, Z)) return launch_few_tn<T, 32, 4>(al, bl, ep, M, N, K, Z, s);
+    }
     switch (few_width(M, N, Z)) {
-      case 16: return launch_few_tn<T, 16>(al, bl, ep, M, N, K, Z, s);
-      case 32: return launch_few_tn<T, 32>(al, bl, ep, M, N, K, Z, s);
-      default: return launch_few_tn<T, 64>(al, bl, ep, M, N, K, Z, s);
+      case 16: return launch_few_tn<T, 16, 1>(al, bl, ep, M, N, K, Z, s);
+      case 32: return launch_few_tn<T, 32, 1>(al, bl, ep, M, N, K, Z, s);
+      default: return launch_few_tn<T, 64, 1>(al, bl, ep, M, N, K, Z, s);
     }
   }
 }
