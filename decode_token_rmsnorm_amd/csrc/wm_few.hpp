@@ -320,6 +320,81 @@ __global__ __launch_bounds__((64 * FewCfg<TN, TR>::NWK)) void gemm_few(AL al, BL
   epi.run(ep, z, m0, n0, part, P, M, N);
 }
 
+// ---------------------------------------------------------------- wide outputs
+// C = A B^T for at most 64 rows and many columns (the vocabulary projection),
+// stored as fp32 by EpiStoreF32.  A block of 8 waves owns 64 rows x 128
+// columns; it stages the 64 A rows of a k chunk in LDS once (so the weight
+// matrix B is the only stream from memory and is read once), each wave takes
+// 16 columns: its B fragments come straight from global memory, all loads of
+// the chunk issued before the first MFMA, and the A fragments of its 4 row
+// blocks from LDS.  The row scales (RMSNorm from partial sums of squares) are
+// loaded before the main loop and reduced over 8 lanes per row.
+constexpr int WM_ROWS = 64, WM_COLS = 128, WM_KC = 1024;  // rows, columns, k bytes per chunk and row
+constexpr int WM_AP = WM_KC + 16;                        // LDS row pitch (bytes)
+
+template <typename T, class AL, class BL>
+__global__ __launch_bounds__(512) void gemm_wide(AL al, BL bl, EpiStoreF32 ep, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) char As[WM_ROWS * WM_AP];
+  __shared__ float rsc[WM_ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int z = blockIdx.z, m0 = blockIdx.y * WM_ROWS, n0 = blockIdx.x * WM_COLS + 16 * wave;
+  const int rl = lane & 15, kl = (lane >> 4) * 16;
+  const int64_t kbytes = (int64_t)K * (int64_t)sizeof(T);
+  // row scales: 8 lanes per row
+  {
+    const int row = tid >> 3, rc = min(m0 + row, M - 1);
+    PartSum<8> ps;
+    if (ep.ss) ps.load(ep.ss, ep.ss_rows ? ep.ss_rows[rc] : rc, ep.nparts, tid & 7);
+    const float s = ep.ss ? ps.sum() : 0.f;
+    if ((tid & 7) == 0) rsc[row] = ep.ss ? rsqrtf(s * ep.invD + ep.eps) : 1.f;
+  }
+  // A rows of a chunk: 64 rows x WM_KC bytes, 16 bytes per load, WM_KC / 128 per thread
+  const int arow = tid >> 3;
+  const typename AL::H ha = al.row(z, m0 + arow, M);
+  const typename BL::H hb = bl.row(z, blockIdx.x * WM_COLS, 16 * wave + rl, N);
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t k0 = 0; k0 < kbytes; k0 += WM_KC) {
+    const int nst = (int)min((int64_t)WM_KC, kbytes - k0) / 64;  // 64-byte k-steps in the chunk
+    constexpr int NA = WM_KC / 128;
+    u32x4 b[WM_KC / 64], a[NA];
+#pragma unroll
+    for (int u = 0; u < WM_KC / 64; ++u) b[u] = bl.load(hb, (int)(k0 + min(u, nst - 1) * 64 + kl));
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int off = min(16 * ((tid & 7) + 8 * i), nst * 64 - 16);
+      a[i] = al.load(ha, (int)(k0 + off));
+    }
+    __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      *(u32x4 *)(&As[arow * WM_AP + min(16 * ((tid & 7) + 8 * i), nst * 64 - 16)]) = a[i];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < WM_KC / 64; ++u) {
+      if (u < nst) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          mma16<T>(acc[i], *(const u32x4 *)(&As[(16 * i + rl) * WM_AP + u * 64 + kl]), b[u]);
+      }
+    }
+  }
+  // lane: rows 16i + 4(lane/16) + e, column n0 + lane%16
+  const int c = n0 + rl;
+  if (c >= N) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rr = 16 * i + 4 * (lane >> 4) + e, r = m0 + rr;
+      if (r < M) {
+        const int64_t orow = ep.out_rows ? ep.out_rows[r] : r;
+        ep.out[z * ep.zstride + orow * ep.ldo + c] = acc[i][e] * rsc[rr];
+      }
+    }
+}
+
 // Waves per block: enough for one round of R k-steps each, and at least 4
 // and enough for one epilogue item per thread.
 template <int TN, int TR, int NT> inline int few_waves(int nks) {
@@ -398,7 +473,11 @@ hipError_t launch_few(const AL &al, const BL &bl, const EP &ep, int M, int N, in
   } else {
     if constexpr (std::is_same<EP, EpiStoreF32>::value) {
       // wide outputs over more than 16 rows: 64-row blocks, the weights read once
-      if (M > FM && few_wide(M, N, Z)) return launch_few_tn<T, 32, 4>(al, bl, ep, M, N, K, Z, s);
+      if (M > FM && few_wide(M, N, Z)) {
+        dim3 grid((N + WM_COLS - 1) / WM_COLS, (M + WM_ROWS - 1) / WM_ROWS, Z);
+        hipLaunchKernelGGL((gemm_wide<T, AL, BL>), grid, dim3(512), 0, s, al, bl, ep, M, N, K);
+        return hipGetLastError();
+      }
     }
     switch (few_width(M, N, Z)) {
       case 16: return launch_few_tn<T, 16, 1>(al, bl, ep, M, N, K, Z, s);

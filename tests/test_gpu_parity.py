@@ -263,10 +263,11 @@ def test_prefill_deep_shapes_fp32(name, B, T, g, npass):
         assert el <= TOL_F32_DEEP
 
 
-def test_decode_deep_shape_fp32():
-    w = WORKLOADS["decode_d512"].replace(B=8, dtype="f32")
+@pytest.mark.parametrize("B", [8, 40])  # 40: the wide vocabulary kernel, one ragged 64-row block
+def test_decode_deep_shape_fp32(B):
+    w = WORKLOADS["decode_d512"].replace(B=B, T_max=512, dtype="f32")
     t = 300
-    print("decode fp32 B=8 t=300", flush=True)
+    print(f"decode fp32 B={B} t=300", flush=True)
     W = make_weights(w, seed=0, gains="perturbed")
     K, V = make_cache(w, w.B, filled=t, seed=3, poison=True)
     tokens = make_tokens(w, seed=1, B=w.B, T=1)[:, 0]
