@@ -201,14 +201,16 @@ template <typename T> struct Run {
 
   template <int KMAX> wm_status mix(const T *S, int rows, RouterOut ro) {
     if constexpr (std::is_same<T, bf16>::value) {  // MFMA mix (wm_pool2.hpp)
-      if (c.k <= 16)
-        hipLaunchKernelGGL((pool_mix2<1>), dim3((rows + PM_RT4 - 1) / PM_RT4), dim3(256), 0, s, S, at<float>(lay.rinvS),
+      // (template: channel blocks of 16, layers staged per chunk at most 16 or 32)
+      auto go = [&](auto kern, int rt) {
+        hipLaunchKernelGGL(kern, dim3((rows + rt - 1) / rt), dim3(256), 0, s, S, at<float>(lay.rinvS),
                            at<float>(lay.Aw), ro.Z, ro.az, ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb),
                            at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
+      };
+      if (c.k <= 16)
+        c.L <= 16 ? go(pool_mix2<1, 16>, PM_RT4) : go(pool_mix2<1, 32>, PM_RT4);
       else
-        hipLaunchKernelGGL((pool_mix2<2>), dim3((rows + PM_RT4 / 2 - 1) / (PM_RT4 / 2)), dim3(256), 0, s, S,
-                           at<float>(lay.rinvS), at<float>(lay.Aw), ro.Z, ro.az, ro.ab, ro.ar, w->src_norm,
-                           w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
+        c.L <= 16 ? go(pool_mix2<2, 16>, PM_RT4 / 2) : go(pool_mix2<2, 32>, PM_RT4 / 2);
     } else {
       hipLaunchKernelGGL((pool_mix<T, KMAX>), dim3(rows), dim3(256), 0, s, S, at<float>(lay.rinvS), at<float>(lay.Aw),
                          ro.Z, ro.az, ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM),

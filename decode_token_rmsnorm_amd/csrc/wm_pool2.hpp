@@ -31,13 +31,13 @@ constexpr int PM_SP = 96;   // staged row pitch (elements): 64 columns + 64 byte
 // Router output A: element (z, beta, row, l*k + j) at z*zstride +
 // beta*bstride + row*rstride + l*k + j, summed over the Z split partials;
 // S [L, rows, D]; mb [2, k, rows, D]; rinvM [2, k, rows].
-template <int KB>
+template <int KB, int LMAX>
 __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *rinvS, const float *A, int Z,
                                                  int64_t zstride, int64_t bstride, int64_t rstride,
                                                  const float *src_gain, const float *chan_gain, bf16 *mb,
                                                  float *rinvM, int rows, int L, int k, int D, float eps) {
-  constexpr int PM_RT = PM_RT4 / KB;                 // token rows per block
-  constexpr int NPT = (PM_RT * 32 * 8 + 255) / 256;  // 16-byte pieces per thread (L <= 32)
+  constexpr int PM_RT = PM_RT4 / KB;                   // token rows per block
+  constexpr int NPT = (PM_RT * LMAX * 8 + 255) / 256;  // 16-byte pieces per thread and chunk (L <= LMAX)
   __shared__ __attribute__((aligned(16))) bf16 Sl[PM_RT * 32 * PM_SP];
   __shared__ __attribute__((aligned(16))) u32x4 Wl[PM_RT][2][KB][64];
   __shared__ float red[4][PM_RT][2][KB][16];
@@ -77,25 +77,30 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
     Wl[rr][beta][kb][lane] = pack16<bf16>(wv);
   }
 
-  // staging of one chunk: piece q = (rr, layer, p), 16 bytes, layer < L
+  // staging of one chunk: piece q = (rr, layer, p), 16 bytes, layer < L; the
+  // loads of the next PD chunks are in flight (a register ring; addresses
+  // past the last chunk re-read it, so every load is unconditional)
+  constexpr int PD = 1;
   const int npieces = PM_RT * L * 8;
-  u32x4 pre[NPT];
-  auto gload = [&](int chunk) {
+  const int nchunk = D / PM_CW;
+  u32x4 pre[PD][NPT];
+  auto gload = [&](u32x4 (&buf)[NPT], int chunk) {
+    chunk = min(chunk, nchunk - 1);
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int q = min(tid + 256 * i, npieces - 1);
       const int rr = q / (L * 8), rem = q - rr * L * 8, l = rem >> 3, p = rem & 7;
       const int row = min(r0 + rr, rows - 1);
-      pre[i] = *(const u32x4 *)(S + ((int64_t)l * rows + row) * D + chunk * PM_CW + 8 * p);
+      buf[i] = *(const u32x4 *)(S + ((int64_t)l * rows + row) * D + chunk * PM_CW + 8 * p);
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](const u32x4 (&buf)[NPT]) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int q = tid + 256 * i;
       if (q < npieces) {
         const int rr = q / (L * 8), rem = q - rr * L * 8, l = rem >> 3, p = rem & 7;
-        *(u32x4 *)(&Sl[(rr * 32 + l) * PM_SP + 8 * p]) = pre[i];
+        *(u32x4 *)(&Sl[(rr * 32 + l) * PM_SP + 8 * p]) = buf[i];
       }
     }
   };
@@ -117,13 +122,17 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
   typedef __attribute__((address_space(3))) v4s lds_v4s;
   const int tr_lo = min(8 * g + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
   const int tr_hi = min(8 * g + 4 + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
-  const int nchunk = D / PM_CW;
 
-  gload(0);
-  for (int chunk = 0; chunk < nchunk; ++chunk) {
+#pragma unroll
+  for (int u = 0; u < PD; ++u) gload(pre[u], u);
+  for (int c0 = 0; c0 < nchunk; c0 += PD)
+#pragma unroll
+  for (int u = 0; u < PD; ++u) {
+    const int chunk = c0 + u;
+    if (chunk >= nchunk) break;
     __syncthreads();  // the previous chunk's reads of Sl are done
-    sstore();
-    if (chunk + 1 < nchunk) gload(chunk + 1);
+    sstore(pre[u]);
+    gload(pre[u], chunk + PD);
     __syncthreads();
     const int col = chunk * PM_CW + 16 * wave + li;
     // gains of this lane's column: source gains for layers 8g..8g+7, channel

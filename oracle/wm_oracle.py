@@ -51,6 +51,7 @@ __all__ = [
     "n_groups_nonempty", "cache_elems", "tokset_rows", "new_cache", "attend",
     "stack_forward", "router_weights", "mix_channels", "pool", "lm_logits", "step",
     "ar", "cyclic_pass", "jacobi_pass", "decode_step", "mix_kv", "channel_attn", "Model",
+    "vanilla_new_cache", "vanilla_forward", "vanilla_decode_step",
 ]
 
 
@@ -333,3 +334,105 @@ def channel_attn(w, layer, q, B, Mrows, s0, s_step, cache):
     bidx, pos = tokset_rows(B, Mrows, s0, s_step)
     o = attend(np.asarray(q, F64), pos, bidx, cache[0], cache[1], channel_of_layer(layer, w.k))
     return o.reshape(len(pos), w.Hq * w.d)
+
+
+# ---------------------------------------------------------------------------
+# vanilla baseline: the model the pages' efficiency figures compare against
+# ---------------------------------------------------------------------------
+# The same decoder with ordinary per-layer attention ([OD-use] Qwen3-style;
+# the comparison model of [OD-diff] / [PL§3]): block l projects its own input
+# to keys and values (W_K^l, W_V^l, key norm, RoPE), and position i attends to
+# positions s <= i of its own layer (standard causal attention). The weight
+# arrays wk / wv / k_norm hold one entry per layer (k = L).
+
+def vanilla_new_cache(w, B):
+    """Per-layer key and value caches [L, B, Hkv, T_max, d], zeros."""
+    shape = (w.L, B, w.Hkv, w.T_max, w.d)
+    return np.zeros(shape, F64), np.zeros(shape, F64)
+
+
+def _vanilla_kv(M, l, a, pos):
+    w, W = M.w, M.W
+    N = a.shape[0]
+    K = rope(rmsnorm((a @ W["wk"][l].T).reshape(N, w.Hkv, w.d), W["k_norm"][l], w.eps), pos, w.rope_base)
+    V = (a @ W["wv"][l].T).reshape(N, w.Hkv, w.d)
+    return K, V
+
+
+def _causal_attention(q, K, V, qpos, kpos, inclusive):
+    """Dense masked softmax attention of one sequence: q [N, Hq, d] at
+    positions qpos, K/V [S, Hkv, d] at positions kpos; key s is visible to
+    query i when kpos[s] <= qpos[i] (inclusive) or < (strict). Queries with no
+    visible key get 0."""
+    N, Hq, d = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    vis = (kpos[None, :] <= qpos[:, None]) if inclusive else (kpos[None, :] < qpos[:, None])
+    out = np.zeros((N, Hq, d), F64)
+    for hq in range(Hq):
+        hk = hq // G
+        sc = q[:, hq] @ K[:, hk].T / math.sqrt(d)
+        sc = np.where(vis, sc, -np.inf)
+        mx = np.max(sc, axis=1, keepdims=True)
+        ok = np.isfinite(mx[:, 0])
+        p = np.where(vis, np.exp(sc - np.where(ok[:, None], mx, 0.0)), 0.0)
+        den = p.sum(axis=1, keepdims=True)
+        out[ok, hq] = (p[ok] / den[ok]) @ V[:, hk]
+    return out
+
+
+def vanilla_forward(M, tokens, inclusive=True, want_logits=True):
+    """Causal forward of whole sequences tokens [B, T] in one pass: every
+    block computes the keys and values of all positions from its own input and
+    attends causally (s <= i; strict s < i when ``inclusive`` is False).
+    Returns (cache [L, B, Hkv, T_max, d] x 2 with positions < T filled,
+    logits [B, T, V] or None)."""
+    w, W = M.w, M.W
+    tokens = np.asarray(tokens)
+    B, T = tokens.shape
+    Kc, Vc = vanilla_new_cache(w, B)
+    logits = np.zeros((B, T, w.V), F64) if want_logits else None
+    pos = np.arange(T)
+    for b in range(B):
+        h = W["embed"][tokens[b]]
+        for l in range(w.L):
+            a = rmsnorm(h, W["attn_norm"][l], w.eps)
+            q = rope(rmsnorm((a @ W["wq"][l].T).reshape(T, w.Hq, w.d), W["q_norm"][l], w.eps), pos, w.rope_base)
+            K, V = _vanilla_kv(M, l, a, pos)
+            Kc[l, b, :, :T] = K.transpose(1, 0, 2)
+            Vc[l, b, :, :T] = V.transpose(1, 0, 2)
+            o = _causal_attention(q, K, V, pos, pos, inclusive)
+            h = h + o.reshape(T, w.Hq * w.d) @ W["wo"][l].T
+            f = rmsnorm(h, W["ffn_norm"][l], w.eps)
+            h = h + (silu(f @ W["w_gate"][l].T) * (f @ W["w_up"][l].T)) @ W["w_down"][l].T
+        if want_logits:
+            logits[b] = lm_logits(M, h)
+    return (Kc, Vc), logits
+
+
+def vanilla_decode_step(M, tokens_t, t, cache):
+    """One decode step of the vanilla model at position t: block l appends the
+    token's key and value at slot t of layer l, then attends to s <= t.
+    ``cache`` (vanilla layout) is updated in place. Returns logits [B, V]."""
+    w, W = M.w, M.W
+    Kc, Vc = cache
+    B = len(tokens_t)
+    out = np.zeros((B, w.V), F64)
+    pos = np.array([t])
+    kpos = np.arange(t + 1)
+    for b in range(B):
+        h = W["embed"][np.asarray(tokens_t)[b:b + 1]]
+        for l in range(w.L):
+            a = rmsnorm(h, W["attn_norm"][l], w.eps)
+            q = rope(rmsnorm((a @ W["wq"][l].T).reshape(1, w.Hq, w.d), W["q_norm"][l], w.eps), pos, w.rope_base)
+            K, V = _vanilla_kv(M, l, a, pos)
+            Kc[l, b, :, t] = K[0]
+            Vc[l, b, :, t] = V[0]
+            Ks = np.asarray(Kc[l, b, :, :t + 1], F64).transpose(1, 0, 2)
+            Vs = np.asarray(Vc[l, b, :, :t + 1], F64).transpose(1, 0, 2)
+            o = _causal_attention(q, Ks, Vs, pos, kpos, True)
+            h = h + o.reshape(1, w.Hq * w.d) @ W["wo"][l].T
+            f = rmsnorm(h, W["ffn_norm"][l], w.eps)
+            h = h + (silu(f @ W["w_gate"][l].T) * (f @ W["w_up"][l].T)) @ W["w_down"][l].T
+        out[b] = lm_logits(M, h)[0]
+    return out
