@@ -154,3 +154,36 @@ def decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits
                                                      tokens.data_ptr(), t, ctypes.byref(cc), logits.data_ptr(),
                                                      ws.data_ptr(), ws.numel(), _stream(stream)))
     return logits
+
+
+def vanilla_prefill(model: Model, tokens: torch.Tensor, chunk: int, cache: Cache, logits_mode: int = 0,
+                    logits=None, ws=None, stream=None):
+    """The vanilla comparison model (per-layer K/V, causal s <= i) over tokens
+    [B, T] (int32, device) in steps of `chunk` consecutive positions; the model
+    needs k = L (one cache slot per layer)."""
+    B, T = tokens.shape
+    if logits_mode and logits is None:
+        shape = (B, model.shape.V) if logits_mode == 1 else (B, T, model.shape.V)
+        logits = torch.empty(shape, dtype=torch.float32, device=tokens.device)
+    ws = _ws(model, ws, B * min(chunk, T))
+    cc = cache.c()
+    C.check("wm_vanilla_prefill",
+            C.lib().wm_vanilla_prefill(ctypes.byref(model.cfg), ctypes.byref(model.w), tokens.data_ptr(), T, chunk,
+                                       ctypes.byref(cc), _ptr(logits), logits_mode, ws.data_ptr(), ws.numel(),
+                                       _stream(stream)))
+    return logits
+
+
+def vanilla_decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits=None, ws=None,
+                        stream=None):
+    """One decode step of the vanilla comparison model at position t."""
+    B = tokens.shape[0]
+    if logits is None:
+        logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)
+    ws = _ws(model, ws, B)
+    cc = cache.c()
+    C.check("wm_vanilla_decode_step",
+            C.lib().wm_vanilla_decode_step(ctypes.byref(model.cfg), ctypes.byref(model.w), tokens.data_ptr(), t,
+                                           ctypes.byref(cc), logits.data_ptr(), ws.data_ptr(), ws.numel(),
+                                           _stream(stream)))
+    return logits

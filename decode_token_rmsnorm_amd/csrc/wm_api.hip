@@ -84,6 +84,10 @@ template <typename T> struct Run {
   hipStream_t s;
   int R;
   int rows_cap;  // rows the workspace was laid out for
+  // The vanilla comparison model: per-layer K/V projection (cache slot l =
+  // layer l, k = L) appended before the layer's attention, which then includes
+  // the query's own position (s <= i); no state stack and no pool.
+  bool vanilla = false;
 
   Run(const wm_config &c_, const wm_weights *w_, const wm_cache *ca, void *ws_, int rows, hipStream_t st)
       : c(c_), w(w_), cache(ca), ws((unsigned char *)ws_), lay(ws_layout(c_, rows)), s(st), R((c_.L + c_.p - 1) / c_.p),
@@ -346,7 +350,26 @@ template <typename T> struct Run {
         else
           WM_TRY((gemm1(a, b, e, rows, QD, D, 1)));
       }
-      wm_status st = attn(l, q, ts, o);
+      if (vanilla) {
+        // K/V of the step's rows for layer l, written before the attention
+        const int hd = c.Hkv * c.d;
+        const T *wkl = (const T *)w->wk + (int64_t)l * hd * D, *wvl = (const T *)w->wv + (int64_t)l * hd * D;
+        EpiKVL<T> e{Kch(l), Vch(l), ss, nparts, invD, c.eps, w->k_norm + (int64_t)l * c.d, w->rope_cos, w->rope_sin,
+                    c.Hkv, c.d, c.T_max, rp};
+        ProfScope prof(WM_K_KVPROJ, s);
+        bool done = false;
+        if constexpr (kBig) {
+          if (big(rows)) {
+            WM_TRY((launch_gemm2(PRows<T>{hb, D, 0, rows}, PKVL<T>{wkl, wvl, D, hd, 2 * hd}, e, rows, 2 * hd, D, 1, s)));
+            done = true;
+          }
+        }
+        if (!done) WM_TRY((gemm1(LoadRows<T>{hb, D, 0, nullptr}, BKVL<T>{wkl, wvl, D, hd}, e, rows, 2 * hd, D, 1)));
+      }
+      // (vanilla: keys s <= i, i.e. the strict mask one position further)
+      wm_tokset tsa = ts;
+      if (vanilla) tsa.s0 += 1;
+      wm_status st = attn(l, q, tsa, o);
       if (st != WM_OK) return st;
       // h += W_O o; hb = h * ffn_norm
       {
@@ -387,7 +410,7 @@ template <typename T> struct Run {
         LoadRows<T> a{act, c.F, 0, nullptr};
         BRows<T> b{LoadRows<T>{wd + (int64_t)l * D * c.F, c.F, 0, nullptr}};
         const float *gnext = l + 1 < L ? w->attn_norm + (int64_t)(l + 1) * D : w->final_norm;
-        T *Snext = l + 1 < L ? S + (int64_t)(l + 1) * rows * D : nullptr;
+        T *Snext = l + 1 < L && !vanilla ? S + (int64_t)(l + 1) * rows * D : nullptr;
         EpiResid<T> e{h, hb, gnext, Snext, ss, parts(rows, D)};
         ProfScope prof(WM_K_DOWN, s);
         if (big(rows))
@@ -396,8 +419,10 @@ template <typename T> struct Run {
           WM_TRY((gemm1(a, b, e, rows, D, c.F, 1)));
       }
     }
-    wm_status st = pool(S, ts);
-    if (st != WM_OK) return st;
+    if (!vanilla) {
+      wm_status st = pool(S, ts);
+      if (st != WM_OK) return st;
+    }
     if (logit_mode) {
       int n = logit_mode == 1 ? ts.B : rows;
       int *rin = at<int>(lay.rowmap), *rout = rin + rows;
@@ -420,6 +445,11 @@ static bool weights_ok(const wm_weights *w, bool stack) {
   if (!stack) return pool;
   return pool && w->embed && w->lm_head && w->final_norm && w->attn_norm && w->wq && w->q_norm && w->wo &&
          w->ffn_norm && w->w_gate && w->w_up && w->w_down;
+}
+
+static bool vanilla_weights_ok(const wm_weights *w) {
+  return w && w->embed && w->lm_head && w->final_norm && w->attn_norm && w->wq && w->q_norm && w->wo && w->ffn_norm &&
+         w->w_gate && w->w_up && w->w_down && w->wk && w->wv && w->k_norm && w->rope_cos && w->rope_sin;
 }
 
 static wm_status check_common(const wm_config *cfg, const wm_cache *cache, void *ws, size_t ws_bytes, int rows) {
@@ -462,6 +492,29 @@ static wm_status prefill_impl(const wm_config *cfg, const wm_weights *w, const i
       msel = (Tseq - 1 - q) / g;
     }
     wm_status st = r.group_step(tokens, Tseq, q, g, ts, lm, msel, Tseq, logits);
+    if (st != WM_OK) return st;
+  }
+  return WM_OK;
+}
+
+// The vanilla comparison model over positions [0, T): steps of `chunk`
+// consecutive positions in order, each appending its K/V before attending.
+template <typename T>
+static wm_status vanilla_prefill_impl(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int Tseq,
+                                      int chunk, const wm_cache *cache, float *logits, int mode, void *ws, int rows,
+                                      hipStream_t s) {
+  Run<T> r(*cfg, w, cache, ws, rows, s);
+  r.vanilla = true;
+  const int B = cache->B;
+  for (int p0 = 0; p0 < Tseq; p0 += chunk) {
+    const int Mc = Tseq - p0 < chunk ? Tseq - p0 : chunk;
+    wm_tokset ts{B, Mc, p0, 1};
+    int lm = mode == 2 ? 2 : 0, msel = 0;
+    if (mode == 1 && Tseq - 1 < p0 + Mc) {
+      lm = 1;
+      msel = Tseq - 1 - p0;
+    }
+    wm_status st = r.group_step(tokens, Tseq, p0, 1, ts, lm, msel, Tseq, logits);
     if (st != WM_OK) return st;
   }
   return WM_OK;
@@ -559,6 +612,52 @@ wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_
     return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
   }
   Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+  return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+}
+
+wm_status wm_vanilla_prefill(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t T,
+                             int32_t chunk, const wm_cache *cache, float *logits, int32_t logits_mode, void *ws,
+                             size_t ws_bytes, wm_stream stream) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cfg->k == cfg->L, WM_ERR_SHAPE, "the vanilla model needs one cache slot per layer: k = %d, L = %d",
+           cfg->k, cfg->L);
+  WM_CHECK(cache && cache->k && cache->v && cache->B >= 1, WM_ERR_ARG, "cache, its pointers or B invalid");
+  WM_CHECK(chunk >= 1, WM_ERR_SHAPE, "chunk = %d must be >= 1", chunk);
+  WM_CHECK(T >= 1 && T <= cfg->T_max, WM_ERR_RANGE, "T = %d outside [1, T_max = %d]", T, cfg->T_max);
+  WM_CHECK(logits_mode >= 0 && logits_mode <= 2, WM_ERR_ARG, "logits_mode %d not in {0, 1, 2}", logits_mode);
+  WM_CHECK(logits_mode == 0 || logits, WM_ERR_ARG, "logits is NULL but logits_mode = %d", logits_mode);
+  WM_CHECK(tokens && vanilla_weights_ok(w), WM_ERR_ARG, "tokens or a weight pointer is NULL");
+  const int rows = cache->B * (chunk < T ? chunk : T);
+  st = check_common(cfg, cache, ws, ws_bytes, rows);
+  if (st != WM_OK) return st;
+  if (cfg->dtype == WM_BF16)
+    return vanilla_prefill_impl<bf16>(cfg, w, tokens, T, chunk, cache, logits, logits_mode, ws, rows,
+                                      (hipStream_t)stream);
+  return vanilla_prefill_impl<float>(cfg, w, tokens, T, chunk, cache, logits, logits_mode, ws, rows,
+                                     (hipStream_t)stream);
+}
+
+wm_status wm_vanilla_decode_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
+                                 const wm_cache *cache, float *logits, void *ws, size_t ws_bytes, wm_stream stream) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cfg->k == cfg->L, WM_ERR_SHAPE, "the vanilla model needs one cache slot per layer: k = %d, L = %d",
+           cfg->k, cfg->L);
+  WM_CHECK(cache && cache->k && cache->v && cache->B >= 1, WM_ERR_ARG, "cache, its pointers or B invalid");
+  WM_CHECK(t >= 0 && t < cfg->T_max, WM_ERR_RANGE, "t = %d outside [0, T_max = %d)", t, cfg->T_max);
+  WM_CHECK(tokens && logits && vanilla_weights_ok(w), WM_ERR_ARG, "tokens, logits or a weight pointer is NULL");
+  const int rows = cache->B;
+  st = check_common(cfg, cache, ws, ws_bytes, rows);
+  if (st != WM_OK) return st;
+  wm_tokset ts{cache->B, 1, t, 1};
+  if (cfg->dtype == WM_BF16) {
+    Run<bf16> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+    r.vanilla = true;
+    return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+  }
+  Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+  r.vanilla = true;
   return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
 }
 

@@ -214,6 +214,39 @@ template <typename T, int TN, int ROWS> struct FewEpi<EpiKV<T>, T, TN, ROWS> {
   }
 };
 
+// Vanilla per-layer K/V projection; TN = head dim, the block's columns are
+// one head: a key head (key norm, RoPE) when n0 < Hkv*d, else a value head.
+template <typename T, int TN, int ROWS> struct FewEpi<EpiKVL<T>, T, TN, ROWS> {
+  static constexpr int LPR = TN / 4, NT = ROWS * LPR;
+  PartSum<LPR> ps;
+  float g[4], cs[1][4], sn[1][4];
+  __device__ __forceinline__ void load(const EpiKVL<T> &e, int z, int m0, int n0, int M, int N) {
+    const int t = min((int)threadIdx.x, NT - 1), rl = t / LPR, cq = t - rl * LPR, rc = min(m0 + rl, M - 1);
+    ps.load(e.ss, rc, e.nparts, cq);
+    ldf<4>(g, e.knorm + 4 * cq);
+    rope_entries<4>(cs[0], sn[0], e.cosT, e.sinT, e.rp.pos(rc), threadIdx.x & 63, TN);
+  }
+  __device__ __forceinline__ void run(const EpiKVL<T> &e, int z, int m0, int n0, const float *Cs, int P, int M,
+                                      int N) {
+    const int t = threadIdx.x;
+    if (t >= NT) return;
+    const int rl = t / LPR, cq = t - rl * LPR, r = m0 + rl;
+    const int hd = e.Hkv * TN;
+    const bool isK = n0 < hd;
+    const int hh = (isK ? n0 : n0 - hd) / TN;
+    const float rs = rsqrtf(ps.sum() * e.invD + e.eps);
+    float x[1][4];
+    ldf<4>(x[0], Cs + rl * P + 4 * cq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[0][i] *= rs;
+    if (isK) head_norm_rope<4, 1>(x, t & 63, TN, e.eps, g, cs, sn);
+    if (r < M) {
+      const int pos = e.rp.pos(r), b = e.rp.seq(r);
+      stT<T, 4>((isK ? e.Kc : e.Vc) + (((int64_t)b * e.Hkv + hh) * e.T_max + pos) * TN + 4 * cq, x[0]);
+    }
+  }
+};
+
 // out[(map ? map[r] : r) * ldo + c] (+ z * zstride) = rs * C, rs from the
 // row's partial sums of squares when ss is given (ss row = ss_rows[r] when
 // that map is given).
@@ -436,6 +469,10 @@ template <typename T> struct FewHead<EpiQ<T>> {
 template <typename T> struct FewHead<EpiKV<T>> {
   static constexpr bool value = true;
   static int width(const EpiKV<T> &e) { return e.d; }
+};
+template <typename T> struct FewHead<EpiKVL<T>> {
+  static constexpr bool value = true;
+  static int width(const EpiKVL<T> &e) { return e.d; }
 };
 
 // Tile width for other epilogues: the narrowest of 16, 32, 64 that keeps the

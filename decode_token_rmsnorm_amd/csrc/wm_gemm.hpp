@@ -418,6 +418,61 @@ __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0
   }
 }
 
+// Per-layer K/V projection of the vanilla comparison model: output columns
+// [0, hd) are keys (per-head key norm, RoPE), [hd, 2*hd) values (hd = Hkv*d);
+// rows scaled by their RMSNorm factor from partial sums of squares; both go to
+// the layer's cache slices Kc / Vc [B, Hkv, T_max, d] at the row's position.
+template <typename T> struct EpiKVL {
+  T *Kc, *Vc;
+  const float *ss;
+  int nparts;
+  float invD, eps;
+  const float *knorm;  // [d]
+  const float *cosT, *sinT;
+  int Hkv, d, T_max;
+  RowPos rp;
+};
+
+template <typename T, int CPL>
+__device__ __forceinline__ void run_epi(const EpiKVL<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
+                                        int nrows, int M, int N, float *rowbuf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
+  const int c0 = n0 + CPL * lane;
+  if (c0 >= N) return;  // no __syncthreads below
+  const int hd = e.Hkv * e.d;
+  const bool isK = c0 < hd;  // (heads never straddle the key/value boundary)
+  const int cc = isK ? c0 : c0 - hd, hh = cc / e.d, dd = cc - hh * e.d;
+  float g[CPL];
+  ldf<CPL>(g, e.knorm + ((CPL * lane) & (e.d - 1)));
+  T *base = isK ? e.Kc : e.Vc;
+  for (int rb = wave * ER; rb < nrows; rb += nwaves() * ER) {
+    float cs[ER][CPL], sn[ER][CPL];
+#pragma unroll
+    for (int u = 0; u < ER; ++u) {
+      int r = m0 + rb + u;
+      rope_entries<CPL>(cs[u], sn[u], e.cosT, e.sinT, e.rp.pos(r < M ? r : M - 1), lane, e.d);
+    }
+    float x[ER][CPL];
+#pragma unroll
+    for (int u = 0; u < ER; ++u) {
+      const int rl = rb + u < nrows ? rb + u : nrows - 1;
+      ldf<CPL>(x[u], Cs + rl * pitch + CPL * lane);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) x[u][i] *= rowbuf[rl];
+    }
+    if (isK) head_norm_rope<CPL, ER>(x, lane, e.d, e.eps, g, cs, sn);
+#pragma unroll
+    for (int u = 0; u < ER; ++u) {
+      const int r = m0 + rb + u;
+      if (rb + u < nrows && r < M) {
+        const int pos = e.rp.pos(r), b = e.rp.seq(r);
+        stT<T, CPL>(base + (((int64_t)b * e.Hkv + hh) * e.T_max + pos) * e.d + dd, x[u]);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- B loaders
 // row(z, n0, jl, N): tile row jl of the block whose first output column is n0.
 template <typename T> struct BRows {
@@ -431,6 +486,19 @@ template <typename T> struct BGateUp {
   typedef const char *H;
   __device__ __forceinline__ H row(int z, int n0, int jl, int N) const { return L.row(n0, jl); }
   __device__ __forceinline__ u32x4 load(H h, int kbyte) const { return L.load(h, kbyte); }
+};
+// Vanilla per-layer K/V weights stacked: rows [0, hd) of wk, then rows of wv.
+template <typename T> struct BKVL {
+  const T *wk, *wv;
+  int64_t ld;
+  int hd;
+  typedef const char *H;
+  __device__ __forceinline__ H row(int z, int n0, int jl, int N) const {
+    int n = n0 + jl;
+    n = n < N ? n : N - 1;
+    return (const char *)(n < hd ? wk + (int64_t)n * ld : wv + (int64_t)(n - hd) * ld);
+  }
+  __device__ __forceinline__ u32x4 load(H h, int kbyte) const { return *(const u32x4 *)(h + kbyte); }
 };
 // Pool projection weights: z = beta*k + j -> wk[j] or wv[j].
 template <typename T> struct BKV {

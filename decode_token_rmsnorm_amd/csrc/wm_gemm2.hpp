@@ -83,6 +83,18 @@ template <typename T> struct PKV {
   }
 };
 
+// vanilla per-layer K/V weights stacked: rows [0, hd) of wk, then wv.
+template <typename T> struct PKVL {
+  const T *wk, *wv;
+  int64_t ld;
+  int hd, N;
+  __device__ __forceinline__ const char *row(int z, int n0, int jl) const {
+    int n = n0 + jl;
+    n = n < N ? n : N - 1;
+    return (const char *)(n < hd ? wk + (int64_t)n * ld : wv + (int64_t)(n - hd) * ld);
+  }
+};
+
 __device__ __forceinline__ void dma16(const void *g, unsigned char *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }

@@ -198,6 +198,34 @@ wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_
                          const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
                          wm_stream stream);
 
+/* ---- the vanilla comparison model --------------------------------------
+ * The decoder the pages measure WhiteMatter against (paperlayer.ai §3 and
+ * onedev.kr "What differs": the per-layer KV cache that the pool replaces):
+ * block l projects its own normed input to keys and values with W_K^l, W_V^l
+ * (keys: per-head key norm k_norm[l], RoPE) and its queries attend causally
+ * to positions s <= i of layer l. It runs on the same kernels; cfg->k must
+ * equal cfg->L (WM_ERR_SHAPE otherwise): wk / wv / k_norm hold one entry per
+ * layer and the cache one slot per layer (slot l = layer l). Weights used:
+ * every stack weight plus wk, wv, k_norm and the RoPE tables (src_norm,
+ * router and chan_norm are not read). */
+
+/* One causal pass over positions [0, T) of tokens [B, T] (int32), in steps
+ * of `chunk` consecutive positions taken in order; each step appends its
+ * keys and values before attending, so every chunk >= 1 gives the same
+ * result. logits_mode as for wm_cyclic_prefill_pass. Requires T <= T_max.
+ * Workspace: wm_workspace_bytes(cfg, B * min(chunk, T)). */
+wm_status wm_vanilla_prefill(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t T,
+                             int32_t chunk, const wm_cache *cache, float *logits, int32_t logits_mode, void *ws,
+                             size_t ws_bytes, wm_stream stream);
+
+/* One vanilla decode step: the token at position t of every sequence writes
+ * its keys and values at slot t of each layer and attends to s <= t.
+ * logits [B, V] float. Requires 0 <= t < T_max. Workspace:
+ * wm_workspace_bytes(cfg, B). */
+wm_status wm_vanilla_decode_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
+                                 const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
+                                 wm_stream stream);
+
 /* ---- per-kernel timing (measurement support) ---------------------------
  * Kernel kinds launched by the calls above. */
 typedef enum {

@@ -25,7 +25,7 @@ def cfg_of(w, dtype=C.WM_BF16, **kw):
 
 def test_library_exports_every_declared_function():
     names = C.header_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     assert set(names) <= exported, set(names) - exported
@@ -127,3 +127,33 @@ def test_entry_points_validate_before_launch():
                                 None) == -5
     # rope table: null output
     assert L.wm_rope_table(ctypes.byref(c), None, FAKE, None) == -1
+
+
+def test_vanilla_entry_points_validate_before_launch():
+    L = C.lib()
+    w = WORKLOADS["small_prefill"]
+    cv = cfg_of(w, k=w.L)   # the vanilla model: one cache slot per layer
+    cw = cfg_of(w)          # k < L: rejected
+    W = _weights()
+    cache = C.WmCache(FAKE, FAKE, w.B)
+    ws = L.wm_workspace_bytes(ctypes.byref(cv), w.B * 128)
+    pre = lambda c, T=w.T, chunk=128, logits=None, mode=0, Wt=W, n=ws: L.wm_vanilla_prefill(
+        ctypes.byref(c), ctypes.byref(Wt), FAKE, T, chunk, ctypes.byref(cache), logits, mode, FAKE, n, None)
+    assert pre(cw) == -2 and b"one cache slot per layer" in L.wm_last_error()
+    assert pre(cv, chunk=0) == -2
+    assert pre(cv, T=w.T_max + 1) == -5
+    assert pre(cv, mode=3, logits=FAKE) == -1
+    assert pre(cv, mode=1) == -1
+    assert pre(cv, n=ws - 256) == -4
+    W0 = _weights()
+    W0.wk = None
+    assert pre(cv, Wt=W0) == -1
+    W1 = _weights()
+    W1.router = None  # not read by the vanilla model: only the launch-free checks run, so use a bad T
+    assert pre(cv, Wt=W1, T=0) == -5
+    wd = L.wm_workspace_bytes(ctypes.byref(cv), w.B)
+    for t in (-1, w.T_max):
+        assert L.wm_vanilla_decode_step(ctypes.byref(cv), ctypes.byref(W), FAKE, t, ctypes.byref(cache), FAKE, FAKE,
+                                        wd, None) == -5
+    assert L.wm_vanilla_decode_step(ctypes.byref(cw), ctypes.byref(W), FAKE, 0, ctypes.byref(cache), FAKE, FAKE, wd,
+                                    None) == -2

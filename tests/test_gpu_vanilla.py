@@ -1,0 +1,134 @@
+"""The vanilla comparison model (per-layer K/V, causal s <= i) on the HIP path
+against the oracle's vanilla forward / decode step, through the C ABI
+(needs an MI355X). Same tolerances as the WhiteMatter tests: 1e-4 in fp32,
+2e-2 in bf16 at reduced depth, TOL_BF16_DEEP at full depth."""
+import numpy as np
+import pytest
+import torch
+
+import decode_token_rmsnorm_amd as wm
+import oracle as O
+from tests.helpers import max_abs_rel
+from tests.test_gpu_parity import DEV, TOL, TOL_BF16_DEEP, gpu_model, np_of
+from wm_inputs import WORKLOADS, make_cache, make_tokens, make_weights
+
+pytestmark = pytest.mark.gpu
+
+
+def _cmp_cache(w, gk, gv, ref, T, tol, b_sel=None):
+    """Slots < T against the oracle's; slots >= T must keep their NaN poison."""
+    K, V = np_of(gk), np_of(gv)
+    if b_sel is not None:
+        K, V = K[:, b_sel:b_sel + 1], V[:, b_sel:b_sel + 1]
+    for got, exp, name in ((K, ref[0], "K"), (V, ref[1], "V")):
+        e = max_abs_rel(got[..., :T, :], exp[..., :T, :])
+        print(f"  {name} slots < {T}: {e:.3e}", flush=True)
+        assert e <= tol, (name, e)
+        assert np.isnan(got[..., T:, :]).all(), f"{name}: a slot >= T was written"
+
+
+@pytest.mark.parametrize("chunk", [128, 16, 5])
+def test_vanilla_prefill_tiny_fp32(chunk):
+    w = WORKLOADS["tiny_fp32"]
+    w = w.replace(k=w.L)
+    print(f"vanilla prefill tiny fp32, chunk {chunk}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, w.B, fill=float("nan"))
+    lg = wm.vanilla_prefill(model, torch.from_numpy(tokens).to(DEV), chunk, cache, logits_mode=2)
+    torch.cuda.synchronize()
+    ref, rl = O.vanilla_forward(O.Model(w, W), tokens)
+    _cmp_cache(w, cache.k, cache.v, ref, w.T, TOL["f32"])
+    el = max_abs_rel(np_of(lg), rl)
+    print(f"  logits {el:.3e}", flush=True)
+    assert el <= TOL["f32"]
+
+
+def test_vanilla_decode_after_prefill_tiny_fp32():
+    w = WORKLOADS["tiny_fp32"]
+    w = w.replace(k=w.L)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    t = w.T - 1
+    print(f"vanilla prefill of {t} positions, then a decode step at t = {t}", flush=True)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, w.B, fill=float("nan"))
+    tok = torch.from_numpy(tokens).to(DEV)
+    wm.vanilla_prefill(model, tok[:, :t].contiguous(), 32, cache)
+    lg = wm.vanilla_decode_step(model, tok[:, t].contiguous(), t, cache)
+    torch.cuda.synchronize()
+    ref, rl = O.vanilla_forward(O.Model(w, W), tokens)
+    _cmp_cache(w, cache.k, cache.v, ref, w.T, TOL["f32"])
+    el = max_abs_rel(np_of(lg), rl[:, t])
+    print(f"  decode logits {el:.3e}", flush=True)
+    assert el <= TOL["f32"]
+
+
+def test_vanilla_prefill_reduced_depth_bf16():
+    w = WORKLOADS["small_prefill"].replace(L=4, k=4, B=2, T=64)
+    print("vanilla prefill bf16, L4, B2, T64, chunk 16", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, w.B, fill=float("nan"))
+    lg = wm.vanilla_prefill(model, torch.from_numpy(tokens).to(DEV), 16, cache, logits_mode=2)
+    torch.cuda.synchronize()
+    ref, rl = O.vanilla_forward(O.Model(w, W), tokens)
+    _cmp_cache(w, cache.k, cache.v, ref, w.T, TOL["bf16"])
+    el = max_abs_rel(np_of(lg), rl)
+    print(f"  logits {el:.3e}", flush=True)
+    assert el <= TOL["bf16"]
+
+
+def test_vanilla_prefill_full_depth_bf16_sampled_sequence():
+    """1.3B-scale stack (28 layers, k = L), 16 sequences x 128 positions in
+    one step of 2048 rows (the large-tile GEMM path); the oracle recomputes
+    one sampled sequence (sequences are independent)."""
+    w = WORKLOADS["prefill_1p3b"]
+    w = w.replace(k=w.L, B=16, T=128)
+    b = 5
+    print(f"vanilla prefill bf16 full depth, B16 T128, sampled sequence {b}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, w.B, fill=float("nan"))
+    lg = wm.vanilla_prefill(model, torch.from_numpy(tokens).to(DEV), 128, cache, logits_mode=1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lg).all()
+    ref, rl = O.vanilla_forward(O.Model(w, W), tokens[b:b + 1])
+    _cmp_cache(w, cache.k, cache.v, ref, w.T, TOL_BF16_DEEP, b_sel=b)
+    el = max_abs_rel(np_of(lg)[b], rl[0, -1])
+    print(f"  logits of position {w.T - 1}: {el:.3e}", flush=True)
+    assert el <= TOL_BF16_DEEP
+
+
+def test_vanilla_decode_full_size():
+    """Decode shape (L = k = 16, B = 64, 2047 cached positions of seeded
+    N(0,1) keys/values per layer); slot t is written, later slots keep their
+    poison."""
+    w = WORKLOADS["decode_d512"]
+    assert w.k == w.L
+    t = 2047
+    print("vanilla decode full size", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    K, V = make_cache(w, w.B, filled=t, seed=3, poison=True)
+    tokens = make_tokens(w, seed=1, B=w.B, T=1)[:, 0]
+    model = gpu_model(w, W)
+    cache = wm.cache_from_host(model, K, V)
+    before = (cache.k[:, :4, :, :t].clone(), cache.v[:, :4, :, :t].clone())
+    lg = wm.vanilla_decode_step(model, torch.from_numpy(tokens).to(DEV), t, cache)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.k[:, :4, :, :t], before[0]) and torch.equal(cache.v[:, :4, :, :t], before[1])
+    del before
+    ref = (np.nan_to_num(K, nan=0.0).astype(np.float64), np.nan_to_num(V, nan=0.0).astype(np.float64))
+    rl = O.vanilla_decode_step(O.Model(w, W), tokens, t, ref)
+    el = max_abs_rel(np_of(lg), rl)
+    print(f"  decode logits {el:.3e}", flush=True)
+    assert el <= TOL_BF16_DEEP
+    gk, gv = np_of(cache.k), np_of(cache.v)
+    for got, exp in ((gk, ref[0]), (gv, ref[1])):
+        e = max_abs_rel(got[:, :, :, t], exp[:, :, :, t])
+        print(f"  slot t: {e:.3e}", flush=True)
+        assert e <= TOL_BF16_DEEP
+        assert np.isnan(got[:, :, :, t + 1:]).all()
