@@ -122,6 +122,7 @@ def bench_prefill(steps, warmup):
     }
     res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
     # whole-pass MFMA fraction: algorithmic FLOP per pass / pass time
+    res["cache_gib"] = 2 * cache.k.numel() * cache.k.element_size() / 2 ** 30
     flop_pass = pass_flops(w)
     res["pass_tflops"] = flop_pass / (wall / steps) / 1e12
     res["pass_flop"] = flop_pass
@@ -225,6 +226,64 @@ def bench_mix(calls, warmup):
                          "algorithmic_per_launch": f"{nbytes:.4e} B = {rows}*{per_tok} + {wbytes} weights"}}
 
 
+def bench_vanilla(steps, decode_steps):
+    """The vanilla comparison model (per-layer K/V, causal s <= i, k = L) on the
+    same kernels: one prefill pass over the 1.3B-scale workload in steps of
+    T/g = 128 positions (the rows per step of the cyclic pass), and decode
+    steps on the decode shape (which already has k = L)."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from wm_inputs import WORKLOADS, make_cache_device, make_tokens, make_weights
+
+    out = {}
+    w = WORKLOADS["prefill_1p3b"]
+    w = w.replace(k=w.L)
+    chunk = -(-w.T // w.g)
+    model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    cache = wm.new_cache(model, w.B)
+    ws = model.workspace(w.B * chunk)
+    logits = torch.empty(w.B, w.V, dtype=torch.float32, device="cuda")
+    wm.vanilla_prefill(model, tok, chunk, cache, 1, logits, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wm.vanilla_prefill(model, tok, chunk, cache, 1, logits, ws)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    assert torch.isfinite(logits).all(), "non-finite logits"
+    cache_bytes = 2 * cache.k.numel() * cache.k.element_size()
+    out["prefill"] = {"workload": f"prefill_1p3b with per-layer K/V (k = L = {w.L}), B{w.B} T{w.T}, one causal pass "
+                                  f"in steps of {chunk} positions, bf16",
+                      "value": w.B * w.T / wall, "unit": "tokens/s", "ms_per_pass": 1e3 * wall, "passes": steps,
+                      "cache_gib": cache_bytes / 2 ** 30}
+    del cache, ws, model, tok
+    torch.cuda.empty_cache()
+
+    w = WORKLOADS["decode_d512"]
+    assert w.k == w.L
+    t = 2047
+    model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    K, V = make_cache_device(w, w.B, filled=t, seed=3)
+    cache = wm.Cache(K, V)
+    tok = torch.from_numpy(make_tokens(w, seed=1, B=w.B, T=1)[:, 0].copy()).cuda()
+    ws = model.workspace(w.B)
+    logits = torch.empty(w.B, w.V, dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        wm.vanilla_decode_step(model, tok, t, cache, logits, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(decode_steps):
+        wm.vanilla_decode_step(model, tok, t, cache, logits, ws)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / decode_steps
+    out["decode"] = {"workload": "decode_d512 with per-layer K/V (k = L = 16), B64, t=2047 cached, bf16",
+                     "value": w.B / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall, "steps": decode_steps}
+    del cache, ws, model, K, V
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline():
     """The float64 oracle on a bounded sample of the prefill workload: the first
     group step (q=0, 128 positions) of sequence 0 against the zero cache."""
@@ -257,7 +316,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-mix", action="store_true")
-    ap.add_argument("--only", choices=["decode", "mix"], default=None,
+    ap.add_argument("--skip-vanilla", action="store_true")
+    ap.add_argument("--only", choices=["decode", "mix", "vanilla"], default=None,
                     help="profiling aid: run only this part and print its object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
@@ -278,12 +338,23 @@ def main():
     import torch
     torch.cuda.set_device(0)
     if a.only:
-        part = bench_decode(a.decode_steps, 5) if a.only == "decode" else bench_mix(20, 3)
+        part = (bench_decode(a.decode_steps, 5) if a.only == "decode" else bench_mix(20, 3) if a.only == "mix"
+                else bench_vanilla(a.steps, a.decode_steps))
         print(json.dumps({a.only: part}), flush=True)
         return
     w, pre = bench_prefill(a.steps, a.warmup)
     dec = None if a.skip_decode else bench_decode(a.decode_steps, 5)
     mix = None if a.skip_mix else bench_mix(20, 3)
+    van = None if a.skip_vanilla else bench_vanilla(a.steps, a.decode_steps)
+    if van is not None:
+        # the pages' comparison: WhiteMatter prefill as a share of vanilla's (one
+        # vanilla pass against one, and against the workload's 3 passes:
+        # 1 no-grad pass + 2), decode tokens/s against vanilla's
+        wm_pass = w.B * w.T / (pre["wall_s"] / a.steps)
+        van["wm_prefill_per_pass_over_vanilla"] = wm_pass / van["prefill"]["value"]
+        van["wm_prefill_3_passes_over_vanilla"] = wm_pass / 3 / van["prefill"]["value"]
+        if dec is not None:
+            van["wm_decode_over_vanilla"] = dec["value"] / van["decode"]["value"]
     cpu = None if a.no_cpu_baseline else cpu_baseline()
     value = w.B * w.T / (pre["wall_s"] / a.steps)
     line = {
@@ -301,6 +372,7 @@ def main():
         "kernels_avg_us": pre["kernels"],
         "decode": dec,
         "mix_kv": mix,
+        "vanilla": van,
     }
     print(json.dumps(line), flush=True)
 
