@@ -284,6 +284,58 @@ def bench_vanilla(steps, decode_steps):
     return out
 
 
+def bench_sweep(tau=1e-4):
+    """The schedule sweep: (a) per-pass time of the cyclic prefill against g on
+    the small bf16 model (L16 D512 k8, B8 T2048), g in {1, 4, 8, 16, 32, T};
+    (b) on the tiny fp32 model (L4 D128 k2, T128), the fixed-point residual
+    after each pass (max-abs-relative distance of the cache from the same
+    implementation's autoregressive cache, i.e. g = T) and n_tau, the first pass
+    within tau, beside the closed form ceil(T/g) of strict causality."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from wm_inputs import WORKLOADS, make_tokens, make_weights
+
+    out = {"pass_time": [], "fixed_point": [], "tau": tau}
+    w = WORKLOADS["small_prefill"]
+    model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    for g in (1, 4, 8, 16, 32, w.T):
+        cache = wm.new_cache(model, w.B)
+        ws = model.workspace(wm.prefill_rows(w.B, w.T, g))
+        wm.cyclic_prefill_pass(model, tok, g, cache, 0, None, ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        wm.cyclic_prefill_pass(model, tok, g, cache, 0, None, ws)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        out["pass_time"].append({"g": g, "ms_per_pass": 1e3 * dt, "tokens_per_s_per_pass": w.B * w.T / dt,
+                                 "rows_per_step": wm.prefill_rows(w.B, w.T, g)})
+        del cache, ws
+    out["pass_time_workload"] = "small_prefill: L16 D512 Hq8 Hkv4 d64 F1536 k8 p2, B8 T2048, bf16"
+    del model, tok
+    torch.cuda.empty_cache()
+
+    w = WORKLOADS["tiny_fp32"]
+    model = wm.Model(w, make_weights(w, seed=0, gains="perturbed"), "f32")
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    ar = wm.new_cache(model, w.B)
+    wm.cyclic_prefill_pass(model, tok, w.T, ar)
+    for g in (1, 4, 8, 16, 32, w.T):
+        cache = wm.new_cache(model, w.B)
+        closed = -(-w.T // g)
+        res = []
+        for n in range(closed + 1):
+            wm.cyclic_prefill_pass(model, tok, g, cache)
+            num = max(float((cache.k - ar.k).abs().max()), float((cache.v - ar.v).abs().max()))
+            den = max(float(ar.k.abs().max()), float(ar.v.abs().max()))
+            res.append(num / den)
+        n_tau = next((i + 1 for i, r in enumerate(res) if r <= tau), None)
+        out["fixed_point"].append({"g": g, "closed_form_passes": closed, "n_tau": n_tau,
+                                   "residual_first_passes": res[:8], "residual_at_closed_form": res[closed - 1]})
+    out["fixed_point_workload"] = "tiny_fp32: L4 D128 Hq4 Hkv4 d32 F384 k2 p2 V512, B1 T128, fp32"
+    return out
+
+
 def cpu_baseline():
     """The float64 oracle on a bounded sample of the prefill workload: the first
     group step (q=0, 128 positions) of sequence 0 against the zero cache."""
@@ -317,7 +369,8 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-mix", action="store_true")
     ap.add_argument("--skip-vanilla", action="store_true")
-    ap.add_argument("--only", choices=["decode", "mix", "vanilla"], default=None,
+    ap.add_argument("--skip-sweep", action="store_true")
+    ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep"], default=None,
                     help="profiling aid: run only this part and print its object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
@@ -339,13 +392,14 @@ def main():
     torch.cuda.set_device(0)
     if a.only:
         part = (bench_decode(a.decode_steps, 5) if a.only == "decode" else bench_mix(20, 3) if a.only == "mix"
-                else bench_vanilla(a.steps, a.decode_steps))
+                else bench_vanilla(a.steps, a.decode_steps) if a.only == "vanilla" else bench_sweep())
         print(json.dumps({a.only: part}), flush=True)
         return
     w, pre = bench_prefill(a.steps, a.warmup)
     dec = None if a.skip_decode else bench_decode(a.decode_steps, 5)
     mix = None if a.skip_mix else bench_mix(20, 3)
     van = None if a.skip_vanilla else bench_vanilla(a.steps, a.decode_steps)
+    sweep = None if a.skip_sweep else bench_sweep()
     if van is not None:
         # the pages' comparison: WhiteMatter prefill as a share of vanilla's (one
         # vanilla pass against one, and against the workload's 3 passes:
@@ -373,6 +427,7 @@ def main():
         "decode": dec,
         "mix_kv": mix,
         "vanilla": van,
+        "schedule_sweep": sweep,
     }
     print(json.dumps(line), flush=True)
 

@@ -214,7 +214,8 @@ def _pass_count(caches, ar, tau):
     return None
 
 
-@pytest.mark.parametrize("T,g,npass", [(128, 16, 9), (32, 1, 33), (128, 5, 27)])
+@pytest.mark.parametrize("T,g,npass", [(128, 16, 9), (32, 1, 33), (128, 5, 27), (128, 4, 33), (128, 8, 17),
+                                        (128, 32, 5)])
 def test_pass_counts_agree_tiny_fp32(tiny, T, g, npass):
     """The first pass whose cache is within 1e-4 of the same implementation's
     autoregressive cache must be the same pass on the GPU and in the oracle
