@@ -23,7 +23,8 @@ class WmConfig(ctypes.Structure):
 
 
 WEIGHT_FIELDS = ["embed", "lm_head", "final_norm", "attn_norm", "wq", "q_norm", "wo", "ffn_norm", "w_gate", "w_up",
-                 "w_down", "src_norm", "router", "chan_norm", "wk", "wv", "k_norm", "rope_cos", "rope_sin"]
+                 "w_down", "src_norm", "router", "chan_norm", "wk", "wv", "k_norm", "rope_cos", "rope_sin",
+                 "static_mix"]
 
 
 class WmWeights(ctypes.Structure):

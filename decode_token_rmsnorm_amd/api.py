@@ -14,7 +14,7 @@ import torch
 
 from . import _lib as C
 
-GAINS = {"final_norm", "attn_norm", "q_norm", "ffn_norm", "src_norm", "chan_norm", "k_norm"}
+GAINS = {"final_norm", "attn_norm", "q_norm", "ffn_norm", "src_norm", "chan_norm", "k_norm", "static_mix"}
 
 
 def torch_dtype(dtype: str):

@@ -203,22 +203,22 @@ template <typename T> struct Run {
     int64_t az, ab, ar;
   };
 
-  template <int KMAX> wm_status mix(const T *S, int rows, RouterOut ro) {
+  template <int KMAX> wm_status mix(const T *S, int rows, RouterOut ro, const float *A) {
     if constexpr (std::is_same<T, bf16>::value) {  // MFMA mix (wm_pool2.hpp)
       // (template: channel blocks of 16, layers staged per chunk at most 16 or 32)
       auto go = [&](auto kern, int rt) {
-        hipLaunchKernelGGL(kern, dim3((rows + rt - 1) / rt), dim3(256), 0, s, S, at<float>(lay.rinvS),
-                           at<float>(lay.Aw), ro.Z, ro.az, ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb),
-                           at<float>(lay.rinvM), rows, c.L, c.k, c.D, c.eps);
+        hipLaunchKernelGGL(kern, dim3((rows + rt - 1) / rt), dim3(256), 0, s, S, at<float>(lay.rinvS), A, ro.Z,
+                           ro.az, ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows,
+                           c.L, c.k, c.D, c.eps);
       };
       if (c.k <= 16)
         c.L <= 16 ? go(pool_mix2<1, 16>, PM_RT4) : go(pool_mix2<1, 32>, PM_RT4);
       else
         c.L <= 16 ? go(pool_mix2<2, 16>, PM_RT4 / 2) : go(pool_mix2<2, 32>, PM_RT4 / 2);
     } else {
-      hipLaunchKernelGGL((pool_mix<T, KMAX>), dim3(rows), dim3(256), 0, s, S, at<float>(lay.rinvS), at<float>(lay.Aw),
-                         ro.Z, ro.az, ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM),
-                         rows, c.L, c.k, c.D, c.eps);
+      hipLaunchKernelGGL((pool_mix<T, KMAX>), dim3(rows), dim3(256), 0, s, S, at<float>(lay.rinvS), A, ro.Z, ro.az,
+                         ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows, c.L, c.k,
+                         c.D, c.eps);
     }
     WM_TRY(hipGetLastError());
     return WM_OK;
@@ -227,7 +227,7 @@ template <typename T> struct Run {
   // Router weights with the source gains folded in, for steps with more than
   // kFewRows rows (once per call; the workspace keeps them).
   wm_status prep_router() {
-    if (rows_cap <= kFewRows) return WM_OK;
+    if (rows_cap <= kFewRows || w->static_mix) return WM_OK;
     const int64_t n = 2 * (int64_t)c.L * c.k * R * c.D / Elt<T>::E16;
     hipLaunchKernelGGL((fold_router<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const T *)w->router,
                        w->src_norm, at<T>(lay.wf), c.L * c.k, c.L, c.p, R, c.D);
@@ -241,7 +241,17 @@ template <typename T> struct Run {
     const int Lk = c.L * c.k;
     const int64_t RD = (int64_t)R * c.D;
     RouterOut ro;
-    if (rows <= kFewRows) {
+    const float *Amix = at<float>(lay.Aw);
+    if (w->static_mix) {
+      // static mixing: every row mixes with the constant [2, L, k] weights
+      // (row stride 0); only the source row scales are needed
+      ProfScope prof(WM_K_MIX, s);
+      hipLaunchKernelGGL((state_rinv<T>), dim3((unsigned)((nl + 3) / 4)), dim3(256), 0, s, S, at<float>(lay.rinvS),
+                         nl, c.D, c.eps);
+      WM_TRY(hipGetLastError());
+      ro = RouterOut{1, 0, Lk, 0};
+      Amix = w->static_mix;
+    } else if (rows <= kFewRows) {
       // few rows: per-branch gained router input and the few-row GEMM, Z = branch
       {
         ProfScope prof(WM_K_MIX, s);
@@ -296,8 +306,10 @@ template <typename T> struct Run {
     wm_status st;
     {
       ProfScope prof(WM_K_MIX, s);
-      st = c.k <= 4 ? mix<4>(S, rows, ro) : c.k <= 8 ? mix<8>(S, rows, ro) : c.k <= 16 ? mix<16>(S, rows, ro)
-                                                                                       : mix<32>(S, rows, ro);
+      st = c.k <= 4    ? mix<4>(S, rows, ro, Amix)
+           : c.k <= 8  ? mix<8>(S, rows, ro, Amix)
+           : c.k <= 16 ? mix<16>(S, rows, ro, Amix)
+                       : mix<32>(S, rows, ro, Amix);
     }
     if (st != WM_OK) return st;
     // per-channel projection, z = beta*k + j
@@ -441,7 +453,9 @@ template <typename T> struct Run {
 
 static bool weights_ok(const wm_weights *w, bool stack) {
   if (!w) return false;
-  bool pool = w->src_norm && w->router && w->chan_norm && w->wk && w->wv && w->k_norm && w->rope_cos && w->rope_sin;
+  // (static mixing: constant weights instead of the router)
+  bool pool = w->src_norm && (w->router || w->static_mix) && w->chan_norm && w->wk && w->wv && w->k_norm &&
+              w->rope_cos && w->rope_sin;
   if (!stack) return pool;
   return pool && w->embed && w->lm_head && w->final_norm && w->attn_norm && w->wq && w->q_norm && w->wo &&
          w->ffn_norm && w->w_gate && w->w_up && w->w_down;

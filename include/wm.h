@@ -83,7 +83,14 @@ typedef struct {
  *                                channel j; column block r = layer r*p
  *   chan_norm [2, k, D] (float)  channel RMSNorm gains
  *   wk [k, Hkv*d, D], wv [k, Hkv*d, D], k_norm [k, d] (float)
- *   rope_cos, rope_sin [T_max, d/2] (float), filled by wm_rope_table().   */
+ *   rope_cos, rope_sin [T_max, d/2] (float), filled by wm_rope_table().
+ *   static_mix [2, L, k] (float), nullable: when set, the static-mixing
+ *                                variant runs (paperlayer.ai §5 analysis,
+ *                                "Dynamic routing"): every token mixes its
+ *                                normalised states with these constant signed
+ *                                weights (element (b, l, j) = weight of source
+ *                                layer l in channel j of branch b) and the
+ *                                router is not read (it may be NULL).      */
 typedef struct {
   const void *embed, *lm_head;
   const float *final_norm;
@@ -99,6 +106,7 @@ typedef struct {
   const void *wk, *wv;
   const float *k_norm;
   const float *rope_cos, *rope_sin;
+  const float *static_mix;
 } wm_weights;
 
 /* Shared KV cache: key and value arrays, each [k, B, Hkv, T_max, d] of

@@ -319,11 +319,12 @@ def decode_step(M, tokens_t, t, cache):
     return step(M, toks, cache, bidx, pos, want_logits=True)
 
 
-def mix_kv(M, S, B, Mrows, s0, s_step, cache):
+def mix_kv(M, S, B, Mrows, s0, s_step, cache, static_A=None):
     """Pool + append for a given state stack S [L, B*Mrows, D] whose rows sit at
-    positions s0 + m*s_step; writes into ``cache`` in place."""
+    positions s0 + m*s_step; writes into ``cache`` in place. ``static_A``:
+    constant [L, k] mixing per branch (the static-mixing variant) or None."""
     bidx, pos = tokset_rows(B, Mrows, s0, s_step)
-    Kn, Vn = pool(M, np.asarray(S, F64), pos)
+    Kn, Vn = pool(M, np.asarray(S, F64), pos, static_A)
     _write(cache[0], cache[1], Kn, Vn, bidx, pos)
 
 

@@ -76,7 +76,9 @@ def test_check_config_rejects(field, value, code):
 
 
 def _weights(fake=FAKE):
-    return C.WmWeights(*[fake] * len(C.WEIGHT_FIELDS))
+    """Every weight pointer set to `fake` except the optional static_mix (NULL:
+    the routed model)."""
+    return C.WmWeights(*[None if n == "static_mix" else fake for n in C.WEIGHT_FIELDS])
 
 
 def test_entry_points_validate_before_launch():
@@ -120,6 +122,11 @@ def test_entry_points_validate_before_launch():
     W0.router = None
     assert L.wm_cyclic_prefill_pass(ctypes.byref(c), ctypes.byref(W0), FAKE, w.T, 16, ctypes.byref(cache), None, 0,
                                     FAKE, ws_p, None) == -1
+    # with static mixing the router is not needed: the null router passes the
+    # weight check and the later (launch-free) workspace check fires instead
+    W0.static_mix = FAKE
+    assert L.wm_cyclic_prefill_pass(ctypes.byref(c), ctypes.byref(W0), FAKE, w.T, 16, ctypes.byref(cache), None, 0,
+                                    FAKE, ws_p - 256, None) == -4
     # decode: t outside [0, T_max)
     ws_d = L.wm_workspace_bytes(ctypes.byref(c), w.B)
     for t in (-1, w.T_max):

@@ -30,7 +30,8 @@ import torch
 import decode_token_rmsnorm_amd as wm
 import oracle as O
 from tests.helpers import max_abs_rel
-from wm_inputs import (WORKLOADS, make_cache, make_queries, make_state_stack, make_tokens, make_weights)
+from wm_inputs import (WORKLOADS, make_cache, make_queries, make_state_stack, make_static_mix, make_tokens,
+                       make_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,6 +99,57 @@ def test_mix_kv_matches_oracle(name, B, M, s0, step):
     O.mix_kv(O.Model(w, W), S, B, M, s0, step, ref)
     bidx, pos = O.tokset_rows(B, M, s0, step)
     assert_cache(w, cache.k, cache.v, ref, written_mask(w, B, bidx, pos), TOL[w.dtype])
+
+
+@pytest.mark.parametrize("name,B,M,s0,step", [
+    ("tiny_fp32", 2, 100, 0, 1),        # fp32 scalar mix
+    ("mix_bf16", 3, 37, 5, 7),          # bf16 MFMA mix, few rows
+    ("mix_bf16", 3, 300, 2, 5),         # bf16, 900 rows
+])
+def test_mix_kv_static_mixing_matches_oracle(name, B, M, s0, step):
+    """The static-mixing variant: constant [2, L, k] weights replace the router
+    (which is not uploaded at all)."""
+    w = WORKLOADS[name].replace(B=B)
+    print(f"mix_kv static {name} B={B} M={M} s0={s0} step={step}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    A = make_static_mix(w)
+    S = make_state_stack(w, B * M, seed=2)
+    up = {n: W[n] for n in ("src_norm", "chan_norm", "wk", "wv", "k_norm")}
+    up["static_mix"] = A
+    model = gpu_model(w, up)
+    cache = wm.new_cache(model, B, fill=float("nan"))
+    St = torch.from_numpy(S).to(DEV, wm.api.torch_dtype(w.dtype))
+    wm.mix_kv(model, St, B, M, s0, step, cache)
+    torch.cuda.synchronize()
+    ref = O.new_cache(w, B)
+    O.mix_kv(O.Model(w, W), S, B, M, s0, step, ref, static_A=(A[0], A[1]))
+    bidx, pos = O.tokset_rows(B, M, s0, step)
+    assert_cache(w, cache.k, cache.v, ref, written_mask(w, B, bidx, pos), TOL[w.dtype])
+
+
+def test_prefill_static_mixing_tiny_fp32():
+    """Two cyclic passes (g = 16) of the tiny model with static mixing."""
+    w = WORKLOADS["tiny_fp32"]
+    W = make_weights(w, seed=0, gains="perturbed")
+    A = make_static_mix(w)
+    tokens = make_tokens(w, seed=1)
+    print("prefill static mixing tiny fp32, g=16, 2 passes", flush=True)
+    up = {n: a for n, a in W.items() if n != "router"}
+    up["static_mix"] = A
+    model = gpu_model(w, up)
+    cache = wm.new_cache(model, w.B)
+    tok = torch.from_numpy(tokens).to(DEV)
+    M = O.Model(w, W)
+    ref = O.new_cache(w, w.B)
+    for n in range(2):
+        lg = wm.cyclic_prefill_pass(model, tok, 16, cache, logits_mode=2)
+        rl = O.cyclic_pass(M, tokens, ref, 16, want_logits=True, static_A=(A[0], A[1]))
+        torch.cuda.synchronize()
+        ek = max_abs_rel(np_of(cache.k), ref[0])
+        ev = max_abs_rel(np_of(cache.v), ref[1])
+        el = max_abs_rel(np_of(lg), rl)
+        print(f"  pass {n + 1}: K {ek:.2e} V {ev:.2e} logits {el:.2e}", flush=True)
+        assert max(ek, ev, el) <= TOL["f32"]
 
 
 def test_mix_kv_full_size_sampled_rows_and_deterministic():

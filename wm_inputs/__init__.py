@@ -155,6 +155,13 @@ def make_weight(w: Workload, name: str, seed: int = 0, gains: str = "ones") -> n
     return _finish(r.standard_normal(size=shape, dtype=np.float32) * np.float32(0.02), w.dtype)
 
 
+def make_static_mix(w: Workload, seed: int = 5) -> np.ndarray:
+    """[2, L, k] float32 constant signed mixing weights (the static-mixing
+    variant): N(0, 1) draws."""
+    r = _rng(seed, "static_mix")
+    return r.standard_normal(size=(2, w.L, w.k), dtype=np.float32)
+
+
 def make_weights(w: Workload, seed: int = 0, gains: str = "ones", names=None) -> dict:
     names = list(weight_shapes(w)) if names is None else list(names)
     return {n: make_weight(w, n, seed, gains) for n in names}
