@@ -51,7 +51,7 @@ __all__ = [
     "n_groups_nonempty", "cache_elems", "tokset_rows", "new_cache", "attend",
     "stack_forward", "router_weights", "mix_channels", "pool", "lm_logits", "step",
     "ar", "cyclic_pass", "jacobi_pass", "decode_step", "mix_kv", "channel_attn", "Model",
-    "vanilla_new_cache", "vanilla_forward", "vanilla_decode_step",
+    "vanilla_new_cache", "vanilla_forward", "vanilla_decode_step", "ff_forward",
 ]
 
 
@@ -437,3 +437,70 @@ def vanilla_decode_step(M, tokens_t, t, cache):
             h = h + (silu(f @ W["w_gate"][l].T) * (f @ W["w_up"][l].T)) @ W["w_down"][l].T
         out[b] = lm_logits(M, h)[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# feedback-free variant
+# ---------------------------------------------------------------------------
+# [PL§5] analysis / [OD] ablations: layer l sees only the states 0..l, so
+# there is no deep-to-shallow feedback and no iteration. Reading (the pages
+# give no more): k = L, consumer layer l reads channel l; channel l of a token
+# mixes only its states 0..l, with router weights computed from the sampled
+# normalised states r <= l (r in 0, p, 2p, ...) and the router rows of
+# channel l; attention stays strictly causal (s < i). Then the channel-l keys
+# and values of every position are known once layer l's input is, so one
+# layer-synchronous pass computes the model.
+
+def _ff_channel(M, S_upto, l, pos):
+    """Keys/values of channel l for rows whose states 0..l are S_upto
+    [l+1, N, D]. Returns K, V [N, Hkv, d]."""
+    w, W = M.w, M.W
+    N = S_upto.shape[1]
+    sampled = [r for r in range(0, w.L, w.p) if r <= l]
+    RD = w.R * w.D
+    out = []
+    for beta in (0, 1):
+        n = [rmsnorm(S_upto[r], W["src_norm"][beta, r], w.eps) for r in range(l + 1)]
+        u = np.concatenate([n[r] for r in sampled], axis=-1)          # [N, |sampled| * D]
+        Wr = W["router"][beta].reshape(w.L, w.k, RD)[:, l, :len(sampled) * w.D]  # rows (src, channel l)
+        A = u @ Wr[:l + 1].T                                              # [N, l+1]: sources 0..l
+        m = np.zeros((N, w.D), F64)
+        for src in range(l + 1):
+            m += A[:, src, None] * n[src]
+        c = rmsnorm(m, W["chan_norm"][beta, l], w.eps)
+        if beta == 0:
+            out.append(rope(rmsnorm((c @ W["wk"][l].T).reshape(N, w.Hkv, w.d), W["k_norm"][l], w.eps), pos,
+                            w.rope_base))
+        else:
+            out.append((c @ W["wv"][l].T).reshape(N, w.Hkv, w.d))
+    return out[0], out[1]
+
+
+def ff_forward(M, tokens, want_logits=True):
+    """The feedback-free model over whole sequences tokens [B, T] in one
+    layer-synchronous pass. Returns (cache [k = L, B, Hkv, T_max, d] x 2 with
+    positions < T filled, logits [B, T, V] or None)."""
+    w, W = M.w, M.W
+    assert w.k == w.L, "the feedback-free model has one channel per layer"
+    tokens = np.asarray(tokens)
+    B, T = tokens.shape
+    Kc, Vc = new_cache(w, B)
+    logits = np.zeros((B, T, w.V), F64) if want_logits else None
+    pos = np.arange(T)
+    for b in range(B):
+        h = W["embed"][tokens[b]]
+        S = np.empty((w.L, T, w.D), F64)
+        for l in range(w.L):
+            S[l] = h
+            K, V = _ff_channel(M, S[:l + 1], l, pos)
+            Kc[l, b, :, :T] = K.transpose(1, 0, 2)
+            Vc[l, b, :, :T] = V.transpose(1, 0, 2)
+            a = rmsnorm(h, W["attn_norm"][l], w.eps)
+            q = rope(rmsnorm((a @ W["wq"][l].T).reshape(T, w.Hq, w.d), W["q_norm"][l], w.eps), pos, w.rope_base)
+            o = _causal_attention(q, K, V, pos, pos, False)
+            h = h + o.reshape(T, w.Hq * w.d) @ W["wo"][l].T
+            f = rmsnorm(h, W["ffn_norm"][l], w.eps)
+            h = h + (silu(f @ W["w_gate"][l].T) * (f @ W["w_up"][l].T)) @ W["w_down"][l].T
+        if want_logits:
+            logits[b] = lm_logits(M, h)
+    return (Kc, Vc), logits

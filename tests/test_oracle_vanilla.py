@@ -14,6 +14,7 @@ the comparison model of the pages' efficiency figures.
     step at t = T, equals the forward over T + 1 tokens at position T.
 """
 import numpy as np
+import pytest
 
 import oracle as O
 from tests.helpers import max_abs_rel
@@ -91,3 +92,53 @@ def test_decode_continues_the_forward():
     assert max_abs_rel(lg, lgf[:, T]) < 1e-12
     assert max_abs_rel(Kc[..., :T + 1, :], Kf[..., :T + 1, :]) < 1e-12
     assert max_abs_rel(Vc[..., :T + 1, :], Vf[..., :T + 1, :]) < 1e-12
+
+
+# ---------------------------------------------------------------- feedback-free variant
+
+def _ff_case(T=20, p=2):
+    w = WORKLOADS["tiny_fp32"]
+    w = w.replace(k=w.L, p=p, T=T, T_max=T)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tok = make_tokens(w, seed=1, B=2, T=T, dist="uniform")
+    return w, W, tok
+
+
+@pytest.mark.parametrize("p", [1, 2, 3])
+def test_feedback_free_is_whitematter_with_a_masked_router(p):
+    """The layer-synchronous feedback-free forward equals the WhiteMatter model
+    (k = L) run token by token once the router rows of channel l are zeroed
+    for sources l' > l and for the input blocks of sampled states r > l: then
+    every channel of the full model depends on states 0..l only."""
+    w, W, tok = _ff_case(p=p)
+    (Kf, Vf), lgf = O.ff_forward(O.Model(w, W), tok)
+    Wm = dict(W)
+    router = W["router"].copy().reshape(2, w.L, w.k, w.R, w.D)
+    for l in range(w.L):            # channel
+        for src in range(w.L):
+            if src > l:
+                router[:, src, l] = 0.0
+        for ri, r in enumerate(range(0, w.L, w.p)):
+            if r > l:
+                router[:, :, l, ri] = 0.0
+    Wm["router"] = router.reshape(W["router"].shape)
+    cache, lg = O.ar(O.Model(w, Wm), tok, want_logits=True)
+    T = tok.shape[1]
+    assert max_abs_rel(Kf[..., :T, :], cache[0][..., :T, :]) < 1e-12
+    assert max_abs_rel(Vf[..., :T, :], cache[1][..., :T, :]) < 1e-12
+    assert max_abs_rel(lgf, lg) < 1e-12
+    # and the unmasked router does give a different model (deep states matter)
+    cache2, lg2 = O.ar(O.Model(w, W), tok, want_logits=True)
+    assert max_abs_rel(lg2, lg) > 1e-4
+
+
+def test_feedback_free_is_causal():
+    w, W, tok = _ff_case()
+    M = O.Model(w, W)
+    (K1, V1), lg1 = O.ff_forward(M, tok)
+    tok2 = tok.copy()
+    tok2[:, -1] = (tok2[:, -1] + 5) % w.V
+    (K2, V2), lg2 = O.ff_forward(M, tok2)
+    T = tok.shape[1]
+    np.testing.assert_array_equal(K1[..., :T - 1, :], K2[..., :T - 1, :])
+    np.testing.assert_array_equal(lg1[:, :T - 1], lg2[:, :T - 1])
