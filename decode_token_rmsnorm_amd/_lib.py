@@ -57,6 +57,10 @@ _SIGS = {
                                    c_size, c_vp]),
     "wm_vanilla_decode_step": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, P(WmCache), c_vp, c_vp, c_size,
                                        c_vp]),
+    "wm_feedback_free_prefill": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, c_i32, P(WmCache), c_vp, c_i32,
+                                         c_vp, c_size, c_vp]),
+    "wm_feedback_free_decode_step": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, P(WmCache), c_vp, c_vp,
+                                             c_size, c_vp]),
     "wm_profile_begin": (c_i32, [ctypes.c_uint32]),
     "wm_profile_read": (c_i32, [P(ctypes.c_int64), P(ctypes.c_double)]),
     "wm_profile_end": (c_i32, []),

@@ -156,6 +156,44 @@ def decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits
     return logits
 
 
+def _chunked_prefill(fn: str, model: Model, tokens: torch.Tensor, chunk: int, cache: Cache, logits_mode: int,
+                     logits, ws, stream):
+    B, T = tokens.shape
+    if logits_mode and logits is None:
+        shape = (B, model.shape.V) if logits_mode == 1 else (B, T, model.shape.V)
+        logits = torch.empty(shape, dtype=torch.float32, device=tokens.device)
+    ws = _ws(model, ws, B * min(chunk, T))
+    cc = cache.c()
+    C.check(fn, getattr(C.lib(), fn)(ctypes.byref(model.cfg), ctypes.byref(model.w), tokens.data_ptr(), T, chunk,
+                                     ctypes.byref(cc), _ptr(logits), logits_mode, ws.data_ptr(), ws.numel(),
+                                     _stream(stream)))
+    return logits
+
+
+def _one_step(fn: str, model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits, ws, stream):
+    B = tokens.shape[0]
+    if logits is None:
+        logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)
+    ws = _ws(model, ws, B)
+    cc = cache.c()
+    C.check(fn, getattr(C.lib(), fn)(ctypes.byref(model.cfg), ctypes.byref(model.w), tokens.data_ptr(), t,
+                                     ctypes.byref(cc), logits.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return logits
+
+
+def feedback_free_prefill(model: Model, tokens: torch.Tensor, chunk: int, cache: Cache, logits_mode: int = 0,
+                          logits=None, ws=None, stream=None):
+    """The feedback-free variant (k = L, channel l from states 0..l) over
+    tokens [B, T] in steps of `chunk` consecutive positions."""
+    return _chunked_prefill("wm_feedback_free_prefill", model, tokens, chunk, cache, logits_mode, logits, ws, stream)
+
+
+def feedback_free_decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits=None, ws=None,
+                              stream=None):
+    """One decode step of the feedback-free variant at position t."""
+    return _one_step("wm_feedback_free_decode_step", model, tokens, t, cache, logits, ws, stream)
+
+
 def vanilla_prefill(model: Model, tokens: torch.Tensor, chunk: int, cache: Cache, logits_mode: int = 0,
                     logits=None, ws=None, stream=None):
     """The vanilla comparison model (per-layer K/V, causal s <= i) over tokens

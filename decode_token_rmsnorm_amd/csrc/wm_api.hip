@@ -88,6 +88,10 @@ template <typename T> struct Run {
   // layer l, k = L) appended before the layer's attention, which then includes
   // the query's own position (s <= i); no state stack and no pool.
   bool vanilla = false;
+  // The feedback-free variant (k = L): channel l mixes the states 0..l of its
+  // token only, so it is built at layer l, before that layer's (strict)
+  // attention, from the states already in place; no pool after the stack.
+  bool ff = false;
 
   Run(const wm_config &c_, const wm_weights *w_, const wm_cache *ca, void *ws_, int rows, hipStream_t st)
       : c(c_), w(w_), cache(ca), ws((unsigned char *)ws_), lay(ws_layout(c_, rows)), s(st), R((c_.L + c_.p - 1) / c_.p),
@@ -203,21 +207,28 @@ template <typename T> struct Run {
     int64_t az, ab, ar;
   };
 
+  // Mix of kk channels over the first LL source states; the gains are the
+  // model's (beta strides L*D and k*D) from src_norm / cg0.
   template <int KMAX> wm_status mix(const T *S, int rows, RouterOut ro, const float *A) {
+    return mix_g<KMAX>(S, rows, ro, A, c.L, c.k, w->chan_norm);
+  }
+  template <int KMAX>
+  wm_status mix_g(const T *S, int rows, RouterOut ro, const float *A, int LL, int kk, const float *cg0) {
+    const int64_t sgb = (int64_t)c.L * c.D, cgb = (int64_t)c.k * c.D;
     if constexpr (std::is_same<T, bf16>::value) {  // MFMA mix (wm_pool2.hpp)
       // (template: channel blocks of 16, layers staged per chunk at most 16 or 32)
       auto go = [&](auto kern, int rt) {
         hipLaunchKernelGGL(kern, dim3((rows + rt - 1) / rt), dim3(256), 0, s, S, at<float>(lay.rinvS), A, ro.Z,
-                           ro.az, ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows,
-                           c.L, c.k, c.D, c.eps);
+                           ro.az, ro.ab, ro.ar, w->src_norm, sgb, cg0, cgb, at<T>(lay.mb), at<float>(lay.rinvM), rows,
+                           LL, kk, c.D, c.eps);
       };
-      if (c.k <= 16)
-        c.L <= 16 ? go(pool_mix2<1, 16>, PM_RT4) : go(pool_mix2<1, 32>, PM_RT4);
+      if (kk <= 16)
+        LL <= 16 ? go(pool_mix2<1, 16>, PM_RT4) : go(pool_mix2<1, 32>, PM_RT4);
       else
-        c.L <= 16 ? go(pool_mix2<2, 16>, PM_RT4 / 2) : go(pool_mix2<2, 32>, PM_RT4 / 2);
+        LL <= 16 ? go(pool_mix2<2, 16>, PM_RT4 / 2) : go(pool_mix2<2, 32>, PM_RT4 / 2);
     } else {
       hipLaunchKernelGGL((pool_mix<T, KMAX>), dim3(rows), dim3(256), 0, s, S, at<float>(lay.rinvS), A, ro.Z, ro.az,
-                         ro.ab, ro.ar, w->src_norm, w->chan_norm, at<T>(lay.mb), at<float>(lay.rinvM), rows, c.L, c.k,
+                         ro.ab, ro.ar, w->src_norm, sgb, cg0, cgb, at<T>(lay.mb), at<float>(lay.rinvM), rows, LL, kk,
                          c.D, c.eps);
     }
     WM_TRY(hipGetLastError());
@@ -261,7 +272,7 @@ template <typename T> struct Run {
       }
       ProfScope prof(WM_K_ROUTER, s);
       hipLaunchKernelGGL((router_input<T>), dim3(rows, 2), dim3(256), 0, s, S, at<float>(lay.rinvS), w->src_norm,
-                         at<T>(lay.u), rows, c.L, c.p, R, c.D);
+                         at<T>(lay.u), rows, c.L, c.p, R, c.D, 0, R);
       WM_TRY(hipGetLastError());
       LoadRows<T> ua{at<T>(lay.u), RD, (int64_t)rows * RD, nullptr};
       BRows<T> rb{LoadRows<T>{(const T *)w->router, RD, (int64_t)Lk * RD, nullptr}};
@@ -330,6 +341,56 @@ template <typename T> struct Run {
     return WM_OK;
   }
 
+  // -------------------------------------------------------- feedback-free channel
+  // Channel l of the step's rows from their states 0..l (S[0..l] in place):
+  // row scale of state l, its block of the gained router input when it is a
+  // router layer (l % p == 0), router weights of sources 0..l for channel l
+  // (router rows src*k + l over the first l/p + 1 input blocks), mix,
+  // channel norm, K/V projection and append into cache channel l.
+  wm_status ff_channel(int l, const T *S, wm_tokset ts) {
+    const int rows = ts.B * ts.M, D = c.D, Nl = l + 1, Rl = l / c.p + 1, Lk = c.L * c.k;
+    const int64_t RD = (int64_t)R * D, HD = (int64_t)c.Hkv * c.d;
+    {
+      ProfScope prof(WM_K_MIX, s);
+      hipLaunchKernelGGL((state_rinv<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                         S + (int64_t)l * rows * D, at<float>(lay.rinvS) + (int64_t)l * rows, (int64_t)rows, D, c.eps);
+      WM_TRY(hipGetLastError());
+      if (l % c.p == 0) {
+        hipLaunchKernelGGL((router_input<T>), dim3(rows, 2), dim3(256), 0, s, S, at<float>(lay.rinvS), w->src_norm,
+                           at<T>(lay.u), rows, c.L, c.p, R, D, l / c.p, l / c.p + 1);
+        WM_TRY(hipGetLastError());
+      }
+    }
+    float *Aw = at<float>(lay.Aw);
+    {
+      ProfScope prof(WM_K_ROUTER, s);
+      LoadRows<T> ua{at<T>(lay.u), RD, (int64_t)rows * RD, nullptr};
+      BRows<T> rb{LoadRows<T>{(const T *)w->router + (int64_t)l * RD, (int64_t)c.k * RD, (int64_t)Lk * RD, nullptr}};
+      EpiStoreF32 re{Aw, Nl, (int64_t)rows * Nl, nullptr, nullptr, nullptr, 0, 0.f, 0.f};
+      WM_TRY((gemm1(ua, rb, re, rows, Nl, Rl * D, 2)));
+    }
+    {
+      ProfScope prof(WM_K_MIX, s);
+      wm_status st = mix_g<4>(S, rows, RouterOut{1, 0, (int64_t)rows * Nl, Nl}, Aw, Nl, 1,
+                              w->chan_norm + (int64_t)l * D);
+      if (st != WM_OK) return st;
+    }
+    const T *wkl = (const T *)w->wk + (int64_t)l * HD * D, *wvl = (const T *)w->wv + (int64_t)l * HD * D;
+    EpiKV<T> pe{Kch(l), Vch(l), at<float>(lay.rinvM), w->k_norm + (int64_t)l * c.d, w->rope_cos, w->rope_sin, 1,
+                cache->B, c.Hkv, c.T_max, c.d, rows, c.eps, RowPos{ts.M, ts.s0, ts.s_step}};
+    ProfScope prof(WM_K_KVPROJ, s);
+    if constexpr (kBig) {
+      if (big(rows)) {
+        WM_TRY((launch_gemm2(PRows<T>{at<T>(lay.mb), D, (int64_t)rows * D, rows},
+                             PKV<T>{wkl, wvl, D, HD * D, 1, (int)HD}, pe, rows, (int)HD, D, 2, s)));
+        return WM_OK;
+      }
+    }
+    WM_TRY((gemm1(LoadRows<T>{at<T>(lay.mb), D, (int64_t)rows * D, nullptr}, BKV<T>{wkl, wvl, D, HD * D, 1}, pe,
+                  rows, (int)HD, D, 2)));
+    return WM_OK;
+  }
+
   // -------------------------------------------------------- one group step
   // Rows of ts; row r = b*M + m takes token tokens[b*tstride + toff + m*tstep].
   // logit_mode 0: none; 1: row m_sel of every sequence -> logits[b]; 2: all
@@ -377,6 +438,10 @@ template <typename T> struct Run {
           }
         }
         if (!done) WM_TRY((gemm1(LoadRows<T>{hb, D, 0, nullptr}, BKVL<T>{wkl, wvl, D, hd}, e, rows, 2 * hd, D, 1)));
+      }
+      if (ff) {
+        wm_status st = ff_channel(l, S, ts);
+        if (st != WM_OK) return st;
       }
       // (vanilla: keys s <= i, i.e. the strict mask one position further)
       wm_tokset tsa = ts;
@@ -431,7 +496,7 @@ template <typename T> struct Run {
           WM_TRY((gemm1(a, b, e, rows, D, c.F, 1)));
       }
     }
-    if (!vanilla) {
+    if (!vanilla && !ff) {
       wm_status st = pool(S, ts);
       if (st != WM_OK) return st;
     }
@@ -514,11 +579,12 @@ static wm_status prefill_impl(const wm_config *cfg, const wm_weights *w, const i
 // The vanilla comparison model over positions [0, T): steps of `chunk`
 // consecutive positions in order, each appending its K/V before attending.
 template <typename T>
-static wm_status vanilla_prefill_impl(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int Tseq,
-                                      int chunk, const wm_cache *cache, float *logits, int mode, void *ws, int rows,
-                                      hipStream_t s) {
+static wm_status chunked_prefill_impl(bool vanilla, const wm_config *cfg, const wm_weights *w, const int32_t *tokens,
+                                      int Tseq, int chunk, const wm_cache *cache, float *logits, int mode, void *ws,
+                                      int rows, hipStream_t s) {
   Run<T> r(*cfg, w, cache, ws, rows, s);
-  r.vanilla = true;
+  r.vanilla = vanilla;
+  r.ff = !vanilla;
   const int B = cache->B;
   for (int p0 = 0; p0 < Tseq; p0 += chunk) {
     const int Mc = Tseq - p0 < chunk ? Tseq - p0 : chunk;
@@ -646,9 +712,9 @@ wm_status wm_vanilla_prefill(const wm_config *cfg, const wm_weights *w, const in
   st = check_common(cfg, cache, ws, ws_bytes, rows);
   if (st != WM_OK) return st;
   if (cfg->dtype == WM_BF16)
-    return vanilla_prefill_impl<bf16>(cfg, w, tokens, T, chunk, cache, logits, logits_mode, ws, rows,
+    return chunked_prefill_impl<bf16>(true, cfg, w, tokens, T, chunk, cache, logits, logits_mode, ws, rows,
                                       (hipStream_t)stream);
-  return vanilla_prefill_impl<float>(cfg, w, tokens, T, chunk, cache, logits, logits_mode, ws, rows,
+  return chunked_prefill_impl<float>(true, cfg, w, tokens, T, chunk, cache, logits, logits_mode, ws, rows,
                                      (hipStream_t)stream);
 }
 
@@ -672,6 +738,58 @@ wm_status wm_vanilla_decode_step(const wm_config *cfg, const wm_weights *w, cons
   }
   Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
   r.vanilla = true;
+  return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+}
+
+static wm_status ff_checks(const wm_config *cfg, const wm_weights *w, const wm_cache *cache) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cfg->k == cfg->L, WM_ERR_SHAPE, "the feedback-free model has one channel per layer: k = %d, L = %d",
+           cfg->k, cfg->L);
+  WM_CHECK(cache && cache->k && cache->v && cache->B >= 1, WM_ERR_ARG, "cache, its pointers or B invalid");
+  WM_CHECK(w && w->router && !w->static_mix, WM_ERR_ARG,
+           "the feedback-free model needs the router (and no static mixing weights)");
+  return WM_OK;
+}
+
+wm_status wm_feedback_free_prefill(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t T,
+                                   int32_t chunk, const wm_cache *cache, float *logits, int32_t logits_mode,
+                                   void *ws, size_t ws_bytes, wm_stream stream) {
+  wm_status st = ff_checks(cfg, w, cache);
+  if (st != WM_OK) return st;
+  WM_CHECK(chunk >= 1, WM_ERR_SHAPE, "chunk = %d must be >= 1", chunk);
+  WM_CHECK(T >= 1 && T <= cfg->T_max, WM_ERR_RANGE, "T = %d outside [1, T_max = %d]", T, cfg->T_max);
+  WM_CHECK(logits_mode >= 0 && logits_mode <= 2, WM_ERR_ARG, "logits_mode %d not in {0, 1, 2}", logits_mode);
+  WM_CHECK(logits_mode == 0 || logits, WM_ERR_ARG, "logits is NULL but logits_mode = %d", logits_mode);
+  WM_CHECK(tokens && weights_ok(w, true), WM_ERR_ARG, "tokens or a weight pointer is NULL");
+  const int rows = cache->B * (chunk < T ? chunk : T);
+  st = check_common(cfg, cache, ws, ws_bytes, rows);
+  if (st != WM_OK) return st;
+  if (cfg->dtype == WM_BF16)
+    return chunked_prefill_impl<bf16>(false, cfg, w, tokens, T, chunk, cache, logits, logits_mode, ws, rows,
+                                      (hipStream_t)stream);
+  return chunked_prefill_impl<float>(false, cfg, w, tokens, T, chunk, cache, logits, logits_mode, ws, rows,
+                                     (hipStream_t)stream);
+}
+
+wm_status wm_feedback_free_decode_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
+                                       const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
+                                       wm_stream stream) {
+  wm_status st = ff_checks(cfg, w, cache);
+  if (st != WM_OK) return st;
+  WM_CHECK(t >= 0 && t < cfg->T_max, WM_ERR_RANGE, "t = %d outside [0, T_max = %d)", t, cfg->T_max);
+  WM_CHECK(tokens && logits && weights_ok(w, true), WM_ERR_ARG, "tokens, logits or a weight pointer is NULL");
+  const int rows = cache->B;
+  st = check_common(cfg, cache, ws, ws_bytes, rows);
+  if (st != WM_OK) return st;
+  wm_tokset ts{cache->B, 1, t, 1};
+  if (cfg->dtype == WM_BF16) {
+    Run<bf16> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+    r.ff = true;
+    return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+  }
+  Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+  r.ff = true;
   return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
 }
 

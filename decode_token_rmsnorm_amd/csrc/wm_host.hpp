@@ -56,9 +56,9 @@ inline WsLayout ws_layout(const wm_config &c, int rows) {
   w.mb = take(2 * (size_t)c.k * R * c.D * es);
   w.rinvM = take(2 * (size_t)c.k * R * 4);
   const size_t nR = (size_t)(c.L + c.p - 1) / c.p;
-  const int sr = rows < kFewRows ? rows : kFewRows;
-  // router input: two gained copies of few rows, or one normalised copy
-  const size_t urows = 2 * (size_t)sr > R ? 2 * (size_t)sr : R;
+  // router input: two gained copies (few-row steps and the feedback-free
+  // variant), or one normalised copy (many rows)
+  const size_t urows = 2 * R;
   w.u = take(urows * nR * c.D * es);
   w.wf = take(rows > kFewRows ? 2 * (size_t)c.L * c.k * nR * c.D * es : 0);
   size_t cap = (size_t)part_rows_cap(rows);

@@ -95,11 +95,13 @@ __global__ __launch_bounds__(256) void fold_router(const T *W, const float *gain
 // Router output A: element (z, beta, row, l*k + j) at z*az + beta*ab +
 // row*ar + l*k + j, summed over Z partials; S [L, rows, D]; mb [2, k, rows,
 // D]; rinvM [2, k, rows].
+// src_gain / chan_gain: element (beta, l, c) at beta*sgb + l*D + c and
+// (beta, j, c) at beta*cgb + j*D + c.
 template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, const float *A, int Z, int64_t az,
-                                                int64_t ab, int64_t ar, const float *src_gain,
-                                                const float *chan_gain, T *mb, float *rinvM, int rows, int L, int k,
-                                                int D, float eps) {
+                                                int64_t ab, int64_t ar, const float *src_gain, int64_t sgb,
+                                                const float *chan_gain, int64_t cgb, T *mb, float *rinvM, int rows,
+                                                int L, int k, int D, float eps) {
   __shared__ float Aw[2][32][KMAX];  // L <= 32
   __shared__ float red[4][2 * KMAX];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, 
     for (int l = 0; l < L; ++l) {
       float x = to_f(S[((int64_t)l * rows + r) * D + c]);
       float xk = x * src_gain[(int64_t)l * D + c];
-      float xv = x * src_gain[((int64_t)L + l) * D + c];
+      float xv = x * src_gain[sgb + (int64_t)l * D + c];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (j < k) {
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, 
         if (j < k) {
           float m = acc[beta][j];
           ss[beta][j] += m * m;
-          mb[(((int64_t)beta * k + j) * rows + r) * D + c] = from_f<T>(m * chan_gain[((int64_t)beta * k + j) * D + c]);
+          mb[(((int64_t)beta * k + j) * rows + r) * D + c] = from_f<T>(m * chan_gain[beta * cgb + (int64_t)j * D + c]);
         }
       }
   }
@@ -155,14 +157,14 @@ __global__ __launch_bounds__(256) void pool_mix(const T *S, const float *rinvS, 
   }
 }
 
-// Router input of few-row steps, both branches:
+// Router input, both branches, blocks b0 <= b < b1 of R:
 // u[beta, r, b*D + c] = S[b*p, r, c] * rinvS[b*p, r] * gain[beta, b*p, c].
 template <typename T>
 __global__ __launch_bounds__(256) void router_input(const T *S, const float *rinvS, const float *gain, T *u, int rows,
-                                                    int L, int p, int R, int D) {
+                                                    int L, int p, int R, int D, int b0, int b1) {
   constexpr int E = Elt<T>::E16;
   const int r = blockIdx.x, beta = blockIdx.y;
-  for (int b = 0; b < R; ++b) {
+  for (int b = b0; b < b1; ++b) {
     const int l = b * p;
     const float s = rinvS[(int64_t)l * rows + r];
     const T *src = S + ((int64_t)l * rows + r) * D;

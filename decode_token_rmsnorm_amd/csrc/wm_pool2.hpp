@@ -31,11 +31,14 @@ constexpr int PM_SP = 96;   // staged row pitch (elements): 64 columns + 64 byte
 // Router output A: element (z, beta, row, l*k + j) at z*zstride +
 // beta*bstride + row*rstride + l*k + j, summed over the Z split partials;
 // S [L, rows, D]; mb [2, k, rows, D]; rinvM [2, k, rows].
+// (gains: src_gain (beta, l, c) at beta*sgb + l*D + c, chan_gain (beta, j, c)
+// at beta*cgb + j*D + c)
 template <int KB, int LMAX>
 __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *rinvS, const float *A, int Z,
                                                  int64_t zstride, int64_t bstride, int64_t rstride,
-                                                 const float *src_gain, const float *chan_gain, bf16 *mb,
-                                                 float *rinvM, int rows, int L, int k, int D, float eps) {
+                                                 const float *src_gain, int64_t sgb, const float *chan_gain,
+                                                 int64_t cgb, bf16 *mb, float *rinvM, int rows, int L, int k, int D,
+                                                 float eps) {
   constexpr int PM_RT = PM_RT4 / KB;                   // token rows per block
   constexpr int NPT = (PM_RT * LMAX * 8 + 255) / 256;  // 16-byte pieces per thread and chunk (L <= LMAX)
   __shared__ __attribute__((aligned(16))) bf16 Sl[PM_RT * 32 * PM_SP];
@@ -141,12 +144,12 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gs[beta][e] = src_gain[((int64_t)beta * L + min(8 * g + e, L - 1)) * D + col];
+      for (int e = 0; e < 8; ++e) gs[beta][e] = src_gain[beta * sgb + (int64_t)min(8 * g + e, L - 1) * D + col];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          gr[beta][kb][i] = chan_gain[((int64_t)beta * k + min(16 * kb + 4 * g + i, k - 1)) * D + col];
+          gr[beta][kb][i] = chan_gain[beta * cgb + (int64_t)min(16 * kb + 4 * g + i, k - 1) * D + col];
     }
 #pragma unroll
     for (int rr = 0; rr < PM_RT; ++rr) {

@@ -234,6 +234,33 @@ wm_status wm_vanilla_decode_step(const wm_config *cfg, const wm_weights *w, cons
                                  const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
                                  wm_stream stream);
 
+/* ---- the feedback-free variant -------------------------------------------
+ * paperlayer.ai §5 analysis ("Deep-to-shallow feedback") and onedev.kr's
+ * ablations: layer l sees only the states 0..l, so there is no deep-to-
+ * shallow feedback and no iteration. Reading: cfg->k must equal cfg->L
+ * (WM_ERR_SHAPE); consumer layer l reads channel l; channel l of a token
+ * mixes its normalised states 0..l with router weights computed from the
+ * sampled states r <= l (r = 0, p, 2p, ...) and router rows src*k + l, then
+ * channel norm, projection, key norm and RoPE as in wm_mix_kv; attention is
+ * strictly causal (s < i). Channel l is appended at layer l, before that
+ * layer's attention, so one layer-synchronous pass computes the model. Needs
+ * the router; static_mix must be NULL (WM_ERR_ARG). */
+
+/* One pass over positions [0, T) of tokens [B, T] in steps of `chunk`
+ * consecutive positions (every chunk >= 1 gives the same result);
+ * logits_mode as for wm_cyclic_prefill_pass. Workspace:
+ * wm_workspace_bytes(cfg, B * min(chunk, T)). */
+wm_status wm_feedback_free_prefill(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t T,
+                                   int32_t chunk, const wm_cache *cache, float *logits, int32_t logits_mode,
+                                   void *ws, size_t ws_bytes, wm_stream stream);
+
+/* One decode step of the feedback-free model at position t (channels of the
+ * token appended at slot t layer by layer; attention to s < t). logits
+ * [B, V] float. Requires 0 <= t < T_max. Workspace: wm_workspace_bytes(cfg, B). */
+wm_status wm_feedback_free_decode_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
+                                       const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
+                                       wm_stream stream);
+
 /* ---- per-kernel timing (measurement support) ---------------------------
  * Kernel kinds launched by the calls above. */
 typedef enum {

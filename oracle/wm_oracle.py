@@ -476,10 +476,11 @@ def _ff_channel(M, S_upto, l, pos):
     return out[0], out[1]
 
 
-def ff_forward(M, tokens, want_logits=True):
+def ff_forward(M, tokens, want_logits=True, states=None):
     """The feedback-free model over whole sequences tokens [B, T] in one
     layer-synchronous pass. Returns (cache [k = L, B, Hkv, T_max, d] x 2 with
-    positions < T filled, logits [B, T, V] or None)."""
+    positions < T filled, logits [B, T, V] or None). If ``states`` is a list,
+    the state stack [L, T, D] of every sequence is appended to it."""
     w, W = M.w, M.W
     assert w.k == w.L, "the feedback-free model has one channel per layer"
     tokens = np.asarray(tokens)
@@ -501,6 +502,8 @@ def ff_forward(M, tokens, want_logits=True):
             h = h + o.reshape(T, w.Hq * w.d) @ W["wo"][l].T
             f = rmsnorm(h, W["ffn_norm"][l], w.eps)
             h = h + (silu(f @ W["w_gate"][l].T) * (f @ W["w_up"][l].T)) @ W["w_down"][l].T
+        if states is not None:
+            states.append(S)
         if want_logits:
             logits[b] = lm_logits(M, h)
     return (Kc, Vc), logits

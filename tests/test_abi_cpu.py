@@ -25,7 +25,7 @@ def cfg_of(w, dtype=C.WM_BF16, **kw):
 
 def test_library_exports_every_declared_function():
     names = C.header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     assert set(names) <= exported, set(names) - exported
@@ -164,3 +164,29 @@ def test_vanilla_entry_points_validate_before_launch():
                                         wd, None) == -5
     assert L.wm_vanilla_decode_step(ctypes.byref(cw), ctypes.byref(W), FAKE, 0, ctypes.byref(cache), FAKE, FAKE, wd,
                                     None) == -2
+
+
+def test_feedback_free_entry_points_validate_before_launch():
+    L = C.lib()
+    w = WORKLOADS["small_prefill"]
+    cf = cfg_of(w, k=w.L)
+    cw = cfg_of(w)
+    W = _weights()
+    cache = C.WmCache(FAKE, FAKE, w.B)
+    ws = L.wm_workspace_bytes(ctypes.byref(cf), w.B * 128)
+    pre = lambda c, T=w.T, chunk=128, Wt=W, n=ws: L.wm_feedback_free_prefill(
+        ctypes.byref(c), ctypes.byref(Wt), FAKE, T, chunk, ctypes.byref(cache), None, 0, FAKE, n, None)
+    assert pre(cw) == -2 and b"one channel per layer" in L.wm_last_error()
+    assert pre(cf, chunk=0) == -2
+    assert pre(cf, T=w.T_max + 1) == -5
+    assert pre(cf, n=ws - 256) == -4
+    Ws = _weights()
+    Ws.static_mix = FAKE
+    assert pre(cf, Wt=Ws) == -1
+    Wr = _weights()
+    Wr.router = None
+    assert pre(cf, Wt=Wr) == -1
+    wd = L.wm_workspace_bytes(ctypes.byref(cf), w.B)
+    for t in (-1, w.T_max):
+        assert L.wm_feedback_free_decode_step(ctypes.byref(cf), ctypes.byref(W), FAKE, t, ctypes.byref(cache), FAKE,
+                                              FAKE, wd, None) == -5

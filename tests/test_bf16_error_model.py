@@ -49,3 +49,27 @@ def test_exact_bf16_rounding_error_bounds(name, L, rows):
         assert max(e_lg, e_k) < TOL_BF16_DEEP / 1.5
     else:
         assert max(e_lg, e_k) < TOL_BF16
+
+
+def test_feedback_free_bf16_rounding_floor():
+    """The feedback-free variant in bf16 (the GPU test shapes: L = k = 4,
+    D512, 2 x 64 and 3 x 256 positions): exact bf16 rounding of the stored and
+    product-feeding tensors alone moves the cached keys by up to 1.6e-1 from
+    the exact definition (a few tokens whose router outputs are small against
+    their terms amplify the rounding of the router input), so 2e-2 is out of
+    reach for any bf16 implementation; the GPU test holds the variant to
+    TOL_FF_BF16 = 2.5e-1 against the oracle, about 1.5 times this floor."""
+    import oracle as O
+    from tests.bf16_error_model import FF_ROUNDING_POINTS, ff_forward
+    for B, T in ((2, 64), (3, 256)):
+        w = WORKLOADS["small_prefill"].replace(L=4, k=4, B=B, T=T)
+        W = make_weights(w, seed=0, gains="perturbed")
+        tok = make_tokens(w, seed=1)
+        K0, V0, lg0 = ff_forward(w, W, tok)
+        (Ko, Vo), lgo = O.ff_forward(O.Model(w, W), tok)
+        assert max_abs_rel(K0, Ko[..., :T, :]) < 1e-12 and max_abs_rel(lg0, lgo) < 1e-12  # no rounding: the oracle
+        K1, V1, lg1 = ff_forward(w, W, tok, FF_ROUNDING_POINTS)
+        ek, ev, el = max_abs_rel(K1, K0), max_abs_rel(V1, V0), max_abs_rel(lg1, lg0)
+        print(f"feedback-free B{B} T{T}: exact bf16 rounding -> K {ek:.2e}, V {ev:.2e}, logits {el:.2e}")
+        assert max(ek, ev) > TOL_BF16                # 2e-2 is out of reach for bf16 here
+        assert max(ek, ev, el) < 2.5e-1 / 1.5

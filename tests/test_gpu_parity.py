@@ -84,9 +84,17 @@ def assert_cache(w, gk, gv, ref, mask, tol, poison=True):
     ("tiny_fp32", 2, 9, 3, 13),         # ragged fp32
     ("tiny_fp32", 2, 100, 0, 1),        # fp32 past the few-row path (200 rows, split router)
     ("mix_bf16", 3, 300, 2, 5),         # bf16, 900 rows: 128x128 router tiles with k splits
+    ("mix_bf16@L4k1", 2, 16, 0, 1),     # one channel over few source layers (MFMA mix)
+    ("mix_bf16@L2k1", 2, 16, 0, 1),
+    ("mix_bf16@L3k1", 3, 50, 1, 2),
 ])
 def test_mix_kv_matches_oracle(name, B, M, s0, step):
-    w = WORKLOADS[name].replace(B=B)
+    if "@" in name:  # shape variant "<workload>@L<l>k<k>"
+        base, var = name.split("@")
+        Lv, kv = var[1:].split("k")
+        w = WORKLOADS[base].replace(B=B, L=int(Lv), k=int(kv))
+    else:
+        w = WORKLOADS[name].replace(B=B)
     print(f"mix_kv {name} B={B} M={M} s0={s0} step={step}", flush=True)
     W = make_weights(w, seed=0, gains="perturbed")
     S = make_state_stack(w, B * M, seed=2)

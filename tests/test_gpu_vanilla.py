@@ -132,3 +132,77 @@ def test_vanilla_decode_full_size():
         print(f"  slot t: {e:.3e}", flush=True)
         assert e <= TOL_BF16_DEEP
         assert np.isnan(got[:, :, :, t + 1:]).all()
+
+
+# ---------------------------------------------------------------- feedback-free variant
+
+@pytest.mark.parametrize("chunk,p", [(128, 2), (16, 2), (7, 1), (32, 3)])
+def test_feedback_free_prefill_tiny_fp32(chunk, p):
+    w = WORKLOADS["tiny_fp32"]
+    w = w.replace(k=w.L, p=p)
+    print(f"feedback-free prefill tiny fp32, chunk {chunk}, p {p}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, w.B, fill=float("nan"))
+    lg = wm.feedback_free_prefill(model, torch.from_numpy(tokens).to(DEV), chunk, cache, logits_mode=2)
+    torch.cuda.synchronize()
+    ref, rl = O.ff_forward(O.Model(w, W), tokens)
+    _cmp_cache(w, cache.k, cache.v, ref, w.T, TOL["f32"])
+    el = max_abs_rel(np_of(lg), rl)
+    print(f"  logits {el:.3e}", flush=True)
+    assert el <= TOL["f32"]
+
+
+def test_feedback_free_decode_after_prefill_tiny_fp32():
+    w = WORKLOADS["tiny_fp32"]
+    w = w.replace(k=w.L)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    t = w.T - 1
+    print(f"feedback-free prefill of {t} positions, then a decode step at t = {t}", flush=True)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, w.B, fill=float("nan"))
+    tok = torch.from_numpy(tokens).to(DEV)
+    wm.feedback_free_prefill(model, tok[:, :t].contiguous(), 32, cache)
+    lg = wm.feedback_free_decode_step(model, tok[:, t].contiguous(), t, cache)
+    torch.cuda.synchronize()
+    ref, rl = O.ff_forward(O.Model(w, W), tokens)
+    _cmp_cache(w, cache.k, cache.v, ref, w.T, TOL["f32"])
+    el = max_abs_rel(np_of(lg), rl[:, t])
+    print(f"  decode logits {el:.3e}", flush=True)
+    assert el <= TOL["f32"]
+
+
+TOL_FF_BF16 = 2.5e-1  # about 1.5x the exact-bf16-rounding floor of the variant (test_bf16_error_model.py)
+
+
+@pytest.mark.parametrize("B,T,chunk", [(2, 64, 16), (3, 256, 128)])
+def test_feedback_free_prefill_reduced_depth_bf16(B, T, chunk):
+    """bf16, 4 layers (k = L = 4): few-row steps (32 rows) and 384-row steps
+    (the 128 x 128 GEMM path for the router and projections). The same kernels
+    match the oracle on every row at 1e-4 in fp32. In bf16, exact rounding of
+    the stored tensors alone moves this variant's keys by up to 1.6e-1 (its
+    error model, tests/bf16_error_model.py): against the oracle the bound is
+    TOL_FF_BF16, and against that error model (the same rounding points in
+    float64; the two still differ in accumulation order, which the same few
+    tokens amplify) within TOL_BF16_DEEP."""
+    from tests.bf16_error_model import FF_ROUNDING_POINTS, ff_forward as ff_rounded
+    w = WORKLOADS["small_prefill"].replace(L=4, k=4, B=B, T=T)
+    print(f"feedback-free prefill bf16, L4, B{B}, T{T}, chunk {chunk}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, w.B, fill=float("nan"))
+    lg = wm.feedback_free_prefill(model, torch.from_numpy(tokens).to(DEV), chunk, cache, logits_mode=2)
+    torch.cuda.synchronize()
+    ref, rl = O.ff_forward(O.Model(w, W), tokens)
+    _cmp_cache(w, cache.k, cache.v, ref, w.T, TOL_FF_BF16)
+    el = max_abs_rel(np_of(lg), rl)
+    print(f"  logits vs oracle {el:.3e}", flush=True)
+    assert el <= TOL_FF_BF16
+    Km, Vm, lm = ff_rounded(w, W, tokens, FF_ROUNDING_POINTS)
+    gk, gv = np_of(cache.k)[..., :w.T, :], np_of(cache.v)[..., :w.T, :]
+    ek, ev, el = max_abs_rel(gk, Km), max_abs_rel(gv, Vm), max_abs_rel(np_of(lg), lm)
+    print(f"  vs the bf16 rounding model: K {ek:.3e} V {ev:.3e} logits {el:.3e}", flush=True)
+    assert max(ek, ev, el) <= TOL_BF16_DEEP
