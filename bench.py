@@ -284,6 +284,67 @@ def bench_vanilla(steps, decode_steps):
     return out
 
 
+def bench_variants(steps):
+    """The analysis variants on the same kernels: the feedback-free model
+    (k = L, channel l from states 0..l, one layer-synchronous pass) on the
+    1.3B-scale prefill workload, and static mixing (constant weights, no
+    router) in wm_mix_kv on the mix workload, beside the routed call."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from wm_inputs import (WORKLOADS, make_state_stack_device, make_static_mix, make_tokens, make_weights)
+
+    out = {}
+    w = WORKLOADS["prefill_1p3b"]
+    w = w.replace(k=w.L)
+    chunk = -(-w.T // w.g)
+    model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    cache = wm.new_cache(model, w.B)
+    ws = model.workspace(w.B * chunk)
+    logits = torch.empty(w.B, w.V, dtype=torch.float32, device="cuda")
+    wm.feedback_free_prefill(model, tok, chunk, cache, 1, logits, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wm.feedback_free_prefill(model, tok, chunk, cache, 1, logits, ws)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    assert torch.isfinite(logits).all(), "non-finite logits"
+    out["feedback_free_prefill"] = {
+        "workload": f"prefill_1p3b, feedback-free (k = L = {w.L}), B{w.B} T{w.T}, one layer-synchronous pass in "
+                    f"steps of {chunk} positions, bf16",
+        "value": w.B * w.T / wall, "unit": "tokens/s", "ms_per_pass": 1e3 * wall, "passes": steps}
+    del cache, ws, model, tok
+    torch.cuda.empty_cache()
+
+    w = WORKLOADS["mix_bf16"]
+    rows = w.B * w.T
+    W = make_weights(w, seed=0)
+    states = make_state_stack_device(w, rows, seed=2)
+    res = {}
+    for name, up in (("routed", {n: W[n] for n in ("src_norm", "router", "chan_norm", "wk", "wv", "k_norm")}),
+                     ("static", {**{n: W[n] for n in ("src_norm", "chan_norm", "wk", "wv", "k_norm")},
+                                 "static_mix": make_static_mix(w)})):
+        model = wm.Model(w, up, "bf16")
+        cache = wm.new_cache(model, w.B)
+        ws = model.workspace(rows)
+        for _ in range(3):
+            wm.mix_kv(model, states, w.B, w.T, 0, 1, cache, ws)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(20):
+            wm.mix_kv(model, states, w.B, w.T, 0, 1, cache, ws)
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = 1e3 * a.elapsed_time(b) / 20
+        del model, cache, ws
+    out["static_mixing_mix_kv"] = {"workload": "wm_mix_kv on the state stack [16, 8*2048, 512], k8, bf16",
+                                   "us_per_call_routed": res["routed"], "us_per_call_static": res["static"]}
+    del states
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_sweep(tau=1e-4):
     """The schedule sweep: (a) per-pass time of the cyclic prefill against g on
     the small bf16 model (L16 D512 k8, B8 T2048), g in {1, 4, 8, 16, 32, T};
@@ -370,7 +431,8 @@ def main():
     ap.add_argument("--skip-mix", action="store_true")
     ap.add_argument("--skip-vanilla", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
-    ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep"], default=None,
+    ap.add_argument("--skip-variants", action="store_true")
+    ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep", "variants"], default=None,
                     help="profiling aid: run only this part and print its object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
@@ -392,7 +454,8 @@ def main():
     torch.cuda.set_device(0)
     if a.only:
         part = (bench_decode(a.decode_steps, 5) if a.only == "decode" else bench_mix(20, 3) if a.only == "mix"
-                else bench_vanilla(a.steps, a.decode_steps) if a.only == "vanilla" else bench_sweep())
+                else bench_vanilla(a.steps, a.decode_steps) if a.only == "vanilla"
+                else bench_variants(a.steps) if a.only == "variants" else bench_sweep())
         print(json.dumps({a.only: part}), flush=True)
         return
     w, pre = bench_prefill(a.steps, a.warmup)
@@ -400,6 +463,7 @@ def main():
     mix = None if a.skip_mix else bench_mix(20, 3)
     van = None if a.skip_vanilla else bench_vanilla(a.steps, a.decode_steps)
     sweep = None if a.skip_sweep else bench_sweep()
+    variants = None if a.skip_variants else bench_variants(a.steps)
     if van is not None:
         # the pages' comparison: WhiteMatter prefill as a share of vanilla's (one
         # vanilla pass against one, and against the workload's 3 passes:
@@ -428,6 +492,7 @@ def main():
         "mix_kv": mix,
         "vanilla": van,
         "schedule_sweep": sweep,
+        "variants": variants,
     }
     print(json.dumps(line), flush=True)
 
