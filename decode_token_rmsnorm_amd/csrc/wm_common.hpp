@@ -97,6 +97,8 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// x * sigmoid(x) with the hardware reciprocal (1 ulp) instead of a full
+// IEEE division.
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 }  // namespace wm

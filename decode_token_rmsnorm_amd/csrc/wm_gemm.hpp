@@ -34,10 +34,19 @@ struct RowPos {
   __device__ __forceinline__ int seq(int r) const { return r / M; }
 };
 
-// 1 / sqrt(mean(x^2) + eps) of a row from `nparts` partial sums of squares.
+// 1 / sqrt(mean(x^2) + eps) of a row from `nparts` partial sums of squares,
+// added in part order; the loads go out 8 at a time (one memory round trip for
+// up to 8 parts instead of one per part).
 __device__ __forceinline__ float rinv_from_parts(const float *ss, int row, int nparts, float invD, float eps) {
+  const float *p = ss + (int64_t)row * nparts;
   float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += ss[(int64_t)row * nparts + p];
+  for (int p0 = 0; p0 < nparts; p0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[min(p0 + i, nparts - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += p0 + i < nparts ? v[i] : 0.f;
+  }
   return rsqrtf(s * invD + eps);
 }
 
@@ -311,19 +320,34 @@ __device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, in
   fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
   const int f0 = n0 / 2 + OPL * lane;
   if (f0 >= e.F) return;  // no __syncthreads below
-  for (int rl = wave; rl < nrows; rl += nwaves()) {
-    int r = m0 + rl;
-    if (r >= M) break;
-    const float rs = rowbuf[rl];
-    const float *row = Cs + rl * pitch + OPL * lane;
-    float y[OPL];
+  // ER rows per wave and step: every LDS read of the step before any use
+  for (int rb = wave * ER; rb < nrows; rb += nwaves() * ER) {
+    float gt[ER][OPL], up[ER][OPL], rs[ER];
 #pragma unroll
-    for (int i = 0; i < OPL; ++i) y[i] = silu(row[i] * rs) * (row[i + 32 * CPL] * rs);
-    T *dst = e.act + (int64_t)r * e.F + f0;
-    if constexpr (OPL == 2) {
-      stT<T, 2>(dst, y);
-    } else {
-      dst[0] = from_f<T>(y[0]);
+    for (int u = 0; u < ER; ++u) {
+      const int rl = rb + u < nrows ? rb + u : nrows - 1;
+      rs[u] = rowbuf[rl];
+      const float *row = Cs + rl * pitch + OPL * lane;
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) {
+        gt[u][i] = row[i];
+        up[u][i] = row[i + 32 * CPL];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < ER; ++u) {
+      const int r = m0 + rb + u;
+      float y[OPL];
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) y[i] = silu(gt[u][i] * rs[u]) * (up[u][i] * rs[u]);
+      if (rb + u < nrows && r < M) {
+        T *dst = e.act + (int64_t)r * e.F + f0;
+        if constexpr (OPL == 2) {
+          stT<T, 2>(dst, y);
+        } else {
+          dst[0] = from_f<T>(y[0]);
+        }
+      }
     }
   }
 }
