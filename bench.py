@@ -27,8 +27,8 @@ CSRC = "decode_token_rmsnorm_amd/csrc/"
 TRAFFIC = {
     "gateup": ("prefill_1p3b_gateup_traffic.md", ["wm_common.hpp", "wm_gemm.hpp", "wm_gemm2.hpp"]),
     "decode_attn": ("decode_d512_attn_traffic.md", ["wm_common.hpp", "wm_attn.hpp", "wm_attn2.hpp"]),
-    "mix_kv": ("mix_bf16_mix_kv_traffic.md", ["wm_common.hpp", "wm_gemm.hpp", "wm_gemm2.hpp", "wm_pool.hpp",
-                                              "wm_pool2.hpp", "wm_api.hip"]),
+    "mix_kv": ("mix_bf16_mix_kv_traffic.md", ["wm_common.hpp", "wm_gemm.hpp", "wm_gemm2.hpp", "wm_few.hpp",
+                                              "wm_pool.hpp", "wm_pool2.hpp", "wm_api.hip"]),
 }
 
 
