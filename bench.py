@@ -425,6 +425,32 @@ def cpu_baseline(budget_s=10.0):
                       f"float64 numpy, {dt:.1f}s"}
 
 
+def device_peaks():
+    """Peaks measured on this GPU in this run: a streaming read and a copy of
+    1 GiB (HIP kernels of the library, hipEvent-timed) and a register-resident
+    bf16 MFMA loop on every compute unit."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    out = {"hbm_read_gbs": wm.peak_stream(src, None, iters=10),
+           "hbm_copy_gbs": wm.peak_stream(src, dst, iters=10),
+           "bf16_mfma_tflops": wm.peak_mfma_bf16(iters=10),
+           "what": "1 GiB streaming read and 1 GiB copy (GB/s, copy counts read + write); 32x32x16 bf16 MFMA loop "
+                   "on register operands, 2 blocks of 4 waves per CU (TFLOP/s)"}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def with_measured(roof, peak):
+    """The roofline object plus its fraction of the peak measured on this GPU."""
+    if roof is not None and peak:
+        roof["peak_measured"] = peak
+        roof["frac_measured"] = roof["achieved"] / peak
+    return roof
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,7 +463,7 @@ def main():
     ap.add_argument("--skip-vanilla", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-variants", action="store_true")
-    ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep", "variants"], default=None,
+    ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep", "variants", "peaks"], default=None,
                     help="profiling aid: run only this part and print its object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
@@ -459,6 +485,7 @@ def main():
     torch.cuda.set_device(0)
     if a.only:
         part = (bench_decode(a.decode_steps, 5) if a.only == "decode" else bench_mix(20, 3) if a.only == "mix"
+                else device_peaks() if a.only == "peaks"
                 else bench_vanilla(a.steps, a.decode_steps) if a.only == "vanilla"
                 else bench_variants(a.steps) if a.only == "variants" else bench_sweep())
         print(json.dumps({a.only: part}), flush=True)
@@ -478,6 +505,12 @@ def main():
         van["wm_prefill_3_passes_over_vanilla"] = wm_pass / 3 / van["prefill"]["value"]
         if dec is not None:
             van["wm_decode_over_vanilla"] = dec["value"] / van["decode"]["value"]
+    peaks = device_peaks()
+    with_measured(pre["roofline"], peaks["bf16_mfma_tflops"])
+    if dec is not None:
+        with_measured(dec["roofline"], peaks["hbm_read_gbs"])
+    if mix is not None:
+        with_measured(mix["roofline"], peaks["hbm_copy_gbs"])
     cpu = None if a.no_cpu_baseline else cpu_baseline()
     value = w.B * w.T / (pre["wall_s"] / a.steps)
     line = {
@@ -492,6 +525,8 @@ def main():
         "per_pass_ms": pre["per_pass_ms"],
         "pass_tflops": pre["pass_tflops"],
         "pass_mfma_frac": pre["pass_tflops"] / BF16_PEAK_TFLOPS,
+        "pass_mfma_frac_measured": pre["pass_tflops"] / peaks["bf16_mfma_tflops"],
+        "device_peaks": peaks,
         "kernels_avg_us": pre["kernels"],
         "decode": dec,
         "mix_kv": mix,

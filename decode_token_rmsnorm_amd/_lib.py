@@ -64,6 +64,8 @@ _SIGS = {
     "wm_profile_begin": (c_i32, [ctypes.c_uint32]),
     "wm_profile_read": (c_i32, [P(ctypes.c_int64), P(ctypes.c_double)]),
     "wm_profile_end": (c_i32, []),
+    "wm_peak_stream": (c_i32, [c_vp, c_vp, ctypes.c_int64, c_i32, c_vp, P(ctypes.c_double)]),
+    "wm_peak_mfma_bf16": (c_i32, [c_i32, c_vp, P(ctypes.c_double)]),
 }
 
 KINDS = ["qproj", "attn", "oproj", "gateup", "down", "router", "mix", "kvproj", "lmhead", "embed"]

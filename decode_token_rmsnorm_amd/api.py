@@ -225,3 +225,23 @@ def vanilla_decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache
                                            ctypes.byref(cc), logits.data_ptr(), ws.data_ptr(), ws.numel(),
                                            _stream(stream)))
     return logits
+
+
+def peak_stream(src: torch.Tensor, dst: torch.Tensor = None, iters: int = 10, stream=None) -> float:
+    """GB/s the device reaches streaming src's bytes: a read (dst None) or a
+    copy into dst (counted as read + write). Measurement support only."""
+    nbytes = src.numel() * src.element_size()
+    if dst is not None and dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    out = ctypes.c_double()
+    C.check("wm_peak_stream", C.lib().wm_peak_stream(src.data_ptr(), _ptr(dst), nbytes, iters, _stream(stream),
+                                                     ctypes.byref(out)))
+    return out.value
+
+
+def peak_mfma_bf16(iters: int = 10, stream=None) -> float:
+    """TFLOP/s of a register-resident 32x32x16 bf16 MFMA loop on every compute
+    unit. Measurement support only."""
+    out = ctypes.c_double()
+    C.check("wm_peak_mfma_bf16", C.lib().wm_peak_mfma_bf16(iters, _stream(stream), ctypes.byref(out)))
+    return out.value

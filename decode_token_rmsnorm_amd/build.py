@@ -6,7 +6,8 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = [os.path.join(HERE, "csrc", "wm_api.hip"), os.path.join(HERE, "csrc", "wm_host.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", "wm_api.hip"), os.path.join(HERE, "csrc", "wm_peaks.hip"),
+           os.path.join(HERE, "csrc", "wm_host.cpp")]
 OUT = os.path.join(HERE, "libwm.so")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # packed fp32 VALU ops are kept off: plain scalar float code only

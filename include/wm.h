@@ -288,6 +288,30 @@ wm_status wm_profile_begin(uint32_t kind_mask);
 wm_status wm_profile_read(int64_t *counts, double *total_ms);
 wm_status wm_profile_end(void);
 
+/* ---- device peaks (measurement support) ---------------------------------
+ * Not part of the method: what the current device reaches on plain
+ * streaming and on dense bf16 MFMA work, so that a kernel's roofline fraction
+ * can be stated against a peak measured on the same GPU beside the datasheet
+ * figures (8 TB/s HBM, 2.5 PFLOP/s dense bf16 on an MI355X).  Both calls run
+ * one untimed launch, then time `iters` (>= 1, WM_ERR_SHAPE otherwise)
+ * launches with hipEvents on `stream` and wait for them (the call blocks).
+ *
+ * wm_peak_stream: reads `bytes` from device buffer `src` and, when `dst` is
+ * not NULL, writes them to device buffer `dst` (16-byte chunks, grid-stride,
+ * coalesced).  bytes > 0 and a multiple of 16, both buffers 16-byte aligned
+ * (WM_ERR_SHAPE otherwise); src and dst must not overlap (WM_ERR_ARG).
+ * *gb_per_s (host) = bytes moved per second / 1e9, where a copy moves
+ * 2 * bytes (read + write) and a read moves bytes.  The caller owns both
+ * buffers; dst's contents become a copy of src.
+ *
+ * wm_peak_mfma_bf16: two blocks of four waves per compute unit, each wave
+ * running 32x32x16 bf16 MFMAs on register-resident operands that keep
+ * changing; no memory traffic.  *tflop_per_s (host) = 2*32*32*16 flop per
+ * MFMA times MFMAs per second / 1e12. */
+wm_status wm_peak_stream(const void *src, void *dst, int64_t bytes, int32_t iters, wm_stream stream,
+                         double *gb_per_s);
+wm_status wm_peak_mfma_bf16(int32_t iters, wm_stream stream, double *tflop_per_s);
+
 #ifdef __cplusplus
 }
 #endif

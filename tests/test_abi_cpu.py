@@ -25,7 +25,7 @@ def cfg_of(w, dtype=C.WM_BF16, **kw):
 
 def test_library_exports_every_declared_function():
     names = C.header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     assert set(names) <= exported, set(names) - exported
@@ -190,3 +190,19 @@ def test_feedback_free_entry_points_validate_before_launch():
     for t in (-1, w.T_max):
         assert L.wm_feedback_free_decode_step(ctypes.byref(cf), ctypes.byref(W), FAKE, t, ctypes.byref(cache), FAKE,
                                               FAKE, wd, None) == -5
+
+
+def test_peak_probes_validate_before_launch():
+    L = C.lib()
+    out = ctypes.c_double()
+    st = lambda src, dst, n, it=1, o=ctypes.byref(out): L.wm_peak_stream(src, dst, n, it, None, o)
+    assert st(None, None, 1024) == -1
+    assert st(FAKE, None, 1024, o=None) == -1
+    assert st(FAKE, None, 0) == -2
+    assert st(FAKE, None, 1000) == -2  # not a multiple of 16
+    assert st(FAKE + 8, None, 1024) == -2  # misaligned
+    assert st(FAKE, FAKE + 4, 1024) == -2  # misaligned dst
+    assert st(FAKE, None, 1024, it=0) == -2
+    assert st(FAKE, FAKE + 512, 1024) == -1 and b"overlap" in L.wm_last_error()
+    assert L.wm_peak_mfma_bf16(1, None, None) == -1
+    assert L.wm_peak_mfma_bf16(0, None, ctypes.byref(out)) == -2
