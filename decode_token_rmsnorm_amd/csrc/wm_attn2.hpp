@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
   bool rvalid[QB];
   int rpos[QB], rrow[QB], rhead[QB];
   u32x4 qf[QB][NCH];
-  int minpos = 0x7fffffff;
+  int minpos = 0x7fffffff, maxpos = 0;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int rho_raw = rb0 + wave * 32 * QB + qb * 32 + ql;
@@ -83,11 +83,17 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
     const bf16 *src = (const bf16 *)a.q + ((int64_t)rrow[qb] * a.Hq + rhead[qb]) * DH + 8 * h;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) qf[qb][c] = *(const u32x4 *)(src + 16 * c);
-    if (rvalid[qb]) minpos = min(minpos, rpos[qb]);
+    if (rvalid[qb]) {
+      minpos = min(minpos, rpos[qb]);
+      maxpos = max(maxpos, rpos[qb]);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries resident before the K/V prefetch starts
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) minpos = min(minpos, __shfl_xor(minpos, off));
+  for (int off = 32; off > 0; off >>= 1) {
+    minpos = min(minpos, __shfl_xor(minpos, off));
+    maxpos = max(maxpos, __shfl_xor(maxpos, off));
+  }
 
   f32x16 o[QB][ND];
   float mrun[QB], lrun[QB];
@@ -147,29 +153,29 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
     // slices (each V fragment feeds QB MFMAs).
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // A half whose keys all lie at or past every query of this wave adds
+      // nothing (its probabilities are 0 and the running max stays), so the
+      // wave skips it; the block still stages every tile up to its own last
+      // query, which the other waves may need.
+      if (key0 + 32 * kb >= maxpos) continue;
       // All K fragments of the half are read before the first MFMA (the
       // scheduler would otherwise place each read just before its MFMA and
-      // wait out the LDS latency every time); even and odd head-dim steps
-      // accumulate separately (two independent MFMA chains).
+      // wait out the LDS latency every time); the head-dim steps accumulate
+      // in one chain (a second chain would cost 16 adds per half, and the
+      // VALU is the busier unit here).
       u32x4 kf[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) kf[c] = *(const u32x4 *)(&Ks[st][(32 * kb + ql) * KP + 16 * c + 8 * h]);
       __builtin_amdgcn_sched_barrier(0);
-      f32x16 s[QB], s2[QB];
+      f32x16 s[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb] = s2[qb] = f32x16{};
+      for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NCH; c += 2) {
+      for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        for (int qb = 0; qb < QB; ++qb)
           s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c]),
                                                           __builtin_bit_cast(bf16x8, qf[qb][c]), s[qb], 0, 0, 0);
-          s2[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c + 1]),
-                                                           __builtin_bit_cast(bf16x8, qf[qb][c + 1]), s2[qb], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb] += s2[qb];
       // element i of s[qb] is key key0 + 32*kb + 8*(i/4) + 4h + i%4
       const int kb0 = key0 + 32 * kb;
       const bool edge = kb0 + 32 > minpos;
