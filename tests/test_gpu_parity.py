@@ -192,6 +192,37 @@ def test_mix_kv_full_size_sampled_rows_and_deterministic():
     assert not np.isnan(K[:, :, :, :M]).any()
 
 
+def test_mix_kv_ragged_large_rows():
+    """2331 rows (3 sequences x 777 positions 5, 7, ..., 1557): the router and
+    K/V projection run on the 256 x 256 tile GEMM with a partial last tile, and
+    the mix has a partial last row block.  Sampled rows, the last partial tile
+    among them, against the oracle; slots between and after the written
+    positions keep their NaN poison."""
+    w = WORKLOADS["mix_bf16"]
+    B, M, s0, step = 3, 777, 5, 2
+    print(f"mix_kv ragged B{B} M{M}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    S = make_state_stack(w, B * M, seed=4)
+    model = gpu_model(w, {n: W[n] for n in ("src_norm", "router", "chan_norm", "wk", "wv", "k_norm")})
+    cache = wm.new_cache(model, B, fill=float("nan"))
+    wm.mix_kv(model, torch.from_numpy(S).to(DEV, torch.bfloat16), B, M, s0, step, cache)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([rng.choice(B * M - 40, 48, replace=False), np.arange(B * M - 40, B * M)]))
+    bidx, pos = rows // M, s0 + (rows % M) * step
+    Kn, Vn = O.pool(O.Model(w, W), S[:, rows], pos)
+    K, V = np_of(cache.k), np_of(cache.v)
+    gotK = np.stack([K[:, b, :, p] for b, p in zip(bidx, pos)], 1)
+    gotV = np.stack([V[:, b, :, p] for b, p in zip(bidx, pos)], 1)
+    eK, eV = max_abs_rel(gotK, Kn), max_abs_rel(gotV, Vn)
+    print(f"ragged mix sampled: K {eK:.3e} V {eV:.3e}", flush=True)
+    assert eK <= TOL["bf16"] and eV <= TOL["bf16"]
+    written = s0 + np.arange(M) * step
+    assert not np.isnan(K[:, :, :, written]).any() and not np.isnan(V[:, :, :, written]).any()
+    unwritten = np.setdiff1d(np.arange(w.T_max), written)
+    assert np.isnan(K[:, :, :, unwritten]).all() and np.isnan(V[:, :, :, unwritten]).all()
+
+
 # ---------------------------------------------------------------- wm_channel_attn
 
 @pytest.mark.parametrize("name,B,M,s0,step,layer", [
@@ -387,19 +418,23 @@ def _first_group_ref(w, W, tokens, b):
     return pos, ref
 
 
-@pytest.mark.parametrize("name,b", [("small_prefill", 5), ("prefill_1p3b", 37)])
-def test_prefill_pass_full_size_bf16_first_group(name, b):
+@pytest.mark.parametrize("name,b,B", [("small_prefill", 5, None), ("prefill_1p3b", 37, None),
+                                     ("small_prefill", 16, 17)])
+def test_prefill_pass_full_size_bf16_first_group(name, b, B):
     """Full-size bf16 pass (B, T = 2048, g = 16) in the launch configuration
     the benchmark times; the oracle recomputes the first group of one sampled
     sequence (128 positions, 28 or 16 layers) and the cache entries written
     there must agree within TOL_BF16_DEEP; entries of every position must be
-    finite and positions >= T must keep their poison."""
+    finite and positions >= T must keep their poison.  With B = 17 every group
+    step has 2176 rows, so the large-tile GEMMs end in a partial 256-row tile,
+    which holds the sampled last sequence."""
     w = WORKLOADS[name]
-    print(f"full-size pass {name}, sampled sequence {b}", flush=True)
+    B = w.B if B is None else B
+    print(f"full-size pass {name}, B {B}, sampled sequence {b}", flush=True)
     W = make_weights(w, seed=0, gains="perturbed")
-    tokens = make_tokens(w, seed=1)
+    tokens = make_tokens(w, seed=1, B=B)
     model = gpu_model(w, W)
-    cache = wm.new_cache(model, w.B)
+    cache = wm.new_cache(model, B)
     tok = torch.from_numpy(tokens).to(DEV)
     logits = wm.cyclic_prefill_pass(model, tok, w.g, cache, logits_mode=1)
     torch.cuda.synchronize()
