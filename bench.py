@@ -479,7 +479,7 @@ def main():
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the method's batch elements are independent "
-              "and would shard as pure data parallelism, which this build does not run.", file=sys.stderr)
+              "and would shard as pure data parallelism over sequences; this benchmark runs one GPU.", file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
