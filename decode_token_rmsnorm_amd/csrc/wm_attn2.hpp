@@ -94,6 +94,8 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
     minpos = min(minpos, __shfl_xor(minpos, off));
     maxpos = max(maxpos, __shfl_xor(maxpos, off));
   }
+  minpos = __builtin_amdgcn_readfirstlane(minpos);  // (wave-uniform: branches on them stay scalar)
+  maxpos = __builtin_amdgcn_readfirstlane(maxpos);
 
   f32x16 o[QB][ND];
   float mrun[QB], lrun[QB];
@@ -150,72 +152,95 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
     const bf16 *vst = &Vs[st][vbase];
     // The tile in two 32-key halves kb: S^T = K Q^T (each K fragment feeds QB
     // MFMAs), online softmax, then O^T += V^T P^T over the half's two 16-key
-    // slices (each V fragment feeds QB MFMAs).
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // A half whose keys all lie at or past every query of this wave adds
-      // nothing (its probabilities are 0 and the running max stays), so the
-      // wave skips it; the block still stages every tile up to its own last
-      // query, which the other waves may need.
-      if (key0 + 32 * kb >= maxpos) continue;
-      // All K fragments of the half are read before the first MFMA (the
-      // scheduler would otherwise place each read just before its MFMA and
-      // wait out the LDS latency every time); the head-dim steps accumulate
-      // in one chain (a second chain would cost 16 adds per half, and the
-      // VALU is the busier unit here).
+    // slices (each V fragment feeds QB MFMAs).  Half 1's scores are computed
+    // and masked before half 0's PV products, so that half 1's softmax, which
+    // has no branch, is issued among those MFMAs (it does not feed them; its
+    // rescale of O waits for them).  O sees the same operations in the same
+    // order as a half-by-half walk.
+    auto qk = [&](int kb, f32x16 (&sc_)[QB]) {
+      // K fragments first (each read would otherwise sit just before its
+      // MFMA and wait out the LDS latency); the head-dim steps accumulate in
+      // one chain
       u32x4 kf[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) kf[c] = *(const u32x4 *)(&Ks[st][(32 * kb + ql) * KP + 16 * c + 8 * h]);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 s[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+      for (int qb = 0; qb < QB; ++qb) sc_[qb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c]),
-                                                          __builtin_bit_cast(bf16x8, qf[qb][c]), s[qb], 0, 0, 0);
-      // element i of s[qb] is key key0 + 32*kb + 8*(i/4) + 4h + i%4
+          sc_[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c]),
+                                                            __builtin_bit_cast(bf16x8, qf[qb][c]), sc_[qb], 0, 0, 0);
+    };
+    // element i of sc_[qb] is key key0 + 32*kb + 8*(i/4) + 4h + i%4; keys at
+    // or past the query's position get -inf (only halves that reach past the
+    // wave's first query need it)
+    auto mask = [&](int kb, f32x16 (&sc_)[QB]) {
       const int kb0 = key0 + 32 * kb;
-      const bool edge = kb0 + 32 > minpos;
+      if (kb0 + 32 > minpos) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (edge) {
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (kb0 + 8 * (i >> 2) + 4 * h + (i & 3) >= rpos[qb]) s[qb][i] = -INFINITY;
-        }
+            if (kb0 + 8 * (i >> 2) + 4 * h + (i & 3) >= rpos[qb]) sc_[qb][i] = -INFINITY;
+      }
+    };
+    // scores -> probabilities in place, running max and sum; alpha = the
+    // factor O must be rescaled by before this half's PV products.  Lazy
+    // rescaling: the reference max moves only when the half's max exceeds it
+    // by more than 2^8, so probabilities stay <= 256 and O is rescaled
+    // rarely; numerator and denominator share the reference, so the result
+    // is unchanged.  Selects instead of branches: alpha = 2^(m_old - m_new)
+    // when the reference moves (0 on the first finite max), else 1; a row
+    // with no unmasked key so far keeps m = -inf and gets p = 0.
+    auto softmax = [&](f32x16 (&sc_)[QB], float (&alpha)[QB]) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
         float tmax = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[qb][i]);
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc_[qb][i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        // Lazy rescaling: the reference max moves only when the tile's max
-        // exceeds it by more than 2^8, so probabilities stay <= 256 and the
-        // output is rescaled rarely; numerator and denominator share the
-        // reference, so the result is unchanged.
         const float tm = tmax * sc;
         const bool upd = tm > mrun[qb] + 8.f;
         const float mnew = upd ? tm : mrun[qb];
-        const float alpha =
-            upd && mrun[qb] != -INFINITY ? __builtin_amdgcn_exp2f(mrun[qb] - mnew) : (upd ? 0.f : 1.f);
+        const float e = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
+        alpha[qb] = upd ? e : 1.f;
         const float nm = mnew == -INFINITY ? 0.f : -mnew;
         float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], sc, nm));
-          s[qb][i] = p;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc_[qb][i], sc, nm));
+          sc_[qb][i] = p;
           psum += p;
         }
         psum += __shfl_xor(psum, 32);
-        lrun[qb] = lrun[qb] * alpha + psum;
+        lrun[qb] = lrun[qb] * alpha[qb] + psum;
         mrun[qb] = mnew;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int u = 0; u < ND; ++u) o[qb][u] *= alpha;
-        }
       }
-      // V^T fragments of the half's two slices, all read before the MFMAs
+    };
+    auto rescale = [&](const float (&alpha)[QB]) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        if (__any(alpha[qb] != 1.f)) {
+#pragma unroll
+          for (int u = 0; u < ND; ++u) o[qb][u] *= alpha[qb];
+        }
+    };
+    // probabilities of a half as bf16 MFMA operands, one per 16-key slice
+    auto pack = [&](const f32x16 (&p_)[QB], u32x4 (&pf)[2][QB]) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float pv_[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv_[j] = p_[qb][8 * half + j];
+          pf[half][qb] = pack16<bf16>(pv_);
+        }
+    };
+    auto pv = [&](int kb, const u32x4 (&pf)[2][QB]) {
+      // V^T fragments of the half's two 16-key slices, all read before the MFMAs
       u32x4 vf[2][ND];
 #pragma unroll
       for (int half = 0; half < 2; ++half)
@@ -227,24 +252,37 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
           const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
           vf[half][u] = u32x4{l2[0], l2[1], h2[0], h2[1]};
         }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 pf[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float pv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pv[j] = s[qb][8 * half + j];
-          pf[qb] = pack16<bf16>(pv);
-        }
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int u = 0; u < ND; ++u)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             o[qb][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[half][u]),
-                                                               __builtin_bit_cast(bf16x8, pf[qb]), o[qb][u], 0, 0, 0);
-      }
+                                                               __builtin_bit_cast(bf16x8, pf[half][qb]), o[qb][u], 0,
+                                                               0, 0);
+    };
+    // A tile whose keys all lie at or past every query of this wave adds
+    // nothing (its probabilities are 0 and the running max stays), so the
+    // wave skips it; the block still stages every tile up to its own last
+    // query, which the other waves may need.  (Half 1 of the last tile a
+    // wave takes may be fully masked; it runs and adds zeros.)
+    if (key0 < maxpos) {
+      f32x16 sc0[QB], sc1[QB];
+      float al0[QB], al1[QB];
+      u32x4 pf0[2][QB], pf1[2][QB];
+      qk(0, sc0);
+      mask(0, sc0);
+      softmax(sc0, al0);
+      pack(sc0, pf0);
+      qk(1, sc1);
+      mask(1, sc1);
+      rescale(al0);
+      pv(0, pf0);
+      softmax(sc1, al1);
+      pack(sc1, pf1);
+      rescale(al1);
+      pv(1, pf1);
     }
     if (t + 1 < t1) sstore(st ^ 1);
     __syncthreads();
