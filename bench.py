@@ -420,9 +420,21 @@ def cpu_baseline(budget_s=10.0):
         O.step(M, tokens[nseq:nseq + 1], cache, bidx, pos, want_logits=False)
         dt += time.perf_counter() - t0
         nseq += 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:
+        blas = "unknown"
     return {"value": nseq * len(pos) / dt, "unit": "tokens/s/pass", "cores": threads, "kind": "oracle",
             "sample": f"sequences 0..{nseq - 1}, group q=0 ({len(pos)} positions each) of the first pass, "
-                      f"float64 numpy, {dt:.1f}s"}
+                      f"float64 numpy, {dt:.1f}s",
+            "cpu_model": cpu_model, "blas": blas}
 
 
 def device_peaks():
