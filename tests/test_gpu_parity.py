@@ -109,6 +109,27 @@ def test_mix_kv_matches_oracle(name, B, M, s0, step):
     assert_cache(w, cache.k, cache.v, ref, written_mask(w, B, bidx, pos), TOL[w.dtype])
 
 
+@pytest.mark.parametrize("B,M", [
+    (1, 127), (2, 64), (3, 43),         # 127, 128, 129 rows: the few-row router and projection and past them
+    (23, 89), (16, 128), (3, 683),      # 2047, 2048, 2049 rows: the 128x128 and the 256x256 tile GEMMs
+])
+def test_mix_kv_row_count_boundaries(B, M):
+    """Row counts on both sides of the library's kernel switches (bf16)."""
+    w = WORKLOADS["mix_bf16"].replace(B=B)
+    s0, step = 1, 1
+    print(f"mix_kv boundary B={B} M={M} rows={B * M}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    S = make_state_stack(w, B * M, seed=6)
+    model = gpu_model(w, {n: W[n] for n in ("src_norm", "router", "chan_norm", "wk", "wv", "k_norm")})
+    cache = wm.new_cache(model, B, fill=float("nan"))
+    wm.mix_kv(model, torch.from_numpy(S).to(DEV, torch.bfloat16), B, M, s0, step, cache)
+    torch.cuda.synchronize()
+    ref = O.new_cache(w, B)
+    O.mix_kv(O.Model(w, W), S, B, M, s0, step, ref)
+    bidx, pos = O.tokset_rows(B, M, s0, step)
+    assert_cache(w, cache.k, cache.v, ref, written_mask(w, B, bidx, pos), TOL["bf16"])
+
+
 @pytest.mark.parametrize("name,B,M,s0,step", [
     ("tiny_fp32", 2, 100, 0, 1),        # fp32 scalar mix
     ("mix_bf16", 3, 37, 5, 7),          # bf16 MFMA mix, few rows
@@ -237,6 +258,27 @@ def test_mix_kv_ragged_large_rows():
     ("decode_d512", 2, 1, 0, 1, 0),            # position 0 only: no keys at all
 ])
 def test_channel_attn_matches_oracle(name, B, M, s0, step, layer):
+    _check_channel_attn(name, B, M, s0, step, layer)
+
+
+@pytest.mark.parametrize("name,B,M,s0,step,layer", [
+    ("small_prefill", 2, 16, 3, 7, 1),     # 32 query rows per sequence and KV head: the few-row kernel
+    ("small_prefill", 2, 17, 3, 7, 1),     # 34: the general kernel
+    ("small_prefill", 2, 63, 0, 3, 4),     # 126
+    ("small_prefill", 2, 64, 0, 3, 4),     # 128: one block of the many-row kernel
+    ("small_prefill", 2, 65, 5, 3, 4),     # 130: and a ragged second block
+    ("prefill_1p3b", 2, 4, 900, 11, 6),    # G = 7: 28 rows, few-row kernel at d = 128
+    ("prefill_1p3b", 2, 5, 900, 11, 6),    # 35
+    ("prefill_1p3b", 2, 18, 10, 13, 6),    # 126
+    ("prefill_1p3b", 2, 19, 10, 13, 6),    # 133: many-row kernel at d = 128
+])
+def test_channel_attn_kernel_boundaries(name, B, M, s0, step, layer):
+    """Query-row counts per (sequence, KV head) on both sides of the
+    attention kernel switches (<= 32, between, >= 128 rows)."""
+    _check_channel_attn(name, B, M, s0, step, layer)
+
+
+def _check_channel_attn(name, B, M, s0, step, layer):
     w = WORKLOADS[name]
     print(f"channel_attn {name} B={B} M={M} s0={s0} step={step} layer={layer}", flush=True)
     maxpos = s0 + (M - 1) * step
