@@ -493,6 +493,36 @@ def test_prefill_pass_full_size_bf16_first_group(name, b, B):
     assert max(ek, ev) <= TOL_BF16_DEEP
 
 
+@pytest.mark.parametrize("B,T,g", [
+    (1, 256, 2),     # 128 rows per group step: the few-row GEMMs
+    (3, 86, 2),      # 129: past them
+    (23, 178, 2),    # 2047: the 128x128 tile GEMMs
+    (16, 256, 2),    # 2048: the 256x256 tile GEMMs
+    (3, 1366, 2),    # 2049: and their ragged last tile
+])
+def test_prefill_first_group_row_boundaries(B, T, g):
+    """One bf16 pass of the small model with a group step of 128, 129, 2047,
+    2048 or 2049 rows, on both sides of the library's GEMM switches; the
+    oracle recomputes the first group of the last sequence."""
+    w = WORKLOADS["small_prefill"].replace(B=B, T=T, g=g)
+    b = B - 1
+    print(f"prefill B{B} T{T} g{g}: {B * ((T + g - 1) // g)} rows per first group step", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, B)
+    wm.cyclic_prefill_pass(model, torch.from_numpy(tokens).to(DEV), g, cache)
+    torch.cuda.synchronize()
+    gk = cache.k[:, b].float().cpu().numpy()
+    gv = cache.v[:, b].float().cpu().numpy()
+    assert np.isfinite(gk[:, :, :T]).all() and np.isfinite(gv[:, :, :T]).all()
+    pos, ref = _first_group_ref(w, W, tokens, b)
+    ek = max_abs_rel(gk[:, :, pos], ref[0][:, 0][:, :, pos])
+    ev = max_abs_rel(gv[:, :, pos], ref[1][:, 0][:, :, pos])
+    print(f"  group 0 of sequence {b}: K {ek:.3e} V {ev:.3e}", flush=True)
+    assert max(ek, ev) <= TOL_BF16_DEEP
+
+
 def test_decode_step_full_size():
     """Decode workload at full size: B=64, 2047 cached positions (seeded N(0,1)
     keys/values in all 16 channels), one new token per sequence at t=2047;
