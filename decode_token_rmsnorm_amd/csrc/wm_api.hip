@@ -687,11 +687,17 @@ wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_
   st = check_common(cfg, cache, ws, ws_bytes, rows);
   if (st != WM_OK) return st;
   wm_tokset ts{cache->B, 1, t, 1};
+  // (more than kFewRows sequences: the pool reads the gain-folded router
+  // weights, which prep_router writes into the workspace)
   if (cfg->dtype == WM_BF16) {
     Run<bf16> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+    st = r.prep_router();
+    if (st != WM_OK) return st;
     return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
   }
   Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+  st = r.prep_router();
+  if (st != WM_OK) return st;
   return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
 }
 

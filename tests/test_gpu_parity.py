@@ -523,6 +523,33 @@ def test_prefill_first_group_row_boundaries(B, T, g):
     assert max(ek, ev) <= TOL_BF16_DEEP
 
 
+@pytest.mark.parametrize("B", [128, 129])
+def test_decode_step_batch_boundary(B):
+    """Decode steps of 128 and 129 sequences (the few-row GEMMs and past them)
+    at t = 300 on the decode model; logits and the appended slot against the
+    oracle, the rest of the cache untouched."""
+    w = WORKLOADS["decode_d512"].replace(B=B, T_max=512)  # (a shorter cache keeps the host copies small)
+    t = 300
+    print(f"decode B{B} t{t}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    K, V = make_cache(w, B, filled=t, seed=3, poison=True)
+    tokens = make_tokens(w, seed=1, B=B, T=1)[:, 0]
+    model = gpu_model(w, W)
+    cache = wm.cache_from_host(model, K, V)
+    lg = wm.decode_step(model, torch.from_numpy(tokens).to(DEV), t, cache)
+    torch.cuda.synchronize()
+    ref = (np.nan_to_num(K, nan=0.0).astype(np.float64), np.nan_to_num(V, nan=0.0).astype(np.float64))
+    rl = O.decode_step(O.Model(w, W), tokens, t, ref)
+    el = max_abs_rel(np_of(lg), rl)
+    print(f"decode logits {el:.3e}", flush=True)
+    assert el <= TOL_BF16_DEEP
+    gk, gv = np_of(cache.k), np_of(cache.v)
+    for got, exp in ((gk, ref[0]), (gv, ref[1])):
+        assert max_abs_rel(got[:, :, :, t], exp[:, :, :, t]) <= TOL_BF16_DEEP
+        assert np.array_equal(got[:, :, :, :t], np.asarray(exp[:, :, :, :t], np.float32))
+        assert np.isnan(got[:, :, :, t + 1:]).all()
+
+
 def test_decode_step_full_size():
     """Decode workload at full size: B=64, 2047 cached positions (seeded N(0,1)
     keys/values in all 16 channels), one new token per sequence at t=2047;
