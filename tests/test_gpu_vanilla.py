@@ -134,6 +134,31 @@ def test_vanilla_decode_full_size():
         assert np.isnan(got[:, :, :, t + 1:]).all()
 
 
+def test_vanilla_decode_batch_boundary():
+    """129 sequences (past the few-row GEMMs) at t = 300 on the decode model
+    (a 512-position cache keeps the host copies small)."""
+    w = WORKLOADS["decode_d512"].replace(B=129, T_max=512)
+    t = 300
+    print("vanilla decode B129", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    K, V = make_cache(w, w.B, filled=t, seed=3, poison=True)
+    tokens = make_tokens(w, seed=1, B=w.B, T=1)[:, 0]
+    model = gpu_model(w, W)
+    cache = wm.cache_from_host(model, K, V)
+    lg = wm.vanilla_decode_step(model, torch.from_numpy(tokens).to(DEV), t, cache)
+    torch.cuda.synchronize()
+    ref = (np.nan_to_num(K, nan=0.0).astype(np.float64), np.nan_to_num(V, nan=0.0).astype(np.float64))
+    rl = O.vanilla_decode_step(O.Model(w, W), tokens, t, ref)
+    el = max_abs_rel(np_of(lg), rl)
+    print(f"  decode logits {el:.3e}", flush=True)
+    assert el <= TOL_BF16_DEEP
+    gk, gv = np_of(cache.k), np_of(cache.v)
+    for got, exp in ((gk, ref[0]), (gv, ref[1])):
+        assert max_abs_rel(got[:, :, :, t], exp[:, :, :, t]) <= TOL_BF16_DEEP
+        assert np.array_equal(got[:, :, :, :t], np.asarray(exp[:, :, :, :t], np.float32))
+        assert np.isnan(got[:, :, :, t + 1:]).all()
+
+
 # ---------------------------------------------------------------- feedback-free variant
 
 @pytest.mark.parametrize("chunk,p", [(128, 2), (16, 2), (7, 1), (32, 3)])
