@@ -397,8 +397,8 @@ def test_prefill_deep_shapes_fp32(name, B, T, g, npass):
         assert el <= TOL_F32_DEEP
 
 
-@pytest.mark.parametrize("B", [8, 40])  # 40: the wide vocabulary kernel, one ragged 64-row block
-def test_decode_deep_shape_fp32(B):
+@pytest.mark.parametrize("B", [8, 40, 129])  # 40: the wide vocabulary kernel, one ragged 64-row block;
+def test_decode_deep_shape_fp32(B):             # 129: the many-row pool (folded router weights)
     w = WORKLOADS["decode_d512"].replace(B=B, T_max=512, dtype="f32")
     t = 300
     print(f"decode fp32 B={B} t=300", flush=True)
