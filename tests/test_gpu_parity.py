@@ -419,6 +419,30 @@ def test_decode_deep_shape_fp32(B):             # 129: the many-row pool (folded
     assert np.isnan(np_of(cache.k)[:, :, :, t + 1:]).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_first_position(dtype):
+    """A decode step at t = 0: no key to attend to (attention gives 0), slot 0
+    appended; every later slot keeps its poison."""
+    w = WORKLOADS["decode_d512"].replace(B=4, T_max=64, dtype=dtype)
+    print(f"decode {dtype} t=0", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    K, V = make_cache(w, w.B, filled=0, seed=3, poison=True)
+    tokens = make_tokens(w, seed=1, B=w.B, T=1)[:, 0]
+    model = gpu_model(w, W)
+    cache = wm.cache_from_host(model, K, V)
+    lg = wm.decode_step(model, torch.from_numpy(tokens).to(DEV), 0, cache)
+    torch.cuda.synchronize()
+    ref = (np.zeros(K.shape), np.zeros(V.shape))
+    rl = O.decode_step(O.Model(w, W), tokens, 0, ref)
+    tol = TOL["f32"] if dtype == "f32" else TOL_BF16_DEEP
+    el = max_abs_rel(np_of(lg), rl)
+    ek = max_abs_rel(np_of(cache.k)[:, :, :, 0], ref[0][:, :, :, 0])
+    ev = max_abs_rel(np_of(cache.v)[:, :, :, 0], ref[1][:, :, :, 0])
+    print(f"decode {dtype} t=0: logits {el:.2e} K {ek:.2e} V {ev:.2e}", flush=True)
+    assert max(el, ek, ev) <= tol
+    assert np.isnan(np_of(cache.k)[:, :, :, 1:]).all() and np.isnan(np_of(cache.v)[:, :, :, 1:]).all()
+
+
 # ---------------------------------------------------------------- bf16, short sequences
 
 @pytest.mark.parametrize("name,B,T,g", [("small_prefill", 2, 8, 8), ("prefill_1p3b", 1, 6, 6)])
