@@ -8,11 +8,11 @@
 // double buffered, and shared by the waves.
 //
 // Both products use 32x32x16 MFMAs, so every K and V element read from LDS
-// serves 32 queries.  Scores are computed transposed, S^T = K Q^T, in two
-// independent 32-key accumulators: a lane holds 32 keys of one query (column
-// lane%32), the other 32 keys of the tile sit in lane ^ 32, so the
+// serves 32 queries.  Scores are computed transposed, S^T = K Q^T, one 32x32
+// accumulator per 32-key half of the tile: a lane holds 16 of the half's keys
+// for one query (column lane%32) and lane ^ 32 the other 16, so the
 // online-softmax statistics need one exchange and the output rescale is
-// lane-local.  The probabilities feed O^T += V^T P^T straight from the
+// lane-local (the halves' order is described at the tile loop).  The probabilities feed O^T += V^T P^T straight from the
 // accumulators: the MFMA k slot j of lane half h stands for key 4h + j
 // (j < 4) or 8 + 4h + (j - 4) of each 16-key slice.  V stays row-major in
 // LDS and its transposed fragments come from the LDS transpose read
