@@ -101,10 +101,12 @@ template <typename T> struct Run {
   // The 256 x 256 kernel (bf16 only) for steps with enough rows to fill the chip.
   static constexpr bool kBig = std::is_same<T, bf16>::value;
   bool big(int M) const { return kBig && M >= 2048; }
+  // column tile of the residual products on M rows
+  int resid_bn(int M, int N) const { return big(M) ? g2_resid_bn(M, N, kComputeUnits) : GN; }
   // partial sums of squares per row written by a residual epilogue on M rows
   int parts(int M, int N) const {
     if (M <= kFewRows) return few_parts(M, N);
-    return (N + (big(M) ? G2N : GN) - 1) / (big(M) ? G2N : GN);
+    return (N + resid_bn(M, N) - 1) / resid_bn(M, N);
   }
   T *Kch(int ch) const { return (T *)cache->k + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
   T *Vch(int ch) const { return (T *)cache->v + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
@@ -114,6 +116,18 @@ template <typename T> struct Run {
   hipError_t gemm2_rows(const T *A, int64_t lda, const T *B, int64_t ldb, const EP &ep, int M, int N, int K) {
     if constexpr (kBig) {
       return launch_gemm2(PRows<T>{A, lda, 0, M}, PBRows<T>{PRows<T>{B, ldb, 0, N}}, ep, M, N, K, 1, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  // The same for the residual products, on the column tile resid_bn(M, N).
+  hipError_t gemm2_resid(const T *A, int64_t lda, const T *B, int64_t ldb, const EpiResid<T> &ep, int M, int N,
+                         int K) {
+    if constexpr (kBig) {
+      const PRows<T> a{A, lda, 0, M};
+      const PBRows<T> b{PRows<T>{B, ldb, 0, N}};
+      if (resid_bn(M, N) == G2Shape<1>::BN) return launch_gemm2<G2KB, G2ST, 2, 1>(a, b, ep, M, N, K, 1, s);
+      return launch_gemm2(a, b, ep, M, N, K, 1, s);
     } else {
       return hipErrorInvalidValue;
     }
@@ -455,7 +469,7 @@ template <typename T> struct Run {
         EpiResid<T> e{h, hb, w->ffn_norm + (int64_t)l * D, nullptr, ss, parts(rows, D)};
         ProfScope prof(WM_K_OPROJ, s);
         if (big(rows))
-          WM_TRY(gemm2_rows(o, QD, wo + (int64_t)l * D * QD, QD, e, rows, D, QD));
+          WM_TRY(gemm2_resid(o, QD, wo + (int64_t)l * D * QD, QD, e, rows, D, QD));
         else
           WM_TRY((gemm1(a, b, e, rows, D, QD, 1)));
         nparts = parts(rows, D);
@@ -491,7 +505,7 @@ template <typename T> struct Run {
         EpiResid<T> e{h, hb, gnext, Snext, ss, parts(rows, D)};
         ProfScope prof(WM_K_DOWN, s);
         if (big(rows))
-          WM_TRY(gemm2_rows(act, c.F, wd + (int64_t)l * D * c.F, c.F, e, rows, D, c.F));
+          WM_TRY(gemm2_resid(act, c.F, wd + (int64_t)l * D * c.F, c.F, e, rows, D, c.F));
         else
           WM_TRY((gemm1(a, b, e, rows, D, c.F, 1)));
       }

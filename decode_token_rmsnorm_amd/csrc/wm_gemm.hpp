@@ -240,7 +240,8 @@ __device__ __forceinline__ void run_epi(const EpiQ<T> &e, int z, int m0, int n0,
 }
 
 // Residual: h += C; hb = h * gain_next; optionally S_next = h; and the row's
-// sum of squares over this tile's columns -> ss_out[r, n0 / tile width].
+// sum of squares over this tile's columns -> ss_out[r, n0 / tile width]
+// (tile width tw: 64 * CPL, or fewer columns with the lanes past it idle).
 template <typename T> struct EpiResid {
   float *h;
   T *hb;
@@ -252,10 +253,10 @@ template <typename T> struct EpiResid {
 
 template <typename T, int CPL>
 __device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
-                                        int nrows, int M, int N, float *rowbuf) {
+                                        int nrows, int M, int N, float *rowbuf, int tw = 64 * CPL) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = n0 + CPL * lane;
-  const bool on = c0 < N;
+  const bool on = c0 < N && CPL * lane < tw;
   const int cl = on ? c0 : N - CPL;  // (off lanes read a valid column and store nothing)
   float g[CPL];
   ldf<CPL>(g, e.gain_next + cl);
@@ -295,7 +296,7 @@ __device__ __forceinline__ void run_epi(const EpiResid<T> &e, int z, int m0, int
 #pragma unroll
       for (int u = 0; u < ERR; ++u) {
         const int r = m0 + rb + u;
-        if (rb + u < nrows && r < M) e.ss_out[(int64_t)r * e.nparts_out + n0 / (64 * CPL)] = sq[u];
+        if (rb + u < nrows && r < M) e.ss_out[(int64_t)r * e.nparts_out + n0 / tw] = sq[u];
       }
     }
   }

@@ -25,6 +25,7 @@ namespace wm {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int G2M = 256, G2N = 256;
+constexpr int kComputeUnits = 256;    // MI355X
 constexpr int G2CP = G2N + 4;         // C tile pitch (floats)
 constexpr int G2CT = 128 * G2CP * 4;  // staged half C tile, bytes
 constexpr int G2KB = 64, G2ST = 4;    // k-tile bytes per row, LDS stages
@@ -125,89 +126,134 @@ __device__ __forceinline__ void g2_tile(int b, int nM, int nN, int &tm, int &tn,
   tn = tt / bm;
 }
 
-template <int KB, int ST, int MAP, class AP, class BP, class EP>
+// Wave arrangements of the 256-row block tile. SH 0: 2 x 2 waves of 128 x 128
+// (4 x 4 MFMA tiles), 256 columns. SH 1: 4 x 1 waves of 64 x 224 (2 x 7 MFMA
+// tiles), 224 columns: a 1792-column product then has 8 column tiles, and
+// 8192 rows give 256 blocks, one per compute unit, where 256 columns give 224.
+template <int SH> struct G2Shape {
+  static constexpr int WN = SH ? 1 : 2;  // waves along N
+  static constexpr int TI = SH ? 2 : 4;  // 32-row MFMA tiles per wave
+  static constexpr int TJ = SH ? 7 : 4;  // 32-column MFMA tiles per wave
+  static constexpr int BN = 32 * TJ * WN;
+};
+
+template <int KB, int ST, int MAP, int SH, class AP, class BP, class EP>
 __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, int N, int K, int nM, int nN) {
-  constexpr int STAGE = (G2M + G2N) * KB;
+  using S = G2Shape<SH>;
+  constexpr int TI = S::TI, TJ = S::TJ, BN = S::BN;
+  constexpr int STAGE = (G2M + BN) * KB;
   constexpr int RPI = 1024 / KB;          // rows per DMA instruction
-  constexpr int NI = G2M / RPI / 4;       // DMA instructions per wave per operand
-  constexpr int PI = 2 * NI;              // DMA instructions per wave per k-tile
+  constexpr int NI = G2M / RPI / 4;       // A DMA instructions per wave
+  constexpr int NBT = BN / RPI;           // B DMA instructions per block
+  constexpr int NIB = (NBT + 3) / 4;      // B DMA slots per wave
+  constexpr int NBF = NBT - 4 * (NIB - 1);  // waves [0, NBF) fill all NIB slots
+  constexpr int PI = NI + NIB;            // DMA instructions per wave per k-tile (waves < NBF)
+  constexpr int PI1 = NBF == 4 ? PI : PI - 1;  // (waves >= NBF)
   constexpr int KS = KB / 32;             // 16-deep MFMA steps per k-tile
+  static_assert(BN % RPI == 0 && TI * 32 * (4 / S::WN) == G2M, "tile shape");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[g2_smem(KB, ST)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / S::WN, wn = wave % S::WN;
+  const bool bfull = NBF == 4 || wave < NBF;
   int tm, tn, z;
   g2_tile<MAP>(blockIdx.x, nM, nN, tm, tn, z);
-  const int m0 = tm * G2M, n0 = tn * G2N;
+  const int m0 = tm * G2M, n0 = tn * BN;
   const int nk = K * 2 / KB;
 
-  // This thread's DMA sources: rows (wave*NI + j)*RPI + lane/(KB/16) of each
-  // operand, chunk chosen so that LDS slot (row, lane % (KB/16)) holds the
-  // swizzled chunk (the swizzle is an XOR, its own inverse).
-  const char *pa[NI], *pb[NI];
+  // This thread's DMA sources: A rows (wave*NI + j)*RPI + lane/(KB/16), B row
+  // blocks wave*NIB + j (256 columns) or 4*j + wave (224 columns, the last slot
+  // of waves >= NBF unused), chunk chosen so that LDS slot (row,
+  // lane % (KB/16)) holds the swizzled chunk (the swizzle is an XOR, its own
+  // inverse).
+  auto bblk = [&](int j) { return SH ? 4 * j + wave : wave * NIB + j; };
+  const char *pa[NI], *pb[NIB];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     int row = (wave * NI + j) * RPI + lane / (KB / 16);
-    int c = g2_swz<KB>(row, lane % (KB / 16));
-    pa[j] = ap.row(z, m0 + row) + c * 16;
-    pb[j] = bp.row(z, n0, row) + c * 16;
+    pa[j] = ap.row(z, m0 + row) + g2_swz<KB>(row, lane % (KB / 16)) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < NIB; ++j) {
+    int row = (bblk(j) < NBT ? bblk(j) : NBT - 1) * RPI + lane / (KB / 16);
+    pb[j] = bp.row(z, n0, row) + g2_swz<KB>(row, lane % (KB / 16)) * 16;
   }
   auto issue = [&](int kt, int stage) {
     unsigned char *As = smem + stage * STAGE, *Bs = As + G2M * KB;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      dma16(pa[j] + kt * KB, As + (wave * NI + j) * 1024);
-      dma16(pb[j] + kt * KB, Bs + (wave * NI + j) * 1024);
+    for (int j = 0; j < NIB; ++j) {
+      if (j < NI) dma16(pa[j] + kt * KB, As + (wave * NI + j) * 1024);
+      if (j + 1 < NIB || bfull) dma16(pb[j] + kt * KB, Bs + bblk(j) * 1024);
     }
+#pragma unroll
+    for (int j = NIB; j < NI; ++j) dma16(pa[j] + kt * KB, As + (wave * NI + j) * 1024);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
   // Fragments of k-step ks+1 are read from LDS while the MFMAs of step ks run.
   auto frags = [&](const unsigned char *As, const unsigned char *Bs, int ks, u32x4 *af, u32x4 *bfr) {
     const int c = 2 * ks + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int r = wm * 128 + i * 32 + (lane & 31);
+    for (int i = 0; i < TI; ++i) {
+      int r = wm * TI * 32 + i * 32 + (lane & 31);
       af[i] = *(const u32x4 *)(As + r * KB + g2_swz<KB>(r, c) * 16);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int r = wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < TJ; ++j) {
+      int r = wn * TJ * 32 + j * 32 + (lane & 31);
       bfr[j] = *(const u32x4 *)(Bs + r * KB + g2_swz<KB>(r, c) * 16);
     }
   };
-  // Wait until at most `later` k-tiles after the awaited one are in flight.
+  // Wait until at most `later` k-tiles after the awaited one are in flight
+  // (counts per wave: the waves issue PI or PI1 DMAs per k-tile).
   auto wait_tiles = [&](int later) {
     if constexpr (ST >= 4) {
-      if (later >= 2) wait_vmcnt<2 * PI>();
-      else if (later == 1) wait_vmcnt<PI>();
-      else wait_vmcnt<0>();
+      if (later >= 2) {
+        if (bfull) wait_vmcnt<2 * PI>();
+        else wait_vmcnt<2 * PI1>();
+      } else if (later == 1) {
+        if (bfull) wait_vmcnt<PI>();
+        else wait_vmcnt<PI1>();
+      } else {
+        wait_vmcnt<0>();
+      }
     } else if constexpr (ST == 3) {
-      if (later >= 1) wait_vmcnt<PI>();
-      else wait_vmcnt<0>();
+      if (later >= 1) {
+        if (bfull) wait_vmcnt<PI>();
+        else wait_vmcnt<PI1>();
+      } else {
+        wait_vmcnt<0>();
+      }
     } else {
       wait_vmcnt<0>();
     }
   };
   auto mfmas = [&](const u32x4 *af, const u32x4 *bfr) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
                                                             __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
   };
-  // 2 MFMAs : 1 fragment read, so LDS latency hides under the MFMAs.
+  // Fragment reads spread over the MFMAs (2 : 1 where there are enough
+  // MFMAs), so LDS latency hides under them.
   auto interleave = [&]() {
+    constexpr int NR = TI + TJ, N2 = TI * TJ - NR;  // reads; groups with 2 MFMAs
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < N2; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+#pragma unroll
+    for (int g = N2; g < NR; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
@@ -219,7 +265,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
   wait_tiles(min(ST - 2, nk - 1));
   __builtin_amdgcn_s_barrier();
   if (ST - 1 < nk) issue(ST - 1, (ST - 1) % ST);
-  u32x4 fa[2][4], fb[2][4];
+  u32x4 fa[2][TI], fb[2][TJ];
   frags(smem, smem + G2M * KB, 0, fa[0], fb[0]);
 
   // Steady state. The barrier that makes k-tile kt+1 visible (and frees the
@@ -242,39 +288,54 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
       frags(An, An + G2M * KB, 0, fa[KS & 1], fb[KS & 1]);
     }
     mfmas(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
-    __builtin_amdgcn_sched_group_barrier(0x020, 2 * NI, 0);  // DMA issue first
+    __builtin_amdgcn_sched_group_barrier(0x020, PI1, 0);  // DMA issue first
     interleave();
   }
   __syncthreads();
 
   // epilogue in two 128-row halves; accumulator (lane, e) of a 32x32 tile is
   // row 8*(e/4) + 4*(lane/32) + e%4, column lane%32.
+  constexpr int CP = BN + 4;  // C tile pitch (floats)
   float *Cs = (float *)smem;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if (wm == h) {
+    const int r0 = wm * TI * 32 - h * 128;  // this wave's first row within the half
+    if (r0 >= 0 && r0 < 128) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            Cs[(i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * G2CP + wn * 128 + j * 32 + (lane & 31)] =
+            Cs[(r0 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * CP + wn * TJ * 32 + j * 32 + (lane & 31)] =
                 acc[i][j][e];
     }
     __syncthreads();
-    run_epi<bf16, G2N / 64>(ep, z, m0 + h * 128, n0, Cs, G2CP, 128, M, N, (float *)(smem + G2CT));
+    if constexpr (BN == G2N)
+      run_epi<bf16, G2N / 64>(ep, z, m0 + h * 128, n0, Cs, CP, 128, M, N, (float *)(smem + G2CT));
+    else  // (only epilogues that take a tile width)
+      run_epi<bf16, 4>(ep, z, m0 + h * 128, n0, Cs, CP, 128, M, N, (float *)(smem + G2CT), BN);
     __syncthreads();
   }
 }
 
-template <int KB = G2KB, int ST = G2ST, int MAP = 2, class AP, class BP, class EP>
+template <int KB = G2KB, int ST = G2ST, int MAP = 2, int SH = 0, class AP, class BP, class EP>
 hipError_t launch_gemm2(const AP &ap, const BP &bp, const EP &ep, int M, int N, int K, int Z, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  const int nM = (M + G2M - 1) / G2M, nN = (N + G2N - 1) / G2N;
-  hipLaunchKernelGGL((gemm2_kernel<KB, ST, MAP, AP, BP, EP>), dim3(nM * nN * Z), dim3(256), 0, s, ap, bp, ep, M, N,
-                     K, nM, nN);
+  constexpr int BN = G2Shape<SH>::BN;
+  const int nM = (M + G2M - 1) / G2M, nN = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm2_kernel<KB, ST, MAP, SH, AP, BP, EP>), dim3(nM * nN * Z), dim3(256), 0, s, ap, bp, ep, M,
+                     N, K, nM, nN);
   return hipGetLastError();
+}
+
+// Column tile of the residual products: 224 where that needs fewer rounds of
+// blocks over the compute units than 256 (e.g. 1792 columns over 8192 rows:
+// 256 blocks instead of 224), counted in column-tile widths per unit.
+inline int g2_resid_bn(int M, int N, int cus) {
+  const long nM = (M + G2M - 1) / G2M;
+  const long r256 = (nM * ((N + 255) / 256) + cus - 1) / cus, r224 = (nM * ((N + 223) / 224) + cus - 1) / cus;
+  return r224 * 224 < r256 * 256 ? 224 : 256;
 }
 
 }  // namespace wm
