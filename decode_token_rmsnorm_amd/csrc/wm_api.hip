@@ -186,7 +186,7 @@ template <typename T> struct Run {
     dim3 grid(nrb, ts.B * c.Hkv, ns);
     ProfScope prof(WM_K_ATTN, s);
     if constexpr (bfd) {
-      if (v2) hipLaunchKernelGGL((attn2_kernel<DH, 1>), grid, dim3(256), 0, s, a);
+      if (v2) hipLaunchKernelGGL((attn2_kernel<DH, 1>), dim3(ts.B * c.Hkv, nrb, ns), dim3(256), 0, s, a);
       if (few) hipLaunchKernelGGL((attn_few<DH, few_nw>), dim3(ns, ts.B * c.Hkv), dim3(64 * few_nw), 0, s, a);
     }
     if (v2 || few)

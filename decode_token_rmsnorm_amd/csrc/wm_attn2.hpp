@@ -1,9 +1,12 @@
 // wm_attn2.hpp — strict-causal channel attention, bf16, for token sets with
 // many query rows per (sequence, KV head) pair (prefill group steps).
 //
-// Same contract as attn_kernel (wm_attn.hpp): grid (row blocks, B*Hkv,
-// splits), rows rho = m*G + g of one (b, hk) pair at position s0 + m*step,
-// keys s < position, partials for the split combine.  A block is 4 waves of
+// Same contract as attn_kernel (wm_attn.hpp), rows rho = m*G + g of one
+// (b, hk) pair at position s0 + m*step, keys s < position, partials for the
+// split combine, except for the grid: (B*Hkv, row blocks, splits) with
+// blockIdx.y = 0 the pair's last row block.  A block's work grows with its
+// last position, so the longest blocks of every pair are dispatched first and
+// the short ones fill in behind them.  A block is 4 waves of
 // 32*QB query rows; 64-key tiles of K and V are staged row-major in LDS,
 // double buffered, and shared by the waves.
 //
@@ -55,9 +58,9 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][KT * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
-  const int pair = blockIdx.y, b = pair / a.Hkv, hk = pair - b * a.Hkv;
+  const int pair = blockIdx.x, b = pair / a.Hkv, hk = pair - b * a.Hkv;
   const int nrows = a.M * a.G;
-  const int rb0 = blockIdx.x * RB;
+  const int rb0 = (gridDim.y - 1 - blockIdx.y) * RB;
   if (rb0 >= nrows) return;
   const int last = min(nrows, rb0 + RB) - 1;
   const int kmax = min(a.s0 + (last / a.G) * a.step, a.T_max);  // keys s < kmax for the block
