@@ -517,6 +517,37 @@ def test_prefill_pass_full_size_bf16_first_group(name, b, B):
     assert max(ek, ev) <= TOL_BF16_DEEP
 
 
+def test_prefill_ragged_rows_and_features_1p3b_widths():
+    """A pass on 8064 rows per group step (B = 63: a ragged last 256-row
+    tile) with F = 4800 (2F = 9600: a ragged last gate/up column tile), on a
+    2-layer stack of the 1.3B widths; the oracle recomputes the first group
+    of the last sequence, whose rows sit in the ragged tile.  Tolerance
+    TOL_BF16_DEEP as for the other reduced-depth stacks (bf16 through two
+    layers of width 1792 gives ~3e-2 here); the oracle's K/V move by 1.4
+    when the features past 4096 are dropped and by 0.24 (K) and 1.3 (V) when
+    only the last 32 are."""
+    w = WORKLOADS["prefill_1p3b"].replace(L=2, k=2, p=1, F=4800)
+    B, b = 63, 62
+    print(f"ragged pass: L{w.L} D{w.D} F{w.F}, B {B}, sampled sequence {b}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1, B=B)
+    model = gpu_model(w, W)
+    cache = wm.new_cache(model, B)
+    tok = torch.from_numpy(tokens).to(DEV)
+    logits = wm.cyclic_prefill_pass(model, tok, w.g, cache, logits_mode=1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(logits).all()
+    gk = cache.k[:, b].float().cpu().numpy()
+    gv = cache.v[:, b].float().cpu().numpy()
+    del cache, model
+    torch.cuda.empty_cache()
+    pos, ref = _first_group_ref(w, W, tokens, b)
+    ek = max_abs_rel(gk[:, :, pos], ref[0][:, 0][:, :, pos])
+    ev = max_abs_rel(gv[:, :, pos], ref[1][:, 0][:, :, pos])
+    print(f"  group 0 of sequence {b}: K {ek:.3e} V {ev:.3e}", flush=True)
+    assert max(ek, ev) <= TOL_BF16_DEEP
+
+
 @pytest.mark.parametrize("B,T,g", [
     (1, 256, 2),     # 128 rows per group step: the few-row GEMMs
     (3, 86, 2),      # 129: past them
