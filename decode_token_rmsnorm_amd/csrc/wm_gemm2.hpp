@@ -3,7 +3,8 @@
 //
 // Block tile 256 x 256, 256 threads = 4 wave64s in a 2 x 2 grid; each wave
 // owns a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 tiles (256 fp32
-// accumulators per lane).  Both operands are copied global -> LDS by the
+// accumulators per lane); or 256 x 224 with the waves stacked along M, 64 x
+// 224 each (2 x 7 MFMA tiles, G2Shape below).  Both operands are copied global -> LDS by the
 // 16-byte LDS DMA (global_load_lds_dwordx4): lane i of a wave writes LDS bytes
 // [16i, 16i + 16) of its 1 KB slot, so one instruction fills 1 KB of rows;
 // which global 16-byte chunk a lane fetches is XOR-swizzled by the row, and
