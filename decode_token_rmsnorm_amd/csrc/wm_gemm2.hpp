@@ -29,7 +29,7 @@ constexpr int G2M = 256, G2N = 256;
 constexpr int kComputeUnits = 256;    // MI355X
 constexpr int G2CP = G2N + 4;         // C tile pitch (floats)
 constexpr int G2CT = 128 * G2CP * 4;  // staged half C tile, bytes
-constexpr int G2KB = 64, G2ST = 4;    // k-tile bytes per row, LDS stages
+constexpr int G2KB = 128, G2ST = 2;  // k-tile bytes per row, LDS stages
 constexpr int g2_smem(int kb, int st) {
   return (st * (G2M + G2N) * kb > G2CT + 512) ? st * (G2M + G2N) * kb : G2CT + 512;
 }
