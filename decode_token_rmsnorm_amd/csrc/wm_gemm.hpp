@@ -100,6 +100,7 @@ template <typename T> struct LoadGateUp {
 // together.  Output widths are multiples of 64, so a lane's CPL columns are
 // either all inside the output or all outside.
 constexpr int ER = 8;    // rows per wave per step (epilogues with RoPE tables)
+constexpr int ERS = 16;  // rows per wave per step (SwiGLU epilogue)
 constexpr int ERR = 16;  // rows per wave per step (residual epilogue)
 
 template <int CPL> struct VecF;
@@ -321,11 +322,11 @@ __device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, in
   fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
   const int f0 = n0 / 2 + OPL * lane;
   if (f0 >= e.F) return;  // no __syncthreads below
-  // ER rows per wave and step: every LDS read of the step before any use
-  for (int rb = wave * ER; rb < nrows; rb += nwaves() * ER) {
-    float gt[ER][OPL], up[ER][OPL], rs[ER];
+  // ERS rows per wave and step: every LDS read of the step before any use
+  for (int rb = wave * ERS; rb < nrows; rb += nwaves() * ERS) {
+    float gt[ERS][OPL], up[ERS][OPL], rs[ERS];
 #pragma unroll
-    for (int u = 0; u < ER; ++u) {
+    for (int u = 0; u < ERS; ++u) {
       const int rl = rb + u < nrows ? rb + u : nrows - 1;
       rs[u] = rowbuf[rl];
       const float *row = Cs + rl * pitch + OPL * lane;
@@ -336,7 +337,7 @@ __device__ __forceinline__ void run_epi(const EpiSwiGLU<T> &e, int z, int m0, in
       }
     }
 #pragma unroll
-    for (int u = 0; u < ER; ++u) {
+    for (int u = 0; u < ERS; ++u) {
       const int r = m0 + rb + u;
       float y[OPL];
 #pragma unroll
