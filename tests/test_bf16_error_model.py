@@ -1,54 +1,137 @@
-"""How far exact bf16 operand rounding alone moves the full-depth stack from the
-exact (float64) definition — the basis of TOL_BF16_DEEP in the GPU tests.
+"""The bf16 error model (tests/bf16_error_model.py): pinned to the oracle, and
+the rounding floors it measures at the bf16 test shapes.
 
-For the 16- and 28-layer bf16 workloads, rounding every matrix-product operand
-and stored state to bf16 (and nothing else) already moves the keys by more
-than 2e-2 max-abs-relative, so no bf16 implementation can meet 2e-2 there
-against the exact oracle; the full-depth parity tests therefore use
-TOL_BF16_DEEP = 1e-1, about twice the error measured here. At 4 layers the
-same rounding stays below 2e-2, and the reduced-depth bf16 tests keep 2e-2.
+With no rounding the model is the WhiteMatter definition, so it must equal the
+oracle on group steps at positions > 0 against a filled cache (both pool
+paths), on cyclic passes, on the vanilla model and on the feedback-free
+variant.  With the rounding points of the HIP path switched on, its distance
+from the exact result is the floor that any bf16 implementation rounding at
+those points reaches.  At every full-depth shape, and already at 4 layers once
+a few positions feed back through the cache, that floor lies above 2e-2
+max-abs-relative, so the bf16 GPU tests compute the floor of the very rows
+they compare and hold the GPU to max(2e-2, FLOOR_FACTOR x floor)
+(tests/test_gpu_parity.py).  The attribution test names the rounding point
+that dominates: the bf16 operand of the normalised-input products, which a
+bf16 matrix-core implementation cannot avoid.  test_floor_factor measures how
+far one bf16 implementation's error can exceed another's on the same rows,
+which sets FLOOR_FACTOR.
 """
 import numpy as np
 import pytest
 
 import oracle as O
-from tests.bf16_error_model import ROUNDING_POINTS, position0
+from tests import bf16_error_model as EM
 from tests.helpers import max_abs_rel
-from wm_inputs import WORKLOADS, make_tokens, make_weights
+from wm_inputs import WORKLOADS, make_cache, make_tokens, make_weights
 
 TOL_BF16 = 2e-2
-TOL_BF16_DEEP = 1e-1
 
 
-def _case(name, L=None, rows=32):
-    w = WORKLOADS[name].replace(B=1)
-    if L is not None:
-        w = w.replace(L=L, k=min(w.k, L))
+def _step_case(name, B, M, s0, step, filled, **kw):
+    w = WORKLOADS[name].replace(B=B, **kw)
     W = make_weights(w, seed=0, gains="perturbed")
-    tok = make_tokens(w, seed=1, B=rows, T=1)[:, 0]
-    return w, W, tok
+    tokens = make_tokens(w, seed=1, B=B, T=w.T_max)
+    K, V = make_cache(w, B, filled=filled, seed=3)
+    bidx, pos = O.tokset_rows(B, M, s0, step)
+    return w, W, tokens, K, V, bidx, pos
 
 
-@pytest.mark.parametrize("name,L,rows", [("decode_d512", None, 32), ("small_prefill", 4, 32),
-                                         ("prefill_1p3b", None, 8)])
-def test_exact_bf16_rounding_error_bounds(name, L, rows):
-    w, W, tok = _case(name, L, rows)
-    lg0, K0 = position0(w, W, tok)
-    # with no rounding the model is the definition: agree with the oracle
+@pytest.mark.parametrize("many_rows", [False, True])
+@pytest.mark.parametrize("name,kw", [("small_prefill", dict(L=4, k=3, T_max=96)),
+                                     ("tiny_fp32", dict())])
+def test_step_without_rounding_is_the_oracle(name, kw, many_rows):
+    """A group step of 2 x 5 rows at positions 7, 20, ..., 59 against a
+    seeded non-zero cache: keys, values and logits equal the oracle's."""
+    w, W, tokens, K, V, bidx, pos = _step_case(name, 2, 5, 7, 13, 64, **kw)
+    Km, Vm, lg, _ = EM.step(w, W, tokens[bidx, pos], pos, bidx, K, V, many_rows=many_rows, want_logits=True)
+    ref = (K.astype(np.float64), V.astype(np.float64))
+    lo = O.step(O.Model(w, W), tokens, ref, bidx, pos, want_logits=True)
+    assert max_abs_rel(Km.transpose(1, 0, 2, 3), ref[0][:, bidx, :, pos]) < 1e-12
+    assert max_abs_rel(Vm.transpose(1, 0, 2, 3), ref[1][:, bidx, :, pos]) < 1e-12
+    assert max_abs_rel(lg, lo) < 1e-12
+
+
+def test_cyclic_pass_without_rounding_is_the_oracle():
+    w = WORKLOADS["small_prefill"].replace(L=3, k=2, B=2, T=24, T_max=24, g=5)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    c = (np.zeros((w.k, w.B, w.Hkv, w.T_max, w.d)), np.zeros((w.k, w.B, w.Hkv, w.T_max, w.d)))
+    ref = O.new_cache(w, w.B)
     M = O.Model(w, W)
-    cache = O.new_cache(w.replace(T_max=1), rows)
-    bidx, pos = np.arange(rows), np.zeros(rows, int)
-    lgo = O.step(M, tok[:, None], cache, bidx, pos, want_logits=True)
-    assert max_abs_rel(lg0, lgo) < 1e-12
-    assert max_abs_rel(K0, cache[0][:, :, :, 0]) < 1e-12
-    lg, K = position0(w, W, tok, ROUNDING_POINTS)
-    e_lg, e_k = max_abs_rel(lg, lg0), max_abs_rel(K, K0)
-    print(f"{name} L={w.L}: exact bf16 rounding -> logits {e_lg:.2e}, keys {e_k:.2e}")
-    if w.L >= 16:
-        assert e_k > TOL_BF16            # 2e-2 is out of reach at this depth
-        assert max(e_lg, e_k) < TOL_BF16_DEEP / 1.5
-    else:
-        assert max(e_lg, e_k) < TOL_BF16
+    for _ in range(2):
+        lg = EM.cyclic_pass(w, W, tokens, c, w.g, want_logits=True)
+        lo = O.cyclic_pass(M, tokens, ref, w.g, want_logits=True)
+        assert max_abs_rel(c[0], ref[0]) < 1e-12 and max_abs_rel(c[1], ref[1]) < 1e-12
+        assert max_abs_rel(lg, lo) < 1e-12
+
+
+def test_vanilla_model_without_rounding_is_the_oracle():
+    w = WORKLOADS["small_prefill"].replace(L=3, k=3, B=2, T=20, T_max=24)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+    K, V, lg = EM.vanilla_forward(w, W, tokens)
+    (Ko, Vo), lo = O.vanilla_forward(O.Model(w, W), tokens)
+    assert max_abs_rel(K, Ko[..., :w.T, :]) < 1e-12 and max_abs_rel(V, Vo[..., :w.T, :]) < 1e-12
+    assert max_abs_rel(lg, lo) < 1e-12
+    Kc, Vc = make_cache(w, w.B, filled=17, seed=3)
+    Kt, Vt, lt = EM.vanilla_decode_step(w, W, tokens[:, 17], 17, Kc, Vc)
+    ref = (Kc.astype(np.float64), Vc.astype(np.float64))
+    lo = O.vanilla_decode_step(O.Model(w, W), tokens[:, 17], 17, ref)
+    assert max_abs_rel(Kt, ref[0][:, :, :, 17]) < 1e-12 and max_abs_rel(Vt, ref[1][:, :, :, 17]) < 1e-12
+    assert max_abs_rel(lt, lo) < 1e-12
+
+
+def test_rounding_floor_at_4_layers_with_cache_feedback():
+    """Exact AR over 8 positions of a 4-layer stack at D = 512 (the shape of a
+    reduced-depth GPU test): with every rounding point the keys and values
+    move by more than 2e-2 from the exact result, although each point alone
+    stays near 1e-2.  At position 0 alone (no cache feedback) they stay below
+    2e-2."""
+    w = WORKLOADS["small_prefill"].replace(B=2, L=4, k=4, T=8, T_max=8)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1)
+
+    def run(rnd, T):
+        c = (np.zeros((w.k, w.B, w.Hkv, T, w.d)), np.zeros((w.k, w.B, w.Hkv, T, w.d)))
+        lg = EM.cyclic_pass(w, W, tokens[:, :T], c, T, rnd, want_logits=True)
+        return c[0], c[1], lg
+
+    K0, V0, L0 = run((), 8)
+    K1, V1, L1 = run(EM.STEP_ROUNDING_POINTS, 8)
+    floor = max(max_abs_rel(K1, K0), max_abs_rel(V1, V0), max_abs_rel(L1, L0))
+    print(f"L4 D512, AR over 8 positions: rounding floor {floor:.2e}")
+    assert floor > TOL_BF16
+    K0, V0, L0 = run((), 1)
+    K1, V1, L1 = run(EM.STEP_ROUNDING_POINTS, 1)
+    floor0 = max(max_abs_rel(K1, K0), max_abs_rel(V1, V0), max_abs_rel(L1, L0))
+    print(f"position 0 only: {floor0:.2e}")
+    assert floor0 < TOL_BF16
+
+
+def test_rounding_floor_at_full_depth_and_its_attribution():
+    """The first group step of a 1.3B-scale sequence (28 layers, D = 1792,
+    16 of its 128 rows, zero cache): every rounding point of the HIP path
+    together moves the keys by more than 2e-2, and the bf16 operand of the
+    normalised-input products (hb) alone does too, while the pool's own
+    rounding points (router input and weights, mix operands, mixed channel)
+    stay well below it."""
+    w = WORKLOADS["prefill_1p3b"].replace(B=1)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1, B=1)
+    pos = np.arange(0, w.T, w.g)[::8]
+    zeros = np.zeros(len(pos), int)
+    Kc = np.zeros((w.k, 1, w.Hkv, w.T_max, w.d))
+
+    def err(rnd):
+        K, V, _, _ = EM.step(w, W, tokens[0, pos], pos, zeros, Kc, Kc, rnd)
+        return max(max_abs_rel(K, K0), max_abs_rel(V, V0))
+
+    K0, V0, _, _ = EM.step(w, W, tokens[0, pos], pos, zeros, Kc, Kc)
+    e_all, e_hb = err(EM.STEP_ROUNDING_POINTS), err(("hb",))
+    e_pool = err(("u", "wf", "mixw", "mixs", "mb"))
+    print(f"1.3B first group: all points {e_all:.2e}, hb alone {e_hb:.2e}, pool points {e_pool:.2e}")
+    assert e_all > TOL_BF16 and e_hb > TOL_BF16
+    assert e_pool < e_hb / 2
 
 
 def test_feedback_free_bf16_rounding_floor():
@@ -57,19 +140,57 @@ def test_feedback_free_bf16_rounding_floor():
     product-feeding tensors alone moves the cached keys by up to 1.6e-1 from
     the exact definition (a few tokens whose router outputs are small against
     their terms amplify the rounding of the router input), so 2e-2 is out of
-    reach for any bf16 implementation; the GPU test holds the variant to
-    TOL_FF_BF16 = 2.5e-1 against the oracle, about 1.5 times this floor."""
-    import oracle as O
-    from tests.bf16_error_model import FF_ROUNDING_POINTS, ff_forward
+    reach for any bf16 implementation there."""
     for B, T in ((2, 64), (3, 256)):
         w = WORKLOADS["small_prefill"].replace(L=4, k=4, B=B, T=T)
         W = make_weights(w, seed=0, gains="perturbed")
         tok = make_tokens(w, seed=1)
-        K0, V0, lg0 = ff_forward(w, W, tok)
+        K0, V0, lg0 = EM.ff_forward(w, W, tok)
         (Ko, Vo), lgo = O.ff_forward(O.Model(w, W), tok)
         assert max_abs_rel(K0, Ko[..., :T, :]) < 1e-12 and max_abs_rel(lg0, lgo) < 1e-12  # no rounding: the oracle
-        K1, V1, lg1 = ff_forward(w, W, tok, FF_ROUNDING_POINTS)
+        K1, V1, lg1 = EM.ff_forward(w, W, tok, EM.FF_ROUNDING_POINTS)
         ek, ev, el = max_abs_rel(K1, K0), max_abs_rel(V1, V0), max_abs_rel(lg1, lg0)
         print(f"feedback-free B{B} T{T}: exact bf16 rounding -> K {ek:.2e}, V {ev:.2e}, logits {el:.2e}")
-        assert max(ek, ev) > TOL_BF16                # 2e-2 is out of reach for bf16 here
-        assert max(ek, ev, el) < 2.5e-1 / 1.5
+        assert max(ek, ev) > TOL_BF16
+
+
+from tests.test_gpu_parity import FLOOR_FACTOR  # noqa: E402  (the factor the GPU tests apply to the floor)
+
+
+def test_floor_factor():
+    """How much one bf16 implementation's error can exceed another's on the
+    same rows.  A GPU that rounds the same tensors in a different float32
+    summation order makes its own, independent draw of the rounding errors;
+    so do runs of the error model whose rounded values are perturbed by
+    ~1e-6 first (bf16_error_model.jittered).  Over group steps of 16 sampled
+    rows of the small model at full depth (16 layers, a filled cache), the
+    error of one draw against the exact result stays below FLOOR_FACTOR times
+    the larger error of two other draws, with room to spare at the 99th
+    percentile; the GPU tests take their floor as the larger of two draws."""
+    import contextlib
+    w = WORKLOADS["small_prefill"].replace(B=1)
+    W = make_weights(w, seed=0, gains="perturbed")
+    tokens = make_tokens(w, seed=1, B=8)
+    K, V = make_cache(w, 8, filled=1500, seed=3)
+    ratios = []
+    for sub in range(6):
+        rng = np.random.default_rng(100 + sub)
+        pos = np.sort(rng.choice(1500, 16, replace=False))
+        bidx = rng.integers(0, 8, 16)
+        tok = tokens[bidx, pos]
+        K0, V0, l0, _ = EM.step(w, W, tok, pos, bidx, K, V, (), many_rows=True, want_logits=True)
+
+        def draw(seed):
+            with EM.jittered(seed) if seed is not None else contextlib.nullcontext():
+                K1, V1, l1, _ = EM.step(w, W, tok, pos, bidx, K, V, EM.STEP_ROUNDING_POINTS, many_rows=True,
+                                        want_logits=True)
+            return max(max_abs_rel(K1, K0), max_abs_rel(V1, V0), max_abs_rel(l1, l0))
+
+        d = [draw(None)] + [draw(s) for s in range(5)]
+        for i in range(len(d)):
+            others = [x for j, x in enumerate(d) if j != i]
+            ratios += [d[i] / max(a, b) for a in others for b in others if a is not b]
+    r = np.array(ratios)
+    print(f"one draw / larger of two others over {len(r)} ratios: max {r.max():.2f}, "
+          f"p99 {np.quantile(r, 0.99):.2f}")
+    assert r.max() < FLOOR_FACTOR and np.quantile(r, 0.99) < FLOOR_FACTOR / 1.3
