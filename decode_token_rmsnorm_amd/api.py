@@ -156,6 +156,19 @@ def decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits
     return logits
 
 
+def decode_step_static(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits=None, stream=None):
+    """wm_decode_step with the library's static scratch (no workspace, no
+    allocation inside the call): tokens [B] (int32, device) at position t."""
+    B = tokens.shape[0]
+    if logits is None:
+        logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)
+    cc = cache.c()
+    C.check("wm_decode_step_static", C.lib().wm_decode_step_static(ctypes.byref(model.cfg), ctypes.byref(model.w),
+                                                                   tokens.data_ptr(), t, ctypes.byref(cc),
+                                                                   logits.data_ptr(), _stream(stream)))
+    return logits
+
+
 def _chunked_prefill(fn: str, model: Model, tokens: torch.Tensor, chunk: int, cache: Cache, logits_mode: int,
                      logits, ws, stream):
     B, T = tokens.shape

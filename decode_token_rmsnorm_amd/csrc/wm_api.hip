@@ -10,6 +10,7 @@
 #include "wm_attn2.hpp"
 #include "wm_pool2.hpp"
 
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -619,6 +620,36 @@ static wm_status chunked_prefill_impl(bool vanilla, const wm_config *cfg, const 
   return WM_OK;
 }
 
+// ------------------------------------------------ allocation-free decode step
+// Scratch of wm_decode_step_static: a static device array, one copy per GPU
+// (each device holds it from the library's load until the process ends).  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address reaches a kernel.  No
+// kernel of the decode path reads a scratch element before writing it in the
+// same call, so nothing is cleared between calls.
+static __device__ __align__(256) unsigned char scratch[WM_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device.
+static wm_status scratch_address(void **out) {
+  int dev = -1;
+  WM_TRY(hipGetDevice(&dev));
+  WM_CHECK(dev >= 0 && dev < kMaxDevices, WM_ERR_ARG, "device index %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    WM_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    WM_CHECK(p != nullptr, WM_ERR_HIP, "hipGetSymbolAddress returned NULL for the static scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WM_OK;
+}
+
 }  // namespace wm
 
 using namespace wm;
@@ -718,6 +749,23 @@ wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_
   st = r.prep_router();
   if (st != WM_OK) return st;
   return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+}
+
+wm_status wm_decode_step_static(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
+                                const wm_cache *cache, float *logits, wm_stream stream) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cache && cache->k && cache->v && cache->B >= 1, WM_ERR_ARG, "cache, its pointers or B invalid");
+  WM_CHECK(t >= 0 && t < cfg->T_max, WM_ERR_RANGE, "t = %d outside [0, T_max = %d)", t, cfg->T_max);
+  WM_CHECK(tokens && logits && weights_ok(w, true), WM_ERR_ARG, "tokens, logits or a weight pointer is NULL");
+  const size_t need = ws_layout(*cfg, cache->B).total;
+  WM_CHECK(need <= (size_t)WM_STATIC_SCRATCH_BYTES, WM_ERR_WORKSPACE,
+           "a decode step of %d sequences needs %zu bytes of scratch; the static scratch holds %zu", cache->B, need,
+           (size_t)WM_STATIC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != WM_OK) return st;
+  return wm_decode_step(cfg, w, tokens, t, cache, logits, ws, need, stream);
 }
 
 wm_status wm_vanilla_prefill(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t T,

@@ -15,7 +15,8 @@
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless marked (host).
  *  - The caller owns and allocates every buffer: weights, caches, workspace,
- *    outputs. The library allocates no device memory.
+ *    outputs. The library allocates no device memory (the one exception,
+ *    wm_decode_step_static's scratch, is a static array of its code object).
  *  - Compute calls are asynchronous on `stream` (a hipStream_t; NULL = the
  *    default stream). Arguments are validated on the host before anything is
  *    launched; on error nothing is launched or written, a negative wm_status
@@ -205,6 +206,25 @@ wm_status wm_cyclic_prefill_pass(const wm_config *cfg, const wm_weights *w, cons
 wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
                          const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
                          wm_stream stream);
+
+/* ---- allocation-free decode step ---------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * step as wm_decode_step (same arguments, kernels and results), with its
+ * scratch taken from a static device array of WM_STATIC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends, instead
+ * of a caller workspace.  The caller still owns the weights, the cache, the
+ * tokens and the logits.  Returns WM_ERR_WORKSPACE, launching nothing, when
+ * wm_workspace_bytes(cfg, cache->B) exceeds WM_STATIC_SCRATCH_BYTES (64 MiB:
+ * up to 128 sequences at the 1.3B shape L28 D1792 F4864, up to 256 at
+ * L16 D512 F1536).  Calls no
+ * allocating routine.  All calls on one GPU share its array, which keeps the
+ * last call's contents (no kernel reads an element before writing it in the
+ * same call); calls that overlap on one GPU (several streams or threads) race
+ * on it and must be serialised by the caller. */
+#define WM_STATIC_SCRATCH_BYTES (64u << 20)
+wm_status wm_decode_step_static(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
+                                const wm_cache *cache, float *logits, wm_stream stream);
 
 /* ---- the vanilla comparison model --------------------------------------
  * The decoder the pages measure WhiteMatter against (paperlayer.ai §3 and

@@ -25,7 +25,7 @@ def cfg_of(w, dtype=C.WM_BF16, **kw):
 
 def test_library_exports_every_declared_function():
     names = C.header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     assert set(names) <= exported, set(names) - exported
@@ -134,6 +134,28 @@ def test_entry_points_validate_before_launch():
                                 None) == -5
     # rope table: null output
     assert L.wm_rope_table(ctypes.byref(c), None, FAKE, None) == -1
+
+
+def test_static_decode_step_validates_before_launch():
+    """wm_decode_step_static checks its arguments, then refuses a step whose
+    scratch would exceed the static array (WM_STATIC_SCRATCH_BYTES = 64 MiB),
+    before it touches the device."""
+    L = C.lib()
+    W = _weights()
+    w = WORKLOADS["prefill_1p3b"]
+    c = cfg_of(w)
+    static_bytes = 64 << 20
+    assert L.wm_workspace_bytes(ctypes.byref(c), 128) <= static_bytes < L.wm_workspace_bytes(ctypes.byref(c), 129)
+    cache = C.WmCache(FAKE, FAKE, 129)
+    assert L.wm_decode_step_static(ctypes.byref(c), ctypes.byref(W), FAKE, 5, ctypes.byref(cache), FAKE, None) == -4
+    assert b"static scratch" in L.wm_last_error()
+    cache = C.WmCache(FAKE, FAKE, 64)
+    for t in (-1, w.T_max):
+        assert L.wm_decode_step_static(ctypes.byref(c), ctypes.byref(W), FAKE, t, ctypes.byref(cache), FAKE,
+                                       None) == -5
+    assert L.wm_decode_step_static(ctypes.byref(c), ctypes.byref(W), None, 5, ctypes.byref(cache), FAKE, None) == -1
+    assert L.wm_decode_step_static(ctypes.byref(c), ctypes.byref(W), FAKE, 5, ctypes.byref(cache), None, None) == -1
+    assert L.wm_decode_step_static(ctypes.byref(c), ctypes.byref(W), FAKE, 5, None, FAKE, None) == -1
 
 
 def test_vanilla_entry_points_validate_before_launch():
