@@ -59,6 +59,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def peak_reset():
+    """Start a peak-memory window (weights already on the device count)."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+
+def peak_gib():
+    """Peak device memory allocated through torch since peak_reset(): weights,
+    cache, workspace, tokens and logits (the library allocates nothing)."""
+    import torch
+    torch.cuda.synchronize()
+    return torch.cuda.max_memory_allocated() / 2 ** 30
+
+
 def profile(kinds_mask):
     from decode_token_rmsnorm_amd import _lib as C
     C.check("wm_profile_begin", C.lib().wm_profile_begin(kinds_mask))
@@ -85,6 +100,7 @@ def bench_prefill(steps, warmup):
     log(f"[prefill] weights generated in {time.time() - t0:.1f}s")
     model = wm.Model(w, W, "bf16")
     del W
+    peak_reset()
     tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
     cache = wm.new_cache(model, w.B)
     rows = wm.prefill_rows(w.B, w.T, w.g)
@@ -130,6 +146,7 @@ def bench_prefill(steps, warmup):
     res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
     # whole-pass MFMA fraction: algorithmic FLOP per pass / pass time
     res["cache_gib"] = 2 * cache.k.numel() * cache.k.element_size() / 2 ** 30
+    res["peak_memory_gib"] = peak_gib()
     flop_pass = pass_flops(w)
     res["pass_tflops"] = flop_pass / (wall / steps) / 1e12
     res["pass_flop"] = flop_pass
@@ -138,14 +155,33 @@ def bench_prefill(steps, warmup):
     return w, res
 
 
-def pass_flops(w):
-    """Algorithmic FLOP of one cyclic pass (strict-causal triangle counted once)."""
-    T, B, L, D, F, k, R = w.T, w.B, w.L, w.D, w.F, w.k, w.R
+def flops_per_token(w, kind="wm", keys=None, lm_head=True):
+    """Algorithmic forward FLOP of one token through the whole model (one
+    multiply-add = 2 FLOP): the L blocks (Q, O, gate/up, down products), the
+    K/V path (WhiteMatter: router, mix and per-channel K/V projections of
+    both branches; vanilla: every layer's own K/V projection), attention
+    (QK^T and PV) over `keys` keys in every layer, and the LM head.
+    keys=None: the average over a whole sequence of w.T positions, (T-1)/2
+    keys under WhiteMatter's strict mask and (T+1)/2 under vanilla's causal
+    one (the triangle counted once)."""
+    T, L, D, F, k, R = w.T, w.L, w.D, w.F, w.k, w.R
     qd, kvd = w.Hq * w.d, w.Hkv * w.d
-    per_tok = L * (2 * D * qd * 2 + 2 * D * 2 * F + 2 * F * D)      # Q, O, gate/up, down
-    per_tok += 2 * (2 * R * D * L * k) + 2 * (2 * k * L * D) + 2 * (2 * k * D * kvd)  # router, mix, K/V proj
-    attn = L * w.Hq * w.d * 4 * (T * (T - 1) / 2) / T                # QK^T + PV over s < i, per token
-    return B * T * (per_tok + attn)
+    f = L * (2 * D * qd * 2 + 2 * D * 2 * F + 2 * F * D)             # Q, O, gate/up, down
+    if kind == "wm":
+        f += 2 * (2 * R * D * L * k) + 2 * (2 * k * L * D) + 2 * (2 * k * D * kvd)  # router, mix, K/V proj
+        keys = (T - 1) / 2 if keys is None else keys
+    else:
+        f += L * 2 * (2 * D * kvd)                                    # per-layer K/V projections
+        keys = (T + 1) / 2 if keys is None else keys
+    f += L * w.Hq * w.d * 4 * keys
+    return f + (2 * D * w.V if lm_head else 0)
+
+
+def pass_flops(w):
+    """Algorithmic FLOP of one cyclic pass over the batch (strict-causal
+    triangle counted once; logits of the last position only, which the LM
+    head adds about 0.02% to, left out)."""
+    return w.B * w.T * flops_per_token(w, "wm", lm_head=False)
 
 
 def bench_decode(steps, warmup):
@@ -157,6 +193,7 @@ def bench_decode(steps, warmup):
     t = 2047
     W = make_weights(w, seed=0)
     model = wm.Model(w, W, "bf16")
+    peak_reset()
     K, V = make_cache_device(w, w.B, filled=t, seed=3)
     cache = wm.Cache(K, V)
     tok = torch.from_numpy(make_tokens(w, seed=1, B=w.B, T=1)[:, 0].copy()).cuda()
@@ -189,11 +226,101 @@ def bench_decode(steps, warmup):
     ach = kv_bytes / (ms_at / n_at * 1e-3) / 1e9
     return {"workload": "decode_d512: L16 D512 Hq8 Hkv4 d64 F1536 k16 p2 V32768 B64, t=2047 cached, bf16",
             "value": w.B * steps / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall / steps, "steps": steps,
+            "peak_memory_gib": peak_gib(), "cache_gib": 2 * K.numel() * K.element_size() / 2 ** 30,
             "kernels_avg_us": kern,
             "roofline": {"kernel": "attn (strict-causal channel attention, attn_few)", "bound": "hbm",
                          "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                          "traffic": profiled_traffic("decode_attn"),
                          "algorithmic_per_launch": f"{kv_bytes:.4e} B = 2*{w.B}*{w.Hkv}*{t}*{w.d}*2"}}
+
+
+def bench_small_prefill():
+    """The small half-cache model (L16 D512 8/4 x 64, F1536, k8, p2, V32768,
+    B8, T2048, cyclic g16): three passes from the zero cache, each timed with
+    events; the pass against the MFMA roofline of its algorithmic FLOP, and
+    per-kind kernel times from one further pass."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from decode_token_rmsnorm_amd import _lib as C
+    from wm_inputs import WORKLOADS, make_tokens, make_weights
+
+    w = WORKLOADS["small_prefill"]
+    model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    rows = wm.prefill_rows(w.B, w.T, w.g)
+    ws = model.workspace(rows)
+    logits = torch.empty(w.B, w.V, dtype=torch.float32, device="cuda")
+    # untimed: one pass on a scratch cache (first launches, code loading)
+    scratch = wm.new_cache(model, w.B)
+    wm.cyclic_prefill_pass(model, tok, w.g, scratch, 1, logits, ws)
+    del scratch
+    cache = wm.new_cache(model, w.B)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.passes)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        wm.cyclic_prefill_pass(model, tok, w.g, cache, 1, logits, ws)
+        b.record()
+    torch.cuda.synchronize()
+    assert torch.isfinite(logits).all(), "non-finite logits"
+    per_pass = [a.elapsed_time(b) for a, b in evs]
+    profile((1 << len(C.KINDS)) - 1)
+    wm.cyclic_prefill_pass(model, tok, w.g, cache, 1, logits, ws)
+    torch.cuda.synchronize()
+    kern = {k: {"launches": c, "avg_us": 1e3 * m / c, "per_pass_us": 1e3 * m} for k, (c, m) in profile_read().items()}
+    flop = pass_flops(w)
+    best = min(per_pass)
+    ach = flop / (best * 1e-3) / 1e12
+    del cache, ws, model
+    torch.cuda.empty_cache()
+    return {"workload": "small_prefill: L16 D512 Hq8 Hkv4 d64 F1536 k8 p2 V32768, B8 T2048, cyclic g16, 3 passes, "
+                        "bf16",
+            "per_pass_ms": per_pass, "value": w.B * w.T / (best * 1e-3), "unit": "tokens/s/pass",
+            "rows_per_group_step": rows,
+            "roofline": {"kernel": "whole pass (all launches of a cyclic pass)", "bound": "mfma", "achieved": ach,
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                         "traffic": None,
+                         "algorithmic_per_launch": f"{flop:.4e} FLOP per pass (B*T*{flops_per_token(w, 'wm', lm_head=False):.4e})"},
+            "kernels_per_pass_us": kern}
+
+
+def bench_decode_1p3b(steps=20):
+    """Decode at the 1.3B-scale shape (L28 D1792 14/2 x 128, F4864, B64,
+    t = 2047 cached positions of seeded keys/values), WhiteMatter half cache
+    (k = 14) against the vanilla model (k = L = 28) on the same kernels:
+    tokens/s and peak device memory, beside the pages' 1.3B-scale batch-64
+    decode figures."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from wm_inputs import WORKLOADS, make_cache_device, make_tokens, make_weights
+
+    out = {}
+    t = 2047
+    base = WORKLOADS["prefill_1p3b"]
+    for name, w, step in (("whitematter", base, wm.decode_step), ("vanilla", base.replace(k=base.L),
+                                                                   wm.vanilla_decode_step)):
+        model = wm.Model(w, make_weights(w, seed=0), "bf16")
+        peak_reset()
+        K, V = make_cache_device(w, w.B, filled=t, seed=3)
+        cache = wm.Cache(K, V)
+        tok = torch.from_numpy(make_tokens(w, seed=1, B=w.B, T=1)[:, 0].copy()).cuda()
+        ws = model.workspace(w.B)
+        logits = torch.empty(w.B, w.V, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            step(model, tok, t, cache, logits, ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(model, tok, t, cache, logits, ws)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        out[name] = {"k": w.k, "value": w.B / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall,
+                     "peak_memory_gib": peak_gib(), "cache_gib": 2 * K.numel() * K.element_size() / 2 ** 30}
+        del model, K, V, cache, ws, logits, tok
+        torch.cuda.empty_cache()
+    out["workload"] = "prefill_1p3b shape decoding: L28 D1792 Hq14 Hkv2 d128 F4864 V32768, B64, t=2047 cached, bf16"
+    out["peak_memory_wm_over_vanilla"] = out["whitematter"]["peak_memory_gib"] / out["vanilla"]["peak_memory_gib"]
+    return out
 
 
 def bench_mix(calls, warmup):
@@ -256,6 +383,7 @@ def bench_vanilla(steps, decode_steps):
     w = w.replace(k=w.L)
     chunk = -(-w.T // w.g)
     model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    peak_reset()
     tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
     cache = wm.new_cache(model, w.B)
     ws = model.workspace(w.B * chunk)
@@ -272,7 +400,7 @@ def bench_vanilla(steps, decode_steps):
     out["prefill"] = {"workload": f"prefill_1p3b with per-layer K/V (k = L = {w.L}), B{w.B} T{w.T}, one causal pass "
                                   f"in steps of {chunk} positions, bf16",
                       "value": w.B * w.T / wall, "unit": "tokens/s", "ms_per_pass": 1e3 * wall, "passes": steps,
-                      "cache_gib": cache_bytes / 2 ** 30}
+                      "cache_gib": cache_bytes / 2 ** 30, "peak_memory_gib": peak_gib()}
     del cache, ws, model, tok
     torch.cuda.empty_cache()
 
@@ -280,6 +408,7 @@ def bench_vanilla(steps, decode_steps):
     assert w.k == w.L
     t = 2047
     model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    peak_reset()
     K, V = make_cache_device(w, w.B, filled=t, seed=3)
     cache = wm.Cache(K, V)
     tok = torch.from_numpy(make_tokens(w, seed=1, B=w.B, T=1)[:, 0].copy()).cuda()
@@ -294,7 +423,8 @@ def bench_vanilla(steps, decode_steps):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / decode_steps
     out["decode"] = {"workload": "decode_d512 with per-layer K/V (k = L = 16), B64, t=2047 cached, bf16",
-                     "value": w.B / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall, "steps": decode_steps}
+                     "value": w.B / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall, "steps": decode_steps,
+                     "peak_memory_gib": peak_gib(), "cache_gib": 2 * K.numel() * K.element_size() / 2 ** 30}
     del cache, ws, model, K, V
     torch.cuda.empty_cache()
     return out
@@ -414,9 +544,11 @@ def bench_sweep(tau=1e-4):
 
 
 def cpu_baseline(budget_s=10.0):
-    """The float64 oracle on a bounded sample of the prefill workload: the first
-    group step (q=0, 128 positions) of sequences 0, 1, ... against the zero
-    cache, one sequence at a time until about `budget_s` seconds of CPU work."""
+    """The float64 oracle on a bounded sample of the prefill workload: the last
+    group step (q = 15: positions 15, 31, ..., 2047, whose attention spans on
+    average as many keys as a whole pass's) of sequences 0, 1, ..., against a
+    filled cache (seeded values at every position), one sequence at a time
+    until about `budget_s` seconds of CPU work."""
     import numpy as np
     import oracle as O
     from wm_inputs import WORKLOADS, make_tokens, make_weights
@@ -425,13 +557,16 @@ def cpu_baseline(budget_s=10.0):
         threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    from wm_inputs import make_cache
     w = WORKLOADS["prefill_1p3b"]
     M = O.Model(w, make_weights(w, seed=0))
     tokens = make_tokens(w, seed=1)
-    bidx, pos = O.tokset_rows(1, len(O.group_positions(w.T, w.g, 0)), 0, w.g)
+    q = w.g - 1
+    bidx, pos = O.tokset_rows(1, len(O.group_positions(w.T, w.g, q)), q, w.g)
+    K0, V0 = make_cache(w, 1, filled=w.T, seed=3)
     dt, nseq = 0.0, 0
     while dt < budget_s and nseq < w.B:
-        cache = O.new_cache(w.replace(T_max=w.T), 1)
+        cache = (K0.astype(np.float64), V0.astype(np.float64))
         t0 = time.perf_counter()
         O.step(M, tokens[nseq:nseq + 1], cache, bidx, pos, want_logits=False)
         dt += time.perf_counter() - t0
@@ -448,8 +583,8 @@ def cpu_baseline(budget_s=10.0):
     except Exception:
         blas = "unknown"
     return {"value": nseq * len(pos) / dt, "unit": "tokens/s/pass", "cores": threads, "kind": "oracle",
-            "sample": f"sequences 0..{nseq - 1}, group q=0 ({len(pos)} positions each) of the first pass, "
-                      f"float64 numpy, {dt:.1f}s",
+            "sample": f"sequences 0..{nseq - 1}, group step q={q} ({len(pos)} positions each, up to {w.T - 1} "
+                      f"keys) against a filled cache, float64 numpy, {dt:.1f}s",
             "cpu_model": cpu_model, "blas": blas}
 
 
@@ -491,7 +626,10 @@ def main():
     ap.add_argument("--skip-vanilla", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-variants", action="store_true")
-    ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep", "variants", "peaks"], default=None,
+    ap.add_argument("--skip-small", action="store_true")
+    ap.add_argument("--skip-decode-1p3b", action="store_true")
+    ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep", "variants", "peaks", "small",
+                                       "decode_1p3b", "cpu"], default=None,
                     help="profiling aid: run only this part and print its object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
@@ -513,7 +651,8 @@ def main():
     torch.cuda.set_device(0)
     if a.only:
         part = (bench_decode(a.decode_steps, 5) if a.only == "decode" else bench_mix(20, 3) if a.only == "mix"
-                else device_peaks() if a.only == "peaks"
+                else device_peaks() if a.only == "peaks" else bench_small_prefill() if a.only == "small"
+                else bench_decode_1p3b() if a.only == "decode_1p3b" else cpu_baseline() if a.only == "cpu"
                 else bench_vanilla(a.steps, a.decode_steps) if a.only == "vanilla"
                 else bench_variants(a.steps) if a.only == "variants" else bench_sweep())
         print(json.dumps({a.only: part}), flush=True)
@@ -524,6 +663,8 @@ def main():
     van = None if a.skip_vanilla else bench_vanilla(a.steps, a.decode_steps)
     sweep = None if a.skip_sweep else bench_sweep()
     variants = None if a.skip_variants else bench_variants(a.steps)
+    small = None if a.skip_small else bench_small_prefill()
+    dec13 = None if a.skip_decode_1p3b else bench_decode_1p3b()
     if van is not None:
         # the pages' comparison: WhiteMatter prefill as a share of vanilla's (one
         # vanilla pass against one, and against the workload's 3 passes:
@@ -531,6 +672,8 @@ def main():
         wm_pass = w.B * w.T / (pre["wall_s"] / a.steps)
         van["wm_prefill_per_pass_over_vanilla"] = wm_pass / van["prefill"]["value"]
         van["wm_prefill_3_passes_over_vanilla"] = wm_pass / 3 / van["prefill"]["value"]
+        van["prefill_peak_memory_gib"] = {"whitematter": pre["peak_memory_gib"],
+                                          "vanilla": van["prefill"]["peak_memory_gib"]}
         if dec is not None:
             van["wm_decode_over_vanilla"] = dec["value"] / van["decode"]["value"]
     peaks = device_peaks()
@@ -556,8 +699,11 @@ def main():
         "pass_mfma_frac_measured": pre["pass_tflops"] / peaks["bf16_mfma_tflops"],
         "device_peaks": peaks,
         "kernels_avg_us": pre["kernels"],
+        "peak_memory_gib": pre["peak_memory_gib"],
         "decode": dec,
         "mix_kv": mix,
+        "small_prefill": small,
+        "decode_1p3b": dec13,
         "vanilla": van,
         "schedule_sweep": sweep,
         "variants": variants,

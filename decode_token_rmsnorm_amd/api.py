@@ -98,10 +98,52 @@ def _ws(model, ws, rows):
     return model.workspace(rows) if ws is None else ws
 
 
+def _same_device(a: torch.device, b: torch.device) -> bool:
+    if a.type != b.type:
+        return False
+    if a.type != "cuda":
+        return True
+    cur = torch.cuda.current_device() if (a.index is None or b.index is None) else None
+    return (cur if a.index is None else a.index) == (cur if b.index is None else b.index)
+
+
+def check_tensor(name: str, t: torch.Tensor, dtype, device, shape=None) -> None:
+    """What the C ABI cannot see in a raw pointer: element type, layout,
+    device and (where given) shape. Raises before anything is launched."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not _same_device(t.device, torch.device(device)):
+        raise ValueError(f"{name} is on {t.device}, the model on {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def check_tokens(tokens: torch.Tensor, cache: "Cache", device, ndim: int) -> None:
+    """tokens: int32, contiguous, on the model's device, [B] (ndim 1) or [B, T]
+    (ndim 2) with B = the cache's sequence count."""
+    check_tensor("tokens", tokens, torch.int32, device)
+    if tokens.dim() != ndim or tokens.shape[0] != cache.B:
+        raise ValueError(f"tokens has shape {tuple(tokens.shape)}; expected {ndim} dims with "
+                         f"{cache.B} sequences (the cache's B)")
+
+
+def check_cache(model: "Model", cache: "Cache") -> None:
+    s = model.shape
+    shape = (s.k, cache.B, s.Hkv, s.T_max, s.d)
+    check_tensor("cache.k", cache.k, torch_dtype(model.dtype), model.device, shape)
+    check_tensor("cache.v", cache.v, torch_dtype(model.dtype), model.device, shape)
+
+
 def mix_kv(model: Model, states: torch.Tensor, B: int, M: int, s0: int, s_step: int, cache: Cache, ws=None,
            stream=None) -> None:
     """Pool + append of the state stack ``states`` [L, B*M, D] (rows b*M + m at
     position s0 + m*s_step) into ``cache``."""
+    check_tensor("states", states, torch_dtype(model.dtype), model.device, (model.shape.L, B * M, model.shape.D))
+    check_cache(model, cache)
     ws = _ws(model, ws, B * M)
     cc = cache.c()
     C.check("wm_mix_kv", C.lib().wm_mix_kv(ctypes.byref(model.cfg), ctypes.byref(model.w), states.data_ptr(),
@@ -113,6 +155,8 @@ def channel_attn(model: Model, layer: int, q: torch.Tensor, B: int, M: int, s0: 
                  out=None, ws=None, stream=None) -> torch.Tensor:
     """Strict-causal attention of consumer layer ``layer`` for q [B*M, Hq, d]."""
     s = model.shape
+    check_tensor("q", q, torch_dtype(model.dtype), model.device, (B * M, s.Hq, s.d))
+    check_cache(model, cache)
     if out is None:
         out = torch.empty(B * M, s.Hq * s.d, dtype=q.dtype, device=q.device)
     ws = _ws(model, ws, B * M)
@@ -130,6 +174,8 @@ def prefill_rows(B: int, T: int, g: int) -> int:
 def cyclic_prefill_pass(model: Model, tokens: torch.Tensor, g: int, cache: Cache, logits_mode: int = 0,
                         logits=None, ws=None, stream=None):
     """One cyclic Gauss-Seidel pass over tokens [B, T] (int32, device)."""
+    check_tokens(tokens, cache, model.device, 2)
+    check_cache(model, cache)
     B, T = tokens.shape
     if logits_mode and logits is None:
         shape = (B, model.shape.V) if logits_mode == 1 else (B, T, model.shape.V)
@@ -145,6 +191,8 @@ def cyclic_prefill_pass(model: Model, tokens: torch.Tensor, g: int, cache: Cache
 
 def decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits=None, ws=None, stream=None):
     """One decode step: tokens [B] (int32, device) at position t."""
+    check_tokens(tokens, cache, model.device, 1)
+    check_cache(model, cache)
     B = tokens.shape[0]
     if logits is None:
         logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)
@@ -159,6 +207,8 @@ def decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits
 def decode_step_static(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits=None, stream=None):
     """wm_decode_step with the library's static scratch (no workspace, no
     allocation inside the call): tokens [B] (int32, device) at position t."""
+    check_tokens(tokens, cache, model.device, 1)
+    check_cache(model, cache)
     B = tokens.shape[0]
     if logits is None:
         logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)
@@ -171,6 +221,8 @@ def decode_step_static(model: Model, tokens: torch.Tensor, t: int, cache: Cache,
 
 def _chunked_prefill(fn: str, model: Model, tokens: torch.Tensor, chunk: int, cache: Cache, logits_mode: int,
                      logits, ws, stream):
+    check_tokens(tokens, cache, model.device, 2)
+    check_cache(model, cache)
     B, T = tokens.shape
     if logits_mode and logits is None:
         shape = (B, model.shape.V) if logits_mode == 1 else (B, T, model.shape.V)
@@ -184,6 +236,8 @@ def _chunked_prefill(fn: str, model: Model, tokens: torch.Tensor, chunk: int, ca
 
 
 def _one_step(fn: str, model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits, ws, stream):
+    check_tokens(tokens, cache, model.device, 1)
+    check_cache(model, cache)
     B = tokens.shape[0]
     if logits is None:
         logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)
@@ -212,6 +266,8 @@ def vanilla_prefill(model: Model, tokens: torch.Tensor, chunk: int, cache: Cache
     """The vanilla comparison model (per-layer K/V, causal s <= i) over tokens
     [B, T] (int32, device) in steps of `chunk` consecutive positions; the model
     needs k = L (one cache slot per layer)."""
+    check_tokens(tokens, cache, model.device, 2)
+    check_cache(model, cache)
     B, T = tokens.shape
     if logits_mode and logits is None:
         shape = (B, model.shape.V) if logits_mode == 1 else (B, T, model.shape.V)
@@ -228,6 +284,8 @@ def vanilla_prefill(model: Model, tokens: torch.Tensor, chunk: int, cache: Cache
 def vanilla_decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits=None, ws=None,
                         stream=None):
     """One decode step of the vanilla comparison model at position t."""
+    check_tokens(tokens, cache, model.device, 1)
+    check_cache(model, cache)
     B = tokens.shape[0]
     if logits is None:
         logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)

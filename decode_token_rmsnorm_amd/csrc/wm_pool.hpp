@@ -180,21 +180,22 @@ __global__ __launch_bounds__(256) void router_input(const T *S, const float *rin
   }
 }
 
-// Row r = b*M + m reads token tokens[b*tstride + toff + m*tstep] (clamped to
-// [0, V)).  Writes h = E[tok] (fp32), S0 = E[tok], hb = E[tok] * gain, and the
-// row's sum of squares (one part).
+// Row r = b*M + m reads token tokens[b*tstride + toff + m*tstep].  Writes
+// h = E[tok] (fp32), S0 = E[tok], hb = E[tok] * gain, and the row's sum of
+// squares (one part).  A token id outside [0, V) reads nothing and makes the
+// row NaN, so the error shows in everything computed from it.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_rows(const int32_t *tokens, const T *E, const float *gain, float *h, T *hb,
                                                   T *S0, float *ss, int M, int tstride, int toff, int tstep, int V,
                                                   int D) {
   const int r = blockIdx.x, tid = threadIdx.x;
   const int b = r / M, m = r - b * M;
-  int tok = tokens[(int64_t)b * tstride + toff + (int64_t)m * tstep];
-  tok = min(max(tok, 0), V - 1);
+  const int tok = tokens[(int64_t)b * tstride + toff + (int64_t)m * tstep];
+  const bool valid = tok >= 0 && tok < V;
   float s = 0.f;
   for (int c = tid; c < D; c += 256) {
-    T e = E[(int64_t)tok * D + c];
-    float v = to_f(e);
+    const T e = valid ? E[(int64_t)tok * D + c] : from_f<T>(__builtin_nanf(""));
+    const float v = to_f(e);
     h[(int64_t)r * D + c] = v;
     S0[(int64_t)r * D + c] = e;
     hb[(int64_t)r * D + c] = from_f<T>(v * gain[c]);

@@ -188,7 +188,10 @@ wm_status wm_channel_attn(const wm_config *cfg, int32_t layer, const void *q, wm
  * L-layer stack against the cache as it stands when the group starts, then
  * the group's pooled K/V are written, so later groups of the same pass read
  * them. g = 1 is a Jacobi pass, g >= T is exact autoregressive execution.
- * tokens [B, T] int32 (ids < V). The cache must hold B = cache->B sequences
+ * tokens [B, T] int32, ids in [0, V): an id outside that range is not read
+ * from the embedding; its row becomes NaN, and so does everything computed
+ * from it (its cache entries, its logits, and the later positions of its
+ * sequence that attend to it). The cache must hold B = cache->B sequences
  * and T <= T_max.
  * logits_mode 0: none (logits may be NULL); 1: logits [B, V] float of
  * position T-1; 2: logits [B, T, V] float of every position. Logits of a
@@ -202,7 +205,9 @@ wm_status wm_cyclic_prefill_pass(const wm_config *cfg, const wm_weights *w, cons
  * channels are appended after its own layer stack): the token tokens[b] at
  * position t of every sequence b < cache->B attends to positions s < t,
  * then its K/V are written at slot t. logits [B, V] float. Requires
- * 0 <= t < T_max. Workspace: wm_workspace_bytes(cfg, B). */
+ * 0 <= t < T_max. tokens [B] int32 in [0, V); an id outside it makes that
+ * sequence's logits and appended entries NaN. Workspace:
+ * wm_workspace_bytes(cfg, B). */
 wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t t,
                          const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
                          wm_stream stream);

@@ -228,3 +228,49 @@ def test_peak_probes_validate_before_launch():
     assert st(FAKE, FAKE + 512, 1024) == -1 and b"overlap" in L.wm_last_error()
     assert L.wm_peak_mfma_bf16(1, None, None) == -1
     assert L.wm_peak_mfma_bf16(0, None, ctypes.byref(out)) == -2
+
+
+def test_binding_checks_tensors_before_calling():
+    """The Python binding rejects what a raw pointer cannot show: token ids of
+    another integer type (an int64 tensor read as int32 pairs), a
+    non-contiguous view, a CPU tensor, a sequence count other than the
+    cache's, and a cache of the wrong element type or shape."""
+    import torch
+
+    from decode_token_rmsnorm_amd import api
+
+    class _Cache:
+        def __init__(self, k, v):
+            self.k, self.v = k, v
+
+        @property
+        def B(self):
+            return self.k.shape[1]
+
+    class _Model:
+        shape = WORKLOADS["decode_d512"].replace(T_max=8)
+        dtype = "bf16"
+        device = torch.device("cpu")
+
+    m = _Model()
+    s = m.shape
+    good = torch.zeros((s.k, 3, s.Hkv, s.T_max, s.d), dtype=torch.bfloat16)
+    cache = _Cache(good, good.clone())
+    api.check_tokens(torch.zeros(3, dtype=torch.int32), cache, m.device, 1)
+    api.check_tokens(torch.zeros(3, 5, dtype=torch.int32), cache, m.device, 2)
+    api.check_cache(m, cache)
+    with pytest.raises(TypeError):
+        api.check_tokens(torch.zeros(3, dtype=torch.int64), cache, m.device, 1)
+    with pytest.raises(ValueError):
+        api.check_tokens(torch.zeros(5, 3, dtype=torch.int32).t(), cache, m.device, 2)
+    with pytest.raises(ValueError):
+        api.check_tokens(torch.zeros(4, dtype=torch.int32), cache, m.device, 1)
+    with pytest.raises(ValueError):
+        api.check_tokens(torch.zeros(3, 1, dtype=torch.int32), cache, m.device, 1)
+    with pytest.raises(TypeError):
+        api.check_cache(m, _Cache(good.float(), good.float()))
+    with pytest.raises(ValueError):
+        api.check_cache(m, _Cache(good[:, :, :, :4], good[:, :, :, :4]))
+    if torch.cuda.is_available():  # (a CPU tensor for a model on the GPU)
+        with pytest.raises(ValueError):
+            api.check_tensor("tokens", torch.zeros(3, dtype=torch.int32), torch.int32, torch.device("cuda"))

@@ -488,6 +488,32 @@ def test_decode_first_position(dtype):
     assert np.isnan(np_of(cache.k)[:, :, :, 1:]).all() and np.isnan(np_of(cache.v)[:, :, :, 1:]).all()
 
 
+def test_out_of_range_token_gives_nan_rows():
+    """A token id outside [0, V) is not read from the embedding: its
+    sequence's logits and appended entries come out NaN, and every other
+    sequence gets, bit for bit, what a run without the bad id gives it."""
+    w = WORKLOADS["decode_d512"].replace(B=4, T_max=64)
+    t = 20
+    print("decode step with ids V and -1", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    K, V = make_cache(w, w.B, filled=t, seed=3)
+    tokens = make_tokens(w, seed=1, B=w.B, T=1)[:, 0]
+    model = gpu_model(w, W)
+    good, bad_cache = wm.cache_from_host(model, K, V), wm.cache_from_host(model, K, V)
+    lg = wm.decode_step(model, torch.from_numpy(tokens).to(DEV), t, good)
+    bad = tokens.copy()
+    bad[1], bad[2] = w.V, -1
+    lb = wm.decode_step(model, torch.from_numpy(bad).to(DEV), t, bad_cache)
+    torch.cuda.synchronize()
+    for b in (1, 2):
+        assert torch.isnan(lb[b]).all()
+        assert torch.isnan(bad_cache.k[:, b, :, t]).all() and torch.isnan(bad_cache.v[:, b, :, t]).all()
+    ok = [0, 3]
+    assert torch.isfinite(lg).all() and torch.equal(lg[ok], lb[ok])
+    assert torch.equal(good.k[:, ok].view(torch.int16), bad_cache.k[:, ok].view(torch.int16))
+    assert torch.equal(good.v[:, ok].view(torch.int16), bad_cache.v[:, ok].view(torch.int16))
+
+
 # ---------------------------------------------------------------- bf16, short sequences
 
 @pytest.mark.parametrize("name,B,T,g", [("small_prefill", 2, 8, 8), ("prefill_1p3b", 1, 6, 6)])
