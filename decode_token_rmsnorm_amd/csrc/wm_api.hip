@@ -16,6 +16,15 @@
 
 namespace wm {
 
+// Group steps of at most this many rows run the layer stack's products with
+// one output row block per 16 rows (Q, O, down, LM head, the vanilla model's
+// K/V) on the few-row kernel: at 1024 rows it launches ~512 blocks where the
+// 128 x 128 kernel launches 32, and Q and O take 10.7 instead of 20.8 and
+// 18.9 us, down 24.8 instead of 33.6 (small model, D512).  The fused gate/up
+// product, 6x wider, stays on the 128 x 128 kernel above kFewRows rows (15.5
+// against 34 us there).
+constexpr int kFewStackRows = 1024;
+
 // ------------------------------------------------------------ launch timing
 struct ProfRec {
   int kind;
@@ -106,7 +115,7 @@ template <typename T> struct Run {
   int resid_bn(int M, int N) const { return big(M) ? g2_resid_bn(M, N, kComputeUnits) : GN; }
   // partial sums of squares per row written by a residual epilogue on M rows
   int parts(int M, int N) const {
-    if (M <= kFewRows) return few_parts(M, N);
+    if (M <= kFewStackRows) return few_parts(M, N);
     return (N + resid_bn(M, N) - 1) / resid_bn(M, N);
   }
   T *Kch(int ch) const { return (T *)cache->k + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
@@ -137,6 +146,14 @@ template <typename T> struct Run {
     } else {
       return hipErrorInvalidValue;
     }
+  }
+
+  // A product of the layer stack below the large-tile size: the few-row
+  // kernel up to kFewStackRows rows, otherwise the 128 x 128 tiled one.
+  template <class AL, class BL, class EP>
+  hipError_t gemm_s(const AL &al, const BL &bl, const EP &ep, int M, int N, int K) {
+    if (M <= kFewStackRows) return launch_few<T>(al, bl, ep, M, N, K, 1, s);
+    return launch_gemm<T>(al, bl, ep, M, N, K, 1, s);
   }
 
   // Few rows: the few-row kernel; otherwise the 128 x 128 tiled one.
@@ -441,7 +458,7 @@ template <typename T> struct Run {
         if (big(rows))
           WM_TRY(gemm2_rows(hb, D, wq + (int64_t)l * QD * D, D, e, rows, QD, D));
         else
-          WM_TRY((gemm1(a, b, e, rows, QD, D, 1)));
+          WM_TRY((gemm_s(a, b, e, rows, QD, D)));
       }
       if (vanilla) {
         // K/V of the step's rows for layer l, written before the attention
@@ -457,7 +474,7 @@ template <typename T> struct Run {
             done = true;
           }
         }
-        if (!done) WM_TRY((gemm1(LoadRows<T>{hb, D, 0, nullptr}, BKVL<T>{wkl, wvl, D, hd}, e, rows, 2 * hd, D, 1)));
+        if (!done) WM_TRY((gemm_s(LoadRows<T>{hb, D, 0, nullptr}, BKVL<T>{wkl, wvl, D, hd}, e, rows, 2 * hd, D)));
       }
       if (ff) {
         wm_status st = ff_channel(l, S, ts);
@@ -477,7 +494,7 @@ template <typename T> struct Run {
         if (big(rows))
           WM_TRY(gemm2_resid(o, QD, wo + (int64_t)l * D * QD, QD, e, rows, D, QD));
         else
-          WM_TRY((gemm1(a, b, e, rows, D, QD, 1)));
+          WM_TRY((gemm_s(a, b, e, rows, D, QD)));
         nparts = parts(rows, D);
       }
       // act = silu(W_gate b) * (W_up b), b = RMSNorm(h)
@@ -499,7 +516,7 @@ template <typename T> struct Run {
           FGateUp<T> bf{wg + (int64_t)l * c.F * D, wu + (int64_t)l * c.F * D, D, c.F, 0};
           WM_TRY((launch_few<T>(a, bf, e, rows, 2 * c.F, D, 1, s)));
         } else if (!done) {
-          WM_TRY((gemm1(a, b, e, rows, 2 * c.F, D, 1)));
+          WM_TRY((launch_gemm<T>(a, b, e, rows, 2 * c.F, D, 1, s)));
         }
       }
       // h += W_down act; next state, next norm operand
@@ -513,7 +530,7 @@ template <typename T> struct Run {
         if (big(rows))
           WM_TRY(gemm2_resid(act, c.F, wd + (int64_t)l * D * c.F, c.F, e, rows, D, c.F));
         else
-          WM_TRY((gemm1(a, b, e, rows, D, c.F, 1)));
+          WM_TRY((gemm_s(a, b, e, rows, D, c.F)));
       }
     }
     if (!vanilla && !ff) {
@@ -530,7 +547,7 @@ template <typename T> struct Run {
       BRows<T> b{LoadRows<T>{(const T *)w->lm_head, D, 0, nullptr}};
       EpiStoreF32 e{logits, c.V, 0, rout, ss, rin, nparts, invD, c.eps};
       ProfScope prof(WM_K_LMHEAD, s);
-      WM_TRY((gemm1(a, b, e, n, c.V, D, 1)));
+      WM_TRY((gemm_s(a, b, e, n, c.V, D)));
     }
     return WM_OK;
   }
