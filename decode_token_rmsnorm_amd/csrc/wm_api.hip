@@ -183,8 +183,11 @@ template <typename T> struct Run {
     if (kmax > c.T_max) kmax = c.T_max;
     const int kt = few ? 32 : AKT;
     const int ntile = (int)((kmax + kt - 1) / kt);
-    // waves in flight; attn_few keeps at least 4 tiles per wave
-    const int64_t target = large ? 2048 : few ? 1024 : 4096;
+    // waves in flight; attn_few keeps at least 4 tiles per wave.  (Many-row
+    // steps: 1024 waves; with 2048 the small model's 1024-row group steps
+    // took 8 key splits and a combine, 25.1 against 23.4 us per layer-step;
+    // with 512, 30.4.  The 1.3B steps reach 1024 waves without splitting.)
+    const int64_t target = large ? 1024 : few ? 1024 : 4096;
     int ns = 1;
     while ((int64_t)blocks * nw * ns < target && ns * 2 <= ACS && ntile / (ns * 2 * (few ? few_nw : 1)) >= (few ? 4 : 2) &&
            (int64_t)(ns * 2) * rows <= part_rows_cap(rows_cap))
