@@ -125,12 +125,20 @@ template <typename T> struct Run {
   // the compute units at the 1.3B shapes): 8-tile M-bands, about 1% faster
   // there than the 4-tile bands the five-round gate/up product runs best with.
   static constexpr int kOneRoundMap = 4;
+// Wave arrangement of the large-tile products (G2Shape): the gate/up product
+  // on 2 x 4 waves of 128 x 64 and the residual products on 224-column tiles
+  // of 8 x 1 waves of 32 x 224 (two waves per SIMD: gate/up 309.6 -> 279.3
+  // us, O 85.5 -> 82.2, down 170.3 -> 163.3 on the 1.3B shapes, A/B on one
+  // GPU each); Q, the router and the K/V projection stay on 2 x 2 waves of
+  // 128 x 128 (their epilogues spill under the two-wave register limit: Q
+  // 88.2 -> 93.5 us).
+  static constexpr int kGUShape = 2, kQShape = 0, kR224Shape = 3, kR256Shape = 0, kPoolShape = 0;
   // A [M, K] (row-major, lda) times B [N, K]^T on the large-tile kernel.
   template <class EP>
   hipError_t gemm2_rows(const T *A, int64_t lda, const T *B, int64_t ldb, const EP &ep, int M, int N, int K) {
     if constexpr (kBig) {
-      return launch_gemm2<G2KB, G2ST, kOneRoundMap>(PRows<T>{A, lda, 0, M}, PBRows<T>{PRows<T>{B, ldb, 0, N}}, ep, M,
-                                                    N, K, 1, s);
+      return launch_gemm2<G2KB, G2ST, kOneRoundMap, kQShape>(PRows<T>{A, lda, 0, M}, PBRows<T>{PRows<T>{B, ldb, 0, N}},
+                                                             ep, M, N, K, 1, s);
     } else {
       return hipErrorInvalidValue;
     }
@@ -141,8 +149,9 @@ template <typename T> struct Run {
     if constexpr (kBig) {
       const PRows<T> a{A, lda, 0, M};
       const PBRows<T> b{PRows<T>{B, ldb, 0, N}};
-      if (resid_bn(M, N) == G2Shape<1>::BN) return launch_gemm2<G2KB, G2ST, kOneRoundMap, 1>(a, b, ep, M, N, K, 1, s);
-      return launch_gemm2<G2KB, G2ST, kOneRoundMap>(a, b, ep, M, N, K, 1, s);
+      if (resid_bn(M, N) == G2Shape<1>::BN)
+        return launch_gemm2<G2KB, G2ST, kOneRoundMap, kR224Shape>(a, b, ep, M, N, K, 1, s);
+      return launch_gemm2<G2KB, G2ST, kOneRoundMap, kR256Shape>(a, b, ep, M, N, K, 1, s);
     } else {
       return hipErrorInvalidValue;
     }
@@ -343,7 +352,7 @@ template <typename T> struct Run {
         if (g2) {
           PRows<T> a2{at<T>(lay.u), RD, Kz, rows};
           PBRows<T> b2{PRows<T>{at<T>(lay.wf), RD, Kz, N}};
-          WM_TRY((launch_gemm2(a2, b2, re, rows, N, (int)Kz, Zs, s)));
+          WM_TRY((launch_gemm2<G2KB, G2ST, 2, kPoolShape>(a2, b2, re, rows, N, (int)Kz, Zs, s)));
           done = true;
         }
       }
@@ -373,7 +382,7 @@ template <typename T> struct Run {
       if (big(rows)) {
         PRows<T> a2{at<T>(lay.mb), c.D, (int64_t)rows * c.D, rows};
         PKV<T> b2{(const T *)w->wk, (const T *)w->wv, c.D, (int64_t)c.Hkv * c.d * c.D, c.k, c.Hkv * c.d};
-        WM_TRY((launch_gemm2(a2, b2, pe, rows, c.Hkv * c.d, c.D, 2 * c.k, s)));
+        WM_TRY((launch_gemm2<G2KB, G2ST, 2, kPoolShape>(a2, b2, pe, rows, c.Hkv * c.d, c.D, 2 * c.k, s)));
         return WM_OK;
       }
     }
@@ -511,7 +520,7 @@ template <typename T> struct Run {
           if (big(rows)) {
             PRows<T> a2{hb, D, 0, rows};
             PGateUp<T> b2{wg + (int64_t)l * c.F * D, wu + (int64_t)l * c.F * D, D, c.F};
-            WM_TRY((launch_gemm2(a2, b2, e, rows, 2 * c.F, D, 1, s)));
+            WM_TRY((launch_gemm2<G2KB, G2ST, 2, kGUShape>(a2, b2, e, rows, 2 * c.F, D, 1, s)));
             done = true;
           }
         }

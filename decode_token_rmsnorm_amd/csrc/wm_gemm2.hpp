@@ -1,7 +1,8 @@
 // wm_gemm2.hpp — large-tile bf16 GEMM  C[M, N] = A[M, K] * B[N, K]^T  for the
 // big projections (rows >= a few thousand).
 //
-// Block tile 256 x 256, 256 threads = 4 wave64s in a 2 x 2 grid; each wave
+// Block tile 256 x 256, 256 threads = 4 wave64s in a 2 x 2 grid (or 512 threads =
+// 8 waves, two per SIMD: G2Shape below); each wave
 // owns a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 tiles (256 fp32
 // accumulators per lane); or 256 x 224 with the waves stacked along M, 64 x
 // 224 each (2 x 7 MFMA tiles, G2Shape below).  Both operands are copied global -> LDS by the
@@ -131,43 +132,49 @@ __device__ __forceinline__ void g2_tile(int b, int nM, int nN, int &tm, int &tn,
 // (4 x 4 MFMA tiles), 256 columns. SH 1: 4 x 1 waves of 64 x 224 (2 x 7 MFMA
 // tiles), 224 columns: a 1792-column product then has 8 column tiles, and
 // 8192 rows give 256 blocks, one per compute unit, where 256 columns give 224.
+// SH 2: 2 x 4 waves of 128 x 64 (4 x 2 MFMA tiles), 256 columns, and SH 3:
+// 8 x 1 waves of 32 x 224 (1 x 7 MFMA tiles), 224 columns: two waves per SIMD
+// with 128 or 112 accumulators each, so one wave's LDS reads and DMA waits
+// overlap the other's MFMAs.
 template <int SH> struct G2Shape {
-  static constexpr int WN = SH ? 1 : 2;  // waves along N
-  static constexpr int TI = SH ? 2 : 4;  // 32-row MFMA tiles per wave
-  static constexpr int TJ = SH ? 7 : 4;  // 32-column MFMA tiles per wave
+  static constexpr int NW = SH >= 2 ? 8 : 4;                               // waves per block
+  static constexpr int WN = SH == 1 || SH == 3 ? 1 : SH == 2 ? 4 : 2;      // waves along N
+  static constexpr int TI = SH == 1 ? 2 : SH == 3 ? 1 : 4;                 // 32-row MFMA tiles per wave
+  static constexpr int TJ = SH == 1 || SH == 3 ? 7 : SH == 2 ? 2 : 4;      // 32-column MFMA tiles per wave
   static constexpr int BN = 32 * TJ * WN;
 };
 
 template <int KB, int ST, int MAP, int SH, class AP, class BP, class EP>
-__global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, int N, int K, int nM, int nN) {
+__global__ __launch_bounds__(64 * G2Shape<SH>::NW) void gemm2_kernel(AP ap, BP bp, EP ep, int M, int N, int K, int nM,
+                                                                     int nN) {
   using S = G2Shape<SH>;
-  constexpr int TI = S::TI, TJ = S::TJ, BN = S::BN;
+  constexpr int NW = S::NW, TI = S::TI, TJ = S::TJ, BN = S::BN;
   constexpr int STAGE = (G2M + BN) * KB;
   constexpr int RPI = 1024 / KB;          // rows per DMA instruction
-  constexpr int NI = G2M / RPI / 4;       // A DMA instructions per wave
+  constexpr int NI = G2M / RPI / NW;      // A DMA instructions per wave
   constexpr int NBT = BN / RPI;           // B DMA instructions per block
-  constexpr int NIB = (NBT + 3) / 4;      // B DMA slots per wave
-  constexpr int NBF = NBT - 4 * (NIB - 1);  // waves [0, NBF) fill all NIB slots
+  constexpr int NIB = (NBT + NW - 1) / NW;     // B DMA slots per wave
+  constexpr int NBF = NBT - NW * (NIB - 1);  // waves [0, NBF) fill all NIB slots
   constexpr int PI = NI + NIB;            // DMA instructions per wave per k-tile (waves < NBF)
-  constexpr int PI1 = NBF == 4 ? PI : PI - 1;  // (waves >= NBF)
+  constexpr int PI1 = NBF == NW ? PI : PI - 1;  // (waves >= NBF)
   constexpr int KS = KB / 32;             // 16-deep MFMA steps per k-tile
-  static_assert(BN % RPI == 0 && TI * 32 * (4 / S::WN) == G2M, "tile shape");
+  static_assert(BN % RPI == 0 && TI * 32 * (NW / S::WN) == G2M && G2M % (RPI * NW) == 0, "tile shape");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[g2_smem(KB, ST)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / S::WN, wn = wave % S::WN;
-  const bool bfull = NBF == 4 || wave < NBF;
+  const bool bfull = NBF == NW || wave < NBF;
   int tm, tn, z;
   g2_tile<MAP>(blockIdx.x, nM, nN, tm, tn, z);
   const int m0 = tm * G2M, n0 = tn * BN;
   const int nk = K * 2 / KB;
 
   // This thread's DMA sources: A rows (wave*NI + j)*RPI + lane/(KB/16), B row
-  // blocks wave*NIB + j (256 columns) or 4*j + wave (224 columns, the last slot
-  // of waves >= NBF unused), chunk chosen so that LDS slot (row,
+  // blocks wave*NIB + j (256 columns) or NW*j + wave (224 columns, the last
+  // slot of waves >= NBF unused), chunk chosen so that LDS slot (row,
   // lane % (KB/16)) holds the swizzled chunk (the swizzle is an XOR, its own
   // inverse).
-  auto bblk = [&](int j) { return SH ? 4 * j + wave : wave * NIB + j; };
+  auto bblk = [&](int j) { return BN == 224 ? NW * j + wave : wave * NIB + j; };
   const char *pa[NI], *pb[NIB];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
@@ -245,14 +252,17 @@ __global__ __launch_bounds__(256) void gemm2_kernel(AP ap, BP bp, EP ep, int M, 
   // Fragment reads spread over the MFMAs (2 : 1 where there are enough
   // MFMAs), so LDS latency hides under them.
   auto interleave = [&]() {
-    constexpr int NR = TI + TJ, N2 = TI * TJ - NR;  // reads; groups with 2 MFMAs
+    // NR reads among NMF MFMAs: N2 groups of 2 MFMAs + 1 read, then N1 of 1 + 1
+    // (with fewer MFMAs than reads the last reads are left to the compiler)
+    constexpr int NR = TI + TJ, NMF = TI * TJ;
+    constexpr int N2 = NMF > NR ? NMF - NR : 0, N1 = NMF > NR ? NR - N2 : NMF;
 #pragma unroll
     for (int g = 0; g < N2; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
 #pragma unroll
-    for (int g = N2; g < NR; ++g) {
+    for (int g = 0; g < N1; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -325,8 +335,8 @@ hipError_t launch_gemm2(const AP &ap, const BP &bp, const EP &ep, int M, int N, 
   if (M <= 0 || N <= 0) return hipSuccess;
   constexpr int BN = G2Shape<SH>::BN;
   const int nM = (M + G2M - 1) / G2M, nN = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm2_kernel<KB, ST, MAP, SH, AP, BP, EP>), dim3(nM * nN * Z), dim3(256), 0, s, ap, bp, ep, M,
-                     N, K, nM, nN);
+  hipLaunchKernelGGL((gemm2_kernel<KB, ST, MAP, SH, AP, BP, EP>), dim3(nM * nN * Z), dim3(64 * G2Shape<SH>::NW), 0, s,
+                     ap, bp, ep, M, N, K, nM, nN);
   return hipGetLastError();
 }
 
