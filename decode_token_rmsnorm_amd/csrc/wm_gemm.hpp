@@ -207,9 +207,15 @@ template <typename T> struct EpiQ {
   RowPos rp;
 };
 
+// Rows per wave per step of the q epilogue: 4, so that it fits the
+// two-waves-per-SIMD register budget of the 8-wave Q product (with 8 it
+// spilled 55 registers there; on 4 waves 4 and 8 rows measure the same).
+constexpr int ERQ = 4;
+
 template <typename T, int CPL>
 __device__ __forceinline__ void run_epi(const EpiQ<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
                                         int nrows, int M, int N, float *rowbuf) {
+  constexpr int ER = ERQ;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   fill_rowbuf_parts(rowbuf, e.ss, nullptr, e.nparts, e.invD, e.eps, m0, nrows, M);
   const int c0 = n0 + CPL * lane;
@@ -402,6 +408,7 @@ template <typename T> struct EpiKV {
 template <typename T, int CPL>
 __device__ __forceinline__ void run_epi(const EpiKV<T> &e, int z, int m0, int n0, const float *Cs, int pitch,
                                         int nrows, int M, int N, float *rowbuf) {
+  constexpr int ER = ERQ;  // (4 rows per step: the 8-wave K/V projection's register budget)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int beta = z / e.k, j = z - beta * e.k;
   for (int rl = threadIdx.x; rl < nrows; rl += blockDim.x) {
