@@ -126,12 +126,14 @@ template <typename T> struct Run {
   // there than the 4-tile bands the five-round gate/up product runs best with.
   static constexpr int kOneRoundMap = 4;
   // Wave arrangement of the large-tile products (G2Shape): gate/up and Q on 2
-  // x 4 waves of 128 x 64 and the residual products on 224-column tiles of 8 x
-  // 1 waves of 32 x 224 (two waves per SIMD: gate/up 309.6 -> 279.3 us, O
-  // 85.5 -> 82.2, down 170.3 -> 163.3, Q 87 -> 71.5 with its epilogue at 4
-  // rows per step, on the 1.3B shapes; the pool's router and K/V projection
-  // 66 -> 54 and 173 -> 149 us on the mix-only workload; A/B on one GPU each).
-  static constexpr int kGUShape = 2, kQShape = 2, kR224Shape = 3, kR256Shape = 0, kPoolShape = 2;
+  // x 4 waves of 128 x 64 and the residual products on 224-column tiles of 4 x
+  // 2 waves of 64 x 112 on the 16x16x32 MFMA (two waves per SIMD: gate/up
+  // 309.6 -> 279.3 us, Q 87 -> 71.5 with its epilogue at 4 rows per step, on
+  // the 1.3B shapes; the pool's router and K/V projection 66 -> 54 and 173 ->
+  // 149 us on the mix-only workload; O 85.5 -> 79.1 -> 74.8 and down 170.3 ->
+  // 157.3 -> 144.1 us through 8 x 1 waves of 32 x 224 to the 4 x 2 waves,
+  // whose fragment reads are 31% fewer; A/B on one GPU each).
+  static constexpr int kGUShape = 2, kQShape = 2, kR224Shape = 4, kR256Shape = 0, kPoolShape = 2;
   // A [M, K] (row-major, lda) times B [N, K]^T on the large-tile kernel.
   template <class EP>
   hipError_t gemm2_rows(const T *A, int64_t lda, const T *B, int64_t ldb, const EP &ep, int M, int N, int K) {

@@ -4,8 +4,9 @@
 // Block tile 256 x 256, 256 threads = 4 wave64s in a 2 x 2 grid (or 512 threads =
 // 8 waves, two per SIMD: G2Shape below); each wave
 // owns a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 tiles (256 fp32
-// accumulators per lane); or 256 x 224 with the waves stacked along M, 64 x
-// 224 each (2 x 7 MFMA tiles, G2Shape below).  Both operands are copied global -> LDS by the
+// accumulators per lane); or 256 x 224, with wave sub-tiles of 64 x 224,
+// 32 x 224 or 64 x 112 (the last on 16x16x32 MFMA tiles; G2Shape below).
+// Both operands are copied global -> LDS by the
 // 16-byte LDS DMA (global_load_lds_dwordx4): lane i of a wave writes LDS bytes
 // [16i, 16i + 16) of its 1 KB slot, so one instruction fills 1 KB of rows;
 // which global 16-byte chunk a lane fetches is XOR-swizzled by the row, and
@@ -19,6 +20,9 @@
 // tile is staged through LDS in two 128-row halves for the same row-wise
 // epilogues as the 128 x 128 kernel (wm_gemm.hpp).
 #pragma once
+
+#include <type_traits>
+#include <utility>
 
 #include "wm_gemm.hpp"
 
@@ -135,20 +139,32 @@ __device__ __forceinline__ void g2_tile(int b, int nM, int nN, int &tm, int &tn,
 // SH 2: 2 x 4 waves of 128 x 64 (4 x 2 MFMA tiles), 256 columns, and SH 3:
 // 8 x 1 waves of 32 x 224 (1 x 7 MFMA tiles), 224 columns: two waves per SIMD
 // with 128 or 112 accumulators each, so one wave's LDS reads and DMA waits
-// overlap the other's MFMAs.
+// overlap the other's MFMAs.  SH 4: 4 x 2 waves of 64 x 112 on the 16x16x32
+// MFMA (4 x 7 tiles of 16 x 16), 224 columns: the same 112 accumulators as
+// SH 3, but a wave reads 176 instead of 256 fragment rows per k-step, which
+// matters because the 224-column kernel is bound by its LDS reads.
 template <int SH> struct G2Shape {
-  static constexpr int NW = SH >= 2 ? 8 : 4;                               // waves per block
-  static constexpr int WN = SH == 1 || SH == 3 ? 1 : SH == 2 ? 4 : 2;      // waves along N
-  static constexpr int TI = SH == 1 ? 2 : SH == 3 ? 1 : 4;                 // 32-row MFMA tiles per wave
-  static constexpr int TJ = SH == 1 || SH == 3 ? 7 : SH == 2 ? 2 : 4;      // 32-column MFMA tiles per wave
-  static constexpr int BN = 32 * TJ * WN;
+  static constexpr int NW = SH >= 2 ? 8 : 4;                                          // waves per block
+  static constexpr int MF = SH == 4 ? 16 : 32;                                        // MFMA tile edge
+  static constexpr int WN = SH == 1 || SH == 3 ? 1 : SH == 2 ? 4 : 2;                 // waves along N
+  static constexpr int TI = SH == 1 ? 2 : SH == 3 ? 1 : 4;                            // MF-row MFMA tiles per wave
+  static constexpr int TJ = SH == 1 || SH == 3 || SH == 4 ? 7 : SH == 2 ? 2 : 4;      // MF-column tiles per wave
+  static constexpr int BN = MF * TJ * WN;
 };
+
+// Scheduling groups: NR fragment reads spread evenly over NMF MFMAs.
+template <int NMF, int NR, int... G> __device__ __forceinline__ void g2_spread(std::integer_sequence<int, G...>) {
+  ((__builtin_amdgcn_sched_group_barrier(0x008, (G + 1) * NMF / NR - G * NMF / NR, 0),
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0)),
+   ...);
+}
 
 template <int KB, int ST, int MAP, int SH, class AP, class BP, class EP>
 __global__ __launch_bounds__(64 * G2Shape<SH>::NW) void gemm2_kernel(AP ap, BP bp, EP ep, int M, int N, int K, int nM,
                                                                      int nN) {
   using S = G2Shape<SH>;
-  constexpr int NW = S::NW, TI = S::TI, TJ = S::TJ, BN = S::BN;
+  constexpr int NW = S::NW, TI = S::TI, TJ = S::TJ, BN = S::BN, MF = S::MF;
+  using Acc = typename std::conditional<MF == 32, f32x16, f32x4>::type;
   constexpr int STAGE = (G2M + BN) * KB;
   constexpr int RPI = 1024 / KB;          // rows per DMA instruction
   constexpr int NI = G2M / RPI / NW;      // A DMA instructions per wave
@@ -157,8 +173,8 @@ __global__ __launch_bounds__(64 * G2Shape<SH>::NW) void gemm2_kernel(AP ap, BP b
   constexpr int NBF = NBT - NW * (NIB - 1);  // waves [0, NBF) fill all NIB slots
   constexpr int PI = NI + NIB;            // DMA instructions per wave per k-tile (waves < NBF)
   constexpr int PI1 = NBF == NW ? PI : PI - 1;  // (waves >= NBF)
-  constexpr int KS = KB / 32;             // 16-deep MFMA steps per k-tile
-  static_assert(BN % RPI == 0 && TI * 32 * (NW / S::WN) == G2M && G2M % (RPI * NW) == 0, "tile shape");
+  constexpr int KS = KB * MF / 1024;      // MFMA k-steps per k-tile (32 or 64 bytes deep)
+  static_assert(BN % RPI == 0 && TI * MF * (NW / S::WN) == G2M && G2M % (RPI * NW) == 0, "tile shape");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[g2_smem(KB, ST)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -197,23 +213,25 @@ __global__ __launch_bounds__(64 * G2Shape<SH>::NW) void gemm2_kernel(AP ap, BP b
     for (int j = NIB; j < NI; ++j) dma16(pa[j] + kt * KB, As + (wave * NI + j) * 1024);
   };
 
-  f32x16 acc[TI][TJ];
+  Acc acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = Acc{};
 
   // Fragments of k-step ks+1 are read from LDS while the MFMAs of step ks run.
+  // A 32x32x16 operand: lane row lane % 32, 16-byte k chunk lane / 32; a
+  // 16x16x32 operand: row lane % 16, chunk lane / 16.
   auto frags = [&](const unsigned char *As, const unsigned char *Bs, int ks, u32x4 *af, u32x4 *bfr) {
-    const int c = 2 * ks + (lane >> 5);
+    const int c = (64 / MF) * ks + lane / MF;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      int r = wm * TI * 32 + i * 32 + (lane & 31);
+      int r = wm * TI * MF + i * MF + lane % MF;
       af[i] = *(const u32x4 *)(As + r * KB + g2_swz<KB>(r, c) * 16);
     }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      int r = wn * TJ * 32 + j * 32 + (lane & 31);
+      int r = wn * TJ * MF + j * MF + lane % MF;
       bfr[j] = *(const u32x4 *)(Bs + r * KB + g2_swz<KB>(r, c) * 16);
     }
   };
@@ -245,9 +263,14 @@ __global__ __launch_bounds__(64 * G2Shape<SH>::NW) void gemm2_kernel(AP ap, BP b
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
-                                                            __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (MF == 32)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                              __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                              __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+      }
   };
   // Fragment reads spread over the MFMAs (2 : 1 where there are enough
   // MFMAs), so LDS latency hides under them.
@@ -255,16 +278,21 @@ __global__ __launch_bounds__(64 * G2Shape<SH>::NW) void gemm2_kernel(AP ap, BP b
     // NR reads among NMF MFMAs: N2 groups of 2 MFMAs + 1 read, then N1 of 1 + 1
     // (with fewer MFMAs than reads the last reads are left to the compiler)
     constexpr int NR = TI + TJ, NMF = TI * TJ;
-    constexpr int N2 = NMF > NR ? NMF - NR : 0, N1 = NMF > NR ? NR - N2 : NMF;
+    if constexpr (NMF > 2 * NR) {
+      // (more than two MFMAs per read: the reads spread evenly)
+      g2_spread<NMF, NR>(std::make_integer_sequence<int, NR>{});
+    } else {
+      constexpr int N2 = NMF > NR ? NMF - NR : 0, N1 = NMF > NR ? NR - N2 : NMF;
 #pragma unroll
-    for (int g = 0; g < N2; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
+      for (int g = 0; g < N2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
 #pragma unroll
-    for (int g = 0; g < N1; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int g = 0; g < N1; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
   };
 
@@ -305,21 +333,29 @@ __global__ __launch_bounds__(64 * G2Shape<SH>::NW) void gemm2_kernel(AP ap, BP b
   __syncthreads();
 
   // epilogue in two 128-row halves; accumulator (lane, e) of a 32x32 tile is
-  // row 8*(e/4) + 4*(lane/32) + e%4, column lane%32.
+  // row 8*(e/4) + 4*(lane/32) + e%4, column lane%32; of a 16x16 tile row
+  // 4*(lane/16) + e, column lane%16.
   constexpr int CP = BN + 4;  // C tile pitch (floats)
   float *Cs = (float *)smem;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int r0 = wm * TI * 32 - h * 128;  // this wave's first row within the half
+    const int r0 = wm * TI * MF - h * 128;  // this wave's first row within the half
     if (r0 >= 0 && r0 < 128) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
+        for (int j = 0; j < TJ; ++j) {
+          if constexpr (MF == 32) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            Cs[(r0 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * CP + wn * TJ * 32 + j * 32 + (lane & 31)] =
-                acc[i][j][e];
+            for (int e = 0; e < 16; ++e)
+              Cs[(r0 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * CP + wn * TJ * 32 + j * 32 +
+                 (lane & 31)] = acc[i][j][e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              Cs[(r0 + i * 16 + 4 * (lane >> 4) + e) * CP + wn * TJ * 16 + j * 16 + (lane & 15)] = acc[i][j][e];
+          }
+        }
     }
     __syncthreads();
     if constexpr (BN == G2N)
