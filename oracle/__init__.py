@@ -14,5 +14,9 @@ Modules
 ``brute``      a separately written scalar-loop implementation of exact
                autoregressive execution, for tiny shapes only; it pins
                ``wm_oracle`` by brute force.
+``wm_train``   the training step with truncated backpropagation: the
+               objective from ``wm_oracle`` passes (for finite differences)
+               and the same forward in torch float64 for autograd (import it
+               as ``oracle.wm_train``; it needs torch).
 """
 from .wm_oracle import *  # noqa: F401,F403
