@@ -31,6 +31,14 @@ class WmWeights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in WEIGHT_FIELDS]
 
 
+GRAD_FIELDS = ["embed", "lm_head", "final_norm", "attn_norm", "wq", "q_norm", "wo", "ffn_norm", "w_gate", "w_up",
+               "w_down", "src_norm", "router", "chan_norm", "wk", "wv", "k_norm"]
+
+
+class WmGrads(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in GRAD_FIELDS]
+
+
 class WmCache(ctypes.Structure):
     _fields_ = [("k", c_vp), ("v", c_vp), ("B", c_i32)]
 
@@ -62,6 +70,9 @@ _SIGS = {
                                          c_vp, c_size, c_vp]),
     "wm_feedback_free_decode_step": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, P(WmCache), c_vp, c_vp,
                                              c_size, c_vp]),
+    "wm_train_workspace_bytes": (c_size, [P(WmConfig), c_i32, c_i32, c_i32, c_i32]),
+    "wm_train_step": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, P(WmGrads), c_vp,
+                              c_vp, c_size, c_vp]),
     "wm_profile_begin": (c_i32, [ctypes.c_uint32]),
     "wm_profile_read": (c_i32, [P(ctypes.c_int64), P(ctypes.c_double)]),
     "wm_profile_end": (c_i32, []),

@@ -316,3 +316,37 @@ def peak_mfma_bf16(iters: int = 10, stream=None) -> float:
     out = ctypes.c_double()
     C.check("wm_peak_mfma_bf16", C.lib().wm_peak_mfma_bf16(iters, _stream(stream), ctypes.byref(out)))
     return out.value
+
+
+def train_workspace(model: Model, B: int, T: int, g: int, n_grad: int = 2) -> torch.Tensor:
+    n = C.lib().wm_train_workspace_bytes(ctypes.byref(model.cfg), B, T, g, n_grad)
+    if n == 0:
+        raise C.WmError("wm_train_workspace_bytes", -2)
+    return torch.empty(n, dtype=torch.uint8, device=model.device)
+
+
+def train_step(model: Model, tokens: torch.Tensor, g: int, n_nograd: int = 1, n_grad: int = 2, grads=None,
+               ws=None, stream=None):
+    """One training step with truncated backpropagation on tokens [B, T]
+    (int32, device), float32 models only: n_nograd cyclic passes without
+    gradient, n_grad with it, next-token cross-entropy of the last pass.
+    Returns (loss: float32 device tensor [1], grads: {name: float32 tensor of
+    the parameter's shape}); ``grads`` may be given to be overwritten."""
+    if model.dtype != "f32":
+        raise ValueError("the training step runs on float32 models only")
+    check_tensor("tokens", tokens, torch.int32, model.device)
+    if tokens.dim() != 2:
+        raise ValueError(f"tokens must be [B, T], got shape {tuple(tokens.shape)}")
+    B, T = tokens.shape
+    if grads is None:
+        grads = {n: torch.empty_like(model.t[n]) for n in C.GRAD_FIELDS}
+    for n in C.GRAD_FIELDS:
+        check_tensor(f"grads[{n}]", grads[n], torch.float32, model.device, tuple(model.t[n].shape))
+    if ws is None:
+        ws = train_workspace(model, B, T, g, n_grad)
+    loss = torch.empty(1, dtype=torch.float32, device=model.device)
+    gw = C.WmGrads(*[grads[n].data_ptr() for n in C.GRAD_FIELDS])
+    C.check("wm_train_step", C.lib().wm_train_step(ctypes.byref(model.cfg), ctypes.byref(model.w), tokens.data_ptr(),
+                                                   B, T, g, n_nograd, n_grad, ctypes.byref(gw), loss.data_ptr(),
+                                                   ws.data_ptr(), ws.numel(), _stream(stream)))
+    return loss, grads

@@ -1,0 +1,1028 @@
+// wm_train.hip — one training step with truncated backpropagation, float32.
+//
+// The step (onedev.kr "What differs": in training, gradients flow only
+// through the last n_g passes; "How used": one cyclic pass without gradients,
+// then two with; paperlayer.ai §3 "Execution schedules": training solves the
+// feedback as a fixed point by passes): from the zero cache, n_nograd cyclic
+// passes without gradient, then n_grad passes with it; the loss is the mean
+// next-token cross-entropy of the last pass's logits (position i < T-1 of
+// sequence b predicts token i+1); the gradient of every parameter is taken
+// with the cache left by the no-gradient passes held constant.
+//
+// Plan.  The cache lives in the workspace in float32 [k, B, Hkv, T, d].  The
+// forward runs every group step of every pass in order; before a gradient
+// pass's group step overwrites its entries, the old values go to an undo
+// log (one slot per gradient step).  The backward walks the gradient steps in
+// reverse.  For each it takes the gradient of the entries the step wrote from
+// dCache (an array shaped like the cache that collects, for every entry, the
+// gradient of the value it holds at that point of the walk), clears it there,
+// puts the old values back (so the cache is as the step found it), recomputes
+// the step's forward with every intermediate kept, and runs the step's
+// backward: the pool first (the written keys/values back to the layer inputs
+// and the pool parameters), then the layers from the top, where the
+// attention of layer l adds the gradient of every cache entry it read into
+// dCache.  A step reads the entries of earlier groups of its own pass and of
+// later groups of the previous pass; both writers come later in the reverse
+// walk, so each finds its gradient complete.  What the first gradient pass
+// reads from the no-gradient cache is left in dCache and dropped.
+//
+// Every kernel here is plain float32 arithmetic on the vector ALUs, written
+// for correctness at training shapes rather than speed: a tiled GEMM with
+// optional transposes, row RMSNorm forward/backward and gain gradients,
+// RoPE and its inverse, strict-causal attention forward (with its softmax
+// statistics) and backward (queries per row; keys and values per key, so no
+// atomics), SwiGLU, the pool's mix and its two backward products, the
+// embedding gather and its backward (rows that share a token summed along
+// a chain in row order), cross-entropy.  All reductions run in a fixed
+// order, so a step is deterministic.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <algorithm>
+
+#include "../../include/wm.h"
+#include "wm_common.hpp"
+#include "wm_host.hpp"
+
+namespace wm {
+namespace tr {
+
+#define TR_TRY(expr)                                                               \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess) {                                                        \
+      set_error("%s failed: %s", #expr, hipGetErrorString(e_));                    \
+      return WM_ERR_HIP;                                                           \
+    }                                                                              \
+  } while (0)
+
+#define TR_CHECK(cond, code, ...) \
+  do {                            \
+    if (!(cond)) {                \
+      set_error(__VA_ARGS__);     \
+      return code;                \
+    }                             \
+  } while (0)
+
+// Rows of a group step: row n = b*M + m is position s0 + m*step of sequence b.
+struct Rows {
+  int M, s0, step;
+  __host__ __device__ int pos(int n) const { return s0 + (n % M) * step; }
+  __host__ __device__ int seq(int n) const { return n / M; }
+};
+
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// ------------------------------------------------------------------ elementwise
+__global__ void k_fill(float *p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+__global__ void k_copy(float *dst, const float *src, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+__global__ void k_add(float *y, const float *x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] += x[i];
+}
+
+// act = silu(G) * U
+__global__ void k_swiglu(const float *G, const float *U, float *act, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float g = G[i], sg = 1.f / (1.f + expf(-g));
+    act[i] = g * sg * U[i];
+  }
+}
+// dG = dact * U * silu'(G), dU = dact * silu(G); silu'(x) = s (1 + x (1 - s)).
+__global__ void k_swiglu_bwd(const float *G, const float *U, const float *dact, float *dG, float *dU, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float g = G[i], sg = 1.f / (1.f + expf(-g)), da = dact[i];
+    dG[i] = da * U[i] * sg * (1.f + g * (1.f - sg));
+    dU[i] = da * g * sg;
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+// C[z] = alpha * op(A[z]) op(B[z]) + beta * C[z], op(A) [M, K], op(B) [K, N],
+// row-major.  TA: A is stored [K, M] (leading dim lda), else [M, K].  TB: B
+// is stored [N, K], else [K, N].  beta = 0 never reads C.  64 x 64 tiles,
+// 256 threads with 4 x 4 outputs each, k in steps of 16 through LDS.
+constexpr int GT = 64, GK = 16;
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64_t sA, const float *B, int64_t ldb,
+                                              int64_t sB, float *C, int64_t ldc, int64_t sC, int M, int N, int K,
+                                              float alpha, float beta) {
+  __shared__ __attribute__((aligned(16))) float As[GK][GT + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[GK][GT + 4];
+  A += blockIdx.z * sA;
+  B += blockIdx.z * sB;
+  C += blockIdx.z * sC;
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += GK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      int mm, kk;
+      if (TA) {
+        mm = e % GT;
+        kk = e / GT;
+      } else {
+        kk = e % GK;
+        mm = e / GK;
+      }
+      const int gm = m0 + mm, gk = k0 + kk;
+      float v = 0.f;
+      if (gm < M && gk < K) v = TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk];
+      As[kk][mm] = v;
+      int nn;
+      if (TB) {
+        kk = e % GK;
+        nn = e / GK;
+      } else {
+        nn = e % GT;
+        kk = e / GT;
+      }
+      const int gn = n0 + nn, gk2 = k0 + kk;
+      float u = 0.f;
+      if (gn < N && gk2 < K) u = TB ? B[(int64_t)gn * ldb + gk2] : B[(int64_t)gk2 * ldb + gn];
+      Bs[kk][nn] = u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < GK; ++kk) {
+      const f32x4 a = *(const f32x4 *)&As[kk][4 * ty];
+      const f32x4 b = *(const f32x4 *)&Bs[kk][4 * tx];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gm = m0 + 4 * ty + i;
+    if (gm >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + 4 * tx + j;
+      if (gn >= N) continue;
+      float *c = C + (int64_t)gm * ldc + gn;
+      *c = beta == 0.f ? alpha * acc[i][j] : alpha * acc[i][j] + beta * *c;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// y = x * r * gain[r / rpg], r = 1 / sqrt(mean(x^2) + eps) per row of D.
+__global__ __launch_bounds__(64) void k_rms(const float *x, const float *gain, int rpg, float *y, float *rinv, int D,
+                                            float eps) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const float *xr = x + (int64_t)r * D;
+  float ss = 0.f;
+  for (int c = lane; c < D; c += 64) ss += xr[c] * xr[c];
+  const float rs = 1.f / sqrtf(wsum(ss) / D + eps);
+  const float *g = gain + (int64_t)(r / rpg) * D;
+  for (int c = lane; c < D; c += 64) y[(int64_t)r * D + c] = xr[c] * rs * g[c];
+  if (lane == 0) rinv[r] = rs;
+}
+// dx (+)= r * (g dy) - x r^3 sum(g dy x) / D
+__global__ __launch_bounds__(64) void k_rms_bwd(const float *x, const float *gain, int rpg, const float *rinv,
+                                                const float *dy, float *dx, int accumulate, int D) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const float *xr = x + (int64_t)r * D, *dyr = dy + (int64_t)r * D, *g = gain + (int64_t)(r / rpg) * D;
+  float dot = 0.f;
+  for (int c = lane; c < D; c += 64) dot += g[c] * dyr[c] * xr[c];
+  dot = wsum(dot);
+  const float rs = rinv[r], k3 = rs * rs * rs * dot / D;
+  for (int c = lane; c < D; c += 64) {
+    const float v = rs * g[c] * dyr[c] - xr[c] * k3;
+    float *o = dx + (int64_t)r * D + c;
+    *o = accumulate ? *o + v : v;
+  }
+}
+// dgain[gi, c] += sum over the rows r of group gi of dy[r, c] x[r, c] rinv[r]
+__global__ void k_gain_grad(const float *x, const float *dy, const float *rinv, float *dg, int rpg, int D) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x, gi = blockIdx.y;
+  if (c >= D) return;
+  float s = 0.f;
+  for (int64_t r = (int64_t)gi * rpg; r < (int64_t)(gi + 1) * rpg; ++r) s += dy[r * D + c] * x[r * D + c] * rinv[r];
+  dg[(int64_t)gi * D + c] += s;
+}
+
+// ------------------------------------------------------------------ RoPE
+// x [rows, H, d], row r at position pos(r % N); element m turns with m + d/2
+// by the angle of the table; inverse = the opposite turn (its own transpose).
+__global__ void k_rope(float *x, Rows rm, int N, int H, int d, const float *cosT, const float *sinT, int inverse,
+                       int64_t total) {
+  const int half = d / 2;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i % half);
+    const int64_t rh = i / half;  // (row, head)
+    const int r = (int)(rh / H);
+    const int p = rm.pos(r % N);
+    const float c = cosT[(int64_t)p * half + m], s = inverse ? -sinT[(int64_t)p * half + m] : sinT[(int64_t)p * half + m];
+    float *v = x + rh * d;
+    const float x1 = v[m], x2 = v[m + half];
+    v[m] = x1 * c - x2 * s;
+    v[m + half] = x1 * s + x2 * c;
+  }
+}
+
+// ------------------------------------------------------------------ embedding
+__global__ void k_embed(const int32_t *tokens, int T, Rows rm, const float *E, float *h, int N, int D, int V) {
+  const int n = blockIdx.x;
+  const int tok = tokens[(int64_t)rm.seq(n) * T + rm.pos(n)];
+  const bool ok = tok >= 0 && tok < V;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) h[(int64_t)n * D + c] = ok ? E[(int64_t)tok * D + c] : NAN;
+}
+// Rows sharing a token, as chains in row order: nxt[n] = the next row with
+// the same token (-1 at the end), head[n] = 1 for the first row of a token.
+__global__ void k_embed_chains(const int32_t *tokens, int T, Rows rm, int N, int *nxt, int *head) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const int tok = tokens[(int64_t)rm.seq(n) * T + rm.pos(n)];
+  int first = 1, next = -1;
+  for (int m = 0; m < N; ++m) {
+    const int t2 = tokens[(int64_t)rm.seq(m) * T + rm.pos(m)];
+    if (t2 != tok) continue;
+    if (m < n) first = 0;
+    if (m > n && next < 0) next = m;
+  }
+  nxt[n] = next;
+  head[n] = first;
+}
+// dE[token] += sum of dh over the token's chain, in row order (one block per
+// chain head; ids outside [0, V) are skipped: their rows are NaN already)
+__global__ void k_embed_bwd(const int32_t *tokens, int T, Rows rm, const float *dh, const int *nxt, const int *head,
+                            float *dE, int D, int V) {
+  const int n = blockIdx.x;
+  if (!head[n]) return;
+  const int tok = tokens[(int64_t)rm.seq(n) * T + rm.pos(n)];
+  if (tok < 0 || tok >= V) return;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float s = 0.f;
+    for (int m = n; m >= 0; m = nxt[m]) s += dh[(int64_t)m * D + c];
+    dE[(int64_t)tok * D + c] += s;
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// Strict causal attention of row n (position i), head h to keys s < i of the
+// channel (K, V: [B, Hkv, Tc, d]); one wave per (n, h), a lane per key in
+// chunks of 64, lanes c and c + 64 own output dims.  Keeps the scaled-score
+// max m and the sum l of exp(score - m) for the backward.
+__global__ __launch_bounds__(64) void k_attn(const float *q, const float *Kc, const float *Vc, Rows rm, int Hq,
+                                             int Hkv, int d, int Tc, float scale, float *out, float *mst,
+                                             float *lst) {
+  __shared__ float qs[128];
+  const int n = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int G = Hq / Hkv, hk = h / G, b = rm.seq(n), i = rm.pos(n);
+  const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * d, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * d;
+  const int64_t qo = ((int64_t)n * Hq + h) * d;
+  for (int c = lane; c < d; c += 64) qs[c] = q[qo + c];
+  __syncthreads();
+  float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int t0 = 0; t0 < i; t0 += 64) {
+    const int t = t0 + lane;
+    float s = -INFINITY;
+    if (t < i) {
+      float dot = 0.f;
+      for (int c = 0; c < d; ++c) dot += qs[c] * K[(int64_t)t * d + c];
+      s = dot * scale;
+    }
+    const float mnew = fmaxf(m, wmax(s));
+    const float p = t < i ? expf(s - mnew) : 0.f, alpha = expf(m - mnew);
+    l = l * alpha + wsum(p);
+    a0 *= alpha;
+    a1 *= alpha;
+    const int nu = min(64, i - t0);
+    for (int u = 0; u < nu; ++u) {
+      const float pu = __shfl(p, u);
+      const float *vr = V + (int64_t)(t0 + u) * d;
+      if (lane < d) a0 += pu * vr[lane];
+      if (lane + 64 < d) a1 += pu * vr[lane + 64];
+    }
+    m = mnew;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (lane < d) out[qo + lane] = a0 * inv;
+  if (lane + 64 < d) out[qo + lane + 64] = a1 * inv;
+  if (lane == 0) {
+    mst[(int64_t)n * Hq + h] = m;
+    lst[(int64_t)n * Hq + h] = l;
+  }
+}
+// dq of row n, head h: dS_t = p_t (dP_t - Dn) with dP_t = dout . V_t and
+// Dn = sum_t p_t dP_t (equal to dout . out; summed from the same p_t dP_t
+// products, so that sum_t dS_t stays 0 to rounding also where the row has
+// few keys and dP_t and Dn nearly cancel); dq = scale * sum_t dS_t K_t.
+// Keeps Dn for the key-side kernel.
+__global__ __launch_bounds__(64) void k_attn_dq(const float *q, const float *Kc, const float *Vc, const float *dout,
+                                                const float *mst, const float *lst, Rows rm, int Hq, int Hkv, int d,
+                                                int Tc, float scale, float *dq, float *Dst) {
+  __shared__ float qs[128], ds[128];
+  const int n = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int G = Hq / Hkv, hk = h / G, b = rm.seq(n), i = rm.pos(n);
+  const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * d, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * d;
+  const int64_t qo = ((int64_t)n * Hq + h) * d;
+  for (int c = lane; c < d; c += 64) {
+    qs[c] = q[qo + c];
+    ds[c] = dout[qo + c];
+  }
+  __syncthreads();
+  const float m = mst[(int64_t)n * Hq + h], l = lst[(int64_t)n * Hq + h], invl = l > 0.f ? 1.f / l : 0.f;
+  // p_t and dP_t of the key this lane takes
+  auto key = [&](int t, float &p, float &dP) {
+    float s = 0.f;
+    dP = 0.f;
+    for (int c = 0; c < d; ++c) {
+      s += qs[c] * K[(int64_t)t * d + c];
+      dP += ds[c] * V[(int64_t)t * d + c];
+    }
+    p = expf(s * scale - m) * invl;
+  };
+  float Dp = 0.f;
+  for (int t0 = 0; t0 < i; t0 += 64) {
+    const int t = t0 + lane;
+    if (t < i) {
+      float p, dP;
+      key(t, p, dP);
+      Dp += p * dP;
+    }
+  }
+  const float Dn = wsum(Dp);
+  float g0 = 0.f, g1 = 0.f;
+  for (int t0 = 0; t0 < i; t0 += 64) {
+    const int t = t0 + lane;
+    float dS = 0.f;
+    if (t < i) {
+      float p, dP;
+      key(t, p, dP);
+      dS = p * (dP - Dn);
+    }
+    const int nu = min(64, i - t0);
+    for (int u = 0; u < nu; ++u) {
+      const float su = __shfl(dS, u);
+      const float *kr = K + (int64_t)(t0 + u) * d;
+      if (lane < d) g0 += su * kr[lane];
+      if (lane + 64 < d) g1 += su * kr[lane + 64];
+    }
+  }
+  if (lane < d) dq[qo + lane] = g0 * scale;
+  if (lane + 64 < d) dq[qo + lane + 64] = g1 * scale;
+  if (lane == 0) Dst[(int64_t)n * Hq + h] = Dn;
+}
+// dK_t += scale * sum dS q, dV_t += sum p dout over the rows n of sequence b
+// with position > t and the heads of KV head hk; one wave per (b, hk, t).
+__global__ __launch_bounds__(64) void k_attn_dkv(const float *q, const float *Kc, const float *Vc, const float *dout,
+                                                 const float *mst, const float *lst, const float *Dst, Rows rm,
+                                                 int Hq, int Hkv, int d, int Tc, float scale, float *dK, float *dV) {
+  const int pair = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+  const int b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
+  const int64_t ko = (((int64_t)b * Hkv + hk) * Tc + t) * d;
+  const float k0 = lane < d ? Kc[ko + lane] : 0.f, k1 = lane + 64 < d ? Kc[ko + lane + 64] : 0.f;
+  const float v0 = lane < d ? Vc[ko + lane] : 0.f, v1 = lane + 64 < d ? Vc[ko + lane + 64] : 0.f;
+  float gk0 = 0.f, gk1 = 0.f, gv0 = 0.f, gv1 = 0.f;
+  bool any = false;
+  for (int mm = 0; mm < rm.M; ++mm) {
+    const int n = b * rm.M + mm;
+    if (rm.pos(n) <= t) continue;
+    any = true;
+    for (int gg = 0; gg < G; ++gg) {
+      const int h = hk * G + gg;
+      const int64_t qo = ((int64_t)n * Hq + h) * d;
+      const float q0 = lane < d ? q[qo + lane] : 0.f, q1 = lane + 64 < d ? q[qo + lane + 64] : 0.f;
+      const float o0 = lane < d ? dout[qo + lane] : 0.f, o1 = lane + 64 < d ? dout[qo + lane + 64] : 0.f;
+      const float s = wsum(q0 * k0 + q1 * k1) * scale, dP = wsum(o0 * v0 + o1 * v1);
+      const float p = expf(s - mst[(int64_t)n * Hq + h]) / lst[(int64_t)n * Hq + h];
+      const float dS = p * (dP - Dst[(int64_t)n * Hq + h]);
+      gk0 += dS * scale * q0;
+      gk1 += dS * scale * q1;
+      gv0 += p * o0;
+      gv1 += p * o1;
+    }
+  }
+  if (!any) return;
+  if (lane < d) {
+    dK[ko + lane] += gk0;
+    dV[ko + lane] += gv0;
+  }
+  if (lane + 64 < d) {
+    dK[ko + lane + 64] += gk1;
+    dV[ko + lane + 64] += gv1;
+  }
+}
+
+// ------------------------------------------------------------------ pool
+// u[n, r*D + c] = nsrc[r*p, n, c]
+__global__ void k_router_in(const float *nsrc, float *u, int p, int R, int N, int D) {
+  const int64_t total = (int64_t)N * R * D;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % D);
+    const int64_t nr = i / D;
+    const int r = (int)(nr % R), n = (int)(nr / R);
+    u[i] = nsrc[((int64_t)r * p * N + n) * D + c];
+  }
+}
+// m[j, n, c] = sum_l A[n, l*k + j] * nsrc[l, n, c] (l ascending)
+__global__ void k_mix(const float *A, const float *nsrc, float *m, int L, int k, int N, int D) {
+  const int64_t total = (int64_t)k * N * D;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % D);
+    const int64_t jn = i / D;
+    const int n = (int)(jn % N), j = (int)(jn / N);
+    float s = 0.f;
+    for (int l = 0; l < L; ++l) s += A[((int64_t)n * L + l) * k + j] * nsrc[((int64_t)l * N + n) * D + c];
+    m[i] = s;
+  }
+}
+// dA[n, l*k + j] = dm[j, n, :] . nsrc[l, n, :]; one wave per (n, l, j)
+__global__ __launch_bounds__(64) void k_mix_dA(const float *dm, const float *nsrc, float *dA, int L, int k, int N,
+                                               int D) {
+  const int n = blockIdx.x, lj = blockIdx.y, l = lj / k, j = lj - l * k, lane = threadIdx.x;
+  const float *a = dm + ((int64_t)j * N + n) * D, *b = nsrc + ((int64_t)l * N + n) * D;
+  float s = 0.f;
+  for (int c = lane; c < D; c += 64) s += a[c] * b[c];
+  s = wsum(s);
+  if (lane == 0) dA[(int64_t)n * L * k + lj] = s;
+}
+// dn[l, n, c] = sum_j A[n, l*k + j] dm[j, n, c]
+__global__ void k_mix_dn(const float *A, const float *dm, float *dn, int L, int k, int N, int D) {
+  const int64_t total = (int64_t)L * N * D;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % D);
+    const int64_t ln = i / D;
+    const int n = (int)(ln % N), l = (int)(ln / N);
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s += A[((int64_t)n * L + l) * k + j] * dm[((int64_t)j * N + n) * D + c];
+    dn[i] = s;
+  }
+}
+// dn[r*p, n, c] += du[n, r*D + c]
+__global__ void k_router_in_bwd(const float *du, float *dn, int p, int R, int N, int D) {
+  const int64_t total = (int64_t)N * R * D;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % D);
+    const int64_t nr = i / D;
+    const int r = (int)(nr % R), n = (int)(nr / R);
+    dn[((int64_t)r * p * N + n) * D + c] += du[i];
+  }
+}
+
+// ------------------------------------------------------------------ cache entries
+// Entries (j, b, h, pos(n), :) of the cache [k, B, Hkv, Tc, d] against a
+// row-ordered array [k, N, Hkv, d].  mode 0: array = cache; 1: cache = array;
+// 2: array = cache, then cache = 0.
+__global__ void k_entries(float *cache, float *arr, Rows rm, int k, int B, int N, int Hkv, int Tc, int d, int mode) {
+  const int64_t total = (int64_t)k * N * Hkv * d;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % d);
+    int64_t r = i / d;
+    const int h = (int)(r % Hkv);
+    r /= Hkv;
+    const int n = (int)(r % N), j = (int)(r / N);
+    float *e = cache + ((((int64_t)j * B + rm.seq(n)) * Hkv + h) * Tc + rm.pos(n)) * d + c;
+    if (mode == 1) {
+      *e = arr[i];
+    } else {
+      arr[i] = *e;
+      if (mode == 2) *e = 0.f;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ loss
+__device__ float block_reduce(float v, bool is_max, float *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = is_max ? wmax(v) : wsum(v);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < nw; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+// Row n of the last pass: loss = logsumexp(z) - z[target] when position
+// i < T-1 (target = token i+1), written to lossrow[b*T + i] (0 otherwise);
+// dz = (softmax(z) - onehot(target)) * inv_count.
+__global__ __launch_bounds__(256) void k_ce(const float *logits, const int32_t *tokens, int T, Rows rm, int V,
+                                            float inv_count, float *lossrow, float *dlogits) {
+  __shared__ float red[4];
+  const int n = blockIdx.x, b = rm.seq(n), i = rm.pos(n);
+  const bool has = i < T - 1;
+  const int tgt = has ? tokens[(int64_t)b * T + i + 1] : -1;
+  const float *z = logits + (int64_t)n * V;
+  float mx = -INFINITY;
+  for (int c = threadIdx.x; c < V; c += blockDim.x) mx = fmaxf(mx, z[c]);
+  mx = block_reduce(mx, true, red);
+  float se = 0.f;
+  for (int c = threadIdx.x; c < V; c += blockDim.x) se += expf(z[c] - mx);
+  se = block_reduce(se, false, red);
+  const float inv = 1.f / se;
+  for (int c = threadIdx.x; c < V; c += blockDim.x)
+    dlogits[(int64_t)n * V + c] = has ? (expf(z[c] - mx) * inv - (c == tgt ? 1.f : 0.f)) * inv_count : 0.f;
+  if (threadIdx.x == 0)
+    lossrow[(int64_t)b * T + i] = has ? (tgt >= 0 && tgt < V ? logf(se) + mx - z[tgt] : NAN) : 0.f;
+}
+// *loss = sum(lossrow) * inv_count, in a fixed order (one block)
+__global__ __launch_bounds__(256) void k_loss_sum(const float *lossrow, int64_t n, float inv_count, float *loss) {
+  __shared__ float red[4];
+  float s = 0.f;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += lossrow[i];
+  s = block_reduce(s, false, red);
+  if (threadIdx.x == 0) *loss = s * inv_count;
+}
+
+// ------------------------------------------------------------------ host side
+inline unsigned grid1(int64_t n, int per = 256) {
+  int64_t g = (n + per - 1) / per;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(g, 65536));
+}
+
+struct Layout {
+  size_t total = 0;
+  size_t take(size_t floats) {
+    const size_t o = total;
+    total += (floats * 4 + 255) & ~(size_t)255;
+    return o;
+  }
+};
+
+// Float offsets into the workspace (bytes / 4 after Layout).
+struct Ws {
+  size_t cK, cV, dK, dV, undo, undo_slot;
+  // tape of one step
+  size_t S, rA, a, qraw, rQ, q, o, mst, lst, h1, rF, bn, G, U, act, hL, rL, xf, logits;
+  // pool (one branch at a time)
+  size_t nsrc, rS, u, A, m, rM, c, kraw, rK, Kn, Vn;
+  // backward
+  size_t dh, dS, da, dq, dout, dG, dU, dact, db, Dst, dKn, dVn, dkraw, dc, dm, dA, dn, du, dz, dxf, lossrow;
+  size_t enext, ehead;  // (int arrays)
+  size_t bytes;
+};
+
+inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad) {
+  const size_t L = c.L, D = c.D, QD = (size_t)c.Hq * c.d, KD = (size_t)c.Hkv * c.d, F = c.F, k = c.k, V = c.V;
+  const size_t R = (c.L + c.p - 1) / c.p, ng = std::min(g, T);
+  const size_t N = (size_t)B * ((T + g - 1) / g), cache = k * B * KD * T;
+  Layout l;
+  Ws w{};
+  auto t = [&](size_t n) { return l.take(n) / 4; };
+  w.cK = t(cache);
+  w.cV = t(cache);
+  w.dK = t(cache);
+  w.dV = t(cache);
+  w.undo_slot = ((2 * k * N * KD * 4 + 255) & ~(size_t)255) / 4;
+  w.undo = t(w.undo_slot * (size_t)n_grad * ng);
+  w.S = t(L * N * D);
+  w.rA = t(L * N);
+  w.a = t(L * N * D);
+  w.qraw = t(L * N * QD);
+  w.rQ = t(L * N * c.Hq);
+  w.q = t(L * N * QD);
+  w.o = t(L * N * QD);
+  w.mst = t(L * N * c.Hq);
+  w.lst = t(L * N * c.Hq);
+  w.h1 = t(L * N * D);
+  w.rF = t(L * N);
+  w.bn = t(L * N * D);
+  w.G = t(L * N * F);
+  w.U = t(L * N * F);
+  w.act = t(L * N * F);
+  w.hL = t(N * D);
+  w.rL = t(N);
+  w.xf = t(N * D);
+  w.logits = t(N * V);
+  w.nsrc = t(L * N * D);
+  w.rS = t(L * N);
+  w.u = t(N * R * D);
+  w.A = t(N * L * k);
+  w.m = t(k * N * D);
+  w.rM = t(k * N);
+  w.c = t(k * N * D);
+  w.kraw = t(k * N * KD);
+  w.rK = t(k * N * c.Hkv);
+  w.Kn = t(k * N * KD);
+  w.Vn = t(k * N * KD);
+  w.dh = t(N * D);
+  w.dS = t(L * N * D);
+  w.da = t(N * D);
+  w.dq = t(N * QD);
+  w.dout = t(N * QD);
+  w.dG = t(N * F);
+  w.dU = t(N * F);
+  w.dact = t(N * F);
+  w.db = t(N * D);
+  w.Dst = t(N * c.Hq);
+  w.dKn = t(k * N * KD);
+  w.dVn = t(k * N * KD);
+  w.dkraw = t(k * N * KD);
+  w.dc = t(k * N * D);
+  w.dm = t(k * N * D);
+  w.dA = t(N * L * k);
+  w.dn = t(L * N * D);
+  w.du = t(N * R * D);
+  w.dz = t(N * V);
+  w.dxf = t(N * D);
+  w.lossrow = t((size_t)B * T);
+  w.enext = t(N);
+  w.ehead = t(N);
+  w.bytes = l.total;
+  return w;
+}
+
+struct Trainer {
+  const wm_config &c;
+  const wm_weights &w;
+  const wm_grads &gr;
+  const int32_t *tokens;
+  int B, T, g;
+  float *base;
+  Ws o;
+  hipStream_t s;
+  int L, D, QD, KD, F, k, V, R;
+
+  Trainer(const wm_config &c_, const wm_weights &w_, const wm_grads &g_, const int32_t *tok, int B_, int T_, int gg,
+          int n_grad, void *ws, hipStream_t st)
+      : c(c_), w(w_), gr(g_), tokens(tok), B(B_), T(T_), g(gg), base((float *)ws), s(st) {
+    o = layout(c, B, T, g, n_grad);
+    L = c.L;
+    D = c.D;
+    QD = c.Hq * c.d;
+    KD = c.Hkv * c.d;
+    F = c.F;
+    k = c.k;
+    V = c.V;
+    R = (L + c.p - 1) / c.p;
+  }
+  float *P(size_t off) const { return base + off; }
+  static const float *W(const void *p) { return (const float *)p; }
+
+  hipError_t fill(float *p, int64_t n, float v) {
+    hipLaunchKernelGGL(k_fill, dim3(grid1(n)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+  }
+  hipError_t copy(float *d, const float *x, int64_t n) {
+    hipLaunchKernelGGL(k_copy, dim3(grid1(n)), dim3(256), 0, s, d, x, n);
+    return hipGetLastError();
+  }
+  hipError_t add(float *y, const float *x, int64_t n) {
+    hipLaunchKernelGGL(k_add, dim3(grid1(n)), dim3(256), 0, s, y, x, n);
+    return hipGetLastError();
+  }
+  // C = alpha op(A) op(B) + beta C, batched over Z with element strides
+  hipError_t gemm(bool ta, bool tb, const float *A, int64_t lda, const float *B_, int64_t ldb, float *C, int64_t ldc,
+                  int M, int N, int K, float beta, int Z = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, Z);
+    if (!ta && !tb)
+      hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, C, ldc, sC, M, N, K,
+                         1.f, beta);
+    else if (!ta && tb)
+      hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, C, ldc, sC, M, N, K,
+                         1.f, beta);
+    else if (ta && !tb)
+      hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, C, ldc, sC, M, N, K,
+                         1.f, beta);
+    else
+      hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, C, ldc, sC, M, N, K,
+                         1.f, beta);
+    return hipGetLastError();
+  }
+  hipError_t rms(const float *x, const float *gain, int rpg, float *y, float *rinv, int rows, int width) {
+    hipLaunchKernelGGL(k_rms, dim3(rows), dim3(64), 0, s, x, gain, rpg, y, rinv, width, c.eps);
+    return hipGetLastError();
+  }
+  // dx (+)= RMSNorm backward; dgain (ngain rows of width) += its gain gradient
+  hipError_t rms_bwd(const float *x, const float *gain, float *dgain, int rpg, int ngain, const float *rinv,
+                     const float *dy, float *dx, bool acc, int rows, int width) {
+    hipLaunchKernelGGL(k_rms_bwd, dim3(rows), dim3(64), 0, s, x, gain, rpg, rinv, dy, dx, acc ? 1 : 0, width);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gain_grad, dim3((width + 255) / 256, ngain), dim3(256), 0, s, x, dy, rinv, dgain, rpg, width);
+    return hipGetLastError();
+  }
+  hipError_t rope(float *x, Rows rm, int N, int rows, int H, bool inverse) {
+    const int64_t total = (int64_t)rows * H * (c.d / 2);
+    hipLaunchKernelGGL(k_rope, dim3(grid1(total)), dim3(256), 0, s, x, rm, N, H, c.d, w.rope_cos, w.rope_sin,
+                       inverse ? 1 : 0, total);
+    return hipGetLastError();
+  }
+  hipError_t entries(float *cache, float *arr, Rows rm, int N, int mode) {
+    const int64_t total = (int64_t)k * N * KD;
+    hipLaunchKernelGGL(k_entries, dim3(grid1(total)), dim3(256), 0, s, cache, arr, rm, k, B, N, c.Hkv, T, c.d, mode);
+    return hipGetLastError();
+  }
+  float *chanK(size_t cacheoff, int ch) const { return P(cacheoff) + (size_t)ch * B * KD * T; }
+
+  // The pool of one branch for the rows of the step (S from the tape):
+  // nsrc, rS, u, A, m, rM, c; keys also kraw, rK and K_new (normed, turned);
+  // values V_new.
+  wm_status pool_fwd(int beta, Rows rm, int N) {
+    TR_TRY(rms(P(o.S), w.src_norm + (size_t)beta * L * D, N, P(o.nsrc), P(o.rS), L * N, D));
+    hipLaunchKernelGGL(k_router_in, dim3(grid1((int64_t)N * R * D)), dim3(256), 0, s, P(o.nsrc), P(o.u), c.p, R, N,
+                       D);
+    TR_TRY(hipGetLastError());
+    TR_TRY(gemm(false, true, P(o.u), (int64_t)R * D, W(w.router) + (size_t)beta * L * k * R * D, (int64_t)R * D,
+                P(o.A), (int64_t)L * k, N, L * k, R * D, 0.f));
+    hipLaunchKernelGGL(k_mix, dim3(grid1((int64_t)k * N * D)), dim3(256), 0, s, P(o.A), P(o.nsrc), P(o.m), L, k, N,
+                       D);
+    TR_TRY(hipGetLastError());
+    TR_TRY(rms(P(o.m), w.chan_norm + (size_t)beta * k * D, N, P(o.c), P(o.rM), k * N, D));
+    if (beta == 0) {
+      TR_TRY(gemm(false, true, P(o.c), D, W(w.wk), D, P(o.kraw), KD, N, KD, D, 0.f, k, (int64_t)N * D,
+                  (int64_t)KD * D, (int64_t)N * KD));
+      TR_TRY(rms(P(o.kraw), w.k_norm, N * c.Hkv, P(o.Kn), P(o.rK), k * N * c.Hkv, c.d));
+      TR_TRY(rope(P(o.Kn), rm, N, k * N, c.Hkv, false));
+    } else {
+      TR_TRY(gemm(false, true, P(o.c), D, W(w.wv), D, P(o.Vn), KD, N, KD, D, 0.f, k, (int64_t)N * D,
+                  (int64_t)KD * D, (int64_t)N * KD));
+    }
+    return WM_OK;
+  }
+
+  // Forward of one group step with every intermediate kept.  The cache is
+  // only read.  want_logits: logits, and the loss rows with their gradient.
+  wm_status step_fwd(Rows rm, int N, bool want_logits, float inv_count) {
+    const float scale = 1.f / sqrtf((float)c.d);
+    hipLaunchKernelGGL(k_embed, dim3(N), dim3(256), 0, s, tokens, T, rm, W(w.embed), P(o.S), N, D, V);
+    TR_TRY(hipGetLastError());
+    for (int l = 0; l < L; ++l) {
+      const size_t nd = (size_t)N * D, nq = (size_t)N * QD, nf = (size_t)N * F;
+      float *S = P(o.S) + l * nd, *a = P(o.a) + l * nd, *qraw = P(o.qraw) + l * nq, *q = P(o.q) + l * nq;
+      float *out = P(o.o) + l * nq, *h1 = P(o.h1) + l * nd, *bn = P(o.bn) + l * nd;
+      float *G = P(o.G) + l * nf, *U = P(o.U) + l * nf, *act = P(o.act) + l * nf;
+      TR_TRY(rms(S, w.attn_norm + (size_t)l * D, N, a, P(o.rA) + (size_t)l * N, N, D));
+      TR_TRY(gemm(false, true, a, D, W(w.wq) + (size_t)l * QD * D, D, qraw, QD, N, QD, D, 0.f));
+      TR_TRY(rms(qraw, w.q_norm + (size_t)l * c.d, N * c.Hq, q, P(o.rQ) + (size_t)l * N * c.Hq, N * c.Hq, c.d));
+      TR_TRY(rope(q, rm, N, N, c.Hq, false));
+      const int ch = l % k;
+      hipLaunchKernelGGL(k_attn, dim3(N, c.Hq), dim3(64), 0, s, q, chanK(o.cK, ch), chanK(o.cV, ch), rm, c.Hq, c.Hkv,
+                         c.d, T, scale, out, P(o.mst) + (size_t)l * N * c.Hq, P(o.lst) + (size_t)l * N * c.Hq);
+      TR_TRY(hipGetLastError());
+      TR_TRY(copy(h1, S, nd));
+      TR_TRY(gemm(false, true, out, QD, W(w.wo) + (size_t)l * D * QD, QD, h1, D, N, D, QD, 1.f));
+      TR_TRY(rms(h1, w.ffn_norm + (size_t)l * D, N, bn, P(o.rF) + (size_t)l * N, N, D));
+      TR_TRY(gemm(false, true, bn, D, W(w.w_gate) + (size_t)l * F * D, D, G, F, N, F, D, 0.f));
+      TR_TRY(gemm(false, true, bn, D, W(w.w_up) + (size_t)l * F * D, D, U, F, N, F, D, 0.f));
+      hipLaunchKernelGGL(k_swiglu, dim3(grid1(nf)), dim3(256), 0, s, G, U, act, (int64_t)nf);
+      TR_TRY(hipGetLastError());
+      float *next = l + 1 < L ? P(o.S) + (l + 1) * nd : P(o.hL);
+      TR_TRY(copy(next, h1, nd));
+      TR_TRY(gemm(false, true, act, F, W(w.w_down) + (size_t)l * D * F, F, next, D, N, D, F, 1.f));
+    }
+    wm_status st = pool_fwd(0, rm, N);
+    if (st != WM_OK) return st;
+    st = pool_fwd(1, rm, N);
+    if (st != WM_OK) return st;
+    if (want_logits) {
+      TR_TRY(rms(P(o.hL), w.final_norm, N, P(o.xf), P(o.rL), N, D));
+      TR_TRY(gemm(false, true, P(o.xf), D, W(w.lm_head), D, P(o.logits), V, N, V, D, 0.f));
+      hipLaunchKernelGGL(k_ce, dim3(N), dim3(256), 0, s, P(o.logits), tokens, T, rm, V, inv_count, P(o.lossrow),
+                         P(o.dz));
+      TR_TRY(hipGetLastError());
+    }
+    return WM_OK;
+  }
+
+  // Backward of one branch of the pool: dout [k, N, KD] = gradient of the
+  // written keys (beta 0, as stored: normed and turned) or values; adds the
+  // gradient of the layer inputs into dS and the branch's parameter
+  // gradients.  Recomputes the branch's forward first.
+  wm_status pool_bwd(int beta, Rows rm, int N, float *dout) {
+    wm_status st = pool_fwd(beta, rm, N);
+    if (st != WM_OK) return st;
+    const int64_t zA = (int64_t)N * KD, zB = (int64_t)KD * D, zC = (int64_t)N * D;
+    if (beta == 0) {
+      TR_TRY(rope(dout, rm, N, k * N, c.Hkv, true));
+      TR_TRY(rms_bwd(P(o.kraw), w.k_norm, gr.k_norm, N * c.Hkv, k, P(o.rK), dout, P(o.dkraw), false, k * N * c.Hkv,
+                     c.d));
+      // dc_j = dkraw_j W_K^j ; dW_K^j += dkraw_j^T c_j
+      TR_TRY(gemm(false, false, P(o.dkraw), KD, W(w.wk), D, P(o.dc), D, N, D, KD, 0.f, k, zA, zB, zC));
+      TR_TRY(gemm(true, false, P(o.dkraw), KD, P(o.c), D, gr.wk, D, KD, D, N, 1.f, k, zA, zC, zB));
+    } else {
+      TR_TRY(gemm(false, false, dout, KD, W(w.wv), D, P(o.dc), D, N, D, KD, 0.f, k, zA, zB, zC));
+      TR_TRY(gemm(true, false, dout, KD, P(o.c), D, gr.wv, D, KD, D, N, 1.f, k, zA, zC, zB));
+    }
+    TR_TRY(rms_bwd(P(o.m), w.chan_norm + (size_t)beta * k * D, gr.chan_norm + (size_t)beta * k * D, N, k, P(o.rM),
+                   P(o.dc), P(o.dm), false, k * N, D));
+    hipLaunchKernelGGL(k_mix_dA, dim3(N, L * k), dim3(64), 0, s, P(o.dm), P(o.nsrc), P(o.dA), L, k, N, D);
+    TR_TRY(hipGetLastError());
+    hipLaunchKernelGGL(k_mix_dn, dim3(grid1((int64_t)L * N * D)), dim3(256), 0, s, P(o.A), P(o.dm), P(o.dn), L, k, N,
+                       D);
+    TR_TRY(hipGetLastError());
+    const float *Wr = W(w.router) + (size_t)beta * L * k * R * D;
+    TR_TRY(gemm(true, false, P(o.dA), (int64_t)L * k, P(o.u), (int64_t)R * D, gr.router + (size_t)beta * L * k * R * D,
+                (int64_t)R * D, L * k, R * D, N, 1.f));
+    TR_TRY(gemm(false, false, P(o.dA), (int64_t)L * k, Wr, (int64_t)R * D, P(o.du), (int64_t)R * D, N, R * D, L * k,
+                0.f));
+    hipLaunchKernelGGL(k_router_in_bwd, dim3(grid1((int64_t)N * R * D)), dim3(256), 0, s, P(o.du), P(o.dn), c.p, R, N,
+                       D);
+    TR_TRY(hipGetLastError());
+    TR_TRY(rms_bwd(P(o.S), w.src_norm + (size_t)beta * L * D, gr.src_norm + (size_t)beta * L * D, N, L, P(o.rS),
+                   P(o.dn), P(o.dS), true, L * N, D));
+    return WM_OK;
+  }
+
+  // Backward of one group step whose forward is in the tape; dKn / dVn hold
+  // the gradient of its written entries.
+  wm_status step_bwd(Rows rm, int N, bool last_pass) {
+    const float scale = 1.f / sqrtf((float)c.d);
+    const size_t nd = (size_t)N * D, nq = (size_t)N * QD, nf = (size_t)N * F;
+    float *dh = P(o.dh);
+    if (last_pass) {
+      TR_TRY(gemm(false, false, P(o.dz), V, W(w.lm_head), D, P(o.dxf), D, N, D, V, 0.f));
+      TR_TRY(gemm(true, false, P(o.dz), V, P(o.xf), D, gr.lm_head, D, V, D, N, 1.f));
+      TR_TRY(rms_bwd(P(o.hL), w.final_norm, gr.final_norm, N, 1, P(o.rL), P(o.dxf), dh, false, N, D));
+    } else {
+      TR_TRY(fill(dh, nd, 0.f));
+    }
+    TR_TRY(fill(P(o.dS), (int64_t)L * nd, 0.f));
+    wm_status st = pool_bwd(0, rm, N, P(o.dKn));
+    if (st != WM_OK) return st;
+    st = pool_bwd(1, rm, N, P(o.dVn));
+    if (st != WM_OK) return st;
+    for (int l = L - 1; l >= 0; --l) {
+      float *S = P(o.S) + l * nd, *a = P(o.a) + l * nd, *qraw = P(o.qraw) + l * nq, *q = P(o.q) + l * nq;
+      float *out = P(o.o) + l * nq, *h1 = P(o.h1) + l * nd, *bn = P(o.bn) + l * nd;
+      float *G = P(o.G) + l * nf, *U = P(o.U) + l * nf, *act = P(o.act) + l * nf;
+      float *mst = P(o.mst) + (size_t)l * N * c.Hq, *lst = P(o.lst) + (size_t)l * N * c.Hq;
+      // FFN: h_out = h1 + act W_down^T
+      TR_TRY(gemm(false, false, dh, D, W(w.w_down) + (size_t)l * D * F, F, P(o.dact), F, N, F, D, 0.f));
+      TR_TRY(gemm(true, false, dh, D, act, F, gr.w_down + (size_t)l * D * F, F, D, F, N, 1.f));
+      hipLaunchKernelGGL(k_swiglu_bwd, dim3(grid1(nf)), dim3(256), 0, s, G, U, P(o.dact), P(o.dG), P(o.dU),
+                         (int64_t)nf);
+      TR_TRY(hipGetLastError());
+      TR_TRY(gemm(false, false, P(o.dG), F, W(w.w_gate) + (size_t)l * F * D, D, P(o.db), D, N, D, F, 0.f));
+      TR_TRY(gemm(false, false, P(o.dU), F, W(w.w_up) + (size_t)l * F * D, D, P(o.db), D, N, D, F, 1.f));
+      TR_TRY(gemm(true, false, P(o.dG), F, bn, D, gr.w_gate + (size_t)l * F * D, D, F, D, N, 1.f));
+      TR_TRY(gemm(true, false, P(o.dU), F, bn, D, gr.w_up + (size_t)l * F * D, D, F, D, N, 1.f));
+      TR_TRY(rms_bwd(h1, w.ffn_norm + (size_t)l * D, gr.ffn_norm + (size_t)l * D, N, 1, P(o.rF) + (size_t)l * N,
+                     P(o.db), dh, true, N, D));
+      // attention: h1 = h_l + out W_O^T
+      TR_TRY(gemm(false, false, dh, D, W(w.wo) + (size_t)l * D * QD, QD, P(o.dout), QD, N, QD, D, 0.f));
+      TR_TRY(gemm(true, false, dh, D, out, QD, gr.wo + (size_t)l * D * QD, QD, D, QD, N, 1.f));
+      const int ch = l % k;
+      hipLaunchKernelGGL(k_attn_dq, dim3(N, c.Hq), dim3(64), 0, s, q, chanK(o.cK, ch), chanK(o.cV, ch), P(o.dout),
+                         mst, lst, rm, c.Hq, c.Hkv, c.d, T, scale, P(o.dq), P(o.Dst));
+      TR_TRY(hipGetLastError());
+      hipLaunchKernelGGL(k_attn_dkv, dim3(B * c.Hkv, T), dim3(64), 0, s, q, chanK(o.cK, ch), chanK(o.cV, ch),
+                         P(o.dout), mst, lst, P(o.Dst), rm, c.Hq, c.Hkv, c.d, T, scale, chanK(o.dK, ch),
+                         chanK(o.dV, ch));
+      TR_TRY(hipGetLastError());
+      TR_TRY(rope(P(o.dq), rm, N, N, c.Hq, true));
+      // (the head-norm backward's output goes to dout, free again)
+      TR_TRY(rms_bwd(qraw, w.q_norm + (size_t)l * c.d, gr.q_norm + (size_t)l * c.d, N * c.Hq, 1,
+                     P(o.rQ) + (size_t)l * N * c.Hq, P(o.dq), P(o.dout), false, N * c.Hq, c.d));
+      TR_TRY(gemm(false, false, P(o.dout), QD, W(w.wq) + (size_t)l * QD * D, D, P(o.da), D, N, D, QD, 0.f));
+      TR_TRY(gemm(true, false, P(o.dout), QD, a, D, gr.wq + (size_t)l * QD * D, D, QD, D, N, 1.f));
+      TR_TRY(rms_bwd(S, w.attn_norm + (size_t)l * D, gr.attn_norm + (size_t)l * D, N, 1, P(o.rA) + (size_t)l * N,
+                     P(o.da), dh, true, N, D));
+      // the block input also feeds the pool
+      TR_TRY(add(dh, P(o.dS) + l * nd, nd));
+    }
+    int *nxt = (int *)P(o.enext), *head = (int *)P(o.ehead);
+    hipLaunchKernelGGL(k_embed_chains, dim3((N + 255) / 256), dim3(256), 0, s, tokens, T, rm, N, nxt, head);
+    TR_TRY(hipGetLastError());
+    hipLaunchKernelGGL(k_embed_bwd, dim3(N), dim3(256), 0, s, tokens, T, rm, dh, nxt, head, gr.embed, D, V);
+    TR_TRY(hipGetLastError());
+    return WM_OK;
+  }
+
+  // Group step of a forward pass: keep the old entries (undo != null), run
+  // the stack and the pool, write the new entries.
+  wm_status fwd_write(Rows rm, int N, float *undo) {
+    if (undo) {
+      TR_TRY(entries(P(o.cK), undo, rm, N, 0));
+      TR_TRY(entries(P(o.cV), undo + (size_t)k * N * KD, rm, N, 0));
+    }
+    wm_status st = step_fwd(rm, N, false, 0.f);
+    if (st != WM_OK) return st;
+    TR_TRY(entries(P(o.cK), P(o.Kn), rm, N, 1));
+    TR_TRY(entries(P(o.cV), P(o.Vn), rm, N, 1));
+    return WM_OK;
+  }
+
+  wm_status run(int n_nograd, int n_grad, float *loss) {
+    const int64_t cache = (int64_t)k * B * KD * T;
+    const int ng = std::min(g, T);
+    const float inv_count = 1.f / ((float)B * (T - 1));
+    TR_TRY(fill(P(o.cK), cache, 0.f));
+    TR_TRY(fill(P(o.cV), cache, 0.f));
+    TR_TRY(fill(P(o.dK), cache, 0.f));
+    TR_TRY(fill(P(o.dV), cache, 0.f));
+    TR_TRY(fill(P(o.lossrow), (int64_t)B * T, 0.f));
+    // gradients start at zero
+    struct G2 {
+      float *p;
+      int64_t n;
+    };
+    const int64_t Ld = (int64_t)L * D;
+    const G2 gz[] = {{gr.embed, (int64_t)V * D},
+                     {gr.lm_head, (int64_t)V * D},
+                     {gr.final_norm, D},
+                     {gr.attn_norm, Ld},
+                     {gr.wq, (int64_t)L * QD * D},
+                     {gr.q_norm, (int64_t)L * c.d},
+                     {gr.wo, (int64_t)L * D * QD},
+                     {gr.ffn_norm, Ld},
+                     {gr.w_gate, (int64_t)L * F * D},
+                     {gr.w_up, (int64_t)L * F * D},
+                     {gr.w_down, (int64_t)L * D * F},
+                     {gr.src_norm, 2 * Ld},
+                     {gr.router, (int64_t)2 * L * k * R * D},
+                     {gr.chan_norm, (int64_t)2 * k * D},
+                     {gr.wk, (int64_t)k * KD * D},
+                     {gr.wv, (int64_t)k * KD * D},
+                     {gr.k_norm, (int64_t)k * c.d}};
+    for (const G2 &z : gz) TR_TRY(fill(z.p, z.n, 0.f));
+    // forward: passes without gradient, then the gradient passes with undo
+    for (int pass = 0; pass < n_nograd + n_grad; ++pass) {
+      const int gp = pass - n_nograd;
+      for (int q = 0; q < ng; ++q) {
+        const int M = (T - q + g - 1) / g;
+        const Rows rm{M, q, g};
+        float *undo = gp >= 0 ? P(o.undo) + ((size_t)gp * ng + q) * o.undo_slot : nullptr;
+        wm_status st = fwd_write(rm, B * M, undo);
+        if (st != WM_OK) return st;
+      }
+    }
+    // backward over the gradient steps in reverse
+    for (int gp = n_grad - 1; gp >= 0; --gp) {
+      for (int q = ng - 1; q >= 0; --q) {
+        const int M = (T - q + g - 1) / g, N = B * M;
+        const Rows rm{M, q, g};
+        float *undo = P(o.undo) + ((size_t)gp * ng + q) * o.undo_slot;
+        TR_TRY(entries(P(o.dK), P(o.dKn), rm, N, 2));
+        TR_TRY(entries(P(o.dV), P(o.dVn), rm, N, 2));
+        TR_TRY(entries(P(o.cK), undo, rm, N, 1));
+        TR_TRY(entries(P(o.cV), undo + (size_t)k * N * KD, rm, N, 1));
+        const bool last = gp == n_grad - 1;
+        wm_status st = step_fwd(rm, N, last, inv_count);
+        if (st != WM_OK) return st;
+        st = step_bwd(rm, N, last);
+        if (st != WM_OK) return st;
+      }
+    }
+    hipLaunchKernelGGL(k_loss_sum, dim3(1), dim3(256), 0, s, P(o.lossrow), (int64_t)B * T, inv_count, loss);
+    TR_TRY(hipGetLastError());
+    return WM_OK;
+  }
+};
+
+}  // namespace tr
+}  // namespace wm
+
+using namespace wm;
+
+extern "C" {
+
+size_t wm_train_workspace_bytes(const wm_config *cfg, int32_t B, int32_t T, int32_t g, int32_t n_grad) {
+  if (!cfg || wm_check_config(cfg) != WM_OK || B < 1 || T < 2 || g < 1 || n_grad < 1) return 0;
+  return tr::layout(*cfg, B, T, g, n_grad).bytes;
+}
+
+wm_status wm_train_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t B, int32_t T,
+                        int32_t g, int32_t n_nograd, int32_t n_grad, const wm_grads *grads, float *loss, void *ws,
+                        size_t ws_bytes, wm_stream stream) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  TR_CHECK(cfg->dtype == WM_F32, WM_ERR_DTYPE, "the training step runs in float32 only (dtype %d)", cfg->dtype);
+  TR_CHECK(B >= 1, WM_ERR_SHAPE, "B = %d must be >= 1", B);
+  TR_CHECK(T >= 2 && T <= cfg->T_max, WM_ERR_RANGE, "T = %d outside [2, T_max = %d]", T, cfg->T_max);
+  TR_CHECK(g >= 1, WM_ERR_SHAPE, "g = %d must be >= 1", g);
+  TR_CHECK(n_nograd >= 0 && n_grad >= 1, WM_ERR_ARG, "n_nograd = %d must be >= 0 and n_grad = %d >= 1", n_nograd,
+           n_grad);
+  TR_CHECK(w && tokens && grads && loss && ws, WM_ERR_ARG, "weights, tokens, grads, loss or workspace is NULL");
+  TR_CHECK(w->static_mix == nullptr, WM_ERR_ARG, "static_mix must be NULL: the training step trains the router");
+  const void *wp[] = {w->embed,  w->lm_head, w->final_norm, w->attn_norm, w->wq,        w->q_norm,
+                      w->wo,     w->ffn_norm, w->w_gate,    w->w_up,      w->w_down,    w->src_norm,
+                      w->router, w->chan_norm, w->wk,       w->wv,        w->k_norm,    w->rope_cos,
+                      w->rope_sin};
+  for (const void *p : wp) TR_CHECK(p, WM_ERR_ARG, "a weight pointer or the rope table is NULL");
+  const float *gp[] = {grads->embed, grads->lm_head, grads->final_norm, grads->attn_norm, grads->wq,
+                       grads->q_norm, grads->wo,     grads->ffn_norm,   grads->w_gate,    grads->w_up,
+                       grads->w_down, grads->src_norm, grads->router,   grads->chan_norm, grads->wk,
+                       grads->wv,     grads->k_norm};
+  for (const float *p : gp) TR_CHECK(p, WM_ERR_ARG, "a gradient pointer is NULL");
+  const size_t need = tr::layout(*cfg, B, T, g, n_grad).bytes;
+  TR_CHECK(ws_bytes >= need, WM_ERR_WORKSPACE, "workspace of %zu bytes, the training step needs %zu", ws_bytes,
+           need);
+  tr::Trainer t(*cfg, *w, *grads, tokens, B, T, g, n_grad, ws, (hipStream_t)stream);
+  return t.run(n_nograd, n_grad, loss);
+}
+
+}  // extern "C"

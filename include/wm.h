@@ -286,6 +286,41 @@ wm_status wm_feedback_free_decode_step(const wm_config *cfg, const wm_weights *w
                                        const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
                                        wm_stream stream);
 
+/* ---- training step with truncated backpropagation -----------------------
+ * onedev.kr "What differs": in training, gradients flow only through the last
+ * n_g passes; "How used": WhiteMatter trains with one cyclic pass without
+ * gradients followed by two passes with gradients; paperlayer.ai §3
+ * "Execution schedules": training treats the feedback as a fixed-point
+ * problem solved by passes.
+ *
+ * From the zero cache, n_nograd cyclic passes over tokens [B, T] (groups
+ * G_q, as wm_cyclic_prefill_pass) run without gradient, then n_grad passes
+ * with it. The loss is the mean next-token cross-entropy of the last pass's
+ * logits: position i < T-1 of sequence b predicts tokens[b, i+1], over the
+ * B*(T-1) predictions. Its gradient with respect to every parameter is
+ * written to `grads`, with the cache left by the no-gradient passes held
+ * constant; inside the gradient passes it flows through every cache entry a
+ * group step reads, back to the group step that wrote it.
+ *
+ * float32 only: cfg->dtype must be WM_F32 (WM_ERR_DTYPE). The weights are
+ * those of wm_weights (float), the RoPE tables included; static_mix must be
+ * NULL (WM_ERR_ARG). tokens [B, T] int32 (device), 2 <= T <= T_max
+ * (WM_ERR_RANGE), g >= 1, n_nograd >= 0, n_grad >= 1 (WM_ERR_ARG). An id
+ * outside [0, V) makes the loss and the gradients NaN. grads: float device
+ * buffers of the parameters' shapes, overwritten (not accumulated); *loss is
+ * a device float. The cache and every intermediate live in the workspace of
+ * wm_train_workspace_bytes(cfg, B, T, g, n_grad) bytes (0 on bad arguments).
+ * Deterministic: the same inputs give bit-identical results. */
+typedef struct {
+  float *embed, *lm_head, *final_norm, *attn_norm, *wq, *q_norm, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+  float *src_norm, *router, *chan_norm, *wk, *wv, *k_norm;
+} wm_grads;
+
+size_t wm_train_workspace_bytes(const wm_config *cfg, int32_t B, int32_t T, int32_t g, int32_t n_grad);
+wm_status wm_train_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t B, int32_t T,
+                        int32_t g, int32_t n_nograd, int32_t n_grad, const wm_grads *grads, float *loss, void *ws,
+                        size_t ws_bytes, wm_stream stream);
+
 /* ---- per-kernel timing (measurement support) ---------------------------
  * Kernel kinds launched by the calls above. */
 typedef enum {

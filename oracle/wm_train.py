@@ -104,7 +104,7 @@ def _rope(x, pos, base):
     d = x.shape[-1]
     h = d // 2
     ang = torch.from_numpy(O.rope_angles(np.asarray(pos), d, base))[:, None, :]
-    c, s = torch.cos(ang), torch.sin(ang)
+    c, s = torch.cos(ang).to(x.dtype), torch.sin(ang).to(x.dtype)
     x1, x2 = x[..., :h], x[..., h:]
     return torch.cat([x1 * c - x2 * s, x1 * s + x2 * c], dim=-1)
 
@@ -177,7 +177,7 @@ def _pass(P, w, tokens, Kc, Vc, g, want_logits):
     into a copy, so the entries an earlier step read stay as they were)."""
     torch = _torch()
     B, T = tokens.shape
-    logits = torch.zeros((B, T, w.V), dtype=torch.float64) if want_logits else None
+    logits = torch.zeros((B, T, w.V), dtype=Kc.dtype) if want_logits else None
     for q in range(O.n_groups_nonempty(T, g)):
         Mq = len(O.group_positions(T, g, q))
         bidx, pos = O.tokset_rows(B, Mq, q, g)
@@ -217,15 +217,18 @@ def forward_passes(M, tokens, g, n_passes):
     return Kc.numpy(), Vc.numpy(), lg.numpy()
 
 
-def train_step(M, tokens, g, n_nograd=1, n_grad=2):
+def train_step(M, tokens, g, n_nograd=1, n_grad=2, dtype=None):
     """R26-R28: loss and gradient of one training step.  Returns (loss,
-    {name: float64 array of the parameter's shape})."""
+    {name: float64 array of the parameter's shape}).  ``dtype`` (a torch
+    float type, float64 by default) is the arithmetic; float32 gives the
+    rounding floor of a float32 implementation of the same steps."""
     torch = _torch()
+    dtype = torch.float64 if dtype is None else dtype
     w = M.w
     tokens = np.asarray(tokens)
-    P = {n: torch.tensor(np.asarray(M.W[n], np.float64), requires_grad=True) for n in PARAM_NAMES}
+    P = {n: torch.tensor(np.asarray(M.W[n], np.float64), dtype=dtype, requires_grad=True) for n in PARAM_NAMES}
     shape = (w.k, tokens.shape[0], w.Hkv, w.T_max, w.d)
-    Kc, Vc = torch.zeros(shape, dtype=torch.float64), torch.zeros(shape, dtype=torch.float64)
+    Kc, Vc = torch.zeros(shape, dtype=dtype), torch.zeros(shape, dtype=dtype)
     with torch.no_grad():
         for _ in range(n_nograd):
             Kc, Vc, _ = _pass(P, w, tokens, Kc, Vc, g, want_logits=False)
@@ -235,4 +238,4 @@ def train_step(M, tokens, g, n_nograd=1, n_grad=2):
         Kc, Vc, logits = _pass(P, w, tokens, Kc, Vc, g, want_logits=(i == n_grad - 1))
     loss = _ce(logits, tokens)
     loss.backward()
-    return float(loss.detach()), {n: P[n].grad.numpy().copy() for n in PARAM_NAMES}
+    return float(loss.detach()), {n: P[n].grad.numpy().astype(np.float64) for n in PARAM_NAMES}

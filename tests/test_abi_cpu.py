@@ -25,7 +25,7 @@ def cfg_of(w, dtype=C.WM_BF16, **kw):
 
 def test_library_exports_every_declared_function():
     names = C.header_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     assert set(names) <= exported, set(names) - exported
@@ -274,3 +274,40 @@ def test_binding_checks_tensors_before_calling():
     if torch.cuda.is_available():  # (a CPU tensor for a model on the GPU)
         with pytest.raises(ValueError):
             api.check_tensor("tokens", torch.zeros(3, dtype=torch.int32), torch.int32, torch.device("cuda"))
+
+
+def test_train_step_validates_before_launch():
+    """wm_train_step: float32 only, the routed model only (no static mixing),
+    2 <= T <= T_max, g >= 1, n_nograd >= 0, n_grad >= 1, every pointer set,
+    workspace of wm_train_workspace_bytes; each refused before any launch."""
+    L = C.lib()
+    w = WORKLOADS["tiny_fp32"]
+    c = cfg_of(w, dtype=C.WM_F32)
+    W = _weights()
+    G = C.WmGrads(*[FAKE for _ in C.GRAD_FIELDS])
+    need = L.wm_train_workspace_bytes(ctypes.byref(c), w.B, w.T, w.g, 2)
+    assert need > 0
+    assert L.wm_train_workspace_bytes(ctypes.byref(c), w.B, w.T, w.g, 3) > need  # one undo slot per gradient step
+    assert L.wm_train_workspace_bytes(ctypes.byref(c), w.B, 1, w.g, 2) == 0
+    assert L.wm_train_workspace_bytes(ctypes.byref(c), w.B, w.T, w.g, 0) == 0
+
+    def call(cfg=c, Wt=W, Gt=G, B=w.B, T=w.T, g=w.g, n0=1, n1=2, n=need, loss=FAKE):
+        return L.wm_train_step(ctypes.byref(cfg), ctypes.byref(Wt), FAKE, B, T, g, n0, n1,
+                               None if Gt is None else ctypes.byref(Gt), loss, FAKE, n, None)
+
+    assert call(cfg=cfg_of(w, dtype=C.WM_BF16)) == -3
+    assert call(T=1) == -5 and call(T=w.T_max + 1) == -5
+    assert call(g=0) == -2
+    assert call(n0=-1) == -1 and call(n1=0) == -1
+    assert call(B=0) == -2
+    assert call(Gt=None) == -1 and call(loss=None) == -1
+    assert call(n=need - 1) == -4
+    Ws = _weights()
+    Ws.static_mix = FAKE
+    assert call(Wt=Ws) == -1 and b"static_mix" in L.wm_last_error()
+    W0 = _weights()
+    W0.rope_cos = None
+    assert call(Wt=W0) == -1
+    G0 = C.WmGrads(*[FAKE for _ in C.GRAD_FIELDS])
+    G0.router = None
+    assert call(Gt=G0) == -1
