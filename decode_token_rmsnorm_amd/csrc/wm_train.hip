@@ -116,21 +116,26 @@ __global__ void k_swiglu_bwd(const float *G, const float *U, const float *dact, 
 // C[z] = alpha * op(A[z]) op(B[z]) + beta * C[z], op(A) [M, K], op(B) [K, N],
 // row-major.  TA: A is stored [K, M] (leading dim lda), else [M, K].  TB: B
 // is stored [N, K], else [K, N].  beta = 0 never reads C.  64 x 64 tiles,
-// 256 threads with 4 x 4 outputs each, k in steps of 16 through LDS.
+// 256 threads with 4 x 4 outputs each, k in steps of 16 through LDS.  With
+// splits > 1, blockIdx.z = batch * splits + split: the block sums k in
+// [split * kchunk, (split + 1) * kchunk) and C[blockIdx.z] is a partial
+// (k_split_sum adds them).
 constexpr int GT = 64, GK = 16;
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64_t sA, const float *B, int64_t ldb,
                                               int64_t sB, float *C, int64_t ldc, int64_t sC, int M, int N, int K,
-                                              float alpha, float beta) {
+                                              float alpha, float beta, int splits, int kchunk) {
   __shared__ __attribute__((aligned(16))) float As[GK][GT + 4];
   __shared__ __attribute__((aligned(16))) float Bs[GK][GT + 4];
-  A += blockIdx.z * sA;
-  B += blockIdx.z * sB;
+  const int batch = blockIdx.z / splits, split = blockIdx.z - batch * splits;
+  A += batch * sA;
+  B += batch * sB;
   C += blockIdx.z * sC;
+  const int kb = split * kchunk, ke = min(K, kb + kchunk);
   const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
   const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += GK) {
+  for (int k0 = kb; k0 < ke; k0 += GK) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 256 * i;
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64
       }
       const int gm = m0 + mm, gk = k0 + kk;
       float v = 0.f;
-      if (gm < M && gk < K) v = TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk];
+      if (gm < M && gk < ke) v = TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk];
       As[kk][mm] = v;
       int nn;
       if (TB) {
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64
       }
       const int gn = n0 + nn, gk2 = k0 + kk;
       float u = 0.f;
-      if (gn < N && gk2 < K) u = TB ? B[(int64_t)gn * ldb + gk2] : B[(int64_t)gk2 * ldb + gn];
+      if (gn < N && gk2 < ke) u = TB ? B[(int64_t)gn * ldb + gk2] : B[(int64_t)gk2 * ldb + gn];
       Bs[kk][nn] = u;
     }
     __syncthreads();
@@ -182,6 +187,20 @@ __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64
       float *c = C + (int64_t)gm * ldc + gn;
       *c = beta == 0.f ? alpha * acc[i][j] : alpha * acc[i][j] + beta * *c;
     }
+  }
+}
+
+// C[z] = beta * C[z] + sum over the splits (in order) of part[z * splits + s], [M, N]
+__global__ void k_split_sum(const float *part, int splits, float *C, int64_t ldc, int64_t sC, int M, int N, int Z,
+                            float beta) {
+  const int64_t MN = (int64_t)M * N, total = MN * Z;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t z = i / MN, e = i - z * MN;
+    const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
+    float t = 0.f;
+    for (int sp = 0; sp < splits; ++sp) t += part[(z * splits + sp) * MN + e];
+    float *c = C + z * sC + (int64_t)m * ldc + n;
+    *c = beta == 0.f ? t : t + beta * *c;
   }
 }
 
@@ -213,13 +232,24 @@ __global__ __launch_bounds__(64) void k_rms_bwd(const float *x, const float *gai
     *o = accumulate ? *o + v : v;
   }
 }
-// dgain[gi, c] += sum over the rows r of group gi of dy[r, c] x[r, c] rinv[r]
-__global__ void k_gain_grad(const float *x, const float *dy, const float *rinv, float *dg, int rpg, int D) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x, gi = blockIdx.y;
-  if (c >= D) return;
+// dgain[gi, c] += sum over the rows r of group gi of dy[r, c] x[r, c] rinv[r].
+// Block: 64 columns x 16 row slices (slice j takes rows j, j + 16, ...); the
+// slices' sums are added in slice order.
+__global__ __launch_bounds__(1024) void k_gain_grad(const float *x, const float *dy, const float *rinv, float *dg,
+                                                    int rpg, int D) {
+  __shared__ float part[16][64];
+  const int cl = threadIdx.x & 63, sl = threadIdx.x >> 6, c = blockIdx.x * 64 + cl, gi = blockIdx.y;
   float s = 0.f;
-  for (int64_t r = (int64_t)gi * rpg; r < (int64_t)(gi + 1) * rpg; ++r) s += dy[r * D + c] * x[r * D + c] * rinv[r];
-  dg[(int64_t)gi * D + c] += s;
+  if (c < D)
+    for (int64_t r = (int64_t)gi * rpg + sl; r < (int64_t)(gi + 1) * rpg; r += 16)
+      s += dy[r * D + c] * x[r * D + c] * rinv[r];
+  part[sl][cl] = s;
+  __syncthreads();
+  if (sl == 0 && c < D) {
+    float t = 0.f;
+    for (int j = 0; j < 16; ++j) t += part[j][cl];
+    dg[(int64_t)gi * D + c] += t;
+  }
 }
 
 // ------------------------------------------------------------------ RoPE
@@ -281,47 +311,65 @@ __global__ void k_embed_bwd(const int32_t *tokens, int T, Rows rm, const float *
 
 // ------------------------------------------------------------------ attention
 // Strict causal attention of row n (position i), head h to keys s < i of the
-// channel (K, V: [B, Hkv, Tc, d]); one wave per (n, h), a lane per key in
-// chunks of 64, lanes c and c + 64 own output dims.  Keeps the scaled-score
-// max m and the sum l of exp(score - m) for the backward.
-__global__ __launch_bounds__(64) void k_attn(const float *q, const float *Kc, const float *Vc, Rows rm, int Hq,
-                                             int Hkv, int d, int Tc, float scale, float *out, float *mst,
-                                             float *lst) {
-  __shared__ float qs[128];
-  const int n = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int G = Hq / Hkv, hk = h / G, b = rm.seq(n), i = rm.pos(n);
-  const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * d, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * d;
-  const int64_t qo = ((int64_t)n * Hq + h) * d;
-  for (int c = lane; c < d; c += 64) qs[c] = q[qo + c];
-  __syncthreads();
-  float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int t0 = 0; t0 < i; t0 += 64) {
-    const int t = t0 + lane;
-    float s = -INFINITY;
-    if (t < i) {
-      float dot = 0.f;
-      for (int c = 0; c < d; ++c) dot += qs[c] * K[(int64_t)t * d + c];
-      s = dot * scale;
+// channel (K, V: [B, Hkv, Tc, d]).  A block of 4 waves takes 4 consecutive
+// query slots (m, g) of one sequence b and KV head hk (slot = m*G + g, head
+// hk*G + g), one per wave; they share the key chunks: 64 K and V rows staged
+// in LDS by coalesced loads (row pitch DH + 1, so lane t reading row t at
+// column c hits bank (t + c) mod 64).  In a chunk, lane t scores key t0 + t;
+// lanes c and c + 64 own output dims.  Keeps the scaled-score max m and the
+// sum l of exp(score - m) for the backward.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, const float *Vc, Rows rm, int Hq,
+                                              int Hkv, int Tc, float scale, float *out, float *mst, float *lst) {
+  constexpr int KP = DH + 1;
+  __shared__ float qs[4][DH], Ks[64 * KP], Vs[64 * KP];
+  const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nslot = rm.M * G;
+  const int slot = blockIdx.y * 4 + wave, last = min(blockIdx.y * 4 + 3, nslot - 1);
+  const bool act = slot < nslot;
+  const int m = act ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act ? slot - m * G : 0);
+  const int i = act ? rm.pos(n) : 0, imax = rm.pos(b * rm.M + last / G);
+  const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * DH, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * DH;
+  const int64_t qo = ((int64_t)n * Hq + h) * DH;
+  for (int c = lane; c < DH; c += 64) qs[wave][c] = act ? q[qo + c] : 0.f;
+  float mx = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int t0 = 0; t0 < imax; t0 += 64) {
+    const int nk = min(64, imax - t0);
+    __syncthreads();  // (the previous chunk's reads are done; qs is written)
+    for (int e = threadIdx.x; e < nk * DH; e += 256) {
+      const int r = e / DH, c = e - r * DH;
+      Ks[r * KP + c] = K[(int64_t)(t0 + r) * DH + c];
+      Vs[r * KP + c] = V[(int64_t)(t0 + r) * DH + c];
     }
-    const float mnew = fmaxf(m, wmax(s));
-    const float p = t < i ? expf(s - mnew) : 0.f, alpha = expf(m - mnew);
-    l = l * alpha + wsum(p);
-    a0 *= alpha;
-    a1 *= alpha;
-    const int nu = min(64, i - t0);
-    for (int u = 0; u < nu; ++u) {
-      const float pu = __shfl(p, u);
-      const float *vr = V + (int64_t)(t0 + u) * d;
-      if (lane < d) a0 += pu * vr[lane];
-      if (lane + 64 < d) a1 += pu * vr[lane + 64];
+    __syncthreads();
+    if (t0 < i) {  // (wave-uniform)
+      const int nv = min(64, i - t0);
+      float sc = -INFINITY;
+      if (lane < nv) {
+        float dot = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < DH; ++c) dot += qs[wave][c] * Ks[lane * KP + c];
+        sc = dot * scale;
+      }
+      const float mnew = fmaxf(mx, wmax(sc));
+      const float p = lane < nv ? expf(sc - mnew) : 0.f, alpha = expf(mx - mnew);
+      l = l * alpha + wsum(p);
+      a0 *= alpha;
+      a1 *= alpha;
+      for (int u = 0; u < nv; ++u) {
+        const float pu = __shfl(p, u);
+        if (lane < DH) a0 += pu * Vs[u * KP + lane];
+        if (lane + 64 < DH) a1 += pu * Vs[u * KP + lane + 64];
+      }
+      mx = mnew;
     }
-    m = mnew;
   }
+  if (!act) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (lane < d) out[qo + lane] = a0 * inv;
-  if (lane + 64 < d) out[qo + lane + 64] = a1 * inv;
+  if (lane < DH) out[qo + lane] = a0 * inv;
+  if (lane + 64 < DH) out[qo + lane + 64] = a1 * inv;
   if (lane == 0) {
-    mst[(int64_t)n * Hq + h] = m;
+    mst[(int64_t)n * Hq + h] = mx;
     lst[(int64_t)n * Hq + h] = l;
   }
 }
@@ -329,62 +377,82 @@ __global__ __launch_bounds__(64) void k_attn(const float *q, const float *Kc, co
 // Dn = sum_t p_t dP_t (equal to dout . out; summed from the same p_t dP_t
 // products, so that sum_t dS_t stays 0 to rounding also where the row has
 // few keys and dP_t and Dn nearly cancel); dq = scale * sum_t dS_t K_t.
-// Keeps Dn for the key-side kernel.
-__global__ __launch_bounds__(64) void k_attn_dq(const float *q, const float *Kc, const float *Vc, const float *dout,
-                                                const float *mst, const float *lst, Rows rm, int Hq, int Hkv, int d,
-                                                int Tc, float scale, float *dq, float *Dst) {
-  __shared__ float qs[128], ds[128];
-  const int n = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int G = Hq / Hkv, hk = h / G, b = rm.seq(n), i = rm.pos(n);
-  const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * d, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * d;
-  const int64_t qo = ((int64_t)n * Hq + h) * d;
-  for (int c = lane; c < d; c += 64) {
-    qs[c] = q[qo + c];
-    ds[c] = dout[qo + c];
+// Keeps Dn for the key-side kernel.  Blocks, slots and staged chunks as in
+// k_attn; the chunks are walked twice (Dn first, then dS and dq).
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc, const float *Vc, const float *dout,
+                                                 const float *mst, const float *lst, Rows rm, int Hq, int Hkv,
+                                                 int Tc, float scale, float *dq, float *Dst) {
+  constexpr int KP = DH + 1;
+  __shared__ float qs[4][DH], ds[4][DH], Ks[64 * KP], Vs[64 * KP];
+  const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nslot = rm.M * G;
+  const int slot = blockIdx.y * 4 + wave, last = min(blockIdx.y * 4 + 3, nslot - 1);
+  const bool act = slot < nslot;
+  const int m = act ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act ? slot - m * G : 0);
+  const int i = act ? rm.pos(n) : 0, imax = rm.pos(b * rm.M + last / G);
+  const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * DH, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * DH;
+  const int64_t qo = ((int64_t)n * Hq + h) * DH;
+  for (int c = lane; c < DH; c += 64) {
+    qs[wave][c] = act ? q[qo + c] : 0.f;
+    ds[wave][c] = act ? dout[qo + c] : 0.f;
   }
-  __syncthreads();
-  const float m = mst[(int64_t)n * Hq + h], l = lst[(int64_t)n * Hq + h], invl = l > 0.f ? 1.f / l : 0.f;
-  // p_t and dP_t of the key this lane takes
-  auto key = [&](int t, float &p, float &dP) {
-    float s = 0.f;
-    dP = 0.f;
-    for (int c = 0; c < d; ++c) {
-      s += qs[c] * K[(int64_t)t * d + c];
-      dP += ds[c] * V[(int64_t)t * d + c];
+  const float mrow = act ? mst[(int64_t)n * Hq + h] : 0.f, lrow = act ? lst[(int64_t)n * Hq + h] : 0.f;
+  const float invl = lrow > 0.f ? 1.f / lrow : 0.f;
+  auto stage = [&](int t0, int nk) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < nk * DH; e += 256) {
+      const int r = e / DH, c = e - r * DH;
+      Ks[r * KP + c] = K[(int64_t)(t0 + r) * DH + c];
+      Vs[r * KP + c] = V[(int64_t)(t0 + r) * DH + c];
     }
-    p = expf(s * scale - m) * invl;
+    __syncthreads();
+  };
+  // p and dP of key t0 + lane (staged)
+  auto key = [&](float &p, float &dP) {
+    float sc = 0.f;
+    dP = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < DH; ++c) {
+      sc += qs[wave][c] * Ks[lane * KP + c];
+      dP += ds[wave][c] * Vs[lane * KP + c];
+    }
+    p = expf(sc * scale - mrow) * invl;
   };
   float Dp = 0.f;
-  for (int t0 = 0; t0 < i; t0 += 64) {
-    const int t = t0 + lane;
-    if (t < i) {
+  for (int t0 = 0; t0 < imax; t0 += 64) {
+    stage(t0, min(64, imax - t0));
+    if (lane < i - t0) {
       float p, dP;
-      key(t, p, dP);
+      key(p, dP);
       Dp += p * dP;
     }
   }
   const float Dn = wsum(Dp);
   float g0 = 0.f, g1 = 0.f;
-  for (int t0 = 0; t0 < i; t0 += 64) {
-    const int t = t0 + lane;
-    float dS = 0.f;
-    if (t < i) {
-      float p, dP;
-      key(t, p, dP);
-      dS = p * (dP - Dn);
-    }
-    const int nu = min(64, i - t0);
-    for (int u = 0; u < nu; ++u) {
-      const float su = __shfl(dS, u);
-      const float *kr = K + (int64_t)(t0 + u) * d;
-      if (lane < d) g0 += su * kr[lane];
-      if (lane + 64 < d) g1 += su * kr[lane + 64];
+  for (int t0 = 0; t0 < imax; t0 += 64) {
+    stage(t0, min(64, imax - t0));
+    if (t0 < i) {  // (wave-uniform)
+      const int nv = min(64, i - t0);
+      float dS = 0.f;
+      if (lane < nv) {
+        float p, dP;
+        key(p, dP);
+        dS = p * (dP - Dn);
+      }
+      for (int u = 0; u < nv; ++u) {
+        const float su = __shfl(dS, u);
+        if (lane < DH) g0 += su * Ks[u * KP + lane];
+        if (lane + 64 < DH) g1 += su * Ks[u * KP + lane + 64];
+      }
     }
   }
-  if (lane < d) dq[qo + lane] = g0 * scale;
-  if (lane + 64 < d) dq[qo + lane + 64] = g1 * scale;
+  if (!act) return;
+  if (lane < DH) dq[qo + lane] = g0 * scale;
+  if (lane + 64 < DH) dq[qo + lane + 64] = g1 * scale;
   if (lane == 0) Dst[(int64_t)n * Hq + h] = Dn;
 }
+
 // dK_t += scale * sum dS q, dV_t += sum p dout over the rows n of sequence b
 // with position > t and the heads of KV head hk; one wave per (b, hk, t).
 __global__ __launch_bounds__(64) void k_attn_dkv(const float *q, const float *Kc, const float *Vc, const float *dout,
@@ -571,6 +639,7 @@ struct Ws {
   // backward
   size_t dh, dS, da, dq, dout, dG, dU, dact, db, Dst, dKn, dVn, dkraw, dc, dm, dA, dn, du, dz, dxf, lossrow;
   size_t enext, ehead;  // (int arrays)
+  size_t split, split_cap;  // split-k partials (floats)
   size_t bytes;
 };
 
@@ -640,6 +709,10 @@ inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad) {
   w.lossrow = t((size_t)B * T);
   w.enext = t(N);
   w.ehead = t(N);
+  // split-k partials: up to 8 of the largest product other than the LM head's
+  const size_t wide = std::max({F, D, QD, R * D, L * k, KD});
+  w.split_cap = 8 * std::max({N * wide, D * F, QD * D, L * k * R * D, k * KD * D, k * N * D});
+  w.split = t(w.split_cap);
   w.bytes = l.total;
   return w;
 }
@@ -683,23 +756,40 @@ struct Trainer {
     hipLaunchKernelGGL(k_add, dim3(grid1(n)), dim3(256), 0, s, y, x, n);
     return hipGetLastError();
   }
-  // C = alpha op(A) op(B) + beta C, batched over Z with element strides
+  // C = op(A) op(B) + beta C, batched over Z with element strides.  Grids
+  // of fewer tiles than compute units split k (chunks of at least 128, up to
+  // 8 splits) into partials in the workspace, summed in split order.
   hipError_t gemm(bool ta, bool tb, const float *A, int64_t lda, const float *B_, int64_t ldb, float *C, int64_t ldc,
                   int M, int N, int K, float beta, int Z = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, Z);
+    const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * Z;
+    int splits = 1;
+    if (tiles < 256) {
+      splits = (int)std::min<int64_t>(8, std::min<int64_t>((256 + tiles - 1) / tiles, K / 128));
+      if (splits < 2 || (size_t)splits * Z * M * N > o.split_cap) splits = 1;
+    }
+    const int kchunk = splits > 1 ? ((K + splits - 1) / splits + GK - 1) / GK * GK : K;
+    if (splits > 1) splits = (K + kchunk - 1) / kchunk;
+    float *Cd = splits > 1 ? P(o.split) : C;
+    const int64_t ldd = splits > 1 ? N : ldc, sD = splits > 1 ? (int64_t)M * N : sC;
+    const float bd = splits > 1 ? 0.f : beta;
+    dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, Z * splits);
     if (!ta && !tb)
-      hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, C, ldc, sC, M, N, K,
-                         1.f, beta);
+      hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N,
+                         K, 1.f, bd, splits, kchunk);
     else if (!ta && tb)
-      hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, C, ldc, sC, M, N, K,
-                         1.f, beta);
+      hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
+                         1.f, bd, splits, kchunk);
     else if (ta && !tb)
-      hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, C, ldc, sC, M, N, K,
-                         1.f, beta);
+      hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
+                         1.f, bd, splits, kchunk);
     else
-      hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, C, ldc, sC, M, N, K,
-                         1.f, beta);
+      hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
+                         1.f, bd, splits, kchunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t total = (int64_t)M * N * Z;
+    hipLaunchKernelGGL(k_split_sum, dim3(grid1(total)), dim3(256), 0, s, P(o.split), splits, C, ldc, sC, M, N, Z, beta);
     return hipGetLastError();
   }
   hipError_t rms(const float *x, const float *gain, int rpg, float *y, float *rinv, int rows, int width) {
@@ -712,7 +802,7 @@ struct Trainer {
     hipLaunchKernelGGL(k_rms_bwd, dim3(rows), dim3(64), 0, s, x, gain, rpg, rinv, dy, dx, acc ? 1 : 0, width);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gain_grad, dim3((width + 255) / 256, ngain), dim3(256), 0, s, x, dy, rinv, dgain, rpg, width);
+    hipLaunchKernelGGL(k_gain_grad, dim3((width + 63) / 64, ngain), dim3(1024), 0, s, x, dy, rinv, dgain, rpg, width);
     return hipGetLastError();
   }
   hipError_t rope(float *x, Rows rm, int N, int rows, int H, bool inverse) {
@@ -727,6 +817,31 @@ struct Trainer {
     return hipGetLastError();
   }
   float *chanK(size_t cacheoff, int ch) const { return P(cacheoff) + (size_t)ch * B * KD * T; }
+  hipError_t attn_fwd(const float *q, const float *K, const float *Vv, Rows rm, int N, float scale, float *out,
+                      float *mst, float *lst) {
+    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 3) / 4);
+    if (c.d == 32)
+      hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
+    else if (c.d == 64)
+      hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
+    else
+      hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
+    return hipGetLastError();
+  }
+  hipError_t attn_dq(const float *q, const float *K, const float *Vv, const float *dout, const float *mst,
+                     const float *lst, Rows rm, int N, float scale, float *dq, float *Dst) {
+    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 3) / 4);
+    if (c.d == 32)
+      hipLaunchKernelGGL(k_attn_dq<32>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
+                         Dst);
+    else if (c.d == 64)
+      hipLaunchKernelGGL(k_attn_dq<64>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
+                         Dst);
+    else
+      hipLaunchKernelGGL(k_attn_dq<128>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale,
+                         dq, Dst);
+    return hipGetLastError();
+  }
 
   // The pool of one branch for the rows of the step (S from the tape):
   // nsrc, rS, u, A, m, rM, c; keys also kraw, rK and K_new (normed, turned);
@@ -770,9 +885,8 @@ struct Trainer {
       TR_TRY(rms(qraw, w.q_norm + (size_t)l * c.d, N * c.Hq, q, P(o.rQ) + (size_t)l * N * c.Hq, N * c.Hq, c.d));
       TR_TRY(rope(q, rm, N, N, c.Hq, false));
       const int ch = l % k;
-      hipLaunchKernelGGL(k_attn, dim3(N, c.Hq), dim3(64), 0, s, q, chanK(o.cK, ch), chanK(o.cV, ch), rm, c.Hq, c.Hkv,
-                         c.d, T, scale, out, P(o.mst) + (size_t)l * N * c.Hq, P(o.lst) + (size_t)l * N * c.Hq);
-      TR_TRY(hipGetLastError());
+      TR_TRY(attn_fwd(q, chanK(o.cK, ch), chanK(o.cV, ch), rm, N, scale, out, P(o.mst) + (size_t)l * N * c.Hq,
+                      P(o.lst) + (size_t)l * N * c.Hq));
       TR_TRY(copy(h1, S, nd));
       TR_TRY(gemm(false, true, out, QD, W(w.wo) + (size_t)l * D * QD, QD, h1, D, N, D, QD, 1.f));
       TR_TRY(rms(h1, w.ffn_norm + (size_t)l * D, N, bn, P(o.rF) + (size_t)l * N, N, D));
@@ -876,9 +990,7 @@ struct Trainer {
       TR_TRY(gemm(false, false, dh, D, W(w.wo) + (size_t)l * D * QD, QD, P(o.dout), QD, N, QD, D, 0.f));
       TR_TRY(gemm(true, false, dh, D, out, QD, gr.wo + (size_t)l * D * QD, QD, D, QD, N, 1.f));
       const int ch = l % k;
-      hipLaunchKernelGGL(k_attn_dq, dim3(N, c.Hq), dim3(64), 0, s, q, chanK(o.cK, ch), chanK(o.cV, ch), P(o.dout),
-                         mst, lst, rm, c.Hq, c.Hkv, c.d, T, scale, P(o.dq), P(o.Dst));
-      TR_TRY(hipGetLastError());
+      TR_TRY(attn_dq(q, chanK(o.cK, ch), chanK(o.cV, ch), P(o.dout), mst, lst, rm, N, scale, P(o.dq), P(o.Dst)));
       hipLaunchKernelGGL(k_attn_dkv, dim3(B * c.Hkv, T), dim3(64), 0, s, q, chanK(o.cK, ch), chanK(o.cV, ch),
                          P(o.dout), mst, lst, P(o.Dst), rm, c.Hq, c.Hkv, c.d, T, scale, chanK(o.dK, ch),
                          chanK(o.dV, ch));
