@@ -20,6 +20,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3   # MI355X float32 vector
 
 
 CSRC = "decode_token_rmsnorm_amd/csrc/"
@@ -232,6 +233,43 @@ def bench_decode(steps, warmup):
                          "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                          "traffic": profiled_traffic("decode_attn"),
                          "algorithmic_per_launch": f"{kv_bytes:.4e} B = 2*{w.B}*{w.Hkv}*{t}*{w.d}*2"}}
+
+
+def bench_train(steps=1, warmup=1):
+    """One training step with truncated backpropagation (wm_train_step: one
+    cyclic pass without gradient, two with, next-token cross-entropy of the
+    last pass) at the small model's widths in float32: L16 D512 8/4 x 64,
+    F1536, k8, p2, V32768, B8 T2048, g16.  tokens/s per step; the
+    algorithmic FLOP (a forward pass per pass plus twice a forward per
+    gradient pass: 7 forward passes) against the float32 vector peak, since
+    every training kernel runs on the vector ALUs in float32."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+    from wm_inputs import WORKLOADS, make_tokens, make_weights
+
+    w = WORKLOADS["small_prefill"].replace(dtype="f32")
+    model = wm.Model(w, make_weights(w, seed=0), "f32")
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    peak_reset()
+    ws = wm.train_workspace(model, w.B, w.T, w.g, 2)
+    grads = None
+    for _ in range(warmup):
+        loss, grads = wm.train_step(model, tok, w.g, 1, 2, grads=grads, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        loss, grads = wm.train_step(model, tok, w.g, 1, 2, grads=grads, ws=ws)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    flop = 7 * w.B * w.T * flops_per_token(w, "wm")
+    ach = flop / dt / 1e12
+    return {"workload": "small model widths, fp32: L16 D512 Hq8 Hkv4 d64 F1536 k8 p2 V32768, B8 T2048, g16, "
+                        "1 pass without + 2 with gradient",
+            "value": w.B * w.T / dt, "unit": "tokens/s (training steps)", "s_per_step": dt, "steps": steps,
+            "loss": float(loss.item()), "peak_memory_gib": peak_gib(),
+            "roofline": {"kernel": "whole training step", "bound": "alu", "achieved": ach, "peak": FP32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": ach / FP32_PEAK_TFLOPS, "traffic": None,
+                         "algorithmic_per_step": f"{flop:.4e} FLOP = 7 forward passes of {w.B}x{w.T} tokens"}}
 
 
 def bench_small_prefill():
@@ -628,8 +666,9 @@ def main():
     ap.add_argument("--skip-variants", action="store_true")
     ap.add_argument("--skip-small", action="store_true")
     ap.add_argument("--skip-decode-1p3b", action="store_true")
+    ap.add_argument("--skip-train", action="store_true")
     ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep", "variants", "peaks", "small",
-                                       "decode_1p3b", "cpu"], default=None,
+                                       "decode_1p3b", "cpu", "train"], default=None,
                     help="profiling aid: run only this part and print its object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for HBM byte counters)")
@@ -653,6 +692,7 @@ def main():
         part = (bench_decode(a.decode_steps, 5) if a.only == "decode" else bench_mix(20, 3) if a.only == "mix"
                 else device_peaks() if a.only == "peaks" else bench_small_prefill() if a.only == "small"
                 else bench_decode_1p3b() if a.only == "decode_1p3b" else cpu_baseline() if a.only == "cpu"
+                else bench_train() if a.only == "train"
                 else bench_vanilla(a.steps, a.decode_steps) if a.only == "vanilla"
                 else bench_variants(a.steps) if a.only == "variants" else bench_sweep())
         print(json.dumps({a.only: part}), flush=True)
@@ -665,6 +705,7 @@ def main():
     variants = None if a.skip_variants else bench_variants(a.steps)
     small = None if a.skip_small else bench_small_prefill()
     dec13 = None if a.skip_decode_1p3b else bench_decode_1p3b()
+    train = None if a.skip_train else bench_train()
     if van is not None:
         # the pages' comparison: WhiteMatter prefill as a share of vanilla's (one
         # vanilla pass against one, and against the workload's 3 passes:
@@ -704,6 +745,7 @@ def main():
         "mix_kv": mix,
         "small_prefill": small,
         "decode_1p3b": dec13,
+        "train_step": train,
         "vanilla": van,
         "schedule_sweep": sweep,
         "variants": variants,

@@ -454,43 +454,86 @@ __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc
 }
 
 // dK_t += scale * sum dS q, dV_t += sum p dout over the rows n of sequence b
-// with position > t and the heads of KV head hk; one wave per (b, hk, t).
-__global__ __launch_bounds__(64) void k_attn_dkv(const float *q, const float *Kc, const float *Vc, const float *dout,
-                                                 const float *mst, const float *lst, const float *Dst, Rows rm,
-                                                 int Hq, int Hkv, int d, int Tc, float scale, float *dK, float *dV) {
-  const int pair = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
-  const int b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
-  const int64_t ko = (((int64_t)b * Hkv + hk) * Tc + t) * d;
-  const float k0 = lane < d ? Kc[ko + lane] : 0.f, k1 = lane + 64 < d ? Kc[ko + lane + 64] : 0.f;
-  const float v0 = lane < d ? Vc[ko + lane] : 0.f, v1 = lane + 64 < d ? Vc[ko + lane + 64] : 0.f;
-  float gk0 = 0.f, gk1 = 0.f, gv0 = 0.f, gv1 = 0.f;
-  bool any = false;
-  for (int mm = 0; mm < rm.M; ++mm) {
-    const int n = b * rm.M + mm;
-    if (rm.pos(n) <= t) continue;
-    any = true;
-    for (int gg = 0; gg < G; ++gg) {
-      const int h = hk * G + gg;
-      const int64_t qo = ((int64_t)n * Hq + h) * d;
-      const float q0 = lane < d ? q[qo + lane] : 0.f, q1 = lane + 64 < d ? q[qo + lane + 64] : 0.f;
-      const float o0 = lane < d ? dout[qo + lane] : 0.f, o1 = lane + 64 < d ? dout[qo + lane + 64] : 0.f;
-      const float s = wsum(q0 * k0 + q1 * k1) * scale, dP = wsum(o0 * v0 + o1 * v1);
-      const float p = expf(s - mst[(int64_t)n * Hq + h]) / lst[(int64_t)n * Hq + h];
-      const float dS = p * (dP - Dst[(int64_t)n * Hq + h]);
-      gk0 += dS * scale * q0;
-      gk1 += dS * scale * q1;
-      gv0 += p * o0;
-      gv1 += p * o1;
+// with position > t and the heads of KV head hk.  A block of 4 waves takes a
+// chunk of 64 keys of (b, hk), staged in LDS as in k_attn; the waves take
+// the query slots round-robin.  For a slot, lane t computes p and dS of key
+// t0 + t from the staged rows; then lane c accumulates dims c (and c + 64,
+// in a second walk for head dim 128) of all 64 keys in registers.  The
+// waves' partial sums are added through LDS in wave order.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_dkv(const float *q, const float *Kc, const float *Vc, const float *dout,
+                                                  const float *mst, const float *lst, const float *Dst, Rows rm,
+                                                  int Hq, int Hkv, int Tc, float scale, float *dK, float *dV) {
+  constexpr int KP = DH + 1;
+  __shared__ float Ks[64 * KP], Vs[64 * KP], qs[4][DH], ds[4][DH], accK[64 * 64], accV[64 * 64];
+  const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t0 = blockIdx.y * 64;
+  const int nk = min(64, Tc - t0), nslot = rm.M * G;
+  const int64_t base = ((int64_t)b * Hkv + hk) * Tc * DH;
+  // first slot whose row reads any key of the chunk (positions grow with m)
+  int m0 = 0;
+  while (m0 < rm.M && rm.pos(b * rm.M + m0) <= t0) ++m0;
+  if (m0 >= rm.M) return;  // (block-uniform)
+  for (int e = threadIdx.x; e < nk * DH; e += 256) {
+    const int r = e / DH, c = e - r * DH;
+    Ks[r * KP + c] = Kc[base + (int64_t)(t0 + r) * DH + c];
+    Vs[r * KP + c] = Vc[base + (int64_t)(t0 + r) * DH + c];
+  }
+  for (int half = 0; half < (DH + 63) / 64; ++half) {
+    const int dim = half * 64 + lane;
+    float gk[64], gv[64];
+#pragma unroll
+    for (int u = 0; u < 64; ++u) gk[u] = gv[u] = 0.f;
+    // every wave runs the same number of rounds (slot past the end: no-op),
+    // so all of them meet every barrier
+    const int rounds = (nslot - m0 * G + 3) / 4;
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int slot = m0 * G + 4 * rd + wave;
+      const bool act = slot < nslot;
+      const int m = act ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act ? slot - m * G : 0);
+      const int i = act ? rm.pos(n) : 0;
+      const int64_t qo = ((int64_t)n * Hq + h) * DH;
+      for (int c = lane; c < DH; c += 64) {
+        qs[wave][c] = act ? q[qo + c] : 0.f;
+        ds[wave][c] = act ? dout[qo + c] : 0.f;
+      }
+      __syncthreads();  // (also orders the staging above before the first use)
+      float p = 0.f, dS = 0.f;
+      if (lane < nk && t0 + lane < i) {
+        float sc = 0.f, dP = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < DH; ++c) {
+          sc += qs[wave][c] * Ks[lane * KP + c];
+          dP += ds[wave][c] * Vs[lane * KP + c];
+        }
+        const int64_t so = (int64_t)n * Hq + h;
+        p = expf(sc * scale - mst[so]) / lst[so];
+        dS = p * (dP - Dst[so]);
+      }
+      const float qd = dim < DH ? qs[wave][dim] * scale : 0.f, od = dim < DH ? ds[wave][dim] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 64; ++u) {
+        gk[u] += __shfl(dS, u) * qd;
+        gv[u] += __shfl(p, u) * od;
+      }
+      __syncthreads();  // (qs / ds of this slot are read)
     }
-  }
-  if (!any) return;
-  if (lane < d) {
-    dK[ko + lane] += gk0;
-    dV[ko + lane] += gv0;
-  }
-  if (lane + 64 < d) {
-    dK[ko + lane + 64] += gk1;
-    dV[ko + lane + 64] += gv1;
+    for (int w = 0; w < 4; ++w) {
+      if (wave == w)
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+          accK[u * 64 + lane] = w == 0 ? gk[u] : accK[u * 64 + lane] + gk[u];
+          accV[u * 64 + lane] = w == 0 ? gv[u] : accV[u * 64 + lane] + gv[u];
+        }
+      __syncthreads();
+    }
+    if (dim < DH)
+      for (int u = wave; u < nk; u += 4) {
+        // (each wave adds its share of the keys)
+        dK[base + (int64_t)(t0 + u) * DH + dim] += accK[u * 64 + lane];
+        dV[base + (int64_t)(t0 + u) * DH + dim] += accV[u * 64 + lane];
+      }
+    __syncthreads();
   }
 }
 
@@ -828,6 +871,20 @@ struct Trainer {
       hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
     return hipGetLastError();
   }
+  hipError_t attn_dkv(const float *q, const float *K, const float *Vv, const float *dout, const float *mst,
+                      const float *lst, const float *Dst, Rows rm, float scale, float *dK, float *dV) {
+    dim3 grid(B * c.Hkv, (T + 63) / 64);
+    if (c.d == 32)
+      hipLaunchKernelGGL(k_attn_dkv<32>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, Dst, rm, c.Hq, c.Hkv, T,
+                         scale, dK, dV);
+    else if (c.d == 64)
+      hipLaunchKernelGGL(k_attn_dkv<64>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, Dst, rm, c.Hq, c.Hkv, T,
+                         scale, dK, dV);
+    else
+      hipLaunchKernelGGL(k_attn_dkv<128>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, Dst, rm, c.Hq, c.Hkv, T,
+                         scale, dK, dV);
+    return hipGetLastError();
+  }
   hipError_t attn_dq(const float *q, const float *K, const float *Vv, const float *dout, const float *mst,
                      const float *lst, Rows rm, int N, float scale, float *dq, float *Dst) {
     dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 3) / 4);
@@ -991,10 +1048,8 @@ struct Trainer {
       TR_TRY(gemm(true, false, dh, D, out, QD, gr.wo + (size_t)l * D * QD, QD, D, QD, N, 1.f));
       const int ch = l % k;
       TR_TRY(attn_dq(q, chanK(o.cK, ch), chanK(o.cV, ch), P(o.dout), mst, lst, rm, N, scale, P(o.dq), P(o.Dst)));
-      hipLaunchKernelGGL(k_attn_dkv, dim3(B * c.Hkv, T), dim3(64), 0, s, q, chanK(o.cK, ch), chanK(o.cV, ch),
-                         P(o.dout), mst, lst, P(o.Dst), rm, c.Hq, c.Hkv, c.d, T, scale, chanK(o.dK, ch),
-                         chanK(o.dV, ch));
-      TR_TRY(hipGetLastError());
+      TR_TRY(attn_dkv(q, chanK(o.cK, ch), chanK(o.cV, ch), P(o.dout), mst, lst, P(o.Dst), rm, scale,
+                      chanK(o.dK, ch), chanK(o.dV, ch)));
       TR_TRY(rope(P(o.dq), rm, N, N, c.Hq, true));
       // (the head-norm backward's output goes to dout, free again)
       TR_TRY(rms_bwd(qraw, w.q_norm + (size_t)l * c.d, gr.q_norm + (size_t)l * c.d, N * c.Hq, 1,
