@@ -17,22 +17,22 @@ Sources:
 Readings (the pages do not spell these out; each is listed with its reason in
 the design notes of this repository):
 
-* R26 the training objective is next-token cross-entropy on the logits of the
+* R25 the training objective is next-token cross-entropy on the logits of the
       last pass: position i < T-1 of sequence b predicts tokens[b, i+1]; the
       loss is the mean over the B*(T-1) predictions.
-* R27 truncation: the passes start from the zero cache (R11); the cache left
+* R26 truncation: the passes start from the zero cache (R11); the cache left
       by the n_nograd passes without gradient is a constant, and the gradient
       flows through the n_grad passes after it, including, inside a pass,
       from a group step back to the earlier group steps whose cache entries
       it read.
-* R28 the gradient is taken with respect to every parameter of the model
+* R27 the gradient is taken with respect to every parameter of the model
       (the wm_inputs.weight_shapes names), summed over the batch through the
-      mean of R26.
+      mean of R25.
 
 Two independent computations of the same objective live here:
 
 ``truncated_loss``  float64 numpy, built only from ``wm_oracle`` (cyclic
-                    passes as defined there, then the R26 cross-entropy); the
+                    passes as defined there, then the R25 cross-entropy); the
                     tests take central finite differences of it.
 ``train_step``      the same forward written with torch float64 CPU ops (the
                     steps of ``wm_oracle.stack_forward`` / ``pool`` /
@@ -58,7 +58,7 @@ PARAM_NAMES = ("embed", "lm_head", "final_norm", "attn_norm", "wq", "q_norm", "w
 # ---------------------------------------------------------------------------
 
 def next_token_ce(logits, tokens):
-    """R26: mean over b, i < T-1 of logsumexp(logits[b, i]) - logits[b, i, tokens[b, i+1]]."""
+    """R25: mean over b, i < T-1 of logsumexp(logits[b, i]) - logits[b, i, tokens[b, i+1]]."""
     z = np.asarray(logits, np.float64)[:, :-1]
     tgt = np.asarray(tokens)[:, 1:]
     zmax = z.max(axis=-1, keepdims=True)
@@ -68,7 +68,7 @@ def next_token_ce(logits, tokens):
 
 
 def truncated_loss(M_nograd, M_grad, tokens, g, n_nograd=1, n_grad=2):
-    """R26/R27 with wm_oracle: n_nograd cyclic passes from the zero cache with
+    """R25/R26 with wm_oracle: n_nograd cyclic passes from the zero cache with
     the weights of ``M_nograd``, then n_grad passes with those of ``M_grad``;
     the loss of the last pass's logits.  With M_nograd fixed at the base
     weights and M_grad perturbed, central differences of this function are
@@ -218,7 +218,7 @@ def forward_passes(M, tokens, g, n_passes):
 
 
 def train_step(M, tokens, g, n_nograd=1, n_grad=2, dtype=None):
-    """R26-R28: loss and gradient of one training step.  Returns (loss,
+    """R25-R27: loss and gradient of one training step.  Returns (loss,
     {name: float64 array of the parameter's shape}).  ``dtype`` (a torch
     float type, float64 by default) is the arithmetic; float32 gives the
     rounding floor of a float32 implementation of the same steps."""

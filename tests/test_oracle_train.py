@@ -1,7 +1,7 @@
 """The training oracle (oracle/wm_train.py) pinned to things other than itself.
 
 * Its torch forward is the numpy oracle's cyclic pass (caches and logits at
-  1e-12 after several passes), and its loss is the numpy R26 cross-entropy of
+  1e-12 after several passes), and its loss is the numpy R25 cross-entropy of
   those logits.
 * Its gradient equals central finite differences of the truncated objective
   computed by the numpy oracle alone (``truncated_loss``, whose no-gradient
@@ -74,7 +74,7 @@ def test_loss_is_the_numpy_cross_entropy():
     M = O.Model(w, W)
     loss, _ = TR.train_step(M, tokens, w.g, 1, 2)
     assert abs(loss - TR.truncated_loss(M, M, tokens, w.g, 1, 2)) < 1e-12
-    # the R26 cross-entropy written out for one prediction
+    # the R25 cross-entropy written out for one prediction
     lg = np.array([[[0.5, -1.0, 2.0], [0.0, 0.0, 0.0]]])
     tok = np.array([[0, 2]])
     assert abs(TR.next_token_ce(lg, tok) - (np.log(np.exp(0.5) + np.exp(-1.0) + np.exp(2.0)) - 2.0)) < 1e-15
