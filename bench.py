@@ -223,11 +223,35 @@ def bench_decode(steps, warmup):
         wm.decode_step(model, tok, t, cache, logits, ws)
     torch.cuda.synchronize()
     kern = {k: {"launches": c, "avg_us": 1e3 * m / c} for k, (c, m) in profile_read().items()}
+    profile(0)
+    # the same step with its position in device memory (wm_decode_step_at),
+    # captured once in a graph and replayed
+    tdev = torch.tensor([t], dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        wm.decode_step_at(model, tok, tdev, cache, logits, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wm.decode_step_at(model, tok, tdev, cache, logits, ws)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    g_wall = time.perf_counter() - t0
+    del graph
     kv_bytes = 2.0 * w.B * w.Hkv * t * w.d * 2  # K and V of one channel, bf16, per layer launch
     ach = kv_bytes / (ms_at / n_at * 1e-3) / 1e9
     return {"workload": "decode_d512: L16 D512 Hq8 Hkv4 d64 F1536 k16 p2 V32768 B64, t=2047 cached, bf16",
             "value": w.B * steps / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall / steps, "steps": steps,
             "peak_memory_gib": peak_gib(), "cache_gib": 2 * K.numel() * K.element_size() / 2 ** 30,
+            "graph_replay": {"ms_per_step": 1e3 * g_wall / steps, "value": w.B * steps / g_wall,
+                             "how": "wm_decode_step_at (position in device memory) captured once, replayed"},
             "kernels_avg_us": kern,
             "roofline": {"kernel": "attn (strict-causal channel attention, attn_few)", "bound": "hbm",
                          "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
@@ -306,6 +330,29 @@ def bench_small_prefill():
     wm.cyclic_prefill_pass(model, tok, w.g, cache, 1, logits, ws)
     torch.cuda.synchronize()
     kern = {k: {"launches": c, "avg_us": 1e3 * m / c, "per_pass_us": 1e3 * m} for k, (c, m) in profile_read().items()}
+    profile(0)
+    # the same three passes replayed from one captured graph of a pass
+    gcache = wm.new_cache(model, w.B)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        wm.cyclic_prefill_pass(model, tok, w.g, gcache, 1, logits, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wm.cyclic_prefill_pass(model, tok, w.g, gcache, 1, logits, ws)
+    gcache.k.zero_()
+    gcache.v.zero_()
+    gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.passes)]
+    torch.cuda.synchronize()
+    for a, b in gevs:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    g_per_pass = [a.elapsed_time(b) for a, b in gevs]
+    del graph, gcache
     flop = pass_flops(w)
     best = min(per_pass)
     ach = flop / (best * 1e-3) / 1e12
@@ -314,6 +361,7 @@ def bench_small_prefill():
     return {"workload": "small_prefill: L16 D512 Hq8 Hkv4 d64 F1536 k8 p2 V32768, B8 T2048, cyclic g16, 3 passes, "
                         "bf16",
             "per_pass_ms": per_pass, "value": w.B * w.T / (best * 1e-3), "unit": "tokens/s/pass",
+            "graph_replay_per_pass_ms": g_per_pass,
             "rows_per_group_step": rows,
             "roofline": {"kernel": "whole pass (all launches of a cyclic pass)", "bound": "mfma", "achieved": ach,
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,

@@ -62,6 +62,7 @@ _SIGS = {
                                        c_vp, c_size, c_vp]),
     "wm_decode_step": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, P(WmCache), c_vp, c_vp, c_size, c_vp]),
     "wm_decode_step_static": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, P(WmCache), c_vp, c_vp]),
+    "wm_decode_step_at": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_vp, P(WmCache), c_vp, c_vp, c_size, c_vp]),
     "wm_vanilla_prefill": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, c_i32, P(WmCache), c_vp, c_i32, c_vp,
                                    c_size, c_vp]),
     "wm_vanilla_decode_step": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, P(WmCache), c_vp, c_vp, c_size,

@@ -204,6 +204,26 @@ def decode_step(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits
     return logits
 
 
+def decode_step_at(model: Model, tokens: torch.Tensor, t: torch.Tensor, cache: Cache, logits=None, ws=None,
+                   stream=None):
+    """wm_decode_step_at: a decode step whose position t (int32 tensor of one
+    element, on the device) is read by the kernels when they run, so that a
+    captured graph of the call replays at whatever position t then holds."""
+    check_tokens(tokens, cache, model.device, 1)
+    check_cache(model, cache)
+    check_tensor("t", t, torch.int32, model.device, (1,))
+    B = tokens.shape[0]
+    if logits is None:
+        logits = torch.empty(B, model.shape.V, dtype=torch.float32, device=tokens.device)
+    ws = _ws(model, ws, B)
+    cc = cache.c()
+    C.check("wm_decode_step_at", C.lib().wm_decode_step_at(ctypes.byref(model.cfg), ctypes.byref(model.w),
+                                                           tokens.data_ptr(), t.data_ptr(), ctypes.byref(cc),
+                                                           logits.data_ptr(), ws.data_ptr(), ws.numel(),
+                                                           _stream(stream)))
+    return logits
+
+
 def decode_step_static(model: Model, tokens: torch.Tensor, t: int, cache: Cache, logits=None, stream=None):
     """wm_decode_step with the library's static scratch (no workspace, no
     allocation inside the call): tokens [B] (int32, device) at position t."""

@@ -118,6 +118,10 @@ template <typename T> struct Run {
     if (M <= kFewStackRows) return few_parts(M, N);
     return (N + resid_bn(M, N) - 1) / resid_bn(M, N);
   }
+  // Decode steps whose position lives in device memory: read by the kernels
+  // when they run (RowPos::s0p, AttnArgs::s0p).
+  const int32_t *pos_dev = nullptr;
+  RowPos rowpos(const wm_tokset &ts) const { return RowPos{ts.M, ts.s0, ts.s_step, pos_dev, c.T_max}; }
   T *Kch(int ch) const { return (T *)cache->k + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
   T *Vch(int ch) const { return (T *)cache->v + (int64_t)ch * cache->B * c.Hkv * c.T_max * c.d; }
 
@@ -219,6 +223,7 @@ template <typename T> struct Run {
     a.T_max = c.T_max;
     a.nsplit = ns;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)c.d);
+    a.s0p = pos_dev;
     dim3 grid(nrb, ts.B * c.Hkv, ns);
     ProfScope prof(WM_K_ATTN, s);
     if constexpr (bfd) {
@@ -377,7 +382,7 @@ template <typename T> struct Run {
     LoadRows<T> pa{at<T>(lay.mb), c.D, (int64_t)rows * c.D, nullptr};
     BKV<T> pb{(const T *)w->wk, (const T *)w->wv, c.D, (int64_t)c.Hkv * c.d * c.D, c.k};
     EpiKV<T> pe{(T *)cache->k, (T *)cache->v, at<float>(lay.rinvM), w->k_norm, w->rope_cos, w->rope_sin, c.k,
-                cache->B, c.Hkv, c.T_max, c.d, rows, c.eps, RowPos{ts.M, ts.s0, ts.s_step}};
+                cache->B, c.Hkv, c.T_max, c.d, rows, c.eps, rowpos(ts)};
     ProfScope prof(WM_K_KVPROJ, s);
     if constexpr (kBig) {
       if (big(rows)) {
@@ -427,7 +432,7 @@ template <typename T> struct Run {
     }
     const T *wkl = (const T *)w->wk + (int64_t)l * HD * D, *wvl = (const T *)w->wv + (int64_t)l * HD * D;
     EpiKV<T> pe{Kch(l), Vch(l), at<float>(lay.rinvM), w->k_norm + (int64_t)l * c.d, w->rope_cos, w->rope_sin, 1,
-                cache->B, c.Hkv, c.T_max, c.d, rows, c.eps, RowPos{ts.M, ts.s0, ts.s_step}};
+                cache->B, c.Hkv, c.T_max, c.d, rows, c.eps, rowpos(ts)};
     ProfScope prof(WM_K_KVPROJ, s);
     if constexpr (kBig) {
       if (big(rows)) {
@@ -453,7 +458,7 @@ template <typename T> struct Run {
     T *hb = at<T>(lay.hb), *q = at<T>(lay.q), *o = at<T>(lay.o), *act = at<T>(lay.act), *S = at<T>(lay.S);
     const T *wq = (const T *)w->wq, *wo = (const T *)w->wo, *wg = (const T *)w->w_gate, *wu = (const T *)w->w_up,
             *wd = (const T *)w->w_down;
-    const RowPos rp{ts.M, ts.s0, ts.s_step};
+    const RowPos rp = rowpos(ts);
     {
     ProfScope prof(WM_K_EMBED, s);
     hipLaunchKernelGGL((embed_rows<T>), dim3(rows), dim3(256), 0, s, tokens, (const T *)w->embed, w->attn_norm, h, hb,
@@ -776,6 +781,33 @@ wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_
     return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
   }
   Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+  st = r.prep_router();
+  if (st != WM_OK) return st;
+  return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+}
+
+wm_status wm_decode_step_at(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, const int32_t *t,
+                            const wm_cache *cache, float *logits, void *ws, size_t ws_bytes, wm_stream stream) {
+  wm_status st = wm_check_config(cfg);
+  if (st != WM_OK) return st;
+  WM_CHECK(cache && cache->k && cache->v && cache->B >= 1, WM_ERR_ARG, "cache, its pointers or B invalid");
+  WM_CHECK(t && tokens && logits && weights_ok(w, true), WM_ERR_ARG,
+           "t, tokens, logits or a weight pointer is NULL");
+  int rows = cache->B;
+  st = check_common(cfg, cache, ws, ws_bytes, rows);
+  if (st != WM_OK) return st;
+  // (host-side choices that depend on the position, the key splits of the
+  // attention, are made for the last position; the kernels read *t)
+  wm_tokset ts{cache->B, 1, cfg->T_max - 1, 1};
+  if (cfg->dtype == WM_BF16) {
+    Run<bf16> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+    r.pos_dev = t;
+    st = r.prep_router();
+    if (st != WM_OK) return st;
+    return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);
+  }
+  Run<float> r(*cfg, w, cache, ws, rows, (hipStream_t)stream);
+  r.pos_dev = t;
   st = r.prep_router();
   if (st != WM_OK) return st;
   return r.group_step(tokens, 1, 0, 0, ts, 1, 0, 1, logits);

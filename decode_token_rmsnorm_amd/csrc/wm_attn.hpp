@@ -31,7 +31,12 @@ struct AttnArgs {
   float *part_ml;      // [splits, B*M, Hq, 2]
   int B, M, s0, step, Hq, Hkv, G, T_max, nsplit;
   float scale_log2;    // log2(e) / sqrt(d)
+  const int32_t *s0p;  // when set: s0 = *s0p read at run time, clamped to [0, T_max)
 };
+
+__device__ __forceinline__ int attn_s0(const AttnArgs &a) {
+  return a.s0p ? min(max(*a.s0p, 0), a.T_max - 1) : a.s0;
+}
 
 // Transposed value tile: row dd (head dim), 64 keys in 16 quads of 4. Quad q
 // of row dd is stored at quad position q ^ (dd / E % 16) (E = elements per 16
@@ -79,7 +84,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int rb0 = blockIdx.x * RB;
   if (rb0 >= nrows) return;
   const int last = min(nrows, rb0 + RB) - 1;
-  int kmax = a.s0 + (last / a.G) * a.step;  // keys s < kmax for the block
+  const int s0 = attn_s0(a);
+  int kmax = s0 + (last / a.G) * a.step;  // keys s < kmax for the block
   kmax = min(kmax, a.T_max);
   const int ntile = (kmax + AKT - 1) / AKT;
   const int tps = (ntile + a.nsplit - 1) / a.nsplit;
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     int rho = rb0 + wave * NQ * 16 + nq * 16 + (lane & 15);
     rvalid[nq] = rho < nrows;
     int m = rvalid[nq] ? rho / a.G : 0, g = rvalid[nq] ? rho - m * a.G : 0;
-    rpos[nq] = rvalid[nq] ? a.s0 + m * a.step : 0;
+    rpos[nq] = rvalid[nq] ? s0 + m * a.step : 0;
     rrow[nq] = b * a.M + m;
     rhead[nq] = hk * a.G + g;
     const T *src = qp + ((int64_t)rrow[nq] * a.Hq + rhead[nq]) * DH;

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
   const int rb0 = (gridDim.y - 1 - blockIdx.y) * RB;
   if (rb0 >= nrows) return;
   const int last = min(nrows, rb0 + RB) - 1;
-  const int kmax = min(a.s0 + (last / a.G) * a.step, a.T_max);  // keys s < kmax for the block
+  const int s0 = attn_s0(a);
+  const int kmax = min(s0 + (last / a.G) * a.step, a.T_max);  // keys s < kmax for the block
   const int ntile = (kmax + KT - 1) / KT;
   const int tps = (ntile + a.nsplit - 1) / a.nsplit;
   const int t0 = blockIdx.z * tps, t1 = min(ntile, t0 + tps);
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
     rvalid[qb] = rho_raw < nrows;
     const int rho = rvalid[qb] ? rho_raw : nrows - 1;
     const int m = rho / a.G, g = rho - m * a.G;
-    rpos[qb] = a.s0 + m * a.step;
+    rpos[qb] = s0 + m * a.step;
     rrow[qb] = b * a.M + m;
     rhead[qb] = hk * a.G + g;
     const bf16 *src = (const bf16 *)a.q + ((int64_t)rrow[qb] * a.Hq + rhead[qb]) * DH + 8 * h;
@@ -351,7 +352,8 @@ __global__ __launch_bounds__(64 * NW) void attn_few(AttnArgs a) {
   bf16 *Vs = (bf16 *)smem + wave * KT * VP;
   const int split = blockIdx.x, pair = blockIdx.y, b = pair / a.Hkv, hk = pair - b * a.Hkv;
   const int nrows = a.M * a.G;  // <= 32
-  const int kmax = min(a.s0 + ((nrows - 1) / a.G) * a.step, a.T_max);
+  const int s0 = attn_s0(a);
+  const int kmax = min(s0 + ((nrows - 1) / a.G) * a.step, a.T_max);
   const int ntile = (kmax + KT - 1) / KT;
   const int tps = (ntile + a.nsplit - 1) / a.nsplit;
   const int t0 = split * tps, t1 = min(ntile, t0 + tps);
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(64 * NW) void attn_few(AttnArgs a) {
   const bool rvalid = ql < nrows;
   const int rho = rvalid ? ql : nrows - 1;
   const int m = rho / a.G, g = rho - m * a.G;
-  const int rpos = a.s0 + m * a.step;
+  const int rpos = s0 + m * a.step;
   const int rrow = b * a.M + m, rhead = hk * a.G + g;
   u32x4 qf[NCH];
   {

@@ -28,9 +28,14 @@ constexpr int GCP = GN + 4;        // C tile pitch in floats
 static_assert(2 * GSTAGE >= GM * GCP * 4 + GM * 4, "C tile and row scales must fit in the operand LDS");
 
 // Position of row r of a token set (row r = b*M + m sits at s0 + m*step).
+// With s0p set (a decode step whose position lives in device memory), s0 is
+// read from *s0p when the kernel runs, clamped to [0, tmax).
 struct RowPos {
   int M, s0, step;
-  __device__ __forceinline__ int pos(int r) const { return s0 + (r % M) * step; }
+  const int32_t *s0p = nullptr;
+  int tmax = 1;
+  __device__ __forceinline__ int base() const { return s0p ? min(max(*s0p, 0), tmax - 1) : s0; }
+  __device__ __forceinline__ int pos(int r) const { return base() + (r % M) * step; }
   __device__ __forceinline__ int seq(int r) const { return r / M; }
 };
 

@@ -212,6 +212,21 @@ wm_status wm_decode_step(const wm_config *cfg, const wm_weights *w, const int32_
                          const wm_cache *cache, float *logits, void *ws, size_t ws_bytes,
                          wm_stream stream);
 
+/* One decode step whose position is read from device memory when the kernels
+ * run (*t, int32) instead of being passed by value; otherwise the step of
+ * wm_decode_step (same kernels and arguments). A caller can capture it once
+ * into a HIP graph and replay the graph at successive positions, writing the
+ * next position and tokens into the same device buffers between replays
+ * (paperlayer.ai §3 "Execution schedules": decoding appends one token's
+ * channels per step). *t must lie in [0, T_max); the kernels clamp a value
+ * outside that range into it. The host cannot read *t, so the attention's
+ * key splits are chosen for position T_max - 1 (splits past the position do
+ * no work), and results at other positions may differ from wm_decode_step's
+ * in the order of the final sums (rounding only). Launches no memset and no
+ * host synchronisation. Workspace: wm_workspace_bytes(cfg, B). */
+wm_status wm_decode_step_at(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, const int32_t *t,
+                            const wm_cache *cache, float *logits, void *ws, size_t ws_bytes, wm_stream stream);
+
 /* ---- allocation-free decode step ---------------------------------------
  * For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same

@@ -25,7 +25,7 @@ def cfg_of(w, dtype=C.WM_BF16, **kw):
 
 def test_library_exports_every_declared_function():
     names = C.header_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     assert set(names) <= exported, set(names) - exported
@@ -311,3 +311,21 @@ def test_train_step_validates_before_launch():
     G0 = C.WmGrads(*[FAKE for _ in C.GRAD_FIELDS])
     G0.router = None
     assert call(Gt=G0) == -1
+
+
+def test_decode_step_at_validates_before_launch():
+    """wm_decode_step_at checks every pointer (the position's included) and the
+    workspace on the host; the position's value lives on the device."""
+    L = C.lib()
+    W = _weights()
+    w = WORKLOADS["decode_d512"]
+    c = cfg_of(w)
+    cache = C.WmCache(FAKE, FAKE, w.B)
+    need = L.wm_workspace_bytes(ctypes.byref(c), w.B)
+    call = lambda t=FAKE, tok=FAKE, lg=FAKE, n=need, Wt=W, cc=cache: L.wm_decode_step_at(
+        ctypes.byref(c), ctypes.byref(Wt), tok, t, None if cc is None else ctypes.byref(cc), lg, FAKE, n, None)
+    assert call(t=None) == -1 and call(tok=None) == -1 and call(lg=None) == -1 and call(cc=None) == -1
+    assert call(n=need - 1) == -4
+    W0 = _weights()
+    W0.lm_head = None
+    assert call(Wt=W0) == -1
