@@ -114,8 +114,8 @@ template <typename T> struct Run {
   // column tile of the residual products on M rows
   int resid_bn(int M, int N) const { return big(M) ? g2_resid_bn(M, N, kComputeUnits) : GN; }
   // partial sums of squares per row written by a residual epilogue on M rows
-  int parts(int M, int N) const {
-    if (M <= kFewStackRows) return few_parts(M, N);
+  int parts(int M, int N, int K) const {
+    if (M <= kFewStackRows) return few_parts(M, N, K);
     return (N + resid_bn(M, N) - 1) / resid_bn(M, N);
   }
   // Decode steps whose position lives in device memory: read by the kernels
@@ -507,13 +507,13 @@ template <typename T> struct Run {
       {
         LoadRows<T> a{o, QD, 0, nullptr};
         BRows<T> b{LoadRows<T>{wo + (int64_t)l * D * QD, QD, 0, nullptr}};
-        EpiResid<T> e{h, hb, w->ffn_norm + (int64_t)l * D, nullptr, ss, parts(rows, D)};
+        EpiResid<T> e{h, hb, w->ffn_norm + (int64_t)l * D, nullptr, ss, parts(rows, D, QD)};
         ProfScope prof(WM_K_OPROJ, s);
         if (big(rows))
           WM_TRY(gemm2_resid(o, QD, wo + (int64_t)l * D * QD, QD, e, rows, D, QD));
         else
           WM_TRY((gemm_s(a, b, e, rows, D, QD)));
-        nparts = parts(rows, D);
+        nparts = parts(rows, D, QD);
       }
       // act = silu(W_gate b) * (W_up b), b = RMSNorm(h)
       {
@@ -543,13 +543,14 @@ template <typename T> struct Run {
         BRows<T> b{LoadRows<T>{wd + (int64_t)l * D * c.F, c.F, 0, nullptr}};
         const float *gnext = l + 1 < L ? w->attn_norm + (int64_t)(l + 1) * D : w->final_norm;
         T *Snext = l + 1 < L && !vanilla ? S + (int64_t)(l + 1) * rows * D : nullptr;
-        EpiResid<T> e{h, hb, gnext, Snext, ss, parts(rows, D)};
+        EpiResid<T> e{h, hb, gnext, Snext, ss, parts(rows, D, c.F)};
         ProfScope prof(WM_K_DOWN, s);
         if (big(rows))
           WM_TRY(gemm2_resid(act, c.F, wd + (int64_t)l * D * c.F, c.F, e, rows, D, c.F));
         else
           WM_TRY((gemm_s(a, b, e, rows, D, c.F)));
       }
+      nparts = parts(rows, D, c.F);
     }
     if (!vanilla && !ff) {
       wm_status st = pool(S, ts);
