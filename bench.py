@@ -185,6 +185,9 @@ def pass_flops(w):
     return w.B * w.T * flops_per_token(w, "wm", lm_head=False)
 
 
+GRAPHS = True  # the graph-replay legs (off for counter-collection runs: --no-graph)
+
+
 def bench_decode(steps, warmup):
     import torch
     import decode_token_rmsnorm_amd as wm
@@ -226,32 +229,35 @@ def bench_decode(steps, warmup):
     profile(0)
     # the same step with its position in device memory (wm_decode_step_at),
     # captured once in a graph and replayed
+    g_wall = None
     tdev = torch.tensor([t], dtype=torch.int32, device="cuda")
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        wm.decode_step_at(model, tok, tdev, cache, logits, ws)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        wm.decode_step_at(model, tok, tdev, cache, logits, ws)
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    g_wall = time.perf_counter() - t0
-    del graph
+    if GRAPHS:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            wm.decode_step_at(model, tok, tdev, cache, logits, ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            wm.decode_step_at(model, tok, tdev, cache, logits, ws)
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_wall = time.perf_counter() - t0
+        del graph
     kv_bytes = 2.0 * w.B * w.Hkv * t * w.d * 2  # K and V of one channel, bf16, per layer launch
     ach = kv_bytes / (ms_at / n_at * 1e-3) / 1e9
     return {"workload": "decode_d512: L16 D512 Hq8 Hkv4 d64 F1536 k16 p2 V32768 B64, t=2047 cached, bf16",
             "value": w.B * steps / wall, "unit": "tokens/s", "ms_per_step": 1e3 * wall / steps, "steps": steps,
             "peak_memory_gib": peak_gib(), "cache_gib": 2 * K.numel() * K.element_size() / 2 ** 30,
-            "graph_replay": {"ms_per_step": 1e3 * g_wall / steps, "value": w.B * steps / g_wall,
-                             "how": "wm_decode_step_at (position in device memory) captured once, replayed"},
+            "graph_replay": None if g_wall is None else {
+                "ms_per_step": 1e3 * g_wall / steps, "value": w.B * steps / g_wall,
+                "how": "wm_decode_step_at (position in device memory) captured once, replayed"},
             "kernels_avg_us": kern,
             "roofline": {"kernel": "attn (strict-causal channel attention, attn_few)", "bound": "hbm",
                          "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
@@ -296,6 +302,36 @@ def bench_train(steps=1, warmup=1):
                          "algorithmic_per_step": f"{flop:.4e} FLOP = 7 forward passes of {w.B}x{w.T} tokens"}}
 
 
+def graph_passes(model, tok, w, logits, ws):
+    """Per-pass ms of w.passes passes from the zero cache, replayed from one
+    captured graph of wm_cyclic_prefill_pass."""
+    import torch
+    import decode_token_rmsnorm_amd as wm
+
+    gcache = wm.new_cache(model, w.B)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        wm.cyclic_prefill_pass(model, tok, w.g, gcache, 1, logits, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wm.cyclic_prefill_pass(model, tok, w.g, gcache, 1, logits, ws)
+    gcache.k.zero_()
+    gcache.v.zero_()
+    gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.passes)]
+    torch.cuda.synchronize()
+    for a, b in gevs:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    out = [a.elapsed_time(b) for a, b in gevs]
+    del graph, gcache
+    return out
+
+
 def bench_small_prefill():
     """The small half-cache model (L16 D512 8/4 x 64, F1536, k8, p2, V32768,
     B8, T2048, cyclic g16): three passes from the zero cache, each timed with
@@ -332,28 +368,9 @@ def bench_small_prefill():
     kern = {k: {"launches": c, "avg_us": 1e3 * m / c, "per_pass_us": 1e3 * m} for k, (c, m) in profile_read().items()}
     profile(0)
     # the same three passes replayed from one captured graph of a pass
-    gcache = wm.new_cache(model, w.B)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        wm.cyclic_prefill_pass(model, tok, w.g, gcache, 1, logits, ws)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        wm.cyclic_prefill_pass(model, tok, w.g, gcache, 1, logits, ws)
-    gcache.k.zero_()
-    gcache.v.zero_()
-    gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.passes)]
-    torch.cuda.synchronize()
-    for a, b in gevs:
-        a.record()
-        graph.replay()
-        b.record()
-    torch.cuda.synchronize()
-    g_per_pass = [a.elapsed_time(b) for a, b in gevs]
-    del graph, gcache
+    g_per_pass = None if not GRAPHS else graph_passes(model, tok, w, logits, ws)
     flop = pass_flops(w)
+
     best = min(per_pass)
     ach = flop / (best * 1e-3) / 1e12
     del cache, ws, model
@@ -715,6 +732,7 @@ def main():
     ap.add_argument("--skip-small", action="store_true")
     ap.add_argument("--skip-decode-1p3b", action="store_true")
     ap.add_argument("--skip-train", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay legs (counter-collection runs)")
     ap.add_argument("--only", choices=["decode", "mix", "vanilla", "sweep", "variants", "peaks", "small",
                                        "decode_1p3b", "cpu", "train"], default=None,
                     help="profiling aid: run only this part and print its object")
@@ -734,6 +752,8 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the method's batch elements are independent "
               "and would shard as pure data parallelism over sequences; this benchmark runs one GPU.", file=sys.stderr)
         sys.exit(2)
+    global GRAPHS
+    GRAPHS = not a.no_graph
     import torch
     torch.cuda.set_device(0)
     if a.only:
