@@ -265,6 +265,30 @@ def bench_decode(steps, warmup):
                          "algorithmic_per_launch": f"{kv_bytes:.4e} B = 2*{w.B}*{w.Hkv}*{t}*{w.d}*2"}}
 
 
+CPU_BASELINE = True  # off with --no-cpu-baseline
+
+
+def train_cpu_baseline(w, T=24, g=4):
+    """The training oracle (float64 torch autograd) on a bounded sample of the
+    training workload: one sequence of T positions at the same widths, g
+    groups, 1 + 2 passes; tokens/s of training steps."""
+    import torch
+    from oracle import wm_train as TR
+    import oracle as O
+    from wm_inputs import make_tokens, make_weights
+
+    ws_ = w.replace(B=1, T=T, T_max=T)
+    M = O.Model(ws_, make_weights(ws_, seed=0))
+    tokens = make_tokens(ws_, seed=1)
+    t0 = time.perf_counter()
+    TR.train_step(M, tokens, g, 1, 2)
+    dt = time.perf_counter() - t0
+    return {"value": T / dt, "unit": "tokens/s (training steps)", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"one sequence of {T} positions at the same widths, g = {g}, 1 + 2 passes, float64 autograd, "
+                      f"{dt:.1f} s (attention over at most {T - 1} keys: cheaper per token than the GPU's T = "
+                      f"{w.T})"}
+
+
 def bench_train(steps=1, warmup=1):
     """One training step with truncated backpropagation (wm_train_step: one
     cyclic pass without gradient, two with, next-token cross-entropy of the
@@ -293,8 +317,10 @@ def bench_train(steps=1, warmup=1):
     dt = (time.perf_counter() - t0) / steps
     flop = 7 * w.B * w.T * flops_per_token(w, "wm")
     ach = flop / dt / 1e12
+    cpu = None if not CPU_BASELINE else train_cpu_baseline(w)
     return {"workload": "small model widths, fp32: L16 D512 Hq8 Hkv4 d64 F1536 k8 p2 V32768, B8 T2048, g16, "
                         "1 pass without + 2 with gradient",
+            "cpu_baseline": cpu,
             "value": w.B * w.T / dt, "unit": "tokens/s (training steps)", "s_per_step": dt, "steps": steps,
             "loss": float(loss.item()), "peak_memory_gib": peak_gib(),
             "roofline": {"kernel": "whole training step", "bound": "alu", "achieved": ach, "peak": FP32_PEAK_TFLOPS,
@@ -752,8 +778,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the method's batch elements are independent "
               "and would shard as pure data parallelism over sequences; this benchmark runs one GPU.", file=sys.stderr)
         sys.exit(2)
-    global GRAPHS
+    global GRAPHS, CPU_BASELINE
     GRAPHS = not a.no_graph
+    CPU_BASELINE = not a.no_cpu_baseline
     import torch
     torch.cuda.set_device(0)
     if a.only:
