@@ -116,78 +116,101 @@ __global__ void k_swiglu_bwd(const float *G, const float *U, const float *dact, 
 // C[z] = alpha * op(A[z]) op(B[z]) + beta * C[z], op(A) [M, K], op(B) [K, N],
 // row-major.  TA: A is stored [K, M] (leading dim lda), else [M, K].  TB: B
 // is stored [N, K], else [K, N].  beta = 0 never reads C.  64 x 64 tiles,
-// 256 threads with 4 x 4 outputs each, k in steps of 16 through LDS.  With
+// k in steps of 16 staged in LDS as [k][m] and [k][n] (either transpose is
+// taken at the store); 4 waves of 32 x 32, each on 2 x 2 float32 16x16x4
+// MFMAs (lane: A row lane % 16 and B column lane % 16 at k lane / 16; the
+// row pitch 80 puts the four k rows a read touches on disjoint banks).  With
 // splits > 1, blockIdx.z = batch * splits + split: the block sums k in
 // [split * kchunk, (split + 1) * kchunk) and C[blockIdx.z] is a partial
 // (k_split_sum adds them).
 constexpr int GT = 64, GK = 16;
+
+// 4 consecutive floats p[0..3], index idx of p[0] along a dimension of
+// extent lim: past-the-end elements read as 0; one 16-byte load when vec
+// (the caller's strides and base allow it) and all four are in range.
+__device__ __forceinline__ f32x4 ld4(const float *p, int idx, int lim, bool vec) {
+  if (vec && idx + 3 < lim) return *(const f32x4 *)p;
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = idx + e < lim ? p[e] : 0.f;
+  return r;
+}
+
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64_t sA, const float *B, int64_t ldb,
                                               int64_t sB, float *C, int64_t ldc, int64_t sC, int M, int N, int K,
-                                              float alpha, float beta, int splits, int kchunk) {
-  __shared__ __attribute__((aligned(16))) float As[GK][GT + 4];
-  __shared__ __attribute__((aligned(16))) float Bs[GK][GT + 4];
+                                              float alpha, float beta, int splits, int kchunk, int vecA, int vecB) {
+  constexpr int LP = GT + 16;
+  __shared__ __attribute__((aligned(16))) float As[GK][LP];
+  __shared__ __attribute__((aligned(16))) float Bs[GK][LP];
   const int batch = blockIdx.z / splits, split = blockIdx.z - batch * splits;
   A += batch * sA;
   B += batch * sB;
   C += blockIdx.z * sC;
   const int kb = split * kchunk, ke = min(K, kb + kchunk);
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
-  float acc[4][4] = {};
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = kb; k0 < ke; k0 += GK) {
+    // one 4-float run per thread of each operand: along k for A [M, K] and
+    // B [N, K] (thread -> row tid / 4, k 4 * (tid % 4)), along m or n for
+    // A [K, M] and B [K, N] (thread -> k row tid / 16, 4 * (tid % 16))
+    if (TA) {
+      const int kk = tid >> 4, mm = 4 * (tid & 15), gk = k0 + kk;
+      const f32x4 v = gk < ke ? ld4(A + (int64_t)gk * lda + m0 + mm, m0 + mm, M, vecA) : f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4 *)&As[kk][mm] = v;
+    } else {
+      const int mm = tid >> 2, kk = 4 * (tid & 3), gm = m0 + mm;
+      const f32x4 v = gm < M ? ld4(A + (int64_t)gm * lda + k0 + kk, k0 + kk, ke, vecA) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i;
-      int mm, kk;
-      if (TA) {
-        mm = e % GT;
-        kk = e / GT;
-      } else {
-        kk = e % GK;
-        mm = e / GK;
-      }
-      const int gm = m0 + mm, gk = k0 + kk;
-      float v = 0.f;
-      if (gm < M && gk < ke) v = TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk];
-      As[kk][mm] = v;
-      int nn;
-      if (TB) {
-        kk = e % GK;
-        nn = e / GK;
-      } else {
-        nn = e % GT;
-        kk = e / GT;
-      }
-      const int gn = n0 + nn, gk2 = k0 + kk;
-      float u = 0.f;
-      if (gn < N && gk2 < ke) u = TB ? B[(int64_t)gn * ldb + gk2] : B[(int64_t)gk2 * ldb + gn];
-      Bs[kk][nn] = u;
+      for (int e = 0; e < 4; ++e) As[kk + e][mm] = v[e];
+    }
+    if (TB) {
+      const int nn = tid >> 2, kk = 4 * (tid & 3), gn = n0 + nn;
+      const f32x4 v = gn < N ? ld4(B + (int64_t)gn * ldb + k0 + kk, k0 + kk, ke, vecB) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Bs[kk + e][nn] = v[e];
+    } else {
+      const int kk = tid >> 4, nn = 4 * (tid & 15), gk = k0 + kk;
+      const f32x4 v = gk < ke ? ld4(B + (int64_t)gk * ldb + n0 + nn, n0 + nn, N, vecB) : f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4 *)&Bs[kk][nn] = v;
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < GK; ++kk) {
-      const f32x4 a = *(const f32x4 *)&As[kk][4 * ty];
-      const f32x4 b = *(const f32x4 *)&Bs[kk][4 * tx];
+    for (int ks = 0; ks < GK; ks += 4) {
+      const int kr = ks + (lane >> 4);
+      float a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i) a[i] = As[kr][wm * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) b[j] = Bs[kr][wn * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
+  // accumulator (lane, e): row 4 * (lane / 16) + e, column lane % 16 of its tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + 4 * ty + i;
-    if (gm >= M) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + 4 * tx + j;
+    for (int j = 0; j < 2; ++j) {
+      const int gn = n0 + wn * 32 + j * 16 + (lane & 15);
       if (gn >= N) continue;
-      float *c = C + (int64_t)gm * ldc + gn;
-      *c = beta == 0.f ? alpha * acc[i][j] : alpha * acc[i][j] + beta * *c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gm = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + e;
+        if (gm >= M) continue;
+        float *c = C + (int64_t)gm * ldc + gn;
+        const float v = acc[i][j][e];
+        *c = beta == 0.f ? alpha * v : alpha * v + beta * *c;
+      }
     }
-  }
 }
 
 // C[z] = beta * C[z] + sum over the splits (in order) of part[z * splits + s], [M, N]
@@ -817,18 +840,21 @@ struct Trainer {
     const int64_t ldd = splits > 1 ? N : ldc, sD = splits > 1 ? (int64_t)M * N : sC;
     const float bd = splits > 1 ? 0.f : beta;
     dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, Z * splits);
+    // 16-byte loads where every row and batch starts on a 16-byte boundary
+    const int va = ((uintptr_t)A % 16 == 0 && lda % 4 == 0 && sA % 4 == 0) ? 1 : 0;
+    const int vb = ((uintptr_t)B_ % 16 == 0 && ldb % 4 == 0 && sB % 4 == 0) ? 1 : 0;
     if (!ta && !tb)
       hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N,
-                         K, 1.f, bd, splits, kchunk);
+                         K, 1.f, bd, splits, kchunk, va, vb);
     else if (!ta && tb)
       hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
-                         1.f, bd, splits, kchunk);
+                         1.f, bd, splits, kchunk, va, vb);
     else if (ta && !tb)
       hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
-                         1.f, bd, splits, kchunk);
+                         1.f, bd, splits, kchunk, va, vb);
     else
       hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
-                         1.f, bd, splits, kchunk);
+                         1.f, bd, splits, kchunk, va, vb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int64_t total = (int64_t)M * N * Z;
