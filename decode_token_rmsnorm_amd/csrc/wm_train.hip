@@ -337,15 +337,15 @@ __global__ void k_embed_bwd(const int32_t *tokens, int T, Rows rm, const float *
 // channel (K, V: [B, Hkv, Tc, d]).  A block of 4 waves takes 4 consecutive
 // query slots (m, g) of one sequence b and KV head hk (slot = m*G + g, head
 // hk*G + g), one per wave; they share the key chunks: 64 K and V rows staged
-// in LDS by coalesced loads (row pitch DH + 1, so lane t reading row t at
-// column c hits bank (t + c) mod 64).  In a chunk, lane t scores key t0 + t;
+// in LDS by coalesced 16-byte loads (row pitch DH + 4, so the 16-byte reads
+// of 8 lanes at rows t..t+7 fall on disjoint banks).  In a chunk, lane t scores key t0 + t;
 // lanes c and c + 64 own output dims.  Keeps the scaled-score max m and the
 // sum l of exp(score - m) for the backward.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, const float *Vc, Rows rm, int Hq,
                                               int Hkv, int Tc, float scale, float *out, float *mst, float *lst) {
-  constexpr int KP = DH + 1;
-  __shared__ float qs[4][DH], Ks[64 * KP], Vs[64 * KP];
+  constexpr int KP = DH + 4;
+  __shared__ __attribute__((aligned(16))) float qs[4][DH], Ks[64 * KP], Vs[64 * KP];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nslot = rm.M * G;
   const int slot = blockIdx.y * 4 + wave, last = min(blockIdx.y * 4 + 3, nslot - 1);
@@ -359,10 +359,10 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, c
   for (int t0 = 0; t0 < imax; t0 += 64) {
     const int nk = min(64, imax - t0);
     __syncthreads();  // (the previous chunk's reads are done; qs is written)
-    for (int e = threadIdx.x; e < nk * DH; e += 256) {
-      const int r = e / DH, c = e - r * DH;
-      Ks[r * KP + c] = K[(int64_t)(t0 + r) * DH + c];
-      Vs[r * KP + c] = V[(int64_t)(t0 + r) * DH + c];
+    for (int e = threadIdx.x; e < nk * (DH / 4); e += 256) {
+      const int r = e / (DH / 4), c = 4 * (e - r * (DH / 4));
+      *(f32x4 *)&Ks[r * KP + c] = *(const f32x4 *)&K[(int64_t)(t0 + r) * DH + c];
+      *(f32x4 *)&Vs[r * KP + c] = *(const f32x4 *)&V[(int64_t)(t0 + r) * DH + c];
     }
     __syncthreads();
     if (t0 < i) {  // (wave-uniform)
@@ -370,8 +370,12 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, c
       float sc = -INFINITY;
       if (lane < nv) {
         float dot = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < DH; ++c) dot += qs[wave][c] * Ks[lane * KP + c];
+#pragma unroll
+        for (int c = 0; c < DH; c += 4) {
+          const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c], qv = *(const f32x4 *)&qs[wave][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot = fmaf(qv[e], kv[e], dot);
+        }
         sc = dot * scale;
       }
       const float mnew = fmaxf(mx, wmax(sc));
@@ -406,8 +410,8 @@ template <int DH>
 __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc, const float *Vc, const float *dout,
                                                  const float *mst, const float *lst, Rows rm, int Hq, int Hkv,
                                                  int Tc, float scale, float *dq, float *Dst) {
-  constexpr int KP = DH + 1;
-  __shared__ float qs[4][DH], ds[4][DH], Ks[64 * KP], Vs[64 * KP];
+  constexpr int KP = DH + 4;
+  __shared__ __attribute__((aligned(16))) float qs[4][DH], ds[4][DH], Ks[64 * KP], Vs[64 * KP];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nslot = rm.M * G;
   const int slot = blockIdx.y * 4 + wave, last = min(blockIdx.y * 4 + 3, nslot - 1);
@@ -424,10 +428,10 @@ __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc
   const float invl = lrow > 0.f ? 1.f / lrow : 0.f;
   auto stage = [&](int t0, int nk) {
     __syncthreads();
-    for (int e = threadIdx.x; e < nk * DH; e += 256) {
-      const int r = e / DH, c = e - r * DH;
-      Ks[r * KP + c] = K[(int64_t)(t0 + r) * DH + c];
-      Vs[r * KP + c] = V[(int64_t)(t0 + r) * DH + c];
+    for (int e = threadIdx.x; e < nk * (DH / 4); e += 256) {
+      const int r = e / (DH / 4), c = 4 * (e - r * (DH / 4));
+      *(f32x4 *)&Ks[r * KP + c] = *(const f32x4 *)&K[(int64_t)(t0 + r) * DH + c];
+      *(f32x4 *)&Vs[r * KP + c] = *(const f32x4 *)&V[(int64_t)(t0 + r) * DH + c];
     }
     __syncthreads();
   };
@@ -435,10 +439,15 @@ __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc
   auto key = [&](float &p, float &dP) {
     float sc = 0.f;
     dP = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < DH; ++c) {
-      sc += qs[wave][c] * Ks[lane * KP + c];
-      dP += ds[wave][c] * Vs[lane * KP + c];
+#pragma unroll
+    for (int c = 0; c < DH; c += 4) {
+      const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c], vv = *(const f32x4 *)&Vs[lane * KP + c];
+      const f32x4 qv = *(const f32x4 *)&qs[wave][c], dv = *(const f32x4 *)&ds[wave][c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc = fmaf(qv[e], kv[e], sc);
+        dP = fmaf(dv[e], vv[e], dP);
+      }
     }
     p = expf(sc * scale - mrow) * invl;
   };
@@ -487,8 +496,9 @@ template <int DH>
 __global__ __launch_bounds__(256) void k_attn_dkv(const float *q, const float *Kc, const float *Vc, const float *dout,
                                                   const float *mst, const float *lst, const float *Dst, Rows rm,
                                                   int Hq, int Hkv, int Tc, float scale, float *dK, float *dV) {
-  constexpr int KP = DH + 1;
-  __shared__ float Ks[64 * KP], Vs[64 * KP], qs[4][DH], ds[4][DH], accK[64 * 64], accV[64 * 64];
+  constexpr int KP = DH + 4;
+  __shared__ __attribute__((aligned(16))) float Ks[64 * KP], Vs[64 * KP], qs[4][DH], ds[4][DH], accK[64 * 64],
+      accV[64 * 64];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t0 = blockIdx.y * 64;
   const int nk = min(64, Tc - t0), nslot = rm.M * G;
@@ -497,10 +507,10 @@ __global__ __launch_bounds__(256) void k_attn_dkv(const float *q, const float *K
   int m0 = 0;
   while (m0 < rm.M && rm.pos(b * rm.M + m0) <= t0) ++m0;
   if (m0 >= rm.M) return;  // (block-uniform)
-  for (int e = threadIdx.x; e < nk * DH; e += 256) {
-    const int r = e / DH, c = e - r * DH;
-    Ks[r * KP + c] = Kc[base + (int64_t)(t0 + r) * DH + c];
-    Vs[r * KP + c] = Vc[base + (int64_t)(t0 + r) * DH + c];
+  for (int e = threadIdx.x; e < nk * (DH / 4); e += 256) {
+    const int r = e / (DH / 4), c = 4 * (e - r * (DH / 4));
+    *(f32x4 *)&Ks[r * KP + c] = *(const f32x4 *)&Kc[base + (int64_t)(t0 + r) * DH + c];
+    *(f32x4 *)&Vs[r * KP + c] = *(const f32x4 *)&Vc[base + (int64_t)(t0 + r) * DH + c];
   }
   for (int half = 0; half < (DH + 63) / 64; ++half) {
     const int dim = half * 64 + lane;
@@ -524,10 +534,15 @@ __global__ __launch_bounds__(256) void k_attn_dkv(const float *q, const float *K
       float p = 0.f, dS = 0.f;
       if (lane < nk && t0 + lane < i) {
         float sc = 0.f, dP = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < DH; ++c) {
-          sc += qs[wave][c] * Ks[lane * KP + c];
-          dP += ds[wave][c] * Vs[lane * KP + c];
+#pragma unroll
+        for (int c = 0; c < DH; c += 4) {
+          const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c], vv = *(const f32x4 *)&Vs[lane * KP + c];
+          const f32x4 qv = *(const f32x4 *)&qs[wave][c], dv = *(const f32x4 *)&ds[wave][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc = fmaf(qv[e], kv[e], sc);
+            dP = fmaf(dv[e], vv[e], dP);
+          }
         }
         const int64_t so = (int64_t)n * Hq + h;
         p = expf(sc * scale - mst[so]) / lst[so];
