@@ -26,9 +26,9 @@
 // walk, so each finds its gradient complete.  What the first gradient pass
 // reads from the no-gradient cache is left in dCache and dropped.
 //
-// Every kernel here is plain float32 arithmetic on the vector ALUs, written
-// for correctness at training shapes rather than speed: a tiled GEMM with
-// optional transposes, row RMSNorm forward/backward and gain gradients,
+// Every kernel here computes in float32, written for correctness at training
+// shapes first: a tiled GEMM with optional transposes on float32 MFMAs, row
+// RMSNorm forward/backward and gain gradients (chunked, summed in order),
 // RoPE and its inverse, strict-causal attention forward (with its softmax
 // statistics) and backward (queries per row; keys and values per key, so no
 // atomics), SwiGLU, the pool's mix and its two backward products, the
@@ -255,24 +255,37 @@ __global__ __launch_bounds__(64) void k_rms_bwd(const float *x, const float *gai
     *o = accumulate ? *o + v : v;
   }
 }
-// dgain[gi, c] += sum over the rows r of group gi of dy[r, c] x[r, c] rinv[r].
-// Block: 64 columns x 16 row slices (slice j takes rows j, j + 16, ...); the
-// slices' sums are added in slice order.
-__global__ __launch_bounds__(1024) void k_gain_grad(const float *x, const float *dy, const float *rinv, float *dg,
+// dgain[gi, c] += sum over the rows r of group gi of dy[r, c] x[r, c] rinv[r],
+// in two passes: k_gain_part sums chunks of GCH rows (block: 64 columns x 16
+// row slices, slice j taking rows j, j + 16, ... of the chunk, the slices
+// added in order) into part[gi, chunk, c]; k_gain_sum adds the chunks in
+// order.
+constexpr int GCH = 256;
+__global__ __launch_bounds__(1024) void k_gain_part(const float *x, const float *dy, const float *rinv, float *part,
                                                     int rpg, int D) {
-  __shared__ float part[16][64];
-  const int cl = threadIdx.x & 63, sl = threadIdx.x >> 6, c = blockIdx.x * 64 + cl, gi = blockIdx.y;
+  __shared__ float sl[16][64];
+  const int cl = threadIdx.x & 63, j = threadIdx.x >> 6, c = blockIdx.x * 64 + cl, gi = blockIdx.y, ch = blockIdx.z;
+  const int nch = gridDim.z;
   float s = 0.f;
-  if (c < D)
-    for (int64_t r = (int64_t)gi * rpg + sl; r < (int64_t)(gi + 1) * rpg; r += 16)
-      s += dy[r * D + c] * x[r * D + c] * rinv[r];
-  part[sl][cl] = s;
-  __syncthreads();
-  if (sl == 0 && c < D) {
-    float t = 0.f;
-    for (int j = 0; j < 16; ++j) t += part[j][cl];
-    dg[(int64_t)gi * D + c] += t;
+  if (c < D) {
+    const int64_t r0 = (int64_t)gi * rpg + (int64_t)ch * GCH, r1 = (int64_t)gi * rpg + min(rpg, (ch + 1) * GCH);
+    for (int64_t r = r0 + j; r < r1; r += 16) s += dy[r * D + c] * x[r * D + c] * rinv[r];
   }
+  sl[j][cl] = s;
+  __syncthreads();
+  if (j == 0 && c < D) {
+    float t = 0.f;
+    for (int i = 0; i < 16; ++i) t += sl[i][cl];
+    part[((int64_t)gi * nch + ch) * D + c] = t;
+  }
+}
+__global__ void k_gain_sum(const float *part, float *dg, int nch, int D, int ngain) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= ngain * D) return;
+  const int gi = i / D, c = i - gi * D;
+  float t = 0.f;
+  for (int ch = 0; ch < nch; ++ch) t += part[((int64_t)gi * nch + ch) * D + c];
+  dg[i] += t;
 }
 
 // ------------------------------------------------------------------ RoPE
@@ -721,6 +734,7 @@ struct Ws {
   size_t dh, dS, da, dq, dout, dG, dU, dact, db, Dst, dKn, dVn, dkraw, dc, dm, dA, dn, du, dz, dxf, lossrow;
   size_t enext, ehead;  // (int arrays)
   size_t split, split_cap;  // split-k partials (floats)
+  size_t gpart;             // gain-gradient chunk sums
   size_t bytes;
 };
 
@@ -794,6 +808,12 @@ inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad) {
   const size_t wide = std::max({F, D, QD, R * D, L * k, KD});
   w.split_cap = 8 * std::max({N * wide, D * F, QD * D, L * k * R * D, k * KD * D, k * N * D});
   w.split = t(w.split_cap);
+  // gain-gradient chunks: ngain * ceil(rows per gain / 256) * width, largest
+  // for the source states [L*N, D], channels [k*N, D], key heads [k*N*Hkv, d]
+  // and query heads [N*Hq, d]
+  auto chunks = [](size_t rows, size_t ngain) { return rows / 256 + ngain; };
+  w.gpart = t(std::max({chunks(L * N, L) * D, chunks(k * N, k) * D, chunks(k * N * c.Hkv, k) * c.d,
+                        chunks(N * c.Hq, 1) * c.d, chunks(N, 1) * D}));
   w.bytes = l.total;
   return w;
 }
@@ -886,7 +906,13 @@ struct Trainer {
     hipLaunchKernelGGL(k_rms_bwd, dim3(rows), dim3(64), 0, s, x, gain, rpg, rinv, dy, dx, acc ? 1 : 0, width);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gain_grad, dim3((width + 63) / 64, ngain), dim3(1024), 0, s, x, dy, rinv, dgain, rpg, width);
+    const int nch = (rpg + GCH - 1) / GCH;
+    hipLaunchKernelGGL(k_gain_part, dim3((width + 63) / 64, ngain, nch), dim3(1024), 0, s, x, dy, rinv, P(o.gpart),
+                       rpg, width);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gain_sum, dim3((ngain * width + 255) / 256), dim3(256), 0, s, P(o.gpart), dgain, nch, width,
+                       ngain);
     return hipGetLastError();
   }
   hipError_t rope(float *x, Rows rm, int N, int rows, int H, bool inverse) {
