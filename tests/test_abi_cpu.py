@@ -329,3 +329,35 @@ def test_decode_step_at_validates_before_launch():
     W0 = _weights()
     W0.lm_head = None
     assert call(Wt=W0) == -1
+
+
+def test_train_binding_checks_before_calling():
+    """train_step's binding: float32 models only, [B, T] int32 tokens, and
+    gradient tensors of the parameters' shapes, all refused before a call."""
+    import torch
+
+    from decode_token_rmsnorm_amd import api
+    from wm_inputs import weight_shapes
+
+    w = WORKLOADS["tiny_fp32"]
+
+    class _Model:
+        shape = w
+        device = torch.device("cpu")
+
+        def __init__(self, dtype):
+            self.dtype = dtype
+            self.t = {n: torch.zeros(sh) for n, sh in weight_shapes(w).items()}
+
+    tok = torch.zeros(1, 16, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        api.train_step(_Model("bf16"), tok, 4)
+    with pytest.raises(ValueError):
+        api.train_step(_Model("f32"), torch.zeros(16, dtype=torch.int32), 4)
+    with pytest.raises(TypeError):
+        api.train_step(_Model("f32"), tok.long(), 4)
+    m = _Model("f32")
+    grads = {n: torch.zeros_like(t) for n, t in m.t.items()}
+    grads["wq"] = torch.zeros(1, 2, 3)
+    with pytest.raises(ValueError):
+        api.train_step(m, tok, 4, grads=grads)
