@@ -71,11 +71,6 @@ struct Rows {
   __host__ __device__ int seq(int n) const { return n / M; }
 };
 
-__device__ __forceinline__ float wsum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 __device__ __forceinline__ float wmax(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -235,7 +230,7 @@ __global__ __launch_bounds__(64) void k_rms(const float *x, const float *gain, i
   const float *xr = x + (int64_t)r * D;
   float ss = 0.f;
   for (int c = lane; c < D; c += 64) ss += xr[c] * xr[c];
-  const float rs = 1.f / sqrtf(wsum(ss) / D + eps);
+  const float rs = 1.f / sqrtf(wave_sum(ss) / D + eps);
   const float *g = gain + (int64_t)(r / rpg) * D;
   for (int c = lane; c < D; c += 64) y[(int64_t)r * D + c] = xr[c] * rs * g[c];
   if (lane == 0) rinv[r] = rs;
@@ -247,7 +242,7 @@ __global__ __launch_bounds__(64) void k_rms_bwd(const float *x, const float *gai
   const float *xr = x + (int64_t)r * D, *dyr = dy + (int64_t)r * D, *g = gain + (int64_t)(r / rpg) * D;
   float dot = 0.f;
   for (int c = lane; c < D; c += 64) dot += g[c] * dyr[c] * xr[c];
-  dot = wsum(dot);
+  dot = wave_sum(dot);
   const float rs = rinv[r], k3 = rs * rs * rs * dot / D;
   for (int c = lane; c < D; c += 64) {
     const float v = rs * g[c] * dyr[c] - xr[c] * k3;
@@ -393,7 +388,7 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, c
       }
       const float mnew = fmaxf(mx, wmax(sc));
       const float p = lane < nv ? expf(sc - mnew) : 0.f, alpha = expf(mx - mnew);
-      l = l * alpha + wsum(p);
+      l = l * alpha + wave_sum(p);
       a0 *= alpha;
       a1 *= alpha;
       for (int u = 0; u < nv; ++u) {
@@ -473,7 +468,7 @@ __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc
       Dp += p * dP;
     }
   }
-  const float Dn = wsum(Dp);
+  const float Dn = wave_sum(Dp);
   float g0 = 0.f, g1 = 0.f;
   for (int t0 = 0; t0 < imax; t0 += 64) {
     stage(t0, min(64, imax - t0));
@@ -618,7 +613,7 @@ __global__ __launch_bounds__(64) void k_mix_dA(const float *dm, const float *nsr
   const float *a = dm + ((int64_t)j * N + n) * D, *b = nsrc + ((int64_t)l * N + n) * D;
   float s = 0.f;
   for (int c = lane; c < D; c += 64) s += a[c] * b[c];
-  s = wsum(s);
+  s = wave_sum(s);
   if (lane == 0) dA[(int64_t)n * L * k + lj] = s;
 }
 // dn[l, n, c] = sum_j A[n, l*k + j] dm[j, n, c]
@@ -669,7 +664,7 @@ __global__ void k_entries(float *cache, float *arr, Rows rm, int k, int B, int N
 // ------------------------------------------------------------------ loss
 __device__ float block_reduce(float v, bool is_max, float *red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  v = is_max ? wmax(v) : wsum(v);
+  v = is_max ? wmax(v) : wave_sum(v);
   __syncthreads();
   if (lane == 0) red[wave] = v;
   __syncthreads();
