@@ -342,28 +342,45 @@ __global__ void k_embed_bwd(const int32_t *tokens, int T, Rows rm, const float *
 
 // ------------------------------------------------------------------ attention
 // Strict causal attention of row n (position i), head h to keys s < i of the
-// channel (K, V: [B, Hkv, Tc, d]).  A block of 4 waves takes 4 consecutive
+// channel (K, V: [B, Hkv, Tc, d]).  A block of 4 waves takes 16 consecutive
 // query slots (m, g) of one sequence b and KV head hk (slot = m*G + g, head
-// hk*G + g), one per wave; they share the key chunks: 64 K and V rows staged
+// hk*G + g), 4 per wave; they share the key chunks: 64 K and V rows staged
 // in LDS by coalesced 16-byte loads (row pitch DH + 4, so the 16-byte reads
-// of 8 lanes at rows t..t+7 fall on disjoint banks).  In a chunk, lane t scores key t0 + t;
-// lanes c and c + 64 own output dims.  Keeps the scaled-score max m and the
-// sum l of exp(score - m) for the backward.
+// of 8 lanes at rows t..t+7 fall on disjoint banks).  In a chunk, lane t
+// scores key t0 + t for the wave's 4 slots (one K row read serves 4 dot
+// products), the probabilities go to LDS as [key][slot], and then lanes c
+// and c + 64 own output dims: one 16-byte read gives a key's 4
+// probabilities, one read its value at the lane's dim.  Keeps the
+// scaled-score max m and the sum l of exp(score - m) for the backward.
+constexpr int AQ = 4;  // query slots per wave
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, const float *Vc, Rows rm, int Hq,
                                               int Hkv, int Tc, float scale, float *out, float *mst, float *lst) {
-  constexpr int KP = DH + 4;
-  __shared__ __attribute__((aligned(16))) float qs[4][DH], Ks[64 * KP], Vs[64 * KP];
+  constexpr int KP = DH + 4, SB = 4 * AQ;
+  __shared__ __attribute__((aligned(16))) float qs[SB][DH], Ks[64 * KP], Vs[64 * KP], ps[4][64][AQ];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nslot = rm.M * G;
-  const int slot = blockIdx.y * 4 + wave, last = min(blockIdx.y * 4 + 3, nslot - 1);
-  const bool act = slot < nslot;
-  const int m = act ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act ? slot - m * G : 0);
-  const int i = act ? rm.pos(n) : 0, imax = rm.pos(b * rm.M + last / G);
+  const int last = min(blockIdx.y * SB + SB - 1, nslot - 1), imax = rm.pos(b * rm.M + last / G);
   const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * DH, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * DH;
-  const int64_t qo = ((int64_t)n * Hq + h) * DH;
-  for (int c = lane; c < DH; c += 64) qs[wave][c] = act ? q[qo + c] : 0.f;
-  float mx = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
+  bool act[AQ];
+  int ipos[AQ];
+  int64_t qo[AQ], so[AQ];
+#pragma unroll
+  for (int s = 0; s < AQ; ++s) {
+    const int slot = blockIdx.y * SB + wave * AQ + s;
+    act[s] = slot < nslot;
+    const int m = act[s] ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act[s] ? slot - m * G : 0);
+    ipos[s] = act[s] ? rm.pos(n) : 0;
+    so[s] = (int64_t)n * Hq + h;
+    qo[s] = so[s] * DH;
+    for (int c = lane; c < DH; c += 64) qs[wave * AQ + s][c] = act[s] ? q[qo[s] + c] : 0.f;
+  }
+  float mx[AQ], l[AQ], a0[AQ], a1[AQ];
+#pragma unroll
+  for (int s = 0; s < AQ; ++s) {
+    mx[s] = -INFINITY;
+    l[s] = a0[s] = a1[s] = 0.f;
+  }
   for (int t0 = 0; t0 < imax; t0 += 64) {
     const int nk = min(64, imax - t0);
     __syncthreads();  // (the previous chunk's reads are done; qs is written)
@@ -373,39 +390,55 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, c
       *(f32x4 *)&Vs[r * KP + c] = *(const f32x4 *)&V[(int64_t)(t0 + r) * DH + c];
     }
     __syncthreads();
-    if (t0 < i) {  // (wave-uniform)
-      const int nv = min(64, i - t0);
-      float sc = -INFINITY;
-      if (lane < nv) {
-        float dot = 0.f;
+    float dot[AQ];
 #pragma unroll
-        for (int c = 0; c < DH; c += 4) {
-          const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c], qv = *(const f32x4 *)&qs[wave][c];
+    for (int s = 0; s < AQ; ++s) dot[s] = 0.f;
+    if (lane < nk) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dot = fmaf(qv[e], kv[e], dot);
+      for (int c = 0; c < DH; c += 4) {
+        const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c];
+#pragma unroll
+        for (int s = 0; s < AQ; ++s) {
+          const f32x4 qv = *(const f32x4 *)&qs[wave * AQ + s][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot[s] = fmaf(qv[e], kv[e], dot[s]);
         }
-        sc = dot * scale;
       }
-      const float mnew = fmaxf(mx, wmax(sc));
-      const float p = lane < nv ? expf(sc - mnew) : 0.f, alpha = expf(mx - mnew);
-      l = l * alpha + wave_sum(p);
-      a0 *= alpha;
-      a1 *= alpha;
-      for (int u = 0; u < nv; ++u) {
-        const float pu = __shfl(p, u);
-        if (lane < DH) a0 += pu * Vs[u * KP + lane];
-        if (lane + 64 < DH) a1 += pu * Vs[u * KP + lane + 64];
+    }
+#pragma unroll
+    for (int s = 0; s < AQ; ++s) {
+      const bool ok = t0 + lane < ipos[s] && lane < nk;
+      const float sc = ok ? dot[s] * scale : -INFINITY;
+      const float mnew = fmaxf(mx[s], wmax(sc));
+      const float p = ok ? expf(sc - mnew) : 0.f;
+      const float alpha = mnew == -INFINITY ? 1.f : expf(mx[s] - mnew);
+      l[s] = l[s] * alpha + wave_sum(p);
+      a0[s] *= alpha;
+      a1[s] *= alpha;
+      mx[s] = mnew;
+      ps[wave][lane][s] = p;
+    }
+    __syncthreads();  // (ps of the wave: written by all its lanes)
+    for (int u = 0; u < nk; ++u) {
+      const f32x4 pu = *(const f32x4 *)&ps[wave][u][0];
+      const float v0 = lane < DH ? Vs[u * KP + lane] : 0.f, v1 = lane + 64 < DH ? Vs[u * KP + lane + 64] : 0.f;
+#pragma unroll
+      for (int s = 0; s < AQ; ++s) {
+        a0[s] = fmaf(pu[s], v0, a0[s]);
+        a1[s] = fmaf(pu[s], v1, a1[s]);
       }
-      mx = mnew;
     }
   }
-  if (!act) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (lane < DH) out[qo + lane] = a0 * inv;
-  if (lane + 64 < DH) out[qo + lane + 64] = a1 * inv;
-  if (lane == 0) {
-    mst[(int64_t)n * Hq + h] = mx;
-    lst[(int64_t)n * Hq + h] = l;
+#pragma unroll
+  for (int s = 0; s < AQ; ++s) {
+    if (!act[s]) continue;
+    const float inv = l[s] > 0.f ? 1.f / l[s] : 0.f;
+    if (lane < DH) out[qo[s] + lane] = a0[s] * inv;
+    if (lane + 64 < DH) out[qo[s] + lane + 64] = a1[s] * inv;
+    if (lane == 0) {
+      mst[so[s]] = mx[s];
+      lst[so[s]] = l[s];
+    }
   }
 }
 // dq of row n, head h: dS_t = p_t (dP_t - Dn) with dP_t = dout . V_t and
@@ -924,7 +957,7 @@ struct Trainer {
   float *chanK(size_t cacheoff, int ch) const { return P(cacheoff) + (size_t)ch * B * KD * T; }
   hipError_t attn_fwd(const float *q, const float *K, const float *Vv, Rows rm, int N, float scale, float *out,
                       float *mst, float *lst) {
-    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 3) / 4);
+    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 4 * AQ - 1) / (4 * AQ));
     if (c.d == 32)
       hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
     else if (c.d == 64)
