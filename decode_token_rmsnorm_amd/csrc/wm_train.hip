@@ -446,27 +446,38 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, c
 // products, so that sum_t dS_t stays 0 to rounding also where the row has
 // few keys and dP_t and Dn nearly cancel); dq = scale * sum_t dS_t K_t.
 // Keeps Dn for the key-side kernel.  Blocks, slots and staged chunks as in
-// k_attn; the chunks are walked twice (Dn first, then dS and dq).
+// k_attn (4 slots per wave); the chunks are walked twice (Dn first, then
+// dS, which goes through LDS as [key][slot], and dq).
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc, const float *Vc, const float *dout,
                                                  const float *mst, const float *lst, Rows rm, int Hq, int Hkv,
                                                  int Tc, float scale, float *dq, float *Dst) {
-  constexpr int KP = DH + 4;
-  __shared__ __attribute__((aligned(16))) float qs[4][DH], ds[4][DH], Ks[64 * KP], Vs[64 * KP];
+  constexpr int KP = DH + 4, SB = 4 * AQ;
+  __shared__ __attribute__((aligned(16))) float qs[SB][DH], ds[SB][DH], Ks[64 * KP], Vs[64 * KP], dsl[4][64][AQ];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nslot = rm.M * G;
-  const int slot = blockIdx.y * 4 + wave, last = min(blockIdx.y * 4 + 3, nslot - 1);
-  const bool act = slot < nslot;
-  const int m = act ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act ? slot - m * G : 0);
-  const int i = act ? rm.pos(n) : 0, imax = rm.pos(b * rm.M + last / G);
+  const int last = min(blockIdx.y * SB + SB - 1, nslot - 1), imax = rm.pos(b * rm.M + last / G);
   const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * DH, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * DH;
-  const int64_t qo = ((int64_t)n * Hq + h) * DH;
-  for (int c = lane; c < DH; c += 64) {
-    qs[wave][c] = act ? q[qo + c] : 0.f;
-    ds[wave][c] = act ? dout[qo + c] : 0.f;
+  bool act[AQ];
+  int ipos[AQ];
+  int64_t qo[AQ], so[AQ];
+  float mrow[AQ], invl[AQ];
+#pragma unroll
+  for (int s = 0; s < AQ; ++s) {
+    const int slot = blockIdx.y * SB + wave * AQ + s;
+    act[s] = slot < nslot;
+    const int m = act[s] ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act[s] ? slot - m * G : 0);
+    ipos[s] = act[s] ? rm.pos(n) : 0;
+    so[s] = (int64_t)n * Hq + h;
+    qo[s] = so[s] * DH;
+    for (int c = lane; c < DH; c += 64) {
+      qs[wave * AQ + s][c] = act[s] ? q[qo[s] + c] : 0.f;
+      ds[wave * AQ + s][c] = act[s] ? dout[qo[s] + c] : 0.f;
+    }
+    mrow[s] = act[s] ? mst[so[s]] : 0.f;
+    const float lr = act[s] ? lst[so[s]] : 0.f;
+    invl[s] = lr > 0.f ? 1.f / lr : 0.f;
   }
-  const float mrow = act ? mst[(int64_t)n * Hq + h] : 0.f, lrow = act ? lst[(int64_t)n * Hq + h] : 0.f;
-  const float invl = lrow > 0.f ? 1.f / lrow : 0.f;
   auto stage = [&](int t0, int nk) {
     __syncthreads();
     for (int e = threadIdx.x; e < nk * (DH / 4); e += 256) {
@@ -476,54 +487,72 @@ __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc
     }
     __syncthreads();
   };
-  // p and dP of key t0 + lane (staged)
-  auto key = [&](float &p, float &dP) {
-    float sc = 0.f;
-    dP = 0.f;
+  // p and dP of key t0 + lane (staged) for the wave's slots (0 past a slot's position)
+  auto keys = [&](int t0, int nk, float (&p)[AQ], float (&dP)[AQ]) {
+    float sc[AQ];
 #pragma unroll
-    for (int c = 0; c < DH; c += 4) {
-      const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c], vv = *(const f32x4 *)&Vs[lane * KP + c];
-      const f32x4 qv = *(const f32x4 *)&qs[wave][c], dv = *(const f32x4 *)&ds[wave][c];
+    for (int s = 0; s < AQ; ++s) sc[s] = dP[s] = 0.f;
+    if (lane < nk) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc = fmaf(qv[e], kv[e], sc);
-        dP = fmaf(dv[e], vv[e], dP);
+      for (int c = 0; c < DH; c += 4) {
+        const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c], vv = *(const f32x4 *)&Vs[lane * KP + c];
+#pragma unroll
+        for (int s = 0; s < AQ; ++s) {
+          const f32x4 qv = *(const f32x4 *)&qs[wave * AQ + s][c], dv = *(const f32x4 *)&ds[wave * AQ + s][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc[s] = fmaf(qv[e], kv[e], sc[s]);
+            dP[s] = fmaf(dv[e], vv[e], dP[s]);
+          }
+        }
       }
     }
-    p = expf(sc * scale - mrow) * invl;
+#pragma unroll
+    for (int s = 0; s < AQ; ++s)
+      p[s] = (lane < nk && t0 + lane < ipos[s]) ? expf(sc[s] * scale - mrow[s]) * invl[s] : 0.f;
   };
-  float Dp = 0.f;
+  float Dp[AQ];
+#pragma unroll
+  for (int s = 0; s < AQ; ++s) Dp[s] = 0.f;
   for (int t0 = 0; t0 < imax; t0 += 64) {
-    stage(t0, min(64, imax - t0));
-    if (lane < i - t0) {
-      float p, dP;
-      key(p, dP);
-      Dp += p * dP;
+    const int nk = min(64, imax - t0);
+    stage(t0, nk);
+    float p[AQ], dP[AQ];
+    keys(t0, nk, p, dP);
+#pragma unroll
+    for (int s = 0; s < AQ; ++s) Dp[s] += p[s] * dP[s];
+  }
+  float Dn[AQ], g0[AQ], g1[AQ];
+#pragma unroll
+  for (int s = 0; s < AQ; ++s) {
+    Dn[s] = wave_sum(Dp[s]);
+    g0[s] = g1[s] = 0.f;
+  }
+  for (int t0 = 0; t0 < imax; t0 += 64) {
+    const int nk = min(64, imax - t0);
+    stage(t0, nk);
+    float p[AQ], dP[AQ];
+    keys(t0, nk, p, dP);
+#pragma unroll
+    for (int s = 0; s < AQ; ++s) dsl[wave][lane][s] = p[s] * (dP[s] - Dn[s]);
+    __syncthreads();  // (dsl of the wave: written by all its lanes)
+    for (int u = 0; u < nk; ++u) {
+      const f32x4 su = *(const f32x4 *)&dsl[wave][u][0];
+      const float k0 = lane < DH ? Ks[u * KP + lane] : 0.f, k1 = lane + 64 < DH ? Ks[u * KP + lane + 64] : 0.f;
+#pragma unroll
+      for (int s = 0; s < AQ; ++s) {
+        g0[s] = fmaf(su[s], k0, g0[s]);
+        g1[s] = fmaf(su[s], k1, g1[s]);
+      }
     }
   }
-  const float Dn = wave_sum(Dp);
-  float g0 = 0.f, g1 = 0.f;
-  for (int t0 = 0; t0 < imax; t0 += 64) {
-    stage(t0, min(64, imax - t0));
-    if (t0 < i) {  // (wave-uniform)
-      const int nv = min(64, i - t0);
-      float dS = 0.f;
-      if (lane < nv) {
-        float p, dP;
-        key(p, dP);
-        dS = p * (dP - Dn);
-      }
-      for (int u = 0; u < nv; ++u) {
-        const float su = __shfl(dS, u);
-        if (lane < DH) g0 += su * Ks[u * KP + lane];
-        if (lane + 64 < DH) g1 += su * Ks[u * KP + lane + 64];
-      }
-    }
+#pragma unroll
+  for (int s = 0; s < AQ; ++s) {
+    if (!act[s]) continue;
+    if (lane < DH) dq[qo[s] + lane] = g0[s] * scale;
+    if (lane + 64 < DH) dq[qo[s] + lane + 64] = g1[s] * scale;
+    if (lane == 0) Dst[so[s]] = Dn[s];
   }
-  if (!act) return;
-  if (lane < DH) dq[qo + lane] = g0 * scale;
-  if (lane + 64 < DH) dq[qo + lane + 64] = g1 * scale;
-  if (lane == 0) Dst[(int64_t)n * Hq + h] = Dn;
 }
 
 // dK_t += scale * sum dS q, dV_t += sum p dout over the rows n of sequence b
@@ -982,7 +1011,7 @@ struct Trainer {
   }
   hipError_t attn_dq(const float *q, const float *K, const float *Vv, const float *dout, const float *mst,
                      const float *lst, Rows rm, int N, float scale, float *dq, float *Dst) {
-    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 3) / 4);
+    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 4 * AQ - 1) / (4 * AQ));
     if (c.d == 32)
       hipLaunchKernelGGL(k_attn_dq<32>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
                          Dst);
