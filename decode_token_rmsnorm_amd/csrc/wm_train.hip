@@ -342,307 +342,347 @@ __global__ void k_embed_bwd(const int32_t *tokens, int T, Rows rm, const float *
 
 // ------------------------------------------------------------------ attention
 // Strict causal attention of row n (position i), head h to keys s < i of the
-// channel (K, V: [B, Hkv, Tc, d]).  A block of 4 waves takes 16 consecutive
-// query slots (m, g) of one sequence b and KV head hk (slot = m*G + g, head
-// hk*G + g), 4 per wave; they share the key chunks: 64 K and V rows staged
-// in LDS by coalesced 16-byte loads (row pitch DH + 4, so the 16-byte reads
-// of 8 lanes at rows t..t+7 fall on disjoint banks).  In a chunk, lane t
-// scores key t0 + t for the wave's 4 slots (one K row read serves 4 dot
-// products), the probabilities go to LDS as [key][slot], and then lanes c
-// and c + 64 own output dims: one 16-byte read gives a key's 4
-// probabilities, one read its value at the lane's dim.  Keeps the
-// scaled-score max m and the sum l of exp(score - m) for the backward.
-constexpr int AQ = 4;  // query slots per wave
+// channel (K, V: [B, Hkv, Tc, d]), on float32 16x16x4 MFMAs in tiles of 16
+// keys x 16 query slots.  A query slot (m, g) of sequence b and KV head hk is
+// row b*M + m at head hk*G + g (slot = m*G + g); the slots of a tile share
+// the tile's keys, so GQA heads reuse every K/V load.
+//
+// MFMA operand lanes (l = lane, li = l % 16, lj = l / 16): A row li and B
+// column li, both at k = lj; accumulator element e: row 4*lj + e, column
+// li.  Products over the head dim take dims 16t + 4*lj + e at step (t, e),
+// so that a lane's four steps read one 16-byte run of a K, V, q or dout
+// row; products over keys (or slots) take key (slot) 4*lj + e at step e,
+// the row of the accumulator element e that feeds them, so scores and
+// probabilities go from accumulators to operands without moving.
+//
+// Forward and query side: a block of 4 waves takes 16 slots; wave w takes
+// the 16-key tiles w, w + 4, ... below the block's last position, loading
+// its K and V rows from memory into registers, and keeps its own running
+// max, sum and output; the block then merges the 4 waves' partial results
+// in wave order.  Scores are kept transposed (keys x slots: S^T = K q^T),
+// so that each lane holds one slot, its statistics included.
+constexpr int ATQ = 16;  // query slots per block (forward and query side)
+
+struct Slot {
+  bool act;
+  int ipos;
+  int64_t so;  // (row, head) index
+};
+__device__ __forceinline__ Slot slot_of(int slot, int nslot, Rows rm, int b, int hk, int G, int Hq) {
+  Slot r;
+  r.act = slot < nslot;
+  const int m = r.act ? slot / G : 0, n = b * rm.M + m, h = hk * G + (r.act ? slot - m * G : 0);
+  r.ipos = r.act ? rm.pos(n) : 0;
+  r.so = (int64_t)n * Hq + h;
+  return r;
+}
+__device__ __forceinline__ f32x4 mf4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Scores and probabilities of out = softmax(scale q K^T over s < i) V.  Keeps
+// the scaled-score max m and the sum l of exp(score - m) for the backward
+// (a slot with no key: m = -inf, l = 0, output 0).  Blocks run longest
+// (last slots) first.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, const float *Vc, Rows rm, int Hq,
                                               int Hkv, int Tc, float scale, float *out, float *mst, float *lst) {
-  constexpr int KP = DH + 4, SB = 4 * AQ;
-  __shared__ __attribute__((aligned(16))) float qs[SB][DH], Ks[64 * KP], Vs[64 * KP], ps[4][64][AQ];
+  constexpr int NT = DH / 16;
+  __shared__ float cm[4][ATQ], cl[4][ATQ], co[4][DH][ATQ + 1];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nslot = rm.M * G;
-  const int last = min(blockIdx.y * SB + SB - 1, nslot - 1), imax = rm.pos(b * rm.M + last / G);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lj = lane >> 4;
+  const int nslot = rm.M * G, sb = (gridDim.y - 1 - blockIdx.y) * ATQ;
+  const int imax = rm.pos(b * rm.M + min(sb + ATQ - 1, nslot - 1) / G);
+  const Slot me = slot_of(sb + li, nslot, rm, b, hk, G, Hq);
   const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * DH, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * DH;
-  bool act[AQ];
-  int ipos[AQ];
-  int64_t qo[AQ], so[AQ];
+  f32x4 qf[NT], o[NT];
 #pragma unroll
-  for (int s = 0; s < AQ; ++s) {
-    const int slot = blockIdx.y * SB + wave * AQ + s;
-    act[s] = slot < nslot;
-    const int m = act[s] ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act[s] ? slot - m * G : 0);
-    ipos[s] = act[s] ? rm.pos(n) : 0;
-    so[s] = (int64_t)n * Hq + h;
-    qo[s] = so[s] * DH;
-    for (int c = lane; c < DH; c += 64) qs[wave * AQ + s][c] = act[s] ? q[qo[s] + c] : 0.f;
+  for (int t = 0; t < NT; ++t) {
+    qf[t] = me.act ? *(const f32x4 *)&q[me.so * DH + 16 * t + 4 * lj] : f32x4{0.f, 0.f, 0.f, 0.f};
+    o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float mx[AQ], l[AQ], a0[AQ], a1[AQ];
+  float mx = -INFINITY, ls = 0.f;
+  for (int k0 = 16 * wave; k0 < imax; k0 += 64) {
+    // (rows past Tc - 1 are clamped: their keys lie past imax, masked)
+    f32x4 kf[NT];
+    float vf[NT][4];
+    const int kr = min(k0 + li, Tc - 1);
 #pragma unroll
-  for (int s = 0; s < AQ; ++s) {
-    mx[s] = -INFINITY;
-    l[s] = a0[s] = a1[s] = 0.f;
-  }
-  for (int t0 = 0; t0 < imax; t0 += 64) {
-    const int nk = min(64, imax - t0);
-    __syncthreads();  // (the previous chunk's reads are done; qs is written)
-    for (int e = threadIdx.x; e < nk * (DH / 4); e += 256) {
-      const int r = e / (DH / 4), c = 4 * (e - r * (DH / 4));
-      *(f32x4 *)&Ks[r * KP + c] = *(const f32x4 *)&K[(int64_t)(t0 + r) * DH + c];
-      *(f32x4 *)&Vs[r * KP + c] = *(const f32x4 *)&V[(int64_t)(t0 + r) * DH + c];
+    for (int t = 0; t < NT; ++t) kf[t] = *(const f32x4 *)&K[(int64_t)kr * DH + 16 * t + 4 * lj];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int vr = min(k0 + 4 * lj + e, Tc - 1);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) vf[i][e] = V[(int64_t)vr * DH + 16 * i + li];
     }
-    __syncthreads();
-    float dot[AQ];
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < AQ; ++s) dot[s] = 0.f;
-    if (lane < nk) {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int c = 0; c < DH; c += 4) {
-        const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c];
+      for (int e = 0; e < 4; ++e) s = mf4(kf[t][e], qf[t][e], s);
+    float sc[4], ml = -INFINITY;
 #pragma unroll
-        for (int s = 0; s < AQ; ++s) {
-          const f32x4 qv = *(const f32x4 *)&qs[wave * AQ + s][c];
+    for (int e = 0; e < 4; ++e) {
+      sc[e] = k0 + 4 * lj + e < me.ipos ? s[e] * scale : -INFINITY;
+      ml = fmaxf(ml, sc[e]);
+    }
+    ml = fmaxf(ml, __shfl_xor(ml, 16));
+    ml = fmaxf(ml, __shfl_xor(ml, 32));
+    const float mn = fmaxf(mx, ml), al = mn == -INFINITY ? 1.f : expf(mx - mn);
+    float p[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dot[s] = fmaf(qv[e], kv[e], dot[s]);
-        }
+    for (int e = 0; e < 4; ++e) p[e] = sc[e] == -INFINITY ? 0.f : expf(sc[e] - mn);
+    ls = ls * al + ((p[0] + p[1]) + (p[2] + p[3]));
+    mx = mn;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      o[i] *= al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[i] = mf4(vf[i][e], p[e], o[i]);  // O^T += V^T P^T
+    }
+  }
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  if (lj == 0) {
+    cm[wave][li] = mx;
+    cl[wave][li] = ls;
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) co[wave][16 * i + 4 * lj + e][li] = o[i][e];
+  __syncthreads();
+  for (int x = threadIdx.x; x < ATQ * DH; x += 256) {
+    const int sl = x / DH, d = x - sl * DH;
+    const Slot r = slot_of(sb + sl, nslot, rm, b, hk, G, Hq);
+    if (!r.act) continue;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w][sl]);
+    if (M != -INFINITY)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = cm[w][sl] == -INFINITY ? 0.f : expf(cm[w][sl] - M);
+        L += f * cl[w][sl];
+        O += f * co[w][d][sl];
       }
-    }
-#pragma unroll
-    for (int s = 0; s < AQ; ++s) {
-      const bool ok = t0 + lane < ipos[s] && lane < nk;
-      const float sc = ok ? dot[s] * scale : -INFINITY;
-      const float mnew = fmaxf(mx[s], wmax(sc));
-      const float p = ok ? expf(sc - mnew) : 0.f;
-      const float alpha = mnew == -INFINITY ? 1.f : expf(mx[s] - mnew);
-      l[s] = l[s] * alpha + wave_sum(p);
-      a0[s] *= alpha;
-      a1[s] *= alpha;
-      mx[s] = mnew;
-      ps[wave][lane][s] = p;
-    }
-    __syncthreads();  // (ps of the wave: written by all its lanes)
-    for (int u = 0; u < nk; ++u) {
-      const f32x4 pu = *(const f32x4 *)&ps[wave][u][0];
-      const float v0 = lane < DH ? Vs[u * KP + lane] : 0.f, v1 = lane + 64 < DH ? Vs[u * KP + lane + 64] : 0.f;
-#pragma unroll
-      for (int s = 0; s < AQ; ++s) {
-        a0[s] = fmaf(pu[s], v0, a0[s]);
-        a1[s] = fmaf(pu[s], v1, a1[s]);
-      }
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < AQ; ++s) {
-    if (!act[s]) continue;
-    const float inv = l[s] > 0.f ? 1.f / l[s] : 0.f;
-    if (lane < DH) out[qo[s] + lane] = a0[s] * inv;
-    if (lane + 64 < DH) out[qo[s] + lane + 64] = a1[s] * inv;
-    if (lane == 0) {
-      mst[so[s]] = mx[s];
-      lst[so[s]] = l[s];
+    out[r.so * DH + d] = L > 0.f ? O / L : 0.f;
+    if (d == 0) {
+      mst[r.so] = M;
+      lst[r.so] = L;
     }
   }
 }
+
 // dq of row n, head h: dS_t = p_t (dP_t - Dn) with dP_t = dout . V_t and
 // Dn = sum_t p_t dP_t (equal to dout . out; summed from the same p_t dP_t
 // products, so that sum_t dS_t stays 0 to rounding also where the row has
 // few keys and dP_t and Dn nearly cancel); dq = scale * sum_t dS_t K_t.
-// Keeps Dn for the key-side kernel.  Blocks, slots and staged chunks as in
-// k_attn (4 slots per wave); the chunks are walked twice (Dn first, then
-// dS, which goes through LDS as [key][slot], and dq).
+// Keeps Dn for the key-side kernel.  Blocks, waves and key tiles as in
+// k_attn; the tiles are walked twice (Dn first, merged over the waves in
+// wave order, then dS and dq^T = K^T dS^T), and the waves' dq are added in
+// wave order.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc, const float *Vc, const float *dout,
                                                  const float *mst, const float *lst, Rows rm, int Hq, int Hkv,
                                                  int Tc, float scale, float *dq, float *Dst) {
-  constexpr int KP = DH + 4, SB = 4 * AQ;
-  __shared__ __attribute__((aligned(16))) float qs[SB][DH], ds[SB][DH], Ks[64 * KP], Vs[64 * KP], dsl[4][64][AQ];
+  constexpr int NT = DH / 16;
+  __shared__ float cD[4][ATQ], cg[4][DH][ATQ + 1];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nslot = rm.M * G;
-  const int last = min(blockIdx.y * SB + SB - 1, nslot - 1), imax = rm.pos(b * rm.M + last / G);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lj = lane >> 4;
+  const int nslot = rm.M * G, sb = (gridDim.y - 1 - blockIdx.y) * ATQ;
+  const int imax = rm.pos(b * rm.M + min(sb + ATQ - 1, nslot - 1) / G);
+  const Slot me = slot_of(sb + li, nslot, rm, b, hk, G, Hq);
   const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * DH, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * DH;
-  bool act[AQ];
-  int ipos[AQ];
-  int64_t qo[AQ], so[AQ];
-  float mrow[AQ], invl[AQ];
+  f32x4 qf[NT], df[NT];
 #pragma unroll
-  for (int s = 0; s < AQ; ++s) {
-    const int slot = blockIdx.y * SB + wave * AQ + s;
-    act[s] = slot < nslot;
-    const int m = act[s] ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act[s] ? slot - m * G : 0);
-    ipos[s] = act[s] ? rm.pos(n) : 0;
-    so[s] = (int64_t)n * Hq + h;
-    qo[s] = so[s] * DH;
-    for (int c = lane; c < DH; c += 64) {
-      qs[wave * AQ + s][c] = act[s] ? q[qo[s] + c] : 0.f;
-      ds[wave * AQ + s][c] = act[s] ? dout[qo[s] + c] : 0.f;
-    }
-    mrow[s] = act[s] ? mst[so[s]] : 0.f;
-    const float lr = act[s] ? lst[so[s]] : 0.f;
-    invl[s] = lr > 0.f ? 1.f / lr : 0.f;
+  for (int t = 0; t < NT; ++t) {
+    qf[t] = me.act ? *(const f32x4 *)&q[me.so * DH + 16 * t + 4 * lj] : f32x4{0.f, 0.f, 0.f, 0.f};
+    df[t] = me.act ? *(const f32x4 *)&dout[me.so * DH + 16 * t + 4 * lj] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  auto stage = [&](int t0, int nk) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < nk * (DH / 4); e += 256) {
-      const int r = e / (DH / 4), c = 4 * (e - r * (DH / 4));
-      *(f32x4 *)&Ks[r * KP + c] = *(const f32x4 *)&K[(int64_t)(t0 + r) * DH + c];
-      *(f32x4 *)&Vs[r * KP + c] = *(const f32x4 *)&V[(int64_t)(t0 + r) * DH + c];
-    }
-    __syncthreads();
-  };
-  // p and dP of key t0 + lane (staged) for the wave's slots (0 past a slot's position)
-  auto keys = [&](int t0, int nk, float (&p)[AQ], float (&dP)[AQ]) {
-    float sc[AQ];
+  const float mrow = me.act ? mst[me.so] : 0.f, lr = me.act ? lst[me.so] : 0.f, invl = lr > 0.f ? 1.f / lr : 0.f;
+  // p and dP of keys k0 + 4 lj + e for the lane's slot (0 past its position)
+  auto tile = [&](int k0, float (&p)[4], f32x4 &dP) {
+    const int kr = min(k0 + li, Tc - 1);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    dP = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < AQ; ++s) sc[s] = dP[s] = 0.f;
-    if (lane < nk) {
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 kf = *(const f32x4 *)&K[(int64_t)kr * DH + 16 * t + 4 * lj];
+      const f32x4 vf = *(const f32x4 *)&V[(int64_t)kr * DH + 16 * t + 4 * lj];
 #pragma unroll
-      for (int c = 0; c < DH; c += 4) {
-        const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c], vv = *(const f32x4 *)&Vs[lane * KP + c];
-#pragma unroll
-        for (int s = 0; s < AQ; ++s) {
-          const f32x4 qv = *(const f32x4 *)&qs[wave * AQ + s][c], dv = *(const f32x4 *)&ds[wave * AQ + s][c];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc[s] = fmaf(qv[e], kv[e], sc[s]);
-            dP[s] = fmaf(dv[e], vv[e], dP[s]);
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        s = mf4(kf[e], qf[t][e], s);    // S^T = K q^T
+        dP = mf4(vf[e], df[t][e], dP);  // dP^T = V dout^T
       }
     }
 #pragma unroll
-    for (int s = 0; s < AQ; ++s)
-      p[s] = (lane < nk && t0 + lane < ipos[s]) ? expf(sc[s] * scale - mrow[s]) * invl[s] : 0.f;
+    for (int e = 0; e < 4; ++e) p[e] = k0 + 4 * lj + e < me.ipos ? expf(s[e] * scale - mrow) * invl : 0.f;
   };
-  float Dp[AQ];
+  float Dp = 0.f;
+  for (int k0 = 16 * wave; k0 < imax; k0 += 64) {
+    float p[4];
+    f32x4 dP;
+    tile(k0, p, dP);
 #pragma unroll
-  for (int s = 0; s < AQ; ++s) Dp[s] = 0.f;
-  for (int t0 = 0; t0 < imax; t0 += 64) {
-    const int nk = min(64, imax - t0);
-    stage(t0, nk);
-    float p[AQ], dP[AQ];
-    keys(t0, nk, p, dP);
-#pragma unroll
-    for (int s = 0; s < AQ; ++s) Dp[s] += p[s] * dP[s];
+    for (int e = 0; e < 4; ++e) Dp = fmaf(p[e], dP[e], Dp);
   }
-  float Dn[AQ], g0[AQ], g1[AQ];
+  Dp += __shfl_xor(Dp, 16);
+  Dp += __shfl_xor(Dp, 32);
+  if (lj == 0) cD[wave][li] = Dp;
+  __syncthreads();
+  const float Dn = ((cD[0][li] + cD[1][li]) + cD[2][li]) + cD[3][li];
+  f32x4 g[NT];
 #pragma unroll
-  for (int s = 0; s < AQ; ++s) {
-    Dn[s] = wave_sum(Dp[s]);
-    g0[s] = g1[s] = 0.f;
-  }
-  for (int t0 = 0; t0 < imax; t0 += 64) {
-    const int nk = min(64, imax - t0);
-    stage(t0, nk);
-    float p[AQ], dP[AQ];
-    keys(t0, nk, p, dP);
+  for (int i = 0; i < NT; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 16 * wave; k0 < imax; k0 += 64) {
+    float p[4];
+    f32x4 dP;
+    tile(k0, p, dP);
 #pragma unroll
-    for (int s = 0; s < AQ; ++s) dsl[wave][lane][s] = p[s] * (dP[s] - Dn[s]);
-    __syncthreads();  // (dsl of the wave: written by all its lanes)
-    for (int u = 0; u < nk; ++u) {
-      const f32x4 su = *(const f32x4 *)&dsl[wave][u][0];
-      const float k0 = lane < DH ? Ks[u * KP + lane] : 0.f, k1 = lane + 64 < DH ? Ks[u * KP + lane + 64] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const float dS = p[e] * (dP[e] - Dn);
+      const int kr = min(k0 + 4 * lj + e, Tc - 1);
 #pragma unroll
-      for (int s = 0; s < AQ; ++s) {
-        g0[s] = fmaf(su[s], k0, g0[s]);
-        g1[s] = fmaf(su[s], k1, g1[s]);
-      }
+      for (int i = 0; i < NT; ++i) g[i] = mf4(K[(int64_t)kr * DH + 16 * i + li], dS, g[i]);  // dq^T += K^T dS^T
     }
   }
 #pragma unroll
-  for (int s = 0; s < AQ; ++s) {
-    if (!act[s]) continue;
-    if (lane < DH) dq[qo[s] + lane] = g0[s] * scale;
-    if (lane + 64 < DH) dq[qo[s] + lane + 64] = g1[s] * scale;
-    if (lane == 0) Dst[so[s]] = Dn[s];
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cg[wave][16 * i + 4 * lj + e][li] = g[i][e];
+  __syncthreads();
+  for (int x = threadIdx.x; x < ATQ * DH; x += 256) {
+    const int sl = x / DH, d = x - sl * DH;
+    const Slot r = slot_of(sb + sl, nslot, rm, b, hk, G, Hq);
+    if (!r.act) continue;
+    dq[r.so * DH + d] = (((cg[0][d][sl] + cg[1][d][sl]) + cg[2][d][sl]) + cg[3][d][sl]) * scale;
+    if (d == 0) Dst[r.so] = ((cD[0][sl] + cD[1][sl]) + cD[2][sl]) + cD[3][sl];
   }
 }
 
 // dK_t += scale * sum dS q, dV_t += sum p dout over the rows n of sequence b
-// with position > t and the heads of KV head hk.  A block of 4 waves takes a
-// chunk of 64 keys of (b, hk), staged in LDS as in k_attn; the waves take
-// the query slots round-robin.  For a slot, lane t computes p and dS of key
-// t0 + t from the staged rows; then lane c accumulates dims c (and c + 64,
-// in a second walk for head dim 128) of all 64 keys in registers.  The
-// waves' partial sums are added through LDS in wave order.
+// with position > t and the heads of KV head hk.  A block of 4 waves takes
+// 64 keys of (b, hk), 16 per wave, with the wave's K and V rows in registers;
+// it walks the query slots from the first row past its first key in tiles
+// of 16, staged in LDS (q, dout and each slot's m, 1/l, Dn and position;
+// two buffers, the next tile loaded into registers while the current one is
+// used, one barrier per tile).  Per tile a wave forms S = q K^T and
+// dP = dout V^T (slots x keys, so the slot is the k index of the products
+// that follow), p and dS, then dV^T += dout^T P and dK^T += q^T dS.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_dkv(const float *q, const float *Kc, const float *Vc, const float *dout,
                                                   const float *mst, const float *lst, const float *Dst, Rows rm,
                                                   int Hq, int Hkv, int Tc, float scale, float *dK, float *dV) {
-  constexpr int KP = DH + 4;
-  __shared__ __attribute__((aligned(16))) float Ks[64 * KP], Vs[64 * KP], qs[4][DH], ds[4][DH], accK[64 * 64],
-      accV[64 * 64];
+  constexpr int NT = DH / 16, QP = DH + 4, NV = (ATQ * DH / 4 + 255) / 256;
+  __shared__ __attribute__((aligned(16))) float qs[2][ATQ][QP], ds[2][ATQ][QP];
+  __shared__ __attribute__((aligned(16))) float sst[2][4][ATQ];  // m, 1/l, Dn, position
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t0 = blockIdx.y * 64;
-  const int nk = min(64, Tc - t0), nslot = rm.M * G;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lj = lane >> 4;
+  const int t0 = blockIdx.y * 64, kb = t0 + 16 * wave, nslot = rm.M * G;
   const int64_t base = ((int64_t)b * Hkv + hk) * Tc * DH;
-  // first slot whose row reads any key of the chunk (positions grow with m)
+  // first row whose position is past the block's first key (positions grow with m)
   int m0 = 0;
   while (m0 < rm.M && rm.pos(b * rm.M + m0) <= t0) ++m0;
   if (m0 >= rm.M) return;  // (block-uniform)
-  for (int e = threadIdx.x; e < nk * (DH / 4); e += 256) {
-    const int r = e / (DH / 4), c = 4 * (e - r * (DH / 4));
-    *(f32x4 *)&Ks[r * KP + c] = *(const f32x4 *)&Kc[base + (int64_t)(t0 + r) * DH + c];
-    *(f32x4 *)&Vs[r * KP + c] = *(const f32x4 *)&Vc[base + (int64_t)(t0 + r) * DH + c];
-  }
-  for (int half = 0; half < (DH + 63) / 64; ++half) {
-    const int dim = half * 64 + lane;
-    float gk[64], gv[64];
+  const int s0 = m0 * G, ntile = (nslot - s0 + ATQ - 1) / ATQ;
+  f32x4 kf[NT], vf[NT], ak[NT], av[NT];
+  {
+    const int kr = min(kb + li, Tc - 1);
 #pragma unroll
-    for (int u = 0; u < 64; ++u) gk[u] = gv[u] = 0.f;
-    // every wave runs the same number of rounds (slot past the end: no-op),
-    // so all of them meet every barrier
-    const int rounds = (nslot - m0 * G + 3) / 4;
-    for (int rd = 0; rd < rounds; ++rd) {
-      const int slot = m0 * G + 4 * rd + wave;
-      const bool act = slot < nslot;
-      const int m = act ? slot / G : 0, n = b * rm.M + m, h = hk * G + (act ? slot - m * G : 0);
-      const int i = act ? rm.pos(n) : 0;
-      const int64_t qo = ((int64_t)n * Hq + h) * DH;
-      for (int c = lane; c < DH; c += 64) {
-        qs[wave][c] = act ? q[qo + c] : 0.f;
-        ds[wave][c] = act ? dout[qo + c] : 0.f;
-      }
-      __syncthreads();  // (also orders the staging above before the first use)
-      float p = 0.f, dS = 0.f;
-      if (lane < nk && t0 + lane < i) {
-        float sc = 0.f, dP = 0.f;
-#pragma unroll
-        for (int c = 0; c < DH; c += 4) {
-          const f32x4 kv = *(const f32x4 *)&Ks[lane * KP + c], vv = *(const f32x4 *)&Vs[lane * KP + c];
-          const f32x4 qv = *(const f32x4 *)&qs[wave][c], dv = *(const f32x4 *)&ds[wave][c];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc = fmaf(qv[e], kv[e], sc);
-            dP = fmaf(dv[e], vv[e], dP);
-          }
-        }
-        const int64_t so = (int64_t)n * Hq + h;
-        p = expf(sc * scale - mst[so]) / lst[so];
-        dS = p * (dP - Dst[so]);
-      }
-      const float qd = dim < DH ? qs[wave][dim] * scale : 0.f, od = dim < DH ? ds[wave][dim] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 64; ++u) {
-        gk[u] += __shfl(dS, u) * qd;
-        gv[u] += __shfl(p, u) * od;
-      }
-      __syncthreads();  // (qs / ds of this slot are read)
+    for (int t = 0; t < NT; ++t) {
+      kf[t] = *(const f32x4 *)&Kc[base + (int64_t)kr * DH + 16 * t + 4 * lj];
+      vf[t] = *(const f32x4 *)&Vc[base + (int64_t)kr * DH + 16 * t + 4 * lj];
+      ak[t] = av[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int w = 0; w < 4; ++w) {
-      if (wave == w)
-#pragma unroll
-        for (int u = 0; u < 64; ++u) {
-          accK[u * 64 + lane] = w == 0 ? gk[u] : accK[u * 64 + lane] + gk[u];
-          accV[u * 64 + lane] = w == 0 ? gv[u] : accV[u * 64 + lane] + gv[u];
-        }
-      __syncthreads();
-    }
-    if (dim < DH)
-      for (int u = wave; u < nk; u += 4) {
-        // (each wave adds its share of the keys)
-        dK[base + (int64_t)(t0 + u) * DH + dim] += accK[u * 64 + lane];
-        dV[base + (int64_t)(t0 + u) * DH + dim] += accV[u * 64 + lane];
-      }
-    __syncthreads();
   }
+  // staging of tile i: thread x holds float4 runs x, x + 256, ... of q and
+  // dout ([16 slots][DH / 4 runs]); threads 0..15 the statistics of slot x
+  f32x4 rq[NV], rd[NV];
+  float rst[4];
+  auto fetch = [&](int i) {
+    const int st = s0 + i * ATQ;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int x = threadIdx.x + 256 * v, sl = x / (DH / 4), c = 4 * (x - sl * (DH / 4));
+      rq[v] = rd[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (sl < ATQ) {
+        const Slot r = slot_of(st + sl, nslot, rm, b, hk, G, Hq);
+        if (r.act) {
+          rq[v] = *(const f32x4 *)&q[r.so * DH + c];
+          rd[v] = *(const f32x4 *)&dout[r.so * DH + c];
+        }
+      }
+    }
+    if (threadIdx.x < ATQ) {
+      const Slot r = slot_of(st + threadIdx.x, nslot, rm, b, hk, G, Hq);
+      const float l = r.act ? lst[r.so] : 0.f;
+      rst[0] = r.act ? mst[r.so] : 0.f;
+      rst[1] = l > 0.f ? 1.f / l : 0.f;
+      rst[2] = r.act ? Dst[r.so] : 0.f;
+      rst[3] = (float)r.ipos;  // (exact: positions < 2^24)
+    }
+  };
+  fetch(0);
+  for (int i = 0; i < ntile; ++i) {
+    const int buf = i & 1;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int x = threadIdx.x + 256 * v, sl = x / (DH / 4), c = 4 * (x - sl * (DH / 4));
+      if (sl < ATQ) {
+        *(f32x4 *)&qs[buf][sl][c] = rq[v];
+        *(f32x4 *)&ds[buf][sl][c] = rd[v];
+      }
+    }
+    if (threadIdx.x < ATQ)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sst[buf][j][threadIdx.x] = rst[j];
+    __syncthreads();  // (tile i staged; every wave is past tile i - 1, so buffer !buf is free)
+    if (i + 1 < ntile) fetch(i + 1);
+    // the tile's last position (positions grow with the slot) past the wave's first key?
+    const int st = s0 + i * ATQ;
+    if (rm.pos(b * rm.M + min(st + ATQ - 1, nslot - 1) / G) <= kb) continue;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 qa = *(const f32x4 *)&qs[buf][li][16 * t + 4 * lj];
+      const f32x4 da = *(const f32x4 *)&ds[buf][li][16 * t + 4 * lj];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = mf4(qa[e], kf[t][e], s);    // S = q K^T
+        dP = mf4(da[e], vf[t][e], dP);  // dP = dout V^T
+      }
+    }
+    const f32x4 sm = *(const f32x4 *)&sst[buf][0][4 * lj], sil = *(const f32x4 *)&sst[buf][1][4 * lj];
+    const f32x4 sD = *(const f32x4 *)&sst[buf][2][4 * lj], sp = *(const f32x4 *)&sst[buf][3][4 * lj];
+    float p[4], dS[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = (float)(kb + li) < sp[e] ? expf(s[e] * scale - sm[e]) * sil[e] : 0.f;
+      dS[e] = p[e] * (dP[e] - sD[e]);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        av[j] = mf4(ds[buf][4 * lj + e][16 * j + li], p[e], av[j]);   // dV^T += dout^T P
+        ak[j] = mf4(qs[buf][4 * lj + e][16 * j + li], dS[e], ak[j]);  // dK^T += q^T dS
+      }
+  }
+  // accumulator element e of lane l: dim 16 j + 4 lj + e of key kb + li
+  if (kb + li < Tc)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t a = base + (int64_t)(kb + li) * DH + 16 * j + 4 * lj;
+      f32x4 xk = *(f32x4 *)&dK[a], xv = *(f32x4 *)&dV[a];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xk[e] += ak[j][e] * scale;
+        xv[e] += av[j][e];
+      }
+      *(f32x4 *)&dK[a] = xk;
+      *(f32x4 *)&dV[a] = xv;
+    }
 }
 
 // ------------------------------------------------------------------ pool
@@ -986,7 +1026,7 @@ struct Trainer {
   float *chanK(size_t cacheoff, int ch) const { return P(cacheoff) + (size_t)ch * B * KD * T; }
   hipError_t attn_fwd(const float *q, const float *K, const float *Vv, Rows rm, int N, float scale, float *out,
                       float *mst, float *lst) {
-    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 4 * AQ - 1) / (4 * AQ));
+    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + ATQ - 1) / ATQ);
     if (c.d == 32)
       hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
     else if (c.d == 64)
@@ -1011,7 +1051,7 @@ struct Trainer {
   }
   hipError_t attn_dq(const float *q, const float *K, const float *Vv, const float *dout, const float *mst,
                      const float *lst, Rows rm, int N, float scale, float *dq, float *Dst) {
-    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + 4 * AQ - 1) / (4 * AQ));
+    dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + ATQ - 1) / ATQ);
     if (c.d == 32)
       hipLaunchKernelGGL(k_attn_dq<32>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
                          Dst);
