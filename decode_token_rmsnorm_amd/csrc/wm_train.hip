@@ -111,14 +111,19 @@ __global__ void k_swiglu_bwd(const float *G, const float *U, const float *dact, 
 // C[z] = alpha * op(A[z]) op(B[z]) + beta * C[z], op(A) [M, K], op(B) [K, N],
 // row-major.  TA: A is stored [K, M] (leading dim lda), else [M, K].  TB: B
 // is stored [N, K], else [K, N].  beta = 0 never reads C.  64 x 64 tiles,
-// k in steps of 16 staged in LDS as [k][m] and [k][n] (either transpose is
-// taken at the store); 4 waves of 32 x 32, each on 2 x 2 float32 16x16x4
-// MFMAs (lane: A row lane % 16 and B column lane % 16 at k lane / 16; the
-// row pitch 80 puts the four k rows a read touches on disjoint banks).  With
-// splits > 1, blockIdx.z = batch * splits + split: the block sums k in
-// [split * kchunk, (split + 1) * kchunk) and C[blockIdx.z] is a partial
-// (k_split_sum adds them).
-constexpr int GT = 64, GK = 16;
+// k in steps of 32 through two LDS buffers: the next step's operands are
+// loaded into registers while the current buffer feeds the MFMAs, then
+// stored into the other buffer (one barrier per step).  An operand stored
+// with k contiguous keeps that layout in LDS ([row][k], pitch 36); one
+// stored with k as the outer index keeps [k][row] (pitch 80); both pitches
+// put a read's 64 lanes on distinct banks.  4 waves of 32 x 32, each on
+// 2 x 2 float32 16x16x4 MFMAs (lane: A row lane % 16 and B column lane % 16
+// at k lane / 16; in a 16-k chunk c, step e takes k = 16c + 4 (lane / 16)
+// + e, so that a [row][k] operand gives a lane its four steps in one
+// 16-byte read).  With splits > 1, blockIdx.z = batch * splits + split: the
+// block sums k in [split * kchunk, (split + 1) * kchunk) and C[blockIdx.z]
+// is a partial (k_split_sum adds them).
+constexpr int GT = 64, GK = 32;
 
 // 4 consecutive floats p[0..3], index idx of p[0] along a dimension of
 // extent lim: past-the-end elements read as 0; one 16-byte load when vec
@@ -131,62 +136,98 @@ __device__ __forceinline__ f32x4 ld4(const float *p, int idx, int lim, bool vec)
   return r;
 }
 
+// One operand's k-step: 2 runs of 4 floats per thread, in registers, and
+// their place in LDS.  KO: k is the outer index in memory ([K, rows]).
+template <bool KO>
+struct GOp {
+  static constexpr int P = KO ? GT + 16 : GK + 4, SZ = KO ? GK * P : GT * P;
+  f32x4 r[2];
+  __device__ __forceinline__ void load(const float *X, int64_t ld, int r0, int R, int k0, int ke, bool vec, int tid) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      if (KO) {
+        const int kk = (tid >> 4) + 16 * v, rr = 4 * (tid & 15);
+        r[v] = k0 + kk < ke ? ld4(X + (int64_t)(k0 + kk) * ld + r0 + rr, r0 + rr, R, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        const int rr = (tid >> 3) + 32 * v, kk = 4 * (tid & 7);
+        r[v] = r0 + rr < R ? ld4(X + (int64_t)(r0 + rr) * ld + k0 + kk, k0 + kk, ke, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float *S, int tid) const {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      if (KO)
+        *(f32x4 *)&S[((tid >> 4) + 16 * v) * P + 4 * (tid & 15)] = r[v];
+      else
+        *(f32x4 *)&S[((tid >> 3) + 32 * v) * P + 4 * (tid & 7)] = r[v];
+    }
+  }
+  // operand values of row `row` (of the tile) for the 4 steps of chunk c
+  __device__ __forceinline__ static f32x4 frag(const float *S, int row, int c, int lj) {
+    if (KO) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = S[(16 * c + 4 * lj + e) * P + row];
+      return x;
+    }
+    return *(const f32x4 *)&S[row * P + 16 * c + 4 * lj];
+  }
+};
+
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64_t sA, const float *B, int64_t ldb,
                                               int64_t sB, float *C, int64_t ldc, int64_t sC, int M, int N, int K,
                                               float alpha, float beta, int splits, int kchunk, int vecA, int vecB) {
-  constexpr int LP = GT + 16;
-  __shared__ __attribute__((aligned(16))) float As[GK][LP];
-  __shared__ __attribute__((aligned(16))) float Bs[GK][LP];
+  typedef GOp<TA> OA;
+  typedef GOp<!TB> OB;
+  __shared__ __attribute__((aligned(16))) float As[2][OA::SZ];
+  __shared__ __attribute__((aligned(16))) float Bs[2][OB::SZ];
   const int batch = blockIdx.z / splits, split = blockIdx.z - batch * splits;
   A += batch * sA;
   B += batch * sB;
   C += blockIdx.z * sC;
   const int kb = split * kchunk, ke = min(K, kb + kchunk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lj = lane >> 4, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = kb; k0 < ke; k0 += GK) {
-    // one 4-float run per thread of each operand: along k for A [M, K] and
-    // B [N, K] (thread -> row tid / 4, k 4 * (tid % 4)), along m or n for
-    // A [K, M] and B [K, N] (thread -> k row tid / 16, 4 * (tid % 16))
-    if (TA) {
-      const int kk = tid >> 4, mm = 4 * (tid & 15), gk = k0 + kk;
-      const f32x4 v = gk < ke ? ld4(A + (int64_t)gk * lda + m0 + mm, m0 + mm, M, vecA) : f32x4{0.f, 0.f, 0.f, 0.f};
-      *(f32x4 *)&As[kk][mm] = v;
-    } else {
-      const int mm = tid >> 2, kk = 4 * (tid & 3), gm = m0 + mm;
-      const f32x4 v = gm < M ? ld4(A + (int64_t)gm * lda + k0 + kk, k0 + kk, ke, vecA) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) As[kk + e][mm] = v[e];
+  OA oa;
+  OB ob;
+  oa.load(A, lda, m0, M, kb, ke, vecA, tid);
+  ob.load(B, ldb, n0, N, kb, ke, vecB, tid);
+  oa.store(As[0], tid);
+  ob.store(Bs[0], tid);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = kb; k0 < ke; k0 += GK, buf ^= 1) {
+    const bool more = k0 + GK < ke;
+    if (more) {
+      oa.load(A, lda, m0, M, k0 + GK, ke, vecA, tid);
+      ob.load(B, ldb, n0, N, k0 + GK, ke, vecB, tid);
     }
-    if (TB) {
-      const int nn = tid >> 2, kk = 4 * (tid & 3), gn = n0 + nn;
-      const f32x4 v = gn < N ? ld4(B + (int64_t)gn * ldb + k0 + kk, k0 + kk, ke, vecB) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Bs[kk + e][nn] = v[e];
-    } else {
-      const int kk = tid >> 4, nn = 4 * (tid & 15), gk = k0 + kk;
-      const f32x4 v = gk < ke ? ld4(B + (int64_t)gk * ldb + n0 + nn, n0 + nn, N, vecB) : f32x4{0.f, 0.f, 0.f, 0.f};
-      *(f32x4 *)&Bs[kk][nn] = v;
+    for (int c = 0; c < GK / 16; ++c) {
+      f32x4 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = OA::frag(As[buf], wm * 32 + i * 16 + li, c, lj);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = OB::frag(Bs[buf], wn * 32 + j * 16 + li, c, lj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < GK; ks += 4) {
-      const int kr = ks + (lane >> 4);
-      float a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = As[kr][wm * 32 + i * 16 + (lane & 15)];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = Bs[kr][wn * 32 + j * 16 + (lane & 15)];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    if (more) {
+      oa.store(As[buf ^ 1], tid);
+      ob.store(Bs[buf ^ 1], tid);
     }
     __syncthreads();
   }
@@ -195,11 +236,11 @@ __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int gn = n0 + wn * 32 + j * 16 + (lane & 15);
+      const int gn = n0 + wn * 32 + j * 16 + li;
       if (gn >= N) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int gm = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + e;
+        const int gm = m0 + wm * 32 + i * 16 + 4 * lj + e;
         if (gm >= M) continue;
         float *c = C + (int64_t)gm * ldc + gn;
         const float v = acc[i][j][e];
