@@ -396,13 +396,15 @@ __global__ void k_embed_bwd(const int32_t *tokens, int T, Rows rm, const float *
 // the row of the accumulator element e that feeds them, so scores and
 // probabilities go from accumulators to operands without moving.
 //
-// Forward and query side: a block of 4 waves takes 16 slots; wave w takes
-// the 16-key tiles w, w + 4, ... below the block's last position, loading
-// its K and V rows from memory into registers, and keeps its own running
-// max, sum and output; the block then merges the 4 waves' partial results
-// in wave order.  Scores are kept transposed (keys x slots: S^T = K q^T),
-// so that each lane holds one slot, its statistics included.
+// Forward and query side: a block of 8 waves takes 16 slots; wave w takes
+// the 16-key tiles w, w + 8, ... below the block's last position, loading
+// its K and V rows from memory into registers one tile ahead of use, and
+// keeps its own running max, sum and output; the block then merges the 8
+// waves' partial results in wave order.  Scores are kept transposed (keys
+// x slots: S^T = K q^T), so that each lane holds one slot, its statistics
+// included.
 constexpr int ATQ = 16;  // query slots per block (forward and query side)
+constexpr int NWF = 8;   // waves per block (forward and query side)
 
 struct Slot {
   bool act;
@@ -426,10 +428,10 @@ __device__ __forceinline__ f32x4 mf4(float a, float b, f32x4 c) {
 // (a slot with no key: m = -inf, l = 0, output 0).  Blocks run longest
 // (last slots) first.
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, const float *Vc, Rows rm, int Hq,
+__global__ __launch_bounds__(64 * NWF) void k_attn(const float *q, const float *Kc, const float *Vc, Rows rm, int Hq,
                                               int Hkv, int Tc, float scale, float *out, float *mst, float *lst) {
   constexpr int NT = DH / 16;
-  __shared__ float cm[4][ATQ], cl[4][ATQ], co[4][DH][ATQ + 1];
+  __shared__ float cm[NWF][ATQ], cl[NWF][ATQ], co[NWF][DH][ATQ + 1];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lj = lane >> 4;
   const int nslot = rm.M * G, sb = (gridDim.y - 1 - blockIdx.y) * ATQ;
@@ -443,19 +445,30 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, c
     o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float mx = -INFINITY, ls = 0.f;
-  for (int k0 = 16 * wave; k0 < imax; k0 += 64) {
-    // (rows past Tc - 1 are clamped: their keys lie past imax, masked)
-    f32x4 kf[NT];
-    float vf[NT][4];
+  f32x4 kn[NT];
+  float vn[NT][4];
+  auto fetch = [&](int k0) {
     const int kr = min(k0 + li, Tc - 1);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) kf[t] = *(const f32x4 *)&K[(int64_t)kr * DH + 16 * t + 4 * lj];
+    for (int t = 0; t < NT; ++t) kn[t] = *(const f32x4 *)&K[(int64_t)kr * DH + 16 * t + 4 * lj];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int vr = min(k0 + 4 * lj + e, Tc - 1);
 #pragma unroll
-      for (int i = 0; i < NT; ++i) vf[i][e] = V[(int64_t)vr * DH + 16 * i + li];
+      for (int i = 0; i < NT; ++i) vn[i][e] = V[(int64_t)vr * DH + 16 * i + li];
     }
+  };
+  if (16 * wave < imax) fetch(16 * wave);
+  for (int k0 = 16 * wave; k0 < imax; k0 += 16 * NWF) {
+    f32x4 kf[NT];
+    float vf[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) kf[t] = kn[t];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vf[i][e] = vn[i][e];
+    if (k0 + 16 * NWF < imax) fetch(k0 + 16 * NWF);
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -493,16 +506,16 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, c
 #pragma unroll
     for (int e = 0; e < 4; ++e) co[wave][16 * i + 4 * lj + e][li] = o[i][e];
   __syncthreads();
-  for (int x = threadIdx.x; x < ATQ * DH; x += 256) {
+  for (int x = threadIdx.x; x < ATQ * DH; x += 64 * NWF) {
     const int sl = x / DH, d = x - sl * DH;
     const Slot r = slot_of(sb + sl, nslot, rm, b, hk, G, Hq);
     if (!r.act) continue;
     float M = -INFINITY, L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w][sl]);
+    for (int w = 0; w < NWF; ++w) M = fmaxf(M, cm[w][sl]);
     if (M != -INFINITY)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NWF; ++w) {
         const float f = cm[w][sl] == -INFINITY ? 0.f : expf(cm[w][sl] - M);
         L += f * cl[w][sl];
         O += f * co[w][d][sl];
@@ -524,11 +537,11 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const float *Kc, c
 // wave order, then dS and dq^T = K^T dS^T), and the waves' dq are added in
 // wave order.
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc, const float *Vc, const float *dout,
-                                                 const float *mst, const float *lst, Rows rm, int Hq, int Hkv,
-                                                 int Tc, float scale, float *dq, float *Dst) {
+__global__ __launch_bounds__(64 * NWF) void k_attn_dq(const float *q, const float *Kc, const float *Vc,
+                                                      const float *dout, const float *mst, const float *lst, Rows rm,
+                                                      int Hq, int Hkv, int Tc, float scale, float *dq, float *Dst) {
   constexpr int NT = DH / 16;
-  __shared__ float cD[4][ATQ], cg[4][DH][ATQ + 1];
+  __shared__ float cD[NWF][ATQ], cg[NWF][DH][ATQ + 1];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lj = lane >> 4;
   const int nslot = rm.M * G, sb = (gridDim.y - 1 - blockIdx.y) * ATQ;
@@ -542,50 +555,82 @@ __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc
     df[t] = me.act ? *(const f32x4 *)&dout[me.so * DH + 16 * t + 4 * lj] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float mrow = me.act ? mst[me.so] : 0.f, lr = me.act ? lst[me.so] : 0.f, invl = lr > 0.f ? 1.f / lr : 0.f;
-  // p and dP of keys k0 + 4 lj + e for the lane's slot (0 past its position)
-  auto tile = [&](int k0, float (&p)[4], f32x4 &dP) {
+  // a tile's K and V rows k0 + li as A operands (16-byte runs), loaded one
+  // tile ahead
+  f32x4 kn[NT], vn[NT];
+  auto fetch = [&](int k0) {
     const int kr = min(k0 + li, Tc - 1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      kn[t] = *(const f32x4 *)&K[(int64_t)kr * DH + 16 * t + 4 * lj];
+      vn[t] = *(const f32x4 *)&V[(int64_t)kr * DH + 16 * t + 4 * lj];
+    }
+  };
+  // p and dP of keys k0 + 4 lj + e for the lane's slot (0 past its position)
+  auto tile = [&](int k0, const f32x4 (&kf)[NT], const f32x4 (&vf)[NT], float (&p)[4], f32x4 &dP) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     dP = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const f32x4 kf = *(const f32x4 *)&K[(int64_t)kr * DH + 16 * t + 4 * lj];
-      const f32x4 vf = *(const f32x4 *)&V[(int64_t)kr * DH + 16 * t + 4 * lj];
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s = mf4(kf[e], qf[t][e], s);    // S^T = K q^T
-        dP = mf4(vf[e], df[t][e], dP);  // dP^T = V dout^T
+        s = mf4(kf[t][e], qf[t][e], s);    // S^T = K q^T
+        dP = mf4(vf[t][e], df[t][e], dP);  // dP^T = V dout^T
       }
-    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[e] = k0 + 4 * lj + e < me.ipos ? expf(s[e] * scale - mrow) * invl : 0.f;
   };
   float Dp = 0.f;
-  for (int k0 = 16 * wave; k0 < imax; k0 += 64) {
+  if (16 * wave < imax) fetch(16 * wave);
+  for (int k0 = 16 * wave; k0 < imax; k0 += 16 * NWF) {
+    f32x4 kf[NT], vf[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      kf[t] = kn[t];
+      vf[t] = vn[t];
+    }
+    if (k0 + 16 * NWF < imax) fetch(k0 + 16 * NWF);
     float p[4];
     f32x4 dP;
-    tile(k0, p, dP);
+    tile(k0, kf, vf, p, dP);
 #pragma unroll
     for (int e = 0; e < 4; ++e) Dp = fmaf(p[e], dP[e], Dp);
   }
   Dp += __shfl_xor(Dp, 16);
   Dp += __shfl_xor(Dp, 32);
   if (lj == 0) cD[wave][li] = Dp;
+  if (16 * wave < imax) fetch(16 * wave);
   __syncthreads();
-  const float Dn = ((cD[0][li] + cD[1][li]) + cD[2][li]) + cD[3][li];
+  float Dn = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWF; ++w) Dn += cD[w][li];
   f32x4 g[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 16 * wave; k0 < imax; k0 += 64) {
+  for (int k0 = 16 * wave; k0 < imax; k0 += 16 * NWF) {
+    // K rows k0 + 4 lj + e as the A operand of dq^T (used after the S and dP products)
+    float kt[NT][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = min(k0 + 4 * lj + e, Tc - 1);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) kt[i][e] = K[(int64_t)r * DH + 16 * i + li];
+    }
+    f32x4 kf[NT], vf[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      kf[t] = kn[t];
+      vf[t] = vn[t];
+    }
+    if (k0 + 16 * NWF < imax) fetch(k0 + 16 * NWF);
     float p[4];
     f32x4 dP;
-    tile(k0, p, dP);
+    tile(k0, kf, vf, p, dP);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float dS = p[e] * (dP[e] - Dn);
-      const int kr = min(k0 + 4 * lj + e, Tc - 1);
 #pragma unroll
-      for (int i = 0; i < NT; ++i) g[i] = mf4(K[(int64_t)kr * DH + 16 * i + li], dS, g[i]);  // dq^T += K^T dS^T
+      for (int i = 0; i < NT; ++i) g[i] = mf4(kt[i][e], dS, g[i]);  // dq^T += K^T dS^T
     }
   }
 #pragma unroll
@@ -593,12 +638,18 @@ __global__ __launch_bounds__(256) void k_attn_dq(const float *q, const float *Kc
 #pragma unroll
     for (int e = 0; e < 4; ++e) cg[wave][16 * i + 4 * lj + e][li] = g[i][e];
   __syncthreads();
-  for (int x = threadIdx.x; x < ATQ * DH; x += 256) {
+  for (int x = threadIdx.x; x < ATQ * DH; x += 64 * NWF) {
     const int sl = x / DH, d = x - sl * DH;
     const Slot r = slot_of(sb + sl, nslot, rm, b, hk, G, Hq);
     if (!r.act) continue;
-    dq[r.so * DH + d] = (((cg[0][d][sl] + cg[1][d][sl]) + cg[2][d][sl]) + cg[3][d][sl]) * scale;
-    if (d == 0) Dst[r.so] = ((cD[0][sl] + cD[1][sl]) + cD[2][sl]) + cD[3][sl];
+    float gs = 0.f, Ds = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWF; ++w) {
+      gs += cg[w][d][sl];
+      Ds += cD[w][sl];
+    }
+    dq[r.so * DH + d] = gs * scale;
+    if (d == 0) Dst[r.so] = Ds;
   }
 }
 
@@ -1069,11 +1120,11 @@ struct Trainer {
                       float *mst, float *lst) {
     dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + ATQ - 1) / ATQ);
     if (c.d == 32)
-      hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
+      hipLaunchKernelGGL(k_attn<32>, grid, dim3(64 * NWF), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
     else if (c.d == 64)
-      hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
+      hipLaunchKernelGGL(k_attn<64>, grid, dim3(64 * NWF), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
     else
-      hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
+      hipLaunchKernelGGL(k_attn<128>, grid, dim3(64 * NWF), 0, s, q, K, Vv, rm, c.Hq, c.Hkv, T, scale, out, mst, lst);
     return hipGetLastError();
   }
   hipError_t attn_dkv(const float *q, const float *K, const float *Vv, const float *dout, const float *mst,
@@ -1094,13 +1145,13 @@ struct Trainer {
                      const float *lst, Rows rm, int N, float scale, float *dq, float *Dst) {
     dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + ATQ - 1) / ATQ);
     if (c.d == 32)
-      hipLaunchKernelGGL(k_attn_dq<32>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
+      hipLaunchKernelGGL(k_attn_dq<32>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
                          Dst);
     else if (c.d == 64)
-      hipLaunchKernelGGL(k_attn_dq<64>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
+      hipLaunchKernelGGL(k_attn_dq<64>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
                          Dst);
     else
-      hipLaunchKernelGGL(k_attn_dq<128>, grid, dim3(256), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale,
+      hipLaunchKernelGGL(k_attn_dq<128>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale,
                          dq, Dst);
     return hipGetLastError();
   }
