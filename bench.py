@@ -20,7 +20,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-FP32_PEAK_TFLOPS = 157.3   # MI355X float32 vector
+FP32_PEAK_TFLOPS = 157.3   # MI355X float32, dense MFMA (the vector ALU has the same peak)
 
 
 CSRC = "decode_token_rmsnorm_amd/csrc/"
@@ -323,7 +323,7 @@ def bench_train(steps=1, warmup=1):
             "cpu_baseline": cpu,
             "value": w.B * w.T / dt, "unit": "tokens/s (training steps)", "s_per_step": dt, "steps": steps,
             "loss": float(loss.item()), "peak_memory_gib": peak_gib(),
-            "roofline": {"kernel": "whole training step", "bound": "alu", "achieved": ach, "peak": FP32_PEAK_TFLOPS,
+            "roofline": {"kernel": "whole training step", "bound": "mfma", "achieved": ach, "peak": FP32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": ach / FP32_PEAK_TFLOPS, "traffic": None,
                          "algorithmic_per_step": f"{flop:.4e} FLOP = 7 forward passes of {w.B}x{w.T} tokens"}}
 
