@@ -24,6 +24,11 @@ namespace wm {
 // product, 6x wider, stays on the 128 x 128 kernel above kFewRows rows (15.5
 // against 34 us there).
 constexpr int kFewStackRows = 1024;
+// bf16 channel attention with at most this many query rows per (sequence, KV
+// head) pair runs on attn_few in blocks of 32 rows (no key split, so no
+// combine launch, where attn2_kernel's 128-row blocks would need splits to
+// fill the GPU).
+constexpr int kFewAttnRows = 512;
 
 // ------------------------------------------------------------ launch timing
 struct ProfRec {
@@ -185,12 +190,14 @@ template <typename T> struct Run {
     const int rows_pair = ts.M * G;
     const bool large = rows_pair >= 128;
     constexpr bool bfd = std::is_same<T, bf16>::value && DH >= 64;
-    // bf16 with many rows: 4 waves of 32 rows on 32x32 MFMAs (attn2_kernel);
-    // bf16 with at most 32 rows: a block of waves per (pair, split) (attn_few)
-    const bool v2 = large && bfd;
-    const bool few = bfd && rows_pair <= 32;
+    // bf16 with up to kFewAttnRows rows per pair: a block of waves per (pair,
+    // split, 32 query rows), the waves splitting the keys and merging in LDS
+    // (attn_few); with more: 4 waves of 32 rows on 32x32 MFMAs sharing LDS
+    // tiles (attn2_kernel)
+    const bool few = bfd && rows_pair <= kFewAttnRows;
+    const bool v2 = large && bfd && !few;
     constexpr int few_nw = DH == 64 ? 8 : 4;
-    const int rb = large ? 128 : few ? 32 : 16, nw = v2 ? 4 : large ? 8 : few ? few_nw : 1;
+    const int rb = few ? 32 : large ? 128 : 16, nw = v2 ? 4 : few ? few_nw : large ? 8 : 1;
     const int nrb = (rows_pair + rb - 1) / rb;
     const int blocks = nrb * ts.B * c.Hkv;
     int64_t kmax = (int64_t)ts.s0 + (int64_t)(ts.M - 1) * ts.s_step;
@@ -228,7 +235,7 @@ template <typename T> struct Run {
     ProfScope prof(WM_K_ATTN, s);
     if constexpr (bfd) {
       if (v2) hipLaunchKernelGGL((attn2_kernel<DH, 1>), dim3(ts.B * c.Hkv, nrb, ns), dim3(256), 0, s, a);
-      if (few) hipLaunchKernelGGL((attn_few<DH, few_nw>), dim3(ns, ts.B * c.Hkv), dim3(64 * few_nw), 0, s, a);
+      if (few) hipLaunchKernelGGL((attn_few<DH, few_nw>), dim3(ns, ts.B * c.Hkv, nrb), dim3(64 * few_nw), 0, s, a);
     }
     if (v2 || few)
       ;

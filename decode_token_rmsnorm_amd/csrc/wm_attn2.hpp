@@ -325,11 +325,12 @@ __global__ __launch_bounds__(256, 3 - QB) void attn2_kernel(AttnArgs a) {
   }
 }
 
-// Few query rows per (sequence, KV head) pair (decode steps): attn_few.
-// A block of NW waves takes one (pair, key split); wave w walks the split's
-// 32-key tiles w, w+NW, ... with up to 32 query rows as the columns of
-// S^T = K Q^T (32x32x16 MFMA; columns past the pair's rows are padding that is
-// computed and never stored).  The K fragments of a tile are loaded straight
+// Few query rows per (sequence, KV head) pair (decode steps, small group
+// steps): attn_few.  A block of NW waves takes one (pair, key split, block of
+// 32 query rows; blockIdx.z = 0 is the pair's last row block, the longest);
+// wave w walks the split's 32-key tiles w, w+NW, ... with the block's query
+// rows as the columns of S^T = K Q^T (32x32x16 MFMA; columns past the pair's
+// rows are padding that is computed and never stored).  The K fragments of a tile are loaded straight
 // from global memory in the MFMA operand layout (lane: key lane%32, head dims
 // 8*(lane/32) of each 16-dim step); the V tile goes through a wave-private LDS
 // buffer for the transpose reads of O^T += V^T P^T, as in attn2_kernel.  The
@@ -351,15 +352,16 @@ __global__ __launch_bounds__(64 * NW) void attn_few(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
   bf16 *Vs = (bf16 *)smem + wave * KT * VP;
   const int split = blockIdx.x, pair = blockIdx.y, b = pair / a.Hkv, hk = pair - b * a.Hkv;
-  const int nrows = a.M * a.G;  // <= 32
+  const int rb0 = (gridDim.z - 1 - blockIdx.z) * 32;  // first row of the block
+  const int nrows = min(32, a.M * a.G - rb0);         // rows of the block
   const int s0 = attn_s0(a);
-  const int kmax = min(s0 + ((nrows - 1) / a.G) * a.step, a.T_max);
+  const int kmax = min(s0 + ((rb0 + nrows - 1) / a.G) * a.step, a.T_max);
   const int ntile = (kmax + KT - 1) / KT;
   const int tps = (ntile + a.nsplit - 1) / a.nsplit;
   const int t0 = split * tps, t1 = min(ntile, t0 + tps);
 
   const bool rvalid = ql < nrows;
-  const int rho = rvalid ? ql : nrows - 1;
+  const int rho = rb0 + (rvalid ? ql : nrows - 1);
   const int m = rho / a.G, g = rho - m * a.G;
   const int rpos = s0 + m * a.step;
   const int rrow = b * a.M + m, rhead = hk * a.G + g;
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(64 * NW) void attn_few(AttnArgs a) {
       lsum += mw == -INFINITY ? 0.f : mls[w][1][q] * __builtin_amdgcn_exp2f(mw - mq);
       acc += *(const f32x4 *)(&Os[(w * 32 + q) * OP + d4]);
     }
-    const int mm = q / a.G, gg = q - mm * a.G;
+    const int mm = (rb0 + q) / a.G, gg = rb0 + q - mm * a.G;
     const int orow = b * a.M + mm, ohead = hk * a.G + gg;
     if (a.nsplit == 1) {
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
