@@ -300,19 +300,24 @@ def test_channel_attn_matches_oracle(name, B, M, s0, step, layer):
 
 
 @pytest.mark.parametrize("name,B,M,s0,step,layer", [
-    ("small_prefill", 2, 16, 3, 7, 1),     # 32 query rows per sequence and KV head: the few-row kernel
-    ("small_prefill", 2, 17, 3, 7, 1),     # 34: the general kernel
+    ("small_prefill", 2, 16, 3, 7, 1),     # 32 query rows per sequence and KV head: one few-row block
+    ("small_prefill", 2, 17, 3, 7, 1),     # 34: a second, ragged few-row block
     ("small_prefill", 2, 63, 0, 3, 4),     # 126
-    ("small_prefill", 2, 64, 0, 3, 4),     # 128: one block of the many-row kernel
-    ("small_prefill", 2, 65, 5, 3, 4),     # 130: and a ragged second block
+    ("small_prefill", 2, 64, 0, 3, 4),     # 128: 4 few-row blocks
+    ("small_prefill", 2, 65, 5, 3, 4),     # 130
+    ("small_prefill", 1, 256, 1, 7, 4),    # 512: the last row count on the few-row kernel
+    ("small_prefill", 1, 257, 1, 7, 4),    # 514: the many-row kernel, a ragged last block
     ("prefill_1p3b", 2, 4, 900, 11, 6),    # G = 7: 28 rows, few-row kernel at d = 128
     ("prefill_1p3b", 2, 5, 900, 11, 6),    # 35
     ("prefill_1p3b", 2, 18, 10, 13, 6),    # 126
-    ("prefill_1p3b", 2, 19, 10, 13, 6),    # 133: many-row kernel at d = 128
+    ("prefill_1p3b", 2, 19, 10, 13, 6),    # 133
+    ("prefill_1p3b", 1, 73, 3, 11, 6),     # 511: few-row kernel, 16 blocks at d = 128
+    ("prefill_1p3b", 1, 74, 3, 11, 6),     # 518: many-row kernel at d = 128
 ])
 def test_channel_attn_kernel_boundaries(name, B, M, s0, step, layer):
     """Query-row counts per (sequence, KV head) on both sides of the
-    attention kernel switches (<= 32, between, >= 128 rows)."""
+    attention kernel switch (few-row kernel in blocks of 32 rows up to 512
+    rows, many-row kernel above) and of the few-row kernel's block edges."""
     _check_channel_attn(name, B, M, s0, step, layer)
 
 
