@@ -21,6 +21,8 @@ ragged groups with several sequences and other pass splits; a head dim of
 F1536, k8) at a short length; T = 2, Jacobi (g = 1) and autoregressive
 (g = T) schedules.  The step is deterministic: two calls give the same bits.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -92,3 +94,74 @@ def test_train_step_is_deterministic():
     assert l1 == l2
     for n in g1:
         assert np.array_equal(g1[n], g2[n]), n
+
+
+def test_train_step_full_size_properties():
+    """At the benchmarked training workload (the small model's widths in
+    float32, V32768, B8 T2048, g16, 1 + 2 passes), where the float64 oracle
+    is out of reach, properties that hold at any size:
+
+    * every gradient is finite;
+    * the step's loss is the next-token cross-entropy of the third pass's
+      logits computed by the inference path (wm_cyclic_prefill_pass on the
+      same float32 model: other kernels, the same definition), within 1e-4
+      relative;
+    * along the gradient of the parameters that act after the cache (the LM
+      head and the final norm: the pass without gradient does not depend on
+      them, so their truncated gradient is the whole derivative of the
+      loss), the central difference L(W + d) - L(W - d) equals <g, d+ - d->
+      within 1%, where d+ and d- are the steps as stored in float32 (so that
+      weight rounding does not enter) and the loss moves by about 2e-2.
+
+    (The other parameters' truncated gradients leave out their effect
+    through the pass without gradient, so a difference of the loss does not
+    check them; with no truncation at this depth the gradient norm is about
+    1e5, so float32 rounding of the weights alone moves the loss by about
+    2e-4 and no step size separates the first-order term from that.  Their
+    parity rests on the oracle cases above.)"""
+    w = WORKLOADS["small_prefill"].replace(dtype="f32")
+    W = make_weights(w, seed=0)
+    model = wm.Model(w, W, "f32")
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    ws = wm.train_workspace(model, w.B, w.T, w.g, 2)
+    print(f"[train full] L{w.L} D{w.D} V{w.V} B{w.B} T{w.T} g{w.g}: 1 + 2 step", flush=True)
+    loss, grads = wm.train_step(model, tok, w.g, 1, 2, ws=ws)
+    torch.cuda.synchronize()
+    for n in grads:
+        assert torch.isfinite(grads[n]).all(), n
+    print("[train full] inference passes", flush=True)
+    cache = wm.new_cache(model, w.B)
+    pws = model.workspace(wm.prefill_rows(w.B, w.T, w.g))
+    for i in range(3):
+        lg = wm.cyclic_prefill_pass(model, tok, w.g, cache, logits_mode=2 if i == 2 else 0, ws=pws)
+    ce = 0.0
+    for b in range(w.B):  # (one sequence at a time in float64)
+        z = lg[b, :-1].double()
+        tgt = tok[b, 1:].long()
+        ce += float((torch.logsumexp(z, -1) - z.gather(-1, tgt[:, None])[:, 0]).sum())
+    ce /= w.B * (w.T - 1)
+    del lg, cache, pws
+    rel = abs(float(loss.item()) - ce) / ce
+    print(f"  step loss {float(loss.item()):.7f}, inference cross-entropy {ce:.7f}, rel {rel:.1e}", flush=True)
+    assert rel <= 1e-4
+
+    print("[train full] central difference along the LM head and final norm gradient", flush=True)
+    names = ["lm_head", "final_norm"]
+    g = {n: grads[n].clone() for n in names}
+    del grads
+    gn = math.sqrt(sum(float((g[n].double() ** 2).sum()) for n in names))
+    e = 1e-2 / gn
+    orig = {n: model.t[n].clone() for n in names}
+    scratch = {n: torch.empty_like(model.t[n]) for n in wm._lib.GRAD_FIELDS}
+    lo, pred = [], 0.0
+    for sign in (1.0, -1.0):
+        for n in names:
+            model.t[n].copy_(orig[n] + (sign * e / gn) * g[n])
+            pred += sign * float((g[n].double() * (model.t[n].double() - orig[n].double())).sum())
+        l1, _ = wm.train_step(model, tok, w.g, 1, 2, grads=scratch, ws=ws)
+        lo.append(float(l1.double().item()))
+    for n in names:
+        model.t[n].copy_(orig[n])
+    meas = lo[0] - lo[1]
+    print(f"  |g| {gn:.6e}: loss difference {meas:.6e}, first-order prediction {pred:.6e}", flush=True)
+    assert abs(meas - pred) <= 1e-2 * abs(pred)
