@@ -96,16 +96,37 @@ def test_train_step_is_deterministic():
         assert np.array_equal(g1[n], g2[n]), n
 
 
+def _inference_ce(model, w, tok, npass):
+    """Mean next-token cross-entropy of the logits of pass npass from the
+    zero cache, by the inference path (float64 on the device)."""
+    cache = wm.new_cache(model, w.B)
+    pws = model.workspace(wm.prefill_rows(w.B, w.T, w.g))
+    for i in range(npass):
+        lg = wm.cyclic_prefill_pass(model, tok, w.g, cache, logits_mode=2 if i == npass - 1 else 0, ws=pws)
+    ce = 0.0
+    for b in range(w.B):  # (one sequence at a time)
+        z = lg[b, :-1].double()
+        tgt = tok[b, 1:].long()
+        ce += float((torch.logsumexp(z, -1) - z.gather(-1, tgt[:, None])[:, 0]).sum())
+    return ce / (w.B * (w.T - 1))
+
+
 def test_train_step_full_size_properties():
     """At the benchmarked training workload (the small model's widths in
-    float32, V32768, B8 T2048, g16, 1 + 2 passes), where the float64 oracle
-    is out of reach, properties that hold at any size:
+    float32, V32768, B8 T2048, g16), where the float64 oracle is out of
+    reach, properties that hold at any size:
 
-    * every gradient is finite;
-    * the step's loss is the next-token cross-entropy of the third pass's
-      logits computed by the inference path (wm_cyclic_prefill_pass on the
-      same float32 model: other kernels, the same definition), within 1e-4
-      relative;
+    * every gradient of the 1 + 2 pass step is finite;
+    * the step's loss is the next-token cross-entropy of the logits the
+      inference path (wm_cyclic_prefill_pass on the same float32 model:
+      other kernels, the same definition) gives after as many passes: within
+      1e-4 relative for one pass; within 2e-3 for 1 + 2 passes, because the
+      passes feed rounding differences back through the cache and amplify
+      them: measured, a 1e-6 relative perturbation of every weight moves the
+      one-pass loss by 4e-6 relative and the two- and three-pass losses by
+      up to 2.5e-5 (3.4e-4 with the other summation order below), and
+      another summation order of the step's products (no split k) moves the
+      three-pass loss by 4.5e-4;
     * along the gradient of the parameters that act after the cache (the LM
       head and the final norm: the pass without gradient does not depend on
       them, so their truncated gradient is the whole derivative of the
@@ -124,26 +145,16 @@ def test_train_step_full_size_properties():
     model = wm.Model(w, W, "f32")
     tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
     ws = wm.train_workspace(model, w.B, w.T, w.g, 2)
-    print(f"[train full] L{w.L} D{w.D} V{w.V} B{w.B} T{w.T} g{w.g}: 1 + 2 step", flush=True)
-    loss, grads = wm.train_step(model, tok, w.g, 1, 2, ws=ws)
-    torch.cuda.synchronize()
+    for n0, n1, bound in ((0, 1, 1e-4), (1, 2, 2e-3)):
+        print(f"[train full] L{w.L} D{w.D} V{w.V} B{w.B} T{w.T} g{w.g}: {n0} + {n1} step", flush=True)
+        loss, grads = wm.train_step(model, tok, w.g, n0, n1, ws=ws)
+        torch.cuda.synchronize()
+        ce = _inference_ce(model, w, tok, n0 + n1)
+        rel = abs(float(loss.item()) - ce) / ce
+        print(f"  step loss {float(loss.item()):.7f}, inference cross-entropy {ce:.7f}, rel {rel:.1e}", flush=True)
+        assert rel <= bound
     for n in grads:
         assert torch.isfinite(grads[n]).all(), n
-    print("[train full] inference passes", flush=True)
-    cache = wm.new_cache(model, w.B)
-    pws = model.workspace(wm.prefill_rows(w.B, w.T, w.g))
-    for i in range(3):
-        lg = wm.cyclic_prefill_pass(model, tok, w.g, cache, logits_mode=2 if i == 2 else 0, ws=pws)
-    ce = 0.0
-    for b in range(w.B):  # (one sequence at a time in float64)
-        z = lg[b, :-1].double()
-        tgt = tok[b, 1:].long()
-        ce += float((torch.logsumexp(z, -1) - z.gather(-1, tgt[:, None])[:, 0]).sum())
-    ce /= w.B * (w.T - 1)
-    del lg, cache, pws
-    rel = abs(float(loss.item()) - ce) / ce
-    print(f"  step loss {float(loss.item()):.7f}, inference cross-entropy {ce:.7f}, rel {rel:.1e}", flush=True)
-    assert rel <= 1e-4
 
     print("[train full] central difference along the LM head and final norm gradient", flush=True)
     names = ["lm_head", "final_norm"]
