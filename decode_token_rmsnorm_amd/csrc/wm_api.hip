@@ -284,7 +284,9 @@ template <typename T> struct Run {
                            ro.az, ro.ab, ro.ar, w->src_norm, sgb, cg0, cgb, at<T>(lay.mb), at<float>(lay.rinvM), rows,
                            LL, kk, c.D, c.eps);
       };
-      if (kk <= 16)
+      if (kk <= 8 && LL <= 16)  // both branches' channels in one MFMA
+        go(pool_mix2<1, 16, true>, PM_RT4);
+      else if (kk <= 16)
         LL <= 16 ? go(pool_mix2<1, 16>, PM_RT4) : go(pool_mix2<1, 32>, PM_RT4);
       else
         LL <= 16 ? go(pool_mix2<2, 16>, PM_RT4 / 2) : go(pool_mix2<2, 32>, PM_RT4 / 2);

@@ -18,6 +18,14 @@
 // once per chunk for all RT rows.  The output m * rho (channel gain folded, its
 // 1/rms applied after the projection) is stored as bf16; the per-channel sums
 // of squares are reduced in a fixed order into rinvM.
+//
+// With k <= 8 and L <= 16 (PB) the two branches share one MFMA per row and
+// slice: A is block diagonal (lane row li = 8 beta + j is channel j of branch
+// beta; k chunks 0-1 = branch 0's 16 layers, 2-3 = branch 1's),
+// and the B fragment's chunks 2-3 carry the same states as 0-1 under branch
+// 1's source gains.  That removes the channel and layer padding of the
+// per-branch MFMAs (half of M and half of K) and half of the gain loads,
+// products and output writes.
 #pragma once
 
 #include "wm_common.hpp"
@@ -33,15 +41,16 @@ constexpr int PM_SP = 96;   // staged row pitch (elements): 64 columns + 64 byte
 // S [L, rows, D]; mb [2, k, rows, D]; rinvM [2, k, rows].
 // (gains: src_gain (beta, l, c) at beta*sgb + l*D + c, chan_gain (beta, j, c)
 // at beta*cgb + j*D + c)
-template <int KB, int LMAX>
+template <int KB, int LMAX, bool PB = false>
 __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *rinvS, const float *A, int Z,
                                                  int64_t zstride, int64_t bstride, int64_t rstride,
                                                  const float *src_gain, int64_t sgb, const float *chan_gain,
                                                  int64_t cgb, bf16 *mb, float *rinvM, int rows, int L, int k, int D,
                                                  float eps) {
+  static_assert(!PB || (KB == 1 && LMAX == 16), "branches share an MFMA only for k <= 8 and L <= 16");
   constexpr int PM_RT = PM_RT4 / KB;                   // token rows per block
   constexpr int NPT = (PM_RT * LMAX * 8 + 255) / 256;  // 16-byte pieces per thread and chunk (L <= LMAX)
-  __shared__ __attribute__((aligned(16))) bf16 Sl[PM_RT * 32 * PM_SP];
+  __shared__ __attribute__((aligned(16))) bf16 Sl[PM_RT * LMAX * PM_SP];
   __shared__ __attribute__((aligned(16))) u32x4 Wl[PM_RT][2][KB][64];
   __shared__ float red[4][PM_RT][2][KB][16];
   // output chunk [beta][row][channel][64 columns], 144-byte rows: the four
@@ -53,16 +62,20 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
   const int r0 = blockIdx.x * PM_RT;
 
   // W fragments: lane holds channel 16*kb + li, layers 8*g .. 8*g + 7
-  for (int item = wave; item < PM_RT * 2 * KB; item += 4) {
-    const int rr = item / (2 * KB), beta = (item / KB) & 1, kb = item % KB;
-    const int row = min(r0 + rr, rows - 1), j = 16 * kb + li;
+  // (PB: one fragment per row, block diagonal: lane row li is channel li % 8
+  // of branch li / 8, k chunk g holds layers 8 (g % 2) .. + 7 of branch g / 2)
+  for (int item = wave; item < (PB ? PM_RT : PM_RT * 2 * KB); item += 4) {
+    const int rr = PB ? item : item / (2 * KB), beta = PB ? li >> 3 : (item / KB) & 1, kb = PB ? 0 : item % KB;
+    const int lb = PB ? 8 * (g & 1) : 8 * g;  // first layer of the lane's k chunk
+    const bool own = !PB || (g >> 1) == beta;  // (PB: the chunk belongs to the lane's branch)
+    const int row = min(r0 + rr, rows - 1), j = PB ? (li & 7) : 16 * kb + li;
     // (every load of the item is issued before any is used: Z <= 4 partials
     // of 8 layers plus their row scales, addresses clamped into range)
     const int jc = min(j, k - 1);
     float part[4][8], rs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int lc = min(8 * g + e, L - 1);
+      const int lc = min(lb + e, L - 1);
 #pragma unroll
       for (int z = 0; z < 4; ++z)
         part[z][e] = A[min(z, Z - 1) * zstride + beta * bstride + row * rstride + lc * k + jc];
@@ -75,9 +88,9 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
 #pragma unroll
       for (int z = 1; z < 4; ++z)
         if (z < Z) a += part[z][e];
-      wv[e] = (j < k && 8 * g + e < L) ? a * rs[e] : 0.f;
+      wv[e] = (own && j < k && lb + e < L) ? a * rs[e] : 0.f;
     }
-    Wl[rr][beta][kb][lane] = pack16<bf16>(wv);
+    Wl[rr][PB ? 0 : beta][kb][lane] = pack16<bf16>(wv);
   }
 
   // staging of one chunk: piece q = (rr, layer, p), 16 bytes, layer < L; the
@@ -103,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
       const int q = tid + 256 * i;
       if (q < npieces) {
         const int rr = q / (L * 8), rem = q - rr * L * 8, l = rem >> 3, p = rem & 7;
-        *(u32x4 *)(&Sl[(rr * 32 + l) * PM_SP + 8 * p]) = buf[i];
+        *(u32x4 *)(&Sl[(rr * LMAX + l) * PM_SP + 8 * p]) = buf[i];
       }
     }
   };
@@ -123,8 +136,9 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
   // column 4*(li%4) of the wave's slice
   typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
   typedef __attribute__((address_space(3))) v4s lds_v4s;
-  const int tr_lo = min(8 * g + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
-  const int tr_hi = min(8 * g + 4 + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
+  const int gl = PB ? (g & 1) : g;  // the lane's layer chunk
+  const int tr_lo = min(8 * gl + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
+  const int tr_hi = min(8 * gl + 4 + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
 
 #pragma unroll
   for (int u = 0; u < PD; ++u) gload(pre[u], u);
@@ -140,6 +154,35 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
     const int col = chunk * PM_CW + 16 * wave + li;
     // gains of this lane's column: source gains for layers 8g..8g+7, channel
     // gains for channels 16kb + 4g + i
+    if constexpr (PB) {
+      // the lane's branch g / 2: source gains of its 8 layers, channel gains
+      // of its 4 output channels 4 (g % 2) + i
+      const int bl = g >> 1;
+      float gs[8], gr[4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gs[e] = src_gain[bl * sgb + (int64_t)min(8 * (g & 1) + e, L - 1) * D + col];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gr[i] = chan_gain[bl * cgb + (int64_t)min(4 * (g & 1) + i, k - 1) * D + col];
+#pragma unroll
+      for (int rr = 0; rr < PM_RT; ++rr) {
+        const bf16 *base = &Sl[rr * LMAX * PM_SP];
+        const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + tr_lo));
+        const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + tr_hi));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        float x[8];
+        unpack16<bf16>(u32x4{l2[0], l2[1], h2[0], h2[1]}, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= gs[e];
+        f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
+        mma16<bf16>(m, Wl[rr][0][0][lane], pack16<bf16>(x));
+        // accumulator row 4g + i: channel 4 (g % 2) + i of branch g / 2
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ss[rr][0][0][i] += m[i] * m[i];
+          Ol[((bl * PM_RT + rr) * 16 * KB + 4 * (g & 1) + i) * OP + 16 * wave + li] = (bf16)(m[i] * gr[i]);
+        }
+      }
+    } else {
     float gs[2][8], gr[2][KB][4];
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta) {
@@ -154,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
 #pragma unroll
     for (int rr = 0; rr < PM_RT; ++rr) {
       const int row = r0 + rr;
-      const bf16 *base = &Sl[rr * 32 * PM_SP];
+      const bf16 *base = &Sl[rr * LMAX * PM_SP];
       const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + tr_lo));
       const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + tr_hi));
       const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -180,6 +223,7 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
         }
       }
     }
+    }
     // the chunk's outputs: 16-byte pieces of 128-byte rows
     __syncthreads();
     for (int q = tid; q < 2 * PM_RT * k * 8; q += 256) {
@@ -198,20 +242,27 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
 #pragma unroll
     for (int rr = 0; rr < PM_RT; ++rr)
 #pragma unroll
-      for (int beta = 0; beta < 2; ++beta)
+      for (int beta = 0; beta < (PB ? 1 : 2); ++beta)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) ss[rr][beta][kb][i] += __shfl_xor(ss[rr][beta][kb][i], o);
   if (li == 0) {
+    if constexpr (PB) {
 #pragma unroll
-    for (int rr = 0; rr < PM_RT; ++rr)
+      for (int rr = 0; rr < PM_RT; ++rr)
 #pragma unroll
-      for (int beta = 0; beta < 2; ++beta)
+        for (int i = 0; i < 4; ++i) red[wave][rr][g >> 1][0][4 * (g & 1) + i] = ss[rr][0][0][i];
+    } else {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+      for (int rr = 0; rr < PM_RT; ++rr)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[wave][rr][beta][kb][4 * g + i] = ss[rr][beta][kb][i];
+        for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][rr][beta][kb][4 * g + i] = ss[rr][beta][kb][i];
+    }
   }
   __syncthreads();
   for (int item = tid; item < PM_RT * 2 * KB * 16; item += 256) {
