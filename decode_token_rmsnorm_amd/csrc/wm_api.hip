@@ -285,7 +285,7 @@ template <typename T> struct Run {
                            LL, kk, c.D, c.eps);
       };
       if (kk <= 8 && LL <= 16)  // both branches' channels in one MFMA
-        go(pool_mix2<1, 16, true>, PM_RT4);
+        go(pool_mix2<1, 16, true>, PM_RTPB);
       else if (kk <= 16)
         LL <= 16 ? go(pool_mix2<1, 16>, PM_RT4) : go(pool_mix2<1, 32>, PM_RT4);
       else

@@ -33,6 +33,7 @@
 namespace wm {
 
 constexpr int PM_RT4 = 4;   // token rows per block with one channel block (k <= 16)
+constexpr int PM_RTPB = 4;  // token rows per block with both branches in one MFMA
 constexpr int PM_CW = 64;   // columns per chunk
 constexpr int PM_SP = 96;   // staged row pitch (elements): 64 columns + 64 bytes
 
@@ -48,15 +49,17 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
                                                  int64_t cgb, bf16 *mb, float *rinvM, int rows, int L, int k, int D,
                                                  float eps) {
   static_assert(!PB || (KB == 1 && LMAX == 16), "branches share an MFMA only for k <= 8 and L <= 16");
-  constexpr int PM_RT = PM_RT4 / KB;                   // token rows per block
+  constexpr int PM_RT = PB ? PM_RTPB : PM_RT4 / KB;    // token rows per block
+  constexpr int NB = PB ? 1 : 2;                       // MFMA A operands per row and channel block
+  constexpr int CH = PB ? 8 : 16 * KB;                 // staged output channels per branch and row
   constexpr int NPT = (PM_RT * LMAX * 8 + 255) / 256;  // 16-byte pieces per thread and chunk (L <= LMAX)
   __shared__ __attribute__((aligned(16))) bf16 Sl[PM_RT * LMAX * PM_SP];
-  __shared__ __attribute__((aligned(16))) u32x4 Wl[PM_RT][2][KB][64];
+  __shared__ __attribute__((aligned(16))) u32x4 Wl[PM_RT][NB][KB][64];
   __shared__ float red[4][PM_RT][2][KB][16];
   // output chunk [beta][row][channel][64 columns], 144-byte rows: the four
   // lane groups of a wave write channels 16 banks apart
   constexpr int OP = 72;
-  __shared__ __attribute__((aligned(16))) bf16 Ol[2 * PM_RT * 16 * KB * OP];
+  __shared__ __attribute__((aligned(16))) bf16 Ol[2 * PM_RT * CH * OP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int r0 = blockIdx.x * PM_RT;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ss[rr][0][0][i] += m[i] * m[i];
-          Ol[((bl * PM_RT + rr) * 16 * KB + 4 * (g & 1) + i) * OP + 16 * wave + li] = (bf16)(m[i] * gr[i]);
+          Ol[((bl * PM_RT + rr) * CH + 4 * (g & 1) + i) * OP + 16 * wave + li] = (bf16)(m[i] * gr[i]);
         }
       }
     } else {
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             ss[rr][beta][kb][i] += m[i] * m[i];
-            Ol[((beta * PM_RT + rr) * 16 * KB + 16 * kb + 4 * g + i) * OP + 16 * wave + li] =
+            Ol[((beta * PM_RT + rr) * CH + 16 * kb + 4 * g + i) * OP + 16 * wave + li] =
                 (bf16)(m[i] * gr[beta][kb][i]);
           }
         }
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
       const int row = r0 + rr;
       if (row < rows)
         *(u32x4 *)(mb + (((int64_t)beta * k + j) * rows + row) * D + chunk * PM_CW + 8 * pc) =
-            *(const u32x4 *)(&Ol[((beta * PM_RT + rr) * 16 * KB + j) * OP + 8 * pc]);
+            *(const u32x4 *)(&Ol[((beta * PM_RT + rr) * CH + j) * OP + 8 * pc]);
     }
   }
 
