@@ -898,6 +898,11 @@ __global__ __launch_bounds__(256) void k_loss_sum(const float *lossrow, int64_t 
 }
 
 // ------------------------------------------------------------------ host side
+// b - a in floats, for batching products over buffers of different allocations
+inline int64_t fdist(const float *a, const float *b) {
+  return (int64_t)(((intptr_t)b - (intptr_t)a) / (intptr_t)sizeof(float));
+}
+
 inline unsigned grid1(int64_t n, int per = 256) {
   int64_t g = (n + per - 1) / per;
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(g, 65536));
@@ -1203,8 +1208,9 @@ struct Trainer {
       TR_TRY(copy(h1, S, nd));
       TR_TRY(gemm(false, true, out, QD, W(w.wo) + (size_t)l * D * QD, QD, h1, D, N, D, QD, 1.f));
       TR_TRY(rms(h1, w.ffn_norm + (size_t)l * D, N, bn, P(o.rF) + (size_t)l * N, N, D));
-      TR_TRY(gemm(false, true, bn, D, W(w.w_gate) + (size_t)l * F * D, D, G, F, N, F, D, 0.f));
-      TR_TRY(gemm(false, true, bn, D, W(w.w_up) + (size_t)l * F * D, D, U, F, N, F, D, 0.f));
+      // gate and up in one launch (z = 0, 1: the two weight matrices and outputs)
+      const float *Wg = W(w.w_gate) + (size_t)l * F * D, *Wu = W(w.w_up) + (size_t)l * F * D;
+      TR_TRY(gemm(false, true, bn, D, Wg, D, G, F, N, F, D, 0.f, 2, 0, fdist(Wg, Wu), fdist(G, U)));
       hipLaunchKernelGGL(k_swiglu, dim3(grid1(nf)), dim3(256), 0, s, G, U, act, (int64_t)nf);
       TR_TRY(hipGetLastError());
       float *next = l + 1 < L ? P(o.S) + (l + 1) * nd : P(o.hL);
@@ -1295,8 +1301,11 @@ struct Trainer {
       TR_TRY(hipGetLastError());
       TR_TRY(gemm(false, false, P(o.dG), F, W(w.w_gate) + (size_t)l * F * D, D, P(o.db), D, N, D, F, 0.f));
       TR_TRY(gemm(false, false, P(o.dU), F, W(w.w_up) + (size_t)l * F * D, D, P(o.db), D, N, D, F, 1.f));
-      TR_TRY(gemm(true, false, P(o.dG), F, bn, D, gr.w_gate + (size_t)l * F * D, D, F, D, N, 1.f));
-      TR_TRY(gemm(true, false, P(o.dU), F, bn, D, gr.w_up + (size_t)l * F * D, D, F, D, N, 1.f));
+      {  // the gate and up weight gradients in one launch
+        float *gg = gr.w_gate + (size_t)l * F * D, *gu = gr.w_up + (size_t)l * F * D;
+        TR_TRY(gemm(true, false, P(o.dG), F, bn, D, gg, D, F, D, N, 1.f, 2, fdist(P(o.dG), P(o.dU)), 0,
+                    fdist(gg, gu)));
+      }
       TR_TRY(rms_bwd(h1, w.ffn_norm + (size_t)l * D, gr.ffn_norm + (size_t)l * D, N, 1, P(o.rF) + (size_t)l * N,
                      P(o.db), dh, true, N, D));
       // attention: h1 = h_l + out W_O^T
