@@ -177,8 +177,9 @@ struct GOp {
 
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64_t sA, const float *B, int64_t ldb,
-                                              int64_t sB, float *C, int64_t ldc, int64_t sC, int M, int N, int K,
-                                              float alpha, float beta, int splits, int kchunk, int vecA, int vecB) {
+                                              int64_t sB, float *C, int64_t ldc, int64_t sC, const float *Cr, int M,
+                                              int N, int K, float alpha, float beta, int splits, int kchunk, int vecA,
+                                              int vecB) {
   typedef GOp<TA> OA;
   typedef GOp<!TB> OB;
   __shared__ __attribute__((aligned(16))) float As[2][OA::SZ];
@@ -187,6 +188,7 @@ __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64
   A += batch * sA;
   B += batch * sB;
   C += blockIdx.z * sC;
+  Cr += blockIdx.z * sC;  // (read only when splits == 1: then blockIdx.z is the batch)
   const int kb = split * kchunk, ke = min(K, kb + kchunk);
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lj = lane >> 4, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -242,24 +244,24 @@ __global__ __launch_bounds__(256) void k_gemm(const float *A, int64_t lda, int64
       for (int e = 0; e < 4; ++e) {
         const int gm = m0 + wm * 32 + i * 16 + 4 * lj + e;
         if (gm >= M) continue;
-        float *c = C + (int64_t)gm * ldc + gn;
+        const int64_t off = (int64_t)gm * ldc + gn;
         const float v = acc[i][j][e];
-        *c = beta == 0.f ? alpha * v : alpha * v + beta * *c;
+        C[off] = beta == 0.f ? alpha * v : alpha * v + beta * Cr[off];
       }
     }
 }
 
-// C[z] = beta * C[z] + sum over the splits (in order) of part[z * splits + s], [M, N]
-__global__ void k_split_sum(const float *part, int splits, float *C, int64_t ldc, int64_t sC, int M, int N, int Z,
-                            float beta) {
+// C[z] = beta * Cr[z] + sum over the splits (in order) of part[z * splits + s], [M, N]
+__global__ void k_split_sum(const float *part, int splits, float *C, const float *Cr, int64_t ldc, int64_t sC, int M,
+                            int N, int Z, float beta) {
   const int64_t MN = (int64_t)M * N, total = MN * Z;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t z = i / MN, e = i - z * MN;
     const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
     float t = 0.f;
     for (int sp = 0; sp < splits; ++sp) t += part[(z * splits + sp) * MN + e];
-    float *c = C + z * sC + (int64_t)m * ldc + n;
-    *c = beta == 0.f ? t : t + beta * *c;
+    const int64_t off = z * sC + (int64_t)m * ldc + n;
+    C[off] = beta == 0.f ? t : t + beta * Cr[off];
   }
 }
 
@@ -1051,11 +1053,13 @@ struct Trainer {
     hipLaunchKernelGGL(k_add, dim3(grid1(n)), dim3(256), 0, s, y, x, n);
     return hipGetLastError();
   }
-  // C = op(A) op(B) + beta C, batched over Z with element strides.  Grids
-  // of fewer tiles than compute units split k (chunks of at least 128, up to
-  // 8 splits) into partials in the workspace, summed in split order.
+  // C = op(A) op(B) + beta Cin (Cin = C unless given; laid out as C), batched
+  // over Z with element strides.  Grids of fewer tiles than compute units
+  // split k (chunks of at least 128, up to 8 splits) into partials in the
+  // workspace, summed in split order.
   hipError_t gemm(bool ta, bool tb, const float *A, int64_t lda, const float *B_, int64_t ldb, float *C, int64_t ldc,
-                  int M, int N, int K, float beta, int Z = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0) {
+                  int M, int N, int K, float beta, int Z = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0,
+                  const float *Cin = nullptr) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * Z;
     int splits = 1;
@@ -1066,6 +1070,7 @@ struct Trainer {
     const int kchunk = splits > 1 ? ((K + splits - 1) / splits + GK - 1) / GK * GK : K;
     if (splits > 1) splits = (K + kchunk - 1) / kchunk;
     float *Cd = splits > 1 ? P(o.split) : C;
+    const float *Cr = Cin ? Cin : C;  // (the beta term's source, laid out as C)
     const int64_t ldd = splits > 1 ? N : ldc, sD = splits > 1 ? (int64_t)M * N : sC;
     const float bd = splits > 1 ? 0.f : beta;
     dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, Z * splits);
@@ -1073,21 +1078,21 @@ struct Trainer {
     const int va = ((uintptr_t)A % 16 == 0 && lda % 4 == 0 && sA % 4 == 0) ? 1 : 0;
     const int vb = ((uintptr_t)B_ % 16 == 0 && ldb % 4 == 0 && sB % 4 == 0) ? 1 : 0;
     if (!ta && !tb)
-      hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N,
+      hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, Cr, M, N,
                          K, 1.f, bd, splits, kchunk, va, vb);
     else if (!ta && tb)
-      hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
+      hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, Cr, M, N, K,
                          1.f, bd, splits, kchunk, va, vb);
     else if (ta && !tb)
-      hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
+      hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, Cr, M, N, K,
                          1.f, bd, splits, kchunk, va, vb);
     else
-      hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, M, N, K,
+      hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(256), 0, s, A, lda, sA, B_, ldb, sB, Cd, ldd, sD, Cr, M, N, K,
                          1.f, bd, splits, kchunk, va, vb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int64_t total = (int64_t)M * N * Z;
-    hipLaunchKernelGGL(k_split_sum, dim3(grid1(total)), dim3(256), 0, s, P(o.split), splits, C, ldc, sC, M, N, Z, beta);
+    hipLaunchKernelGGL(k_split_sum, dim3(grid1(total)), dim3(256), 0, s, P(o.split), splits, C, Cr, ldc, sC, M, N, Z, beta);
     return hipGetLastError();
   }
   hipError_t rms(const float *x, const float *gain, int rpg, float *y, float *rinv, int rows, int width) {
@@ -1205,8 +1210,7 @@ struct Trainer {
       const int ch = l % k;
       TR_TRY(attn_fwd(q, chanK(o.cK, ch), chanK(o.cV, ch), rm, N, scale, out, P(o.mst) + (size_t)l * N * c.Hq,
                       P(o.lst) + (size_t)l * N * c.Hq));
-      TR_TRY(copy(h1, S, nd));
-      TR_TRY(gemm(false, true, out, QD, W(w.wo) + (size_t)l * D * QD, QD, h1, D, N, D, QD, 1.f));
+      TR_TRY(gemm(false, true, out, QD, W(w.wo) + (size_t)l * D * QD, QD, h1, D, N, D, QD, 1.f, 1, 0, 0, 0, S));
       TR_TRY(rms(h1, w.ffn_norm + (size_t)l * D, N, bn, P(o.rF) + (size_t)l * N, N, D));
       // gate and up in one launch (z = 0, 1: the two weight matrices and outputs)
       const float *Wg = W(w.w_gate) + (size_t)l * F * D, *Wu = W(w.w_up) + (size_t)l * F * D;
@@ -1214,8 +1218,7 @@ struct Trainer {
       hipLaunchKernelGGL(k_swiglu, dim3(grid1(nf)), dim3(256), 0, s, G, U, act, (int64_t)nf);
       TR_TRY(hipGetLastError());
       float *next = l + 1 < L ? P(o.S) + (l + 1) * nd : P(o.hL);
-      TR_TRY(copy(next, h1, nd));
-      TR_TRY(gemm(false, true, act, F, W(w.w_down) + (size_t)l * D * F, F, next, D, N, D, F, 1.f));
+      TR_TRY(gemm(false, true, act, F, W(w.w_down) + (size_t)l * D * F, F, next, D, N, D, F, 1.f, 1, 0, 0, 0, h1));
     }
     wm_status st = pool_fwd(0, rm, N);
     if (st != WM_OK) return st;
