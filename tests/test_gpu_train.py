@@ -19,7 +19,8 @@ Shapes: the tiny model's own configuration (B1, T128, g16, 1 + 2 passes);
 ragged groups with several sequences and other pass splits; a head dim of
 128 (the 1.3B model's); the small model's widths (L16, D512, 8/4 heads of 64,
 F1536, k8) at a short length; T = 2, Jacobi (g = 1) and autoregressive
-(g = T) schedules.  The step is deterministic: two calls give the same bits.
+(g = T) schedules; three query heads per KV head (ragged 16-slot attention
+tiles); T = 300 (keys in several rounds of each wave's 16-key tiles).  The step is deterministic: two calls give the same bits.
 """
 import math
 
@@ -47,6 +48,8 @@ CASES = {
     "tiny_T2_g1_1+2": (TINY.replace(B=2, T=2), 1, 1, 2),
     "tiny_B2_T12_jacobi_1+2": (TINY.replace(B=2, T=12), 1, 1, 2),
     "tiny_B2_T12_ar_1+2": (TINY.replace(B=2, T=12), 12, 1, 2),
+    "gqa3_B2_T20_g3_1+2": (TINY.replace(L=2, Hq=6, Hkv=2, F=256, V=300, B=2, T=20), 3, 1, 2),
+    "tiny_B1_T300_g8_1+2": (TINY.replace(T=300, T_max=300), 8, 1, 2),
 }
 
 
