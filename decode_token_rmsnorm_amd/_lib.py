@@ -72,6 +72,7 @@ _SIGS = {
     "wm_feedback_free_decode_step": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, P(WmCache), c_vp, c_vp,
                                              c_size, c_vp]),
     "wm_train_workspace_bytes": (c_size, [P(WmConfig), c_i32, c_i32, c_i32, c_i32]),
+    "wm_train_workspace_min_bytes": (c_size, [P(WmConfig), c_i32, c_i32, c_i32, c_i32]),
     "wm_train_step": (c_i32, [P(WmConfig), P(WmWeights), c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, P(WmGrads), c_vp,
                               c_vp, c_size, c_vp]),
     "wm_profile_begin": (c_i32, [ctypes.c_uint32]),

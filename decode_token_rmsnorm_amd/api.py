@@ -338,10 +338,14 @@ def peak_mfma_bf16(iters: int = 10, stream=None) -> float:
     return out.value
 
 
-def train_workspace(model: Model, B: int, T: int, g: int, n_grad: int = 2) -> torch.Tensor:
-    n = C.lib().wm_train_workspace_bytes(ctypes.byref(model.cfg), B, T, g, n_grad)
+def train_workspace(model: Model, B: int, T: int, g: int, n_grad: int = 2, keep_tapes: bool = True) -> torch.Tensor:
+    """Workspace of a training step: with keep_tapes the size that also keeps
+    every gradient step's forward intermediates (when that stays within 64
+    GiB), else the minimum, with which the step recomputes them."""
+    fn = "wm_train_workspace_bytes" if keep_tapes else "wm_train_workspace_min_bytes"
+    n = getattr(C.lib(), fn)(ctypes.byref(model.cfg), B, T, g, n_grad)
     if n == 0:
-        raise C.WmError("wm_train_workspace_bytes", -2)
+        raise C.WmError(fn, -2)
     return torch.empty(n, dtype=torch.uint8, device=model.device)
 
 

@@ -931,10 +931,29 @@ struct Ws {
   size_t enext, ehead;  // (int arrays)
   size_t split, split_cap;  // split-k partials (floats)
   size_t gpart;             // gain-gradient chunk sums
+  // The step tape (S .. hL) is one slot of tape_stride floats at its fields'
+  // offsets; with nslot > 1 the gradient steps keep their tapes in slots
+  // 1 .. nslot - 1, from extra0 on, and the reverse walk does not recompute
+  // their forward.
+  size_t tape0, tape_stride, extra0;
+  int nslot;
   size_t bytes;
+  Ws slot(int i) const {
+    Ws w = *this;
+    const size_t sh = i == 0 ? 0 : extra0 + (size_t)(i - 1) * tape_stride - tape0;
+    for (size_t *f : {&w.S, &w.rA, &w.a, &w.qraw, &w.rQ, &w.q, &w.o, &w.mst, &w.lst, &w.h1, &w.rF, &w.bn, &w.G,
+                      &w.U, &w.act, &w.hL})
+      *f += sh;
+    return w;
+  }
 };
 
-inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad) {
+// Gradient-step tapes are kept when the whole workspace stays within this
+// many bytes (a quarter of the device's HBM at the sizes benchmarked here);
+// beyond it the reverse walk recomputes each step's forward instead.
+constexpr size_t kTapeBudget = (size_t)64 << 30;
+
+inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad, bool tapes = true) {
   const size_t L = c.L, D = c.D, QD = (size_t)c.Hq * c.d, KD = (size_t)c.Hkv * c.d, F = c.F, k = c.k, V = c.V;
   const size_t R = (c.L + c.p - 1) / c.p, ng = std::min(g, T);
   const size_t N = (size_t)B * ((T + g - 1) / g), cache = k * B * KD * T;
@@ -947,6 +966,7 @@ inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad) {
   w.dV = t(cache);
   w.undo_slot = ((2 * k * N * KD * 4 + 255) & ~(size_t)255) / 4;
   w.undo = t(w.undo_slot * (size_t)n_grad * ng);
+  w.tape0 = l.total / 4;
   w.S = t(L * N * D);
   w.rA = t(L * N);
   w.a = t(L * N * D);
@@ -963,6 +983,7 @@ inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad) {
   w.U = t(L * N * F);
   w.act = t(L * N * F);
   w.hL = t(N * D);
+  w.tape_stride = l.total / 4 - w.tape0;
   w.rL = t(N);
   w.xf = t(N * D);
   w.logits = t(N * V);
@@ -1010,6 +1031,13 @@ inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad) {
   auto chunks = [](size_t rows, size_t ngain) { return rows / 256 + ngain; };
   w.gpart = t(std::max({chunks(L * N, L) * D, chunks(k * N, k) * D, chunks(k * N * c.Hkv, k) * c.d,
                         chunks(N * c.Hq, 1) * c.d, chunks(N, 1) * D}));
+  const size_t extra = (size_t)n_grad * ng * w.tape_stride;
+  w.nslot = 1;
+  w.extra0 = 0;
+  if (tapes && l.total + extra * 4 <= kTapeBudget) {
+    w.extra0 = t(extra);
+    w.nslot = 1 + n_grad * (int)ng;
+  }
   w.bytes = l.total;
   return w;
 }
@@ -1026,9 +1054,9 @@ struct Trainer {
   int L, D, QD, KD, F, k, V, R;
 
   Trainer(const wm_config &c_, const wm_weights &w_, const wm_grads &g_, const int32_t *tok, int B_, int T_, int gg,
-          int n_grad, void *ws, hipStream_t st)
+          int n_grad, bool tapes, void *ws, hipStream_t st)
       : c(c_), w(w_), gr(g_), tokens(tok), B(B_), T(T_), g(gg), base((float *)ws), s(st) {
-    o = layout(c, B, T, g, n_grad);
+    o = layout(c, B, T, g, n_grad, tapes);
     L = c.L;
     D = c.D;
     QD = c.Hq * c.d;
@@ -1194,7 +1222,7 @@ struct Trainer {
 
   // Forward of one group step with every intermediate kept.  The cache is
   // only read.  want_logits: logits, and the loss rows with their gradient.
-  wm_status step_fwd(Rows rm, int N, bool want_logits, float inv_count) {
+  wm_status step_fwd(Rows rm, int N, bool want_logits, float inv_count, bool with_pool = true) {
     const float scale = 1.f / sqrtf((float)c.d);
     hipLaunchKernelGGL(k_embed, dim3(N), dim3(256), 0, s, tokens, T, rm, W(w.embed), P(o.S), N, D, V);
     TR_TRY(hipGetLastError());
@@ -1220,17 +1248,21 @@ struct Trainer {
       float *next = l + 1 < L ? P(o.S) + (l + 1) * nd : P(o.hL);
       TR_TRY(gemm(false, true, act, F, W(w.w_down) + (size_t)l * D * F, F, next, D, N, D, F, 1.f, 1, 0, 0, 0, h1));
     }
-    wm_status st = pool_fwd(0, rm, N);
-    if (st != WM_OK) return st;
-    st = pool_fwd(1, rm, N);
-    if (st != WM_OK) return st;
-    if (want_logits) {
-      TR_TRY(rms(P(o.hL), w.final_norm, N, P(o.xf), P(o.rL), N, D));
-      TR_TRY(gemm(false, true, P(o.xf), D, W(w.lm_head), D, P(o.logits), V, N, V, D, 0.f));
-      hipLaunchKernelGGL(k_ce, dim3(N), dim3(256), 0, s, P(o.logits), tokens, T, rm, V, inv_count, P(o.lossrow),
-                         P(o.dz));
-      TR_TRY(hipGetLastError());
+    if (with_pool) {
+      wm_status st = pool_fwd(0, rm, N);
+      if (st != WM_OK) return st;
+      st = pool_fwd(1, rm, N);
+      if (st != WM_OK) return st;
     }
+    return want_logits ? head_fwd(rm, N, inv_count) : WM_OK;
+  }
+  // final norm, logits, the loss rows and their gradient dz
+  wm_status head_fwd(Rows rm, int N, float inv_count) {
+    TR_TRY(rms(P(o.hL), w.final_norm, N, P(o.xf), P(o.rL), N, D));
+    TR_TRY(gemm(false, true, P(o.xf), D, W(w.lm_head), D, P(o.logits), V, N, V, D, 0.f));
+    hipLaunchKernelGGL(k_ce, dim3(N), dim3(256), 0, s, P(o.logits), tokens, T, rm, V, inv_count, P(o.lossrow),
+                       P(o.dz));
+    TR_TRY(hipGetLastError());
     return WM_OK;
   }
 
@@ -1385,17 +1417,24 @@ struct Trainer {
                      {gr.k_norm, (int64_t)k * c.d}};
     for (const G2 &z : gz) TR_TRY(fill(z.p, z.n, 0.f));
     // forward: passes without gradient, then the gradient passes with undo
+    // (and, when they fit, each gradient step's tape in its own slot)
+    const Ws base = o;
+    const bool keep = base.nslot > 1;
     for (int pass = 0; pass < n_nograd + n_grad; ++pass) {
       const int gp = pass - n_nograd;
       for (int q = 0; q < ng; ++q) {
         const int M = (T - q + g - 1) / g;
         const Rows rm{M, q, g};
         float *undo = gp >= 0 ? P(o.undo) + ((size_t)gp * ng + q) * o.undo_slot : nullptr;
+        o = keep && gp >= 0 ? base.slot(1 + gp * ng + q) : base;
         wm_status st = fwd_write(rm, B * M, undo);
+        o = base;
         if (st != WM_OK) return st;
       }
     }
-    // backward over the gradient steps in reverse
+    // backward over the gradient steps in reverse: the step's tape (kept, or
+    // recomputed from the cache as the step found it; the pool's forward is
+    // redone branch by branch in its backward either way)
     for (int gp = n_grad - 1; gp >= 0; --gp) {
       for (int q = ng - 1; q >= 0; --q) {
         const int M = (T - q + g - 1) / g, N = B * M;
@@ -1406,9 +1445,15 @@ struct Trainer {
         TR_TRY(entries(P(o.cK), undo, rm, N, 1));
         TR_TRY(entries(P(o.cV), undo + (size_t)k * N * KD, rm, N, 1));
         const bool last = gp == n_grad - 1;
-        wm_status st = step_fwd(rm, N, last, inv_count);
-        if (st != WM_OK) return st;
-        st = step_bwd(rm, N, last);
+        wm_status st = WM_OK;
+        if (keep) {
+          o = base.slot(1 + gp * ng + q);
+          if (last) st = head_fwd(rm, N, inv_count);
+        } else {
+          st = step_fwd(rm, N, last, inv_count, false);
+        }
+        if (st == WM_OK) st = step_bwd(rm, N, last);
+        o = base;
         if (st != WM_OK) return st;
       }
     }
@@ -1427,7 +1472,12 @@ extern "C" {
 
 size_t wm_train_workspace_bytes(const wm_config *cfg, int32_t B, int32_t T, int32_t g, int32_t n_grad) {
   if (!cfg || wm_check_config(cfg) != WM_OK || B < 1 || T < 2 || g < 1 || n_grad < 1) return 0;
-  return tr::layout(*cfg, B, T, g, n_grad).bytes;
+  return tr::layout(*cfg, B, T, g, n_grad, true).bytes;
+}
+
+size_t wm_train_workspace_min_bytes(const wm_config *cfg, int32_t B, int32_t T, int32_t g, int32_t n_grad) {
+  if (!cfg || wm_check_config(cfg) != WM_OK || B < 1 || T < 2 || g < 1 || n_grad < 1) return 0;
+  return tr::layout(*cfg, B, T, g, n_grad, false).bytes;
 }
 
 wm_status wm_train_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t B, int32_t T,
@@ -1453,10 +1503,12 @@ wm_status wm_train_step(const wm_config *cfg, const wm_weights *w, const int32_t
                        grads->w_down, grads->src_norm, grads->router,   grads->chan_norm, grads->wk,
                        grads->wv,     grads->k_norm};
   for (const float *p : gp) TR_CHECK(p, WM_ERR_ARG, "a gradient pointer is NULL");
-  const size_t need = tr::layout(*cfg, B, T, g, n_grad).bytes;
+  // the kept-tape layout when the workspace holds it, else the recomputing one
+  const bool tapes = ws_bytes >= tr::layout(*cfg, B, T, g, n_grad, true).bytes;
+  const size_t need = tr::layout(*cfg, B, T, g, n_grad, false).bytes;
   TR_CHECK(ws_bytes >= need, WM_ERR_WORKSPACE, "workspace of %zu bytes, the training step needs %zu", ws_bytes,
            need);
-  tr::Trainer t(*cfg, *w, *grads, tokens, B, T, g, n_grad, ws, (hipStream_t)stream);
+  tr::Trainer t(*cfg, *w, *grads, tokens, B, T, g, n_grad, tapes, ws, (hipStream_t)stream);
   return t.run(n_nograd, n_grad, loss);
 }
 

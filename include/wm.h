@@ -323,8 +323,14 @@ wm_status wm_feedback_free_decode_step(const wm_config *cfg, const wm_weights *w
  * (WM_ERR_RANGE), g >= 1, n_nograd >= 0, n_grad >= 1 (WM_ERR_ARG). An id
  * outside [0, V) makes the loss and the gradients NaN. grads: float device
  * buffers of the parameters' shapes, overwritten (not accumulated); *loss is
- * a device float. The cache and every intermediate live in the workspace of
- * wm_train_workspace_bytes(cfg, B, T, g, n_grad) bytes (0 on bad arguments).
+ * a device float. The cache and every intermediate live in the caller's
+ * workspace. wm_train_workspace_bytes(cfg, B, T, g, n_grad) bytes (0 on bad
+ * arguments) hold, besides, the intermediates of every gradient group step
+ * from the forward passes, so the reverse walk does not recompute them,
+ * whenever that total stays within 64 GiB (else it equals the minimum);
+ * wm_train_workspace_min_bytes gives the least the step accepts
+ * (WM_ERR_WORKSPACE below it), with which it recomputes each gradient step's
+ * forward during the reverse walk. Both layouts give bit-identical results.
  * Deterministic: the same inputs give bit-identical results. */
 typedef struct {
   float *embed, *lm_head, *final_norm, *attn_norm, *wq, *q_norm, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
@@ -332,6 +338,7 @@ typedef struct {
 } wm_grads;
 
 size_t wm_train_workspace_bytes(const wm_config *cfg, int32_t B, int32_t T, int32_t g, int32_t n_grad);
+size_t wm_train_workspace_min_bytes(const wm_config *cfg, int32_t B, int32_t T, int32_t g, int32_t n_grad);
 wm_status wm_train_step(const wm_config *cfg, const wm_weights *w, const int32_t *tokens, int32_t B, int32_t T,
                         int32_t g, int32_t n_nograd, int32_t n_grad, const wm_grads *grads, float *loss, void *ws,
                         size_t ws_bytes, wm_stream stream);

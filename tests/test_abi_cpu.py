@@ -25,7 +25,7 @@ def cfg_of(w, dtype=C.WM_BF16, **kw):
 
 def test_library_exports_every_declared_function():
     names = C.header_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     assert set(names) <= exported, set(names) - exported
@@ -279,17 +279,23 @@ def test_binding_checks_tensors_before_calling():
 def test_train_step_validates_before_launch():
     """wm_train_step: float32 only, the routed model only (no static mixing),
     2 <= T <= T_max, g >= 1, n_nograd >= 0, n_grad >= 1, every pointer set,
-    workspace of wm_train_workspace_bytes; each refused before any launch."""
+    workspace of at least wm_train_workspace_min_bytes; each refused before any
+    launch."""
     L = C.lib()
     w = WORKLOADS["tiny_fp32"]
     c = cfg_of(w, dtype=C.WM_F32)
     W = _weights()
     G = C.WmGrads(*[FAKE for _ in C.GRAD_FIELDS])
-    need = L.wm_train_workspace_bytes(ctypes.byref(c), w.B, w.T, w.g, 2)
+    need = L.wm_train_workspace_min_bytes(ctypes.byref(c), w.B, w.T, w.g, 2)
     assert need > 0
-    assert L.wm_train_workspace_bytes(ctypes.byref(c), w.B, w.T, w.g, 3) > need  # one undo slot per gradient step
-    assert L.wm_train_workspace_bytes(ctypes.byref(c), w.B, 1, w.g, 2) == 0
-    assert L.wm_train_workspace_bytes(ctypes.byref(c), w.B, w.T, w.g, 0) == 0
+    # (one undo slot per gradient step; the full size adds one tape per gradient step)
+    assert L.wm_train_workspace_min_bytes(ctypes.byref(c), w.B, w.T, w.g, 3) > need
+    assert L.wm_train_workspace_bytes(ctypes.byref(c), w.B, w.T, w.g, 2) > need
+    assert L.wm_train_workspace_bytes(ctypes.byref(c), w.B, w.T, w.g, 3) > L.wm_train_workspace_bytes(
+        ctypes.byref(c), w.B, w.T, w.g, 2)
+    for fn in (L.wm_train_workspace_bytes, L.wm_train_workspace_min_bytes):
+        assert fn(ctypes.byref(c), w.B, 1, w.g, 2) == 0
+        assert fn(ctypes.byref(c), w.B, w.T, w.g, 0) == 0
 
     def call(cfg=c, Wt=W, Gt=G, B=w.B, T=w.T, g=w.g, n0=1, n1=2, n=need, loss=FAKE):
         return L.wm_train_step(ctypes.byref(cfg), ctypes.byref(Wt), FAKE, B, T, g, n0, n1,

@@ -88,6 +88,29 @@ def test_train_step_matches_oracle(case):
           ", ".join(f"{n} {e:.1e} (f32 floor {f:.1e})" for _, n, e, f in worst[:3]), flush=True)
 
 
+@pytest.mark.parametrize("case", ["tiny_B2_T20_g3_0+2", "small_widths_B2_T24_g4_1+2", "tiny_B1_T300_g8_1+2"])
+def test_recomputing_layout_gives_the_same_bits(case):
+    """With the minimum workspace the reverse walk recomputes each gradient
+    step's forward (from the cache as the step found it) instead of reading
+    the intermediates kept from the forward passes: the same loss and
+    gradients, bit for bit."""
+    w, g, n0, n1 = CASES[case]
+    W = make_weights(w, seed=0, gains="perturbed")
+    model = wm.Model(w, W, "f32")
+    tok = torch.from_numpy(make_tokens(w, seed=1)).cuda()
+    out = []
+    for keep in (True, False):
+        ws = wm.train_workspace(model, w.B, w.T, g, n1, keep_tapes=keep)
+        print(f"[train] {case}: keep_tapes={keep}, workspace {ws.numel()} B", flush=True)
+        loss, grads = wm.train_step(model, tok, g, n0, n1, ws=ws)
+        torch.cuda.synchronize()
+        out.append((float(loss.item()), {n: grads[n].clone() for n in grads}))
+        del ws
+    assert out[0][0] == out[1][0]
+    for n in out[0][1]:
+        assert torch.equal(out[0][1][n], out[1][1][n]), n
+
+
 def test_train_step_is_deterministic():
     w, g, n0, n1 = CASES["tiny_B2_T20_g3_0+2"]
     W = make_weights(w, seed=0, gains="perturbed")
@@ -119,7 +142,9 @@ def test_train_step_full_size_properties():
     float32, V32768, B8 T2048, g16), where the float64 oracle is out of
     reach, properties that hold at any size:
 
-    * every gradient of the 1 + 2 pass step is finite;
+    * every gradient of the 1 + 2 pass step is finite, and the step with the
+      minimum workspace (forward recomputed in the reverse walk) gives the
+      same loss bits as the one that keeps the gradient steps' tapes;
     * the step's loss is the next-token cross-entropy of the logits the
       inference path (wm_cyclic_prefill_pass on the same float32 model:
       other kernels, the same definition) gives after as many passes: within
@@ -158,6 +183,12 @@ def test_train_step_full_size_properties():
         assert rel <= bound
     for n in grads:
         assert torch.isfinite(grads[n]).all(), n
+    # the recomputing layout (minimum workspace) gives the same loss bits
+    ws_min = wm.train_workspace(model, w.B, w.T, w.g, 2, keep_tapes=False)
+    assert ws_min.numel() < ws.numel()
+    l_min, _ = wm.train_step(model, tok, w.g, 1, 2, ws=ws_min)
+    assert float(l_min.item()) == float(loss.item())
+    del ws_min
 
     print("[train full] central difference along the LM head and final norm gradient", flush=True)
     names = ["lm_head", "final_norm"]
