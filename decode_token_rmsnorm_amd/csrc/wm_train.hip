@@ -16,8 +16,10 @@
 // reverse.  For each it takes the gradient of the entries the step wrote from
 // dCache (an array shaped like the cache that collects, for every entry, the
 // gradient of the value it holds at that point of the walk), clears it there,
-// puts the old values back (so the cache is as the step found it), recomputes
-// the step's forward with every intermediate kept, and runs the step's
+// puts the old values back (so the cache is as the step found it), takes
+// the step's forward intermediates (kept from the forward pass in a slot of
+// the workspace when it holds one per gradient step, else recomputed from
+// the restored cache; both give the same bits), and runs the step's
 // backward: the pool first (the written keys/values back to the layer inputs
 // and the pool parameters), then the layers from the top, where the
 // attention of layer l adds the gradient of every cache entry it read into
