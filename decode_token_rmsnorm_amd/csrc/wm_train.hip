@@ -143,26 +143,31 @@ __device__ __forceinline__ f32x4 ld4(const float *p, int idx, int lim, bool vec)
 template <bool KO>
 struct GOp {
   static constexpr int P = KO ? GT + 16 : GK + 4, SZ = KO ? GK * P : GT * P;
-  f32x4 r[2];
+  static constexpr int NV = GT * GK / 4 / 256;  // 16-byte runs per thread
+  // thread -> run v: k-row (tid / 16) + 16 v, rows 4 (tid % 16) .. + 3 when
+  // k is the outer index; else row (tid / (GK / 4)) + (1024 / GK) v, k
+  // 4 (tid % (GK / 4)) .. + 3
+  static constexpr int KQ = GK / 4, RS = 256 / KQ;
+  f32x4 r[NV];
   __device__ __forceinline__ void load(const float *X, int64_t ld, int r0, int R, int k0, int ke, bool vec, int tid) {
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
+    for (int v = 0; v < NV; ++v) {
       if (KO) {
         const int kk = (tid >> 4) + 16 * v, rr = 4 * (tid & 15);
         r[v] = k0 + kk < ke ? ld4(X + (int64_t)(k0 + kk) * ld + r0 + rr, r0 + rr, R, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
       } else {
-        const int rr = (tid >> 3) + 32 * v, kk = 4 * (tid & 7);
+        const int rr = tid / KQ + RS * v, kk = 4 * (tid % KQ);
         r[v] = r0 + rr < R ? ld4(X + (int64_t)(r0 + rr) * ld + k0 + kk, k0 + kk, ke, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
   __device__ __forceinline__ void store(float *S, int tid) const {
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
+    for (int v = 0; v < NV; ++v) {
       if (KO)
         *(f32x4 *)&S[((tid >> 4) + 16 * v) * P + 4 * (tid & 15)] = r[v];
       else
-        *(f32x4 *)&S[((tid >> 3) + 32 * v) * P + 4 * (tid & 7)] = r[v];
+        *(f32x4 *)&S[(tid / KQ + RS * v) * P + 4 * (tid % KQ)] = r[v];
     }
   }
   // operand values of row `row` (of the tile) for the 4 steps of chunk c
