@@ -361,19 +361,31 @@ __global__ void k_embed(const int32_t *tokens, int T, Rows rm, const float *E, f
 }
 // Rows sharing a token, as chains in row order: nxt[n] = the next row with
 // the same token (-1 at the end), head[n] = 1 for the first row of a token.
-__global__ void k_embed_chains(const int32_t *tokens, int T, Rows rm, int N, int *nxt, int *head) {
+__global__ __launch_bounds__(64) void k_embed_chains(const int32_t *tokens, int T, Rows rm, int N, int *nxt,
+                                                     int *head) {
+  // the step's tokens pass through LDS in chunks; every lane of a wave reads
+  // the same entry (a broadcast) while comparing it with its own row's token
+  constexpr int CH = 2048;
+  __shared__ int tl[CH];
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  const int tok = tokens[(int64_t)rm.seq(n) * T + rm.pos(n)];
+  const int tok = n < N ? tokens[(int64_t)rm.seq(n) * T + rm.pos(n)] : 0;
   int first = 1, next = -1;
-  for (int m = 0; m < N; ++m) {
-    const int t2 = tokens[(int64_t)rm.seq(m) * T + rm.pos(m)];
-    if (t2 != tok) continue;
-    if (m < n) first = 0;
-    if (m > n && next < 0) next = m;
+  for (int m0 = 0; m0 < N; m0 += CH) {
+    const int cnt = min(CH, N - m0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) tl[i] = tokens[(int64_t)rm.seq(m0 + i) * T + rm.pos(m0 + i)];
+    __syncthreads();
+    for (int i = 0; i < cnt; ++i) {
+      const int m = m0 + i;
+      if (tl[i] != tok) continue;
+      if (m < n) first = 0;
+      if (m > n && next < 0) next = m;
+    }
   }
-  nxt[n] = next;
-  head[n] = first;
+  if (n < N) {
+    nxt[n] = next;
+    head[n] = first;
+  }
 }
 // dE[token] += sum of dh over the token's chain, in row order (one block per
 // chain head; ids outside [0, V) are skipped: their rows are NaN already)
@@ -1369,7 +1381,7 @@ struct Trainer {
       TR_TRY(add(dh, P(o.dS) + l * nd, nd));
     }
     int *nxt = (int *)P(o.enext), *head = (int *)P(o.ehead);
-    hipLaunchKernelGGL(k_embed_chains, dim3((N + 255) / 256), dim3(256), 0, s, tokens, T, rm, N, nxt, head);
+    hipLaunchKernelGGL(k_embed_chains, dim3((N + 63) / 64), dim3(64), 0, s, tokens, T, rm, N, nxt, head);
     TR_TRY(hipGetLastError());
     hipLaunchKernelGGL(k_embed_bwd, dim3(N), dim3(256), 0, s, tokens, T, rm, dh, nxt, head, gr.embed, D, V);
     TR_TRY(hipGetLastError());
