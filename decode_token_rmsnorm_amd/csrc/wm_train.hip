@@ -285,6 +285,28 @@ __global__ __launch_bounds__(64) void k_rms(const float *x, const float *gain, i
   for (int c = lane; c < D; c += 64) y[(int64_t)r * D + c] = xr[c] * rs * g[c];
   if (lane == 0) rinv[r] = rs;
 }
+// k_rms of x = sum over the splits (in order) of part[s] (+ beta * Cin),
+// the rows of a split-k product whose sum was left to this kernel; x is
+// stored too (exactly what k_split_sum would have written).  part[s] holds
+// the rows at s * ps.
+__global__ __launch_bounds__(64) void k_rms_parts(const float *part, int splits, int64_t ps, const float *Cin,
+                                                  float beta, float *x, const float *gain, int rpg, float *y,
+                                                  float *rinv, int D, float eps) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const int64_t ro = (int64_t)r * D;
+  float ss = 0.f;
+  for (int c = lane; c < D; c += 64) {
+    float t = 0.f;
+    for (int sp = 0; sp < splits; ++sp) t += part[sp * ps + ro + c];
+    if (beta != 0.f) t = t + beta * Cin[ro + c];
+    x[ro + c] = t;
+    ss += t * t;
+  }
+  const float rs = 1.f / sqrtf(wave_sum(ss) / D + eps);
+  const float *g = gain + (int64_t)(r / rpg) * D;
+  for (int c = lane; c < D; c += 64) y[ro + c] = x[ro + c] * rs * g[c];  // (this lane's own stores)
+  if (lane == 0) rinv[r] = rs;
+}
 // dx (+)= r * (g dy) - x r^3 sum(g dy x) / D
 __global__ __launch_bounds__(64) void k_rms_bwd(const float *x, const float *gain, int rpg, const float *rinv,
                                                 const float *dy, float *dx, int accumulate, int D) {
@@ -1061,6 +1083,16 @@ inline Ws layout(const wm_config &c, int B, int T, int g, int n_grad, bool tapes
   return w;
 }
 
+// A split-k product whose partial sum was left to the consumer of its rows:
+// C = sum over the splits of the partials (ps floats apart) + beta * Cin.
+struct Pending {
+  int splits = 1;  // (1: nothing pending)
+  int64_t ps = 0;
+  float *C = nullptr;
+  const float *Cin = nullptr;
+  float beta = 0.f;
+};
+
 struct Trainer {
   const wm_config &c;
   const wm_weights &w;
@@ -1106,7 +1138,8 @@ struct Trainer {
   // workspace, summed in split order.
   hipError_t gemm(bool ta, bool tb, const float *A, int64_t lda, const float *B_, int64_t ldb, float *C, int64_t ldc,
                   int M, int N, int K, float beta, int Z = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0,
-                  const float *Cin = nullptr) {
+                  const float *Cin = nullptr, Pending *defer = nullptr) {
+    if (defer) *defer = Pending{};
     if (M <= 0 || N <= 0) return hipSuccess;
     const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * Z;
     int splits = 1;
@@ -1138,12 +1171,25 @@ struct Trainer {
                          1.f, bd, splits, kchunk, va, vb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
+    if (defer && Z == 1 && ldc == N) {  // (the sum is left to the rows' consumer: rms_in)
+      *defer = Pending{splits, (int64_t)M * N, C, Cr, beta};
+      return hipSuccess;
+    }
     const int64_t total = (int64_t)M * N * Z;
     hipLaunchKernelGGL(k_split_sum, dim3(grid1(total)), dim3(256), 0, s, P(o.split), splits, C, Cr, ldc, sC, M, N, Z, beta);
     return hipGetLastError();
   }
   hipError_t rms(const float *x, const float *gain, int rpg, float *y, float *rinv, int rows, int width) {
     hipLaunchKernelGGL(k_rms, dim3(rows), dim3(64), 0, s, x, gain, rpg, y, rinv, width, c.eps);
+    return hipGetLastError();
+  }
+  // rms of x, or, when x's split-k sum was left pending, of that sum (which
+  // is also written to x: pd.C == x)
+  hipError_t rms_in(const Pending &pd, const float *x, const float *gain, int rpg, float *y, float *rinv, int rows,
+                    int width) {
+    if (pd.splits <= 1) return rms(x, gain, rpg, y, rinv, rows, width);
+    hipLaunchKernelGGL(k_rms_parts, dim3(rows), dim3(64), 0, s, P(o.split), pd.splits, pd.ps, pd.Cin, pd.beta, pd.C,
+                       gain, rpg, y, rinv, width, c.eps);
     return hipGetLastError();
   }
   // dx (+)= RMSNorm backward; dgain (ngain rows of width) += its gain gradient
@@ -1245,27 +1291,32 @@ struct Trainer {
     const float scale = 1.f / sqrtf((float)c.d);
     hipLaunchKernelGGL(k_embed, dim3(N), dim3(256), 0, s, tokens, T, rm, W(w.embed), P(o.S), N, D, V);
     TR_TRY(hipGetLastError());
+    // (split-k sums of Q, O and down are left to the RMSNorm that reads them)
+    Pending pd;
     for (int l = 0; l < L; ++l) {
       const size_t nd = (size_t)N * D, nq = (size_t)N * QD, nf = (size_t)N * F;
       float *S = P(o.S) + l * nd, *a = P(o.a) + l * nd, *qraw = P(o.qraw) + l * nq, *q = P(o.q) + l * nq;
       float *out = P(o.o) + l * nq, *h1 = P(o.h1) + l * nd, *bn = P(o.bn) + l * nd;
       float *G = P(o.G) + l * nf, *U = P(o.U) + l * nf, *act = P(o.act) + l * nf;
-      TR_TRY(rms(S, w.attn_norm + (size_t)l * D, N, a, P(o.rA) + (size_t)l * N, N, D));
-      TR_TRY(gemm(false, true, a, D, W(w.wq) + (size_t)l * QD * D, D, qraw, QD, N, QD, D, 0.f));
-      TR_TRY(rms(qraw, w.q_norm + (size_t)l * c.d, N * c.Hq, q, P(o.rQ) + (size_t)l * N * c.Hq, N * c.Hq, c.d));
+      TR_TRY(rms_in(pd, S, w.attn_norm + (size_t)l * D, N, a, P(o.rA) + (size_t)l * N, N, D));
+      TR_TRY(gemm(false, true, a, D, W(w.wq) + (size_t)l * QD * D, D, qraw, QD, N, QD, D, 0.f, 1, 0, 0, 0, nullptr,
+                  &pd));
+      TR_TRY(rms_in(pd, qraw, w.q_norm + (size_t)l * c.d, N * c.Hq, q, P(o.rQ) + (size_t)l * N * c.Hq, N * c.Hq,
+                    c.d));
       TR_TRY(rope(q, rm, N, N, c.Hq, false));
       const int ch = l % k;
       TR_TRY(attn_fwd(q, chanK(o.cK, ch), chanK(o.cV, ch), rm, N, scale, out, P(o.mst) + (size_t)l * N * c.Hq,
                       P(o.lst) + (size_t)l * N * c.Hq));
-      TR_TRY(gemm(false, true, out, QD, W(w.wo) + (size_t)l * D * QD, QD, h1, D, N, D, QD, 1.f, 1, 0, 0, 0, S));
-      TR_TRY(rms(h1, w.ffn_norm + (size_t)l * D, N, bn, P(o.rF) + (size_t)l * N, N, D));
+      TR_TRY(gemm(false, true, out, QD, W(w.wo) + (size_t)l * D * QD, QD, h1, D, N, D, QD, 1.f, 1, 0, 0, 0, S, &pd));
+      TR_TRY(rms_in(pd, h1, w.ffn_norm + (size_t)l * D, N, bn, P(o.rF) + (size_t)l * N, N, D));
       // gate and up in one launch (z = 0, 1: the two weight matrices and outputs)
       const float *Wg = W(w.w_gate) + (size_t)l * F * D, *Wu = W(w.w_up) + (size_t)l * F * D;
       TR_TRY(gemm(false, true, bn, D, Wg, D, G, F, N, F, D, 0.f, 2, 0, fdist(Wg, Wu), fdist(G, U)));
       hipLaunchKernelGGL(k_swiglu, dim3(grid1(nf)), dim3(256), 0, s, G, U, act, (int64_t)nf);
       TR_TRY(hipGetLastError());
       float *next = l + 1 < L ? P(o.S) + (l + 1) * nd : P(o.hL);
-      TR_TRY(gemm(false, true, act, F, W(w.w_down) + (size_t)l * D * F, F, next, D, N, D, F, 1.f, 1, 0, 0, 0, h1));
+      TR_TRY(gemm(false, true, act, F, W(w.w_down) + (size_t)l * D * F, F, next, D, N, D, F, 1.f, 1, 0, 0, 0, h1,
+                  l + 1 < L ? &pd : nullptr));
     }
     if (with_pool) {
       wm_status st = pool_fwd(0, rm, N);
