@@ -572,19 +572,18 @@ __global__ __launch_bounds__(64 * NWF) void k_attn(const float *q, const float *
 }
 
 // dq of row n, head h: dS_t = p_t (dP_t - Dn) with dP_t = dout . V_t and
-// Dn = sum_t p_t dP_t (equal to dout . out; summed from the same p_t dP_t
-// products, so that sum_t dS_t stays 0 to rounding also where the row has
-// few keys and dP_t and Dn nearly cancel); dq = scale * sum_t dS_t K_t.
-// Keeps Dn for the key-side kernel.  Blocks, waves and key tiles as in
-// k_attn; the tiles are walked twice (Dn first, merged over the waves in
-// wave order, then dS and dq^T = K^T dS^T), and the waves' dq are added in
-// wave order.
+// Dn = dout . out (out: the forward's attention output, which equals
+// sum_t p_t V_t, so Dn = sum_t p_t dP_t); dq = scale * sum_t dS_t K_t.  Keeps
+// Dn for the key-side kernel.  Blocks, waves and key tiles as in k_attn;
+// each wave walks its tiles once (S^T and dP^T, then dq^T = K^T dS^T) and
+// the waves' dq are added in wave order.
 template <int DH>
 __global__ __launch_bounds__(64 * NWF) void k_attn_dq(const float *q, const float *Kc, const float *Vc,
-                                                      const float *dout, const float *mst, const float *lst, Rows rm,
-                                                      int Hq, int Hkv, int Tc, float scale, float *dq, float *Dst) {
+                                                      const float *dout, const float *outf, const float *mst,
+                                                      const float *lst, Rows rm, int Hq, int Hkv, int Tc, float scale,
+                                                      float *dq, float *Dst) {
   constexpr int NT = DH / 16;
-  __shared__ float cD[NWF][ATQ], cg[NWF][DH][ATQ + 1];
+  __shared__ float cg[NWF][DH][ATQ + 1];
   const int pair = blockIdx.x, b = pair / Hkv, hk = pair - b * Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lj = lane >> 4;
   const int nslot = rm.M * G, sb = (gridDim.y - 1 - blockIdx.y) * ATQ;
@@ -592,11 +591,18 @@ __global__ __launch_bounds__(64 * NWF) void k_attn_dq(const float *q, const floa
   const Slot me = slot_of(sb + li, nslot, rm, b, hk, G, Hq);
   const float *K = Kc + ((int64_t)b * Hkv + hk) * Tc * DH, *V = Vc + ((int64_t)b * Hkv + hk) * Tc * DH;
   f32x4 qf[NT], df[NT];
+  float Dp = 0.f;  // (the lane's dims of dout . out; summed over the lane groups below)
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    qf[t] = me.act ? *(const f32x4 *)&q[me.so * DH + 16 * t + 4 * lj] : f32x4{0.f, 0.f, 0.f, 0.f};
-    df[t] = me.act ? *(const f32x4 *)&dout[me.so * DH + 16 * t + 4 * lj] : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    qf[t] = me.act ? *(const f32x4 *)&q[me.so * DH + 16 * t + 4 * lj] : z;
+    df[t] = me.act ? *(const f32x4 *)&dout[me.so * DH + 16 * t + 4 * lj] : z;
+    const f32x4 of = me.act ? *(const f32x4 *)&outf[me.so * DH + 16 * t + 4 * lj] : z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Dp = fmaf(df[t][e], of[e], Dp);
   }
+  Dp += __shfl_xor(Dp, 16);
+  const float Dn = Dp + __shfl_xor(Dp, 32);
   const float mrow = me.act ? mst[me.so] : 0.f, lr = me.act ? lst[me.so] : 0.f, invl = lr > 0.f ? 1.f / lr : 0.f;
   // a tile's K and V rows k0 + li as A operands (16-byte runs), loaded one
   // tile ahead
@@ -609,47 +615,10 @@ __global__ __launch_bounds__(64 * NWF) void k_attn_dq(const float *q, const floa
       vn[t] = *(const f32x4 *)&V[(int64_t)kr * DH + 16 * t + 4 * lj];
     }
   };
-  // p and dP of keys k0 + 4 lj + e for the lane's slot (0 past its position)
-  auto tile = [&](int k0, const f32x4 (&kf)[NT], const f32x4 (&vf)[NT], float (&p)[4], f32x4 &dP) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    dP = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s = mf4(kf[t][e], qf[t][e], s);    // S^T = K q^T
-        dP = mf4(vf[t][e], df[t][e], dP);  // dP^T = V dout^T
-      }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = k0 + 4 * lj + e < me.ipos ? expf(s[e] * scale - mrow) * invl : 0.f;
-  };
-  float Dp = 0.f;
-  if (16 * wave < imax) fetch(16 * wave);
-  for (int k0 = 16 * wave; k0 < imax; k0 += 16 * NWF) {
-    f32x4 kf[NT], vf[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      kf[t] = kn[t];
-      vf[t] = vn[t];
-    }
-    if (k0 + 16 * NWF < imax) fetch(k0 + 16 * NWF);
-    float p[4];
-    f32x4 dP;
-    tile(k0, kf, vf, p, dP);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Dp = fmaf(p[e], dP[e], Dp);
-  }
-  Dp += __shfl_xor(Dp, 16);
-  Dp += __shfl_xor(Dp, 32);
-  if (lj == 0) cD[wave][li] = Dp;
-  if (16 * wave < imax) fetch(16 * wave);
-  __syncthreads();
-  float Dn = 0.f;
-#pragma unroll
-  for (int w = 0; w < NWF; ++w) Dn += cD[w][li];
   f32x4 g[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (16 * wave < imax) fetch(16 * wave);
   for (int k0 = 16 * wave; k0 < imax; k0 += 16 * NWF) {
     // K rows k0 + 4 lj + e as the A operand of dq^T (used after the S and dP products)
     float kt[NT][4];
@@ -666,12 +635,18 @@ __global__ __launch_bounds__(64 * NWF) void k_attn_dq(const float *q, const floa
       vf[t] = vn[t];
     }
     if (k0 + 16 * NWF < imax) fetch(k0 + 16 * NWF);
-    float p[4];
-    f32x4 dP;
-    tile(k0, kf, vf, p, dP);
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc = mf4(kf[t][e], qf[t][e], sc);  // S^T = K q^T
+        dP = mf4(vf[t][e], df[t][e], dP);  // dP^T = V dout^T
+      }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float dS = p[e] * (dP[e] - Dn);
+      const float p = k0 + 4 * lj + e < me.ipos ? expf(sc[e] * scale - mrow) * invl : 0.f;
+      const float dS = p * (dP[e] - Dn);
 #pragma unroll
       for (int i = 0; i < NT; ++i) g[i] = mf4(kt[i][e], dS, g[i]);  // dq^T += K^T dS^T
     }
@@ -685,15 +660,12 @@ __global__ __launch_bounds__(64 * NWF) void k_attn_dq(const float *q, const floa
     const int sl = x / DH, d = x - sl * DH;
     const Slot r = slot_of(sb + sl, nslot, rm, b, hk, G, Hq);
     if (!r.act) continue;
-    float gs = 0.f, Ds = 0.f;
+    float gs = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWF; ++w) {
-      gs += cg[w][d][sl];
-      Ds += cD[w][sl];
-    }
+    for (int w = 0; w < NWF; ++w) gs += cg[w][d][sl];
     dq[r.so * DH + d] = gs * scale;
-    if (d == 0) Dst[r.so] = Ds;
   }
+  if (wave == 0 && lj == 0 && me.act) Dst[me.so] = Dn;
 }
 
 // dK_t += scale * sum dS q, dV_t += sum p dout over the rows n of sequence b
@@ -1244,18 +1216,18 @@ struct Trainer {
                          scale, dK, dV);
     return hipGetLastError();
   }
-  hipError_t attn_dq(const float *q, const float *K, const float *Vv, const float *dout, const float *mst,
-                     const float *lst, Rows rm, int N, float scale, float *dq, float *Dst) {
+  hipError_t attn_dq(const float *q, const float *K, const float *Vv, const float *dout, const float *outf,
+                     const float *mst, const float *lst, Rows rm, int N, float scale, float *dq, float *Dst) {
     dim3 grid(B * c.Hkv, (rm.M * (c.Hq / c.Hkv) + ATQ - 1) / ATQ);
     if (c.d == 32)
-      hipLaunchKernelGGL(k_attn_dq<32>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
+      hipLaunchKernelGGL(k_attn_dq<32>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, outf, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
                          Dst);
     else if (c.d == 64)
-      hipLaunchKernelGGL(k_attn_dq<64>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
+      hipLaunchKernelGGL(k_attn_dq<64>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, outf, mst, lst, rm, c.Hq, c.Hkv, T, scale, dq,
                          Dst);
     else
-      hipLaunchKernelGGL(k_attn_dq<128>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, mst, lst, rm, c.Hq, c.Hkv, T, scale,
-                         dq, Dst);
+      hipLaunchKernelGGL(k_attn_dq<128>, grid, dim3(64 * NWF), 0, s, q, K, Vv, dout, outf, mst, lst, rm, c.Hq, c.Hkv, T,
+                         scale, dq, Dst);
     return hipGetLastError();
   }
 
@@ -1417,7 +1389,8 @@ struct Trainer {
       TR_TRY(gemm(false, false, dh, D, W(w.wo) + (size_t)l * D * QD, QD, P(o.dout), QD, N, QD, D, 0.f));
       TR_TRY(gemm(true, false, dh, D, out, QD, gr.wo + (size_t)l * D * QD, QD, D, QD, N, 1.f));
       const int ch = l % k;
-      TR_TRY(attn_dq(q, chanK(o.cK, ch), chanK(o.cV, ch), P(o.dout), mst, lst, rm, N, scale, P(o.dq), P(o.Dst)));
+      TR_TRY(attn_dq(q, chanK(o.cK, ch), chanK(o.cV, ch), P(o.dout), out, mst, lst, rm, N, scale, P(o.dq),
+                     P(o.Dst)));
       TR_TRY(attn_dkv(q, chanK(o.cK, ch), chanK(o.cV, ch), P(o.dout), mst, lst, P(o.Dst), rm, scale,
                       chanK(o.dK, ch), chanK(o.dV, ch)));
       TR_TRY(rope(P(o.dq), rm, N, N, c.Hq, true));
