@@ -9,6 +9,7 @@
 #include "wm_few.hpp"
 #include "wm_attn2.hpp"
 #include "wm_pool2.hpp"
+#include "wm_kvs.hpp"
 
 #include <mutex>
 #include <type_traits>
@@ -116,6 +117,9 @@ template <typename T> struct Run {
   // The 256 x 256 kernel (bf16 only) for steps with enough rows to fill the chip.
   static constexpr bool kBig = std::is_same<T, bf16>::value;
   bool big(int M) const { return kBig && M >= 2048; }
+  // rows from which the pool's width-512 K/V projection streams past a
+  // register-held matrix (below, the tiled kernels)
+  static constexpr int kKvsMinRows = 256;
   // column tile of the residual products on M rows
   int resid_bn(int M, int N) const { return big(M) ? g2_resid_bn(M, N, kComputeUnits) : GN; }
   // partial sums of squares per row written by a residual epilogue on M rows
@@ -394,6 +398,15 @@ template <typename T> struct Run {
                 cache->B, c.Hkv, c.T_max, c.d, rows, c.eps, rowpos(ts)};
     ProfScope prof(WM_K_KVPROJ, s);
     if constexpr (kBig) {
+      if (c.D == KVS_D && c.d == KVS_HD && c.Hkv * c.d == KVS_N && rows >= kKvsMinRows) {
+        // width 512, 4 KV heads of 64: the matrix stays in registers
+        // and the mixed rows stream past it (wm_kvs.hpp)
+        const int P = kvs_blocks_per_channel(2 * c.k);
+        hipLaunchKernelGGL(kv_stream, dim3(2 * c.k * P), dim3(512), 0, s, (const bf16 *)at<T>(lay.mb),
+                           (const bf16 *)w->wk, (const bf16 *)w->wv, pe, rows, P);
+        WM_TRY(hipGetLastError());
+        return WM_OK;
+      }
       if (big(rows)) {
         PRows<T> a2{at<T>(lay.mb), c.D, (int64_t)rows * c.D, rows};
         PKV<T> b2{(const T *)w->wk, (const T *)w->wv, c.D, (int64_t)c.Hkv * c.d * c.D, c.k, c.Hkv * c.d};

@@ -150,6 +150,8 @@ def test_mix_kv_matches_oracle(name, B, M, s0, step):
 @pytest.mark.parametrize("B,M", [
     (1, 127), (2, 64), (3, 43),         # 127, 128, 129 rows: the few-row router and projection and past them
     (23, 89), (16, 128), (3, 683),      # 2047, 2048, 2049 rows: the 128x128 and the 256x256 tile GEMMs
+    (1, 255), (2, 128), (1, 257),       # 255, 256, 257 rows: the tiled projection and the streamed one
+    (5, 61),                            # 305 rows: 10 chunks of 32 rows for 16 blocks per channel, the last ragged
 ])
 def test_mix_kv_row_count_boundaries(B, M):
     """Row counts on both sides of the library's kernel switches (bf16)."""
