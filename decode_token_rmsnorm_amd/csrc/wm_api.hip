@@ -288,10 +288,13 @@ template <typename T> struct Run {
                            ro.az, ro.ab, ro.ar, w->src_norm, sgb, cg0, cgb, at<T>(lay.mb), at<float>(lay.rinvM), rows,
                            LL, kk, c.D, c.eps);
       };
+      // (up to kFewRows rows: one row per block)
+      const bool one = rows <= kFewRows;
       if (kk <= 8 && LL <= 16)  // both branches' channels in one MFMA
-        go(pool_mix2<1, 16, true>, PM_RTPB);
+        one ? go(pool_mix2<1, 16, true, 1>, 1) : go(pool_mix2<1, 16, true>, PM_RTPB);
       else if (kk <= 16)
-        LL <= 16 ? go(pool_mix2<1, 16>, PM_RT4) : go(pool_mix2<1, 32>, PM_RT4);
+        one ? (LL <= 16 ? go(pool_mix2<1, 16, false, 1>, 1) : go(pool_mix2<1, 32, false, 1>, 1))
+            : (LL <= 16 ? go(pool_mix2<1, 16>, PM_RT4) : go(pool_mix2<1, 32>, PM_RT4));
       else
         LL <= 16 ? go(pool_mix2<2, 16>, PM_RT4 / 2) : go(pool_mix2<2, 32>, PM_RT4 / 2);
     } else {
@@ -481,10 +484,14 @@ template <typename T> struct Run {
     const T *wq = (const T *)w->wq, *wo = (const T *)w->wo, *wg = (const T *)w->w_gate, *wu = (const T *)w->w_up,
             *wd = (const T *)w->w_down;
     const RowPos rp = rowpos(ts);
+    // (the LM head's row lists are written by the embedding launch)
+    const int nlog = logit_mode == 1 ? ts.B : rows;
+    int *rin = at<int>(lay.rowmap), *rout = rin + rows;
+    const RowMap rmap{logit_mode ? rin : nullptr, rout, nlog, logit_mode, m_sel, Tseq, ts.s0, ts.s_step};
     {
     ProfScope prof(WM_K_EMBED, s);
     hipLaunchKernelGGL((embed_rows<T>), dim3(rows), dim3(256), 0, s, tokens, (const T *)w->embed, w->attn_norm, h, hb,
-                       S, ss, ts.M, tstride, toff, tstep, c.V, D);
+                       S, ss, ts.M, tstride, toff, tstep, c.V, D, rmap);
     WM_TRY(hipGetLastError());
     }
     int nparts = 1;
@@ -579,11 +586,7 @@ template <typename T> struct Run {
       if (st != WM_OK) return st;
     }
     if (logit_mode) {
-      int n = logit_mode == 1 ? ts.B : rows;
-      int *rin = at<int>(lay.rowmap), *rout = rin + rows;
-      hipLaunchKernelGGL(fill_rowmap, dim3((n + 255) / 256), dim3(256), 0, s, rin, rout, n, logit_mode, ts.M, m_sel, Tseq,
-                         ts.s0, ts.s_step);
-      WM_TRY(hipGetLastError());
+      const int n = nlog;
       LoadRows<T> a{hb, D, 0, rin};
       BRows<T> b{LoadRows<T>{(const T *)w->lm_head, D, 0, nullptr}};
       EpiStoreF32 e{logits, c.V, 0, rout, ss, rin, nparts, invD, c.eps};

@@ -13,7 +13,6 @@
 //  embed_rows   h_0 = E[token] (+ the first state, the next GEMM's operand and
 //               its sum of squares)
 //  rope_table   cos/sin of s * base^(-2m/d), double precision, rounded
-//  fill_rowmap  gather/scatter row lists of the LM head
 #pragma once
 
 #include "wm_common.hpp"
@@ -184,11 +183,30 @@ __global__ __launch_bounds__(256) void router_input(const T *S, const float *rin
 // h = E[tok] (fp32), S0 = E[tok], hb = E[tok] * gain, and the row's sum of
 // squares (one part).  A token id outside [0, V) reads nothing and makes the
 // row NaN, so the error shows in everything computed from it.
+// Gather/scatter row lists of the LM head, n entries (rows_in null: none):
+// mode 1: rows_in[b] = b*M + m_sel, rows_out[b] = b;
+// mode 2: rows_in[r] = r, rows_out[r] = b*T + s0 + m*step (r = b*M + m).
+struct RowMap {
+  int *rows_in, *rows_out;
+  int n, mode, m_sel, T, s0, step;
+  __device__ __forceinline__ void fill(int i, int M) const {
+    if (mode == 1) {
+      rows_in[i] = i * M + m_sel;
+      rows_out[i] = i;
+    } else {
+      const int b = i / M, m = i - b * M;
+      rows_in[i] = i;
+      rows_out[i] = b * T + s0 + m * step;
+    }
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void embed_rows(const int32_t *tokens, const T *E, const float *gain, float *h, T *hb,
                                                   T *S0, float *ss, int M, int tstride, int toff, int tstep, int V,
-                                                  int D) {
+                                                  int D, RowMap map) {
   const int r = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0 && map.rows_in && r < map.n) map.fill(r, M);
   const int b = r / M, m = r - b * M;
   const int tok = tokens[(int64_t)b * tstride + toff + (int64_t)m * tstep];
   const bool valid = tok >= 0 && tok < V;
@@ -217,19 +235,5 @@ __global__ void rope_table(float *cosT, float *sinT, int T_max, int half, double
   sinT[i] = (float)sin(ang);
 }
 
-// mode 1: rows_in[b] = b*M + m_sel, rows_out[b] = b
-// mode 2: rows_in[r] = r, rows_out[r] = b*T + s0 + m*step
-__global__ void fill_rowmap(int *rows_in, int *rows_out, int n, int mode, int M, int m_sel, int T, int s0, int step) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  if (mode == 1) {
-    rows_in[i] = i * M + m_sel;
-    rows_out[i] = i;
-  } else {
-    int b = i / M, m = i - b * M;
-    rows_in[i] = i;
-    rows_out[i] = b * T + s0 + m * step;
-  }
-}
 
 }  // namespace wm

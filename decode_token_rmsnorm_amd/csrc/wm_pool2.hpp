@@ -42,14 +42,16 @@ constexpr int PM_SP = 96;   // staged row pitch (elements): 64 columns + 64 byte
 // S [L, rows, D]; mb [2, k, rows, D]; rinvM [2, k, rows].
 // (gains: src_gain (beta, l, c) at beta*sgb + l*D + c, chan_gain (beta, j, c)
 // at beta*cgb + j*D + c)
-template <int KB, int LMAX, bool PB = false>
+template <int KB, int LMAX, bool PB = false, int RT = 0>
 __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *rinvS, const float *A, int Z,
                                                  int64_t zstride, int64_t bstride, int64_t rstride,
                                                  const float *src_gain, int64_t sgb, const float *chan_gain,
                                                  int64_t cgb, bf16 *mb, float *rinvM, int rows, int L, int k, int D,
                                                  float eps) {
   static_assert(!PB || (KB == 1 && LMAX == 16), "branches share an MFMA only for k <= 8 and L <= 16");
-  constexpr int PM_RT = PB ? PM_RTPB : PM_RT4 / KB;    // token rows per block
+  // token rows per block (RT > 0: set by the caller, one row for the few-row
+  // steps of decoding, whose 64 rows would otherwise fill only 16 blocks)
+  constexpr int PM_RT = RT > 0 ? RT : PB ? PM_RTPB : PM_RT4 / KB;
   constexpr int NB = PB ? 1 : 2;                       // MFMA A operands per row and channel block
   constexpr int CH = PB ? 8 : 16 * KB;                 // staged output channels per branch and row
   constexpr int NPT = (PM_RT * LMAX * 8 + 255) / 256;  // 16-byte pieces per thread and chunk (L <= LMAX)
