@@ -334,16 +334,11 @@ template <typename T> struct Run {
       ro = RouterOut{1, 0, Lk, 0};
       Amix = w->static_mix;
     } else if (rows <= kFewRows) {
-      // few rows: per-branch gained router input and the few-row GEMM, Z = branch
-      {
-        ProfScope prof(WM_K_MIX, s);
-        hipLaunchKernelGGL((state_rinv<T>), dim3((unsigned)((nl + 3) / 4)), dim3(256), 0, s, S, at<float>(lay.rinvS),
-                           nl, c.D, c.eps);
-        WM_TRY(hipGetLastError());
-      }
+      // few rows: row scales and per-branch gained router input in one launch,
+      // then the few-row GEMM, Z = branch
       ProfScope prof(WM_K_ROUTER, s);
-      hipLaunchKernelGGL((router_input<T>), dim3(rows, 2), dim3(256), 0, s, S, at<float>(lay.rinvS), w->src_norm,
-                         at<T>(lay.u), rows, c.L, c.p, R, c.D, 0, R);
+      hipLaunchKernelGGL((rinv_router_input<T>), dim3(rows, 2), dim3(256), 0, s, S, at<float>(lay.rinvS), w->src_norm,
+                         at<T>(lay.u), rows, c.L, c.p, R, c.D, c.eps);
       WM_TRY(hipGetLastError());
       LoadRows<T> ua{at<T>(lay.u), RD, (int64_t)rows * RD, nullptr};
       BRows<T> rb{LoadRows<T>{(const T *)w->router, RD, (int64_t)Lk * RD, nullptr}};

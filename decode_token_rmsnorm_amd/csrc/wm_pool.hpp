@@ -7,11 +7,13 @@
 //               stores rho_j (.) m_j (channel gain folded in; the channel's
 //               1/rms is applied after the projection, which is linear) and
 //               1/rms(m_j) for the projection epilogue.
-//  router_input the router's normalised input rows, written out (few rows)
+//  router_input the router's normalised input rows, written out (the
+//               feedback-free variant's channel steps)
+//  rinv_router_input  state_rinv and router_input in one launch (few rows)
 //  state_rinv_u state_rinv plus the normalised router-layer rows (many rows)
 //  fold_router  router weights times the source gains
 //  embed_rows   h_0 = E[token] (+ the first state, the next GEMM's operand and
-//               its sum of squares)
+//               its sum of squares, and the LM head's row lists)
 //  rope_table   cos/sin of s * base^(-2m/d), double precision, rounded
 #pragma once
 
@@ -179,10 +181,6 @@ __global__ __launch_bounds__(256) void router_input(const T *S, const float *rin
   }
 }
 
-// Row r = b*M + m reads token tokens[b*tstride + toff + m*tstep].  Writes
-// h = E[tok] (fp32), S0 = E[tok], hb = E[tok] * gain, and the row's sum of
-// squares (one part).  A token id outside [0, V) reads nothing and makes the
-// row NaN, so the error shows in everything computed from it.
 // Gather/scatter row lists of the LM head, n entries (rows_in null: none):
 // mode 1: rows_in[b] = b*M + m_sel, rows_out[b] = b;
 // mode 2: rows_in[r] = r, rows_out[r] = b*T + s0 + m*step (r = b*M + m).
@@ -201,6 +199,53 @@ struct RowMap {
   }
 };
 
+// state_rinv and router_input in one launch for steps of few rows: block
+// (r, beta) computes the row scales of all L states of row r (the same wave
+// sums as state_rinv; the beta = 0 block stores them), then writes the row's
+// gained router input of branch beta.
+template <typename T>
+__global__ __launch_bounds__(256) void rinv_router_input(const T *S, float *rinvS, const float *gain, T *u, int rows,
+                                                         int L, int p, int R, int D, float eps) {
+  constexpr int E = Elt<T>::E16;
+  const int r = blockIdx.x, beta = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float rs[32];  // (L <= 32)
+  for (int l = wave; l < L; l += 4) {
+    const T *x = S + ((int64_t)l * rows + r) * D;
+    float s = 0.f;
+    for (int c = lane * E; c < D; c += 64 * E) {
+      float f[E];
+      unpack16<T>(*(const u32x4 *)(x + c), f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += f[e] * f[e];
+    }
+    s = wave_sum(s);
+    const float v = rsqrtf(s / D + eps);
+    if (lane == 0) {
+      rs[l] = v;
+      if (beta == 0) rinvS[(int64_t)l * rows + r] = v;
+    }
+  }
+  __syncthreads();
+  for (int b = 0; b < R; ++b) {
+    const int l = b * p;
+    const float s = rs[l];
+    const T *src = S + ((int64_t)l * rows + r) * D;
+    const float *g = gain + ((int64_t)beta * L + l) * D;
+    T *dst = u + ((int64_t)beta * rows + r) * R * D + (int64_t)b * D;
+    for (int c = threadIdx.x * E; c < D; c += 256 * E) {
+      float f[E];
+      unpack16<T>(*(const u32x4 *)(src + c), f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] *= s * g[c + e];
+      *(u32x4 *)(dst + c) = pack16<T>(f);
+    }
+  }
+}
+
+// Row r = b*M + m reads token tokens[b*tstride + toff + m*tstep].  Writes
+// h = E[tok] (fp32), S0 = E[tok], hb = E[tok] * gain, and the row's sum of
+// squares (one part).  A token id outside [0, V) reads nothing and makes the
+// row NaN, so the error shows in everything computed from it.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_rows(const int32_t *tokens, const T *E, const float *gain, float *h, T *hb,
                                                   T *S0, float *ss, int M, int tstride, int toff, int tstep, int V,
