@@ -451,9 +451,18 @@ template <typename T, int TN, int TR, class AL, class BL, class EP>
 hipError_t launch_few_tn(const AL &al, const BL &bl, const EP &ep, int M, int N, int K, int Z, hipStream_t s) {
   constexpr int ROWS = FewCfg<TN, TR>::ROWS;
   const int nks = (int)((int64_t)K * (int64_t)sizeof(T) / 64);
-  dim3 grid((N + TN - 1) / TN, (M + ROWS - 1) / ROWS, Z);
-  const int nw = few_waves<TN, TR, FewEpi<EP, T, TN, ROWS>::NT>(nks);
-  hipLaunchKernelGGL((gemm_few<T, TN, TR, AL, BL, EP>), grid, dim3(64 * nw), 0, s, al, few_bind(bl, TN), ep, M, N, K);
+  const int nX = (N + TN - 1) / TN, nY = (M + ROWS - 1) / ROWS;
+  int nw = few_waves<TN, TR, FewEpi<EP, T, TN, ROWS>::NT>(nks);
+  // more blocks than compute units: the fewest waves the epilogue allows, so
+  // that more blocks are resident at once (at 8 waves, blocks whose
+  // registers admit 12 waves per CU run one per CU; the 1.3B-shape decode's
+  // gate/up product, 608 blocks: 37.5 -> 34.3 us)
+  {
+    constexpr int NT = FewEpi<EP, T, TN, ROWS>::NT, lo = NT / 64 > 4 ? NT / 64 : 4;
+    if ((int64_t)nX * nY * Z > 256 && nw > lo) nw = lo;
+  }
+  hipLaunchKernelGGL((gemm_few<T, TN, TR, AL, BL, EP>), dim3(nX, nY, Z), dim3(64 * nw), 0, s, al, few_bind(bl, TN), ep,
+                     M, N, K);
   return hipGetLastError();
 }
 
