@@ -464,6 +464,30 @@ def test_decode_deep_shape_fp32(B):             # 129: the many-row pool (folded
     assert np.isnan(np_of(cache.k)[:, :, :, t + 1:]).all()
 
 
+def test_decode_1p3b_widths_fp32():
+    """A decode step of 64 sequences at the 1.3B widths (two layers): its
+    gate/up product has more few-row blocks than compute units (608), so the
+    blocks run with fewer waves, each taking a longer k range."""
+    w = WORKLOADS["prefill_1p3b"].replace(L=2, k=2, p=1, B=64, T_max=64, dtype="f32")
+    t = 40
+    print(f"decode fp32 1.3B widths L2 B64 t={t}", flush=True)
+    W = make_weights(w, seed=0, gains="perturbed")
+    K, V = make_cache(w, w.B, filled=t, seed=3, poison=True)
+    tokens = make_tokens(w, seed=1, B=w.B, T=1)[:, 0]
+    model = gpu_model(w, W)
+    cache = wm.cache_from_host(model, K, V)
+    lg = wm.decode_step(model, torch.from_numpy(tokens).to(DEV), t, cache)
+    torch.cuda.synchronize()
+    ref = (np.nan_to_num(K, nan=0.0).astype(np.float64), np.nan_to_num(V, nan=0.0).astype(np.float64))
+    rl = O.decode_step(O.Model(w, W), tokens, t, ref)
+    el = max_abs_rel(np_of(lg), rl)
+    ek = max_abs_rel(np_of(cache.k)[:, :, :, t], ref[0][:, :, :, t])
+    ev = max_abs_rel(np_of(cache.v)[:, :, :, t], ref[1][:, :, :, t])
+    print(f"decode fp32 1.3B widths: logits {el:.2e} K {ek:.2e} V {ev:.2e}", flush=True)
+    assert max(el, ek, ev) <= TOL["f32"]
+    assert np.isnan(np_of(cache.k)[:, :, :, t + 1:]).all()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_first_position(dtype):
     """A decode step at t = 0: no key to attend to (attention gives 0), slot 0
