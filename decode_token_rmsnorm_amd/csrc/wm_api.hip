@@ -497,10 +497,22 @@ template <typename T> struct Run {
         BRows<T> b{LoadRows<T>{wq + (int64_t)l * QD * D, D, 0, nullptr}};
         EpiQ<T> e{q, ss, nparts, invD, c.eps, w->q_norm + (int64_t)l * c.d, w->rope_cos, w->rope_sin, c.d, rp};
         ProfScope prof(WM_K_QPROJ, s);
-        if (big(rows))
+        if (big(rows)) {
           WM_TRY(gemm2_rows(hb, D, wq + (int64_t)l * QD * D, D, e, rows, QD, D));
-        else
+        } else if (rows <= kFewRows && c.d == 128) {
+          // (128-dim heads, few rows: the product on narrow tiles into a raw
+          // buffer, then the q epilogue; the attention partials' region is
+          // free until the attention below)
+          float *qraw = at<float>(lay.part_o);
+          EpiStoreF32 er{qraw, QD, 0, nullptr, nullptr, nullptr, 0, 0.f, 0.f};
+          WM_TRY((gemm_s(a, b, er, rows, QD, D)));
+          hipLaunchKernelGGL((q_epi128<T>), dim3((unsigned)((rows * c.Hq + 3) / 4)), dim3(256), 0, s, qraw, q, ss,
+                             nparts, invD, c.eps, w->q_norm + (int64_t)l * c.d, w->rope_cos, w->rope_sin, rp, rows,
+                             c.Hq);
+          WM_TRY(hipGetLastError());
+        } else {
           WM_TRY((gemm_s(a, b, e, rows, QD, D)));
+        }
       }
       if (vanilla) {
         // K/V of the step's rows for layer l, written before the attention

@@ -182,6 +182,30 @@ template <typename T, int TN, int ROWS> struct FewEpi<EpiQ<T>, T, TN, ROWS> {
   }
 };
 
+// The q epilogue on its own, for few-row Q products with 128-dim heads, whose
+// fused form (one 128-column head per block) leaves most compute units idle
+// at the 1.3B widths (14 column tiles): the product then runs on narrow tiles
+// into a raw fp32 buffer C [rows, Hq*d], and one wave per (row, head) applies
+// q = RoPE(RMSNorm_head(rinv_row * C; q_norm)), two elements per lane.
+template <typename T>
+__global__ __launch_bounds__(256) void q_epi128(const float *C, T *q, const float *ss, int nparts, float invD,
+                                                float eps, const float *qnorm, const float *cosT, const float *sinT,
+                                                RowPos rp, int rows, int Hq) {
+  constexpr int D = 128, CPL = 2;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wv >= rows * Hq) return;  // (a whole wave)
+  const int r = wv / Hq, hd = wv - r * Hq, c = CPL * lane;
+  const float rs = rinv_from_parts(ss, r, nparts, invD, eps);
+  float x[1][CPL], g[CPL], cs[1][CPL], sn[1][CPL];
+  ldf<CPL>(x[0], C + ((int64_t)r * Hq + hd) * D + c);
+  ldf<CPL>(g, qnorm + c);
+  rope_entries<CPL>(cs[0], sn[0], cosT, sinT, rp.pos(r), lane, D);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) x[0][i] *= rs;
+  head_norm_rope<CPL, 1>(x, lane, D, eps, g, cs, sn);
+  stT<T, CPL>(q + ((int64_t)r * Hq + hd) * D + c, x[0]);
+}
+
 // Pool projection, z = beta*k + j: rows scaled by the channel's 1/rms; keys
 // get the per-head key norm and RoPE; both go to cache[j, b, h, pos, :].
 // TN = head dim, so the block's columns are head n0 / TN.
