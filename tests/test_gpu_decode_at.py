@@ -9,6 +9,9 @@ and that step captured once in a graph and replayed at successive positions.
   wm_decode_step's bit for bit at positions 2047, 1500 and 1 (at that shape
   the attention takes no key split at any position, so the host's choice
   for the last position is the same choice).
+* With 256 sequences (the pool's K/V projection on the streamed kernel,
+  reading the position from device memory) it equals wm_decode_step bit for
+  bit and writes slot t only.
 * Graph replay: one call captured in a torch CUDA graph replays at positions
   2044, 2045, 2046, 1200; before each replay the test writes the next
   position and tokens into the captured buffers, runs the eager
@@ -79,6 +82,33 @@ def test_decode_bit_exact_against_host_position():
         torch.cuda.synchronize()
         assert torch.equal(l1, l2)
         assert torch.equal(c1.k[:, :, :, t], c2.k[:, :, :, t]) and torch.equal(c1.v[:, :, :, t], c2.v[:, :, :, t])
+        del c1, c2
+
+
+def test_decode_256_sequences_device_position():
+    """256 sequences: the pool's K/V projection runs on the streamed kernel
+    (at least 256 rows), which reads the position from device memory in
+    wm_decode_step_at; logits and appended entries equal wm_decode_step's bit
+    for bit, and only slot t was written."""
+    w = WORKLOADS["decode_d512"].replace(B=256, T_max=256)
+    model = wm.Model(w, make_weights(w, seed=0), "bf16")
+    K, V = make_cache_device(w, w.B, filled=w.T_max, seed=3)
+    toks = make_tokens(w, seed=1, B=w.B, T=2)
+    ws = model.workspace(w.B)
+    for i, t in enumerate((255, 3)):
+        print(f"[decode_at] decode_d512 B{w.B} t={t}", flush=True)
+        tok = torch.from_numpy(toks[:, i].copy()).cuda()
+        c1 = wm.Cache(K.clone(), V.clone())
+        c2 = wm.Cache(K.clone(), V.clone())
+        l1 = wm.decode_step(model, tok, t, c1, ws=ws)
+        l2 = wm.decode_step_at(model, tok, torch.tensor([t], dtype=torch.int32, device="cuda"), c2, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(l1).all()
+        assert torch.equal(l1, l2)
+        assert torch.equal(c1.k, c2.k) and torch.equal(c1.v, c2.v)
+        keep = [s for s in range(w.T_max) if s != t]
+        assert torch.equal(c2.k[:, :, :, keep], K[:, :, :, keep]) and torch.equal(c2.v[:, :, :, keep], V[:, :, :, keep])
+        assert not torch.equal(c2.k[:, :, :, t], K[:, :, :, t])
         del c1, c2
 
 
