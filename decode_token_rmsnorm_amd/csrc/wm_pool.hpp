@@ -202,42 +202,72 @@ struct RowMap {
 // state_rinv and router_input in one launch for steps of few rows: block
 // (r, beta) computes the row scales of all L states of row r (the same wave
 // sums as state_rinv; the beta = 0 block stores them), then writes the row's
-// gained router input of branch beta.
+// gained router input of branch beta.  The launch is latency-bound (a few MB
+// per step), so each wave issues the loads of four layers before it reduces
+// any of them, and the router input is written by all 256 threads, four
+// 16-byte pieces each per round, every load of a round issued before its
+// stores.
 template <typename T>
 __global__ __launch_bounds__(256) void rinv_router_input(const T *S, float *rinvS, const float *gain, T *u, int rows,
                                                          int L, int p, int R, int D, float eps) {
   constexpr int E = Elt<T>::E16;
+  constexpr int LB = 4;  // layers in flight per wave
   const int r = blockIdx.x, beta = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __shared__ float rs[32];  // (L <= 32)
-  for (int l = wave; l < L; l += 4) {
-    const T *x = S + ((int64_t)l * rows + r) * D;
-    float s = 0.f;
+  for (int l0 = wave; l0 < L; l0 += 4 * LB) {
+    float s[LB] = {};
     for (int c = lane * E; c < D; c += 64 * E) {
-      float f[E];
-      unpack16<T>(*(const u32x4 *)(x + c), f);
+      u32x4 v[LB] = {};
 #pragma unroll
-      for (int e = 0; e < E; ++e) s += f[e] * f[e];
+      for (int j = 0; j < LB; ++j)
+        if (l0 + 4 * j < L) v[j] = *(const u32x4 *)(S + ((int64_t)(l0 + 4 * j) * rows + r) * D + c);
+#pragma unroll
+      for (int j = 0; j < LB; ++j) {
+        float f[E];
+        unpack16<T>(v[j], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[j] += f[e] * f[e];
+      }
     }
-    s = wave_sum(s);
-    const float v = rsqrtf(s / D + eps);
-    if (lane == 0) {
-      rs[l] = v;
-      if (beta == 0) rinvS[(int64_t)l * rows + r] = v;
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+      const int l = l0 + 4 * j;
+      if (l >= L) break;  // wave-uniform
+      const float v = rsqrtf(wave_sum(s[j]) / D + eps);
+      if (lane == 0) {
+        rs[l] = v;
+        if (beta == 0) rinvS[(int64_t)l * rows + r] = v;
+      }
     }
   }
   __syncthreads();
-  for (int b = 0; b < R; ++b) {
-    const int l = b * p;
-    const float s = rs[l];
-    const T *src = S + ((int64_t)l * rows + r) * D;
-    const float *g = gain + ((int64_t)beta * L + l) * D;
-    T *dst = u + ((int64_t)beta * rows + r) * R * D + (int64_t)b * D;
-    for (int c = threadIdx.x * E; c < D; c += 256 * E) {
-      float f[E];
-      unpack16<T>(*(const u32x4 *)(src + c), f);
+  constexpr int PU = 4;  // 16-byte pieces per thread and round
+  const int npc = D / E, n = R * npc;
+  T *urow = u + ((int64_t)beta * rows + r) * R * D;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 256 * PU) {
+    u32x4 v[PU] = {};
+    float g[PU][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) f[e] *= s * g[c + e];
-      *(u32x4 *)(dst + c) = pack16<T>(f);
+    for (int j = 0; j < PU; ++j) {
+      const int i = i0 + 256 * j;
+      if (i >= n) break;
+      const int b = i / npc, c = (i - b * npc) * E, l = b * p;
+      v[j] = *(const u32x4 *)(S + ((int64_t)l * rows + r) * D + c);
+      const float *gp = gain + ((int64_t)beta * L + l) * D + c;
+#pragma unroll
+      for (int e = 0; e < E; ++e) g[j][e] = gp[e];
+    }
+#pragma unroll
+    for (int j = 0; j < PU; ++j) {
+      const int i = i0 + 256 * j;
+      if (i >= n) break;
+      const int b = i / npc, c = (i - b * npc) * E;
+      const float sc = rs[b * p];
+      float f[E];
+      unpack16<T>(v[j], f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] *= sc * g[j][e];
+      *(u32x4 *)(urow + (int64_t)b * D + c) = pack16<T>(f);
     }
   }
 }
