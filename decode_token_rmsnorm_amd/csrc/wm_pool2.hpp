@@ -145,8 +145,31 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
   const int tr_lo = min(8 * gl + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
   const int tr_hi = min(8 * gl + 4 + (li >> 2), L - 1) * PM_SP + 16 * wave + 4 * (li & 3);
 
+  // one token row per block (RT = 1, both branches on their own MFMAs): the
+  // gains of the next chunk are loaded while the current one is computed, in
+  // flight with its staged states, so a chunk waits for one memory round
+  // trip instead of two (no other rows' work hides them); with more rows
+  // per block the registers this takes would cost a block per CU
+  constexpr bool GP = !PB && PM_RT == 1;
+  float gsn[2][8], grn[2][KB][4];
+  auto gainload = [&](int chunk) {
+    chunk = min(chunk, nchunk - 1);
+    const int col = chunk * PM_CW + 16 * wave + li;
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gsn[beta][e] = src_gain[beta * sgb + (int64_t)min(8 * g + e, L - 1) * D + col];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          grn[beta][kb][i] = chan_gain[beta * cgb + (int64_t)min(16 * kb + 4 * g + i, k - 1) * D + col];
+    }
+  };
+
 #pragma unroll
   for (int u = 0; u < PD; ++u) gload(pre[u], u);
+  if constexpr (GP) gainload(0);
   for (int c0 = 0; c0 < nchunk; c0 += PD)
 #pragma unroll
   for (int u = 0; u < PD; ++u) {
@@ -188,17 +211,19 @@ __global__ __launch_bounds__(256, 2) void pool_mix2(const bf16 *S, const float *
         }
       }
     } else {
+    // (GP: the gains loaded during the previous chunk)
+    if constexpr (!GP) gainload(chunk);
     float gs[2][8], gr[2][KB][4];
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gs[beta][e] = src_gain[beta * sgb + (int64_t)min(8 * g + e, L - 1) * D + col];
+      for (int e = 0; e < 8; ++e) gs[beta][e] = gsn[beta][e];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          gr[beta][kb][i] = chan_gain[beta * cgb + (int64_t)min(16 * kb + 4 * g + i, k - 1) * D + col];
+        for (int i = 0; i < 4; ++i) gr[beta][kb][i] = grn[beta][kb][i];
     }
+    if constexpr (GP) gainload(chunk + 1);
 #pragma unroll
     for (int rr = 0; rr < PM_RT; ++rr) {
       const int row = r0 + rr;

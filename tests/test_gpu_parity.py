@@ -125,6 +125,8 @@ def assert_cache(w, gk, gv, ref, mask, tol, poison=True):
     ("mix_bf16@L4k1", 2, 16, 0, 1),     # one channel over few source layers (MFMA mix)
     ("mix_bf16@L2k1", 2, 16, 0, 1),
     ("mix_bf16@L3k1", 3, 50, 1, 2),
+    ("mix_bf16@L16k16", 2, 40, 3, 1),   # few rows, one row per mix block, branches on their own MFMAs
+    ("mix_bf16@L28k14", 1, 100, 0, 1),  # the same at 28 source layers (32-layer staging)
 ])
 def test_mix_kv_matches_oracle(name, B, M, s0, step):
     if "@" in name:  # shape variant "<workload>@L<l>k<k>"
